@@ -1,0 +1,286 @@
+"""CPU oracle for the Krea 2 single-stream MMDiT block, its text fusion, time path and backbone.
+
+TEST INFRASTRUCTURE ONLY. Only tests/, __graft_entry__.smoke() and the CPU-baseline leg of
+bench.py may import this module. The product path (flow_matching_diffusion_amd) never imports,
+calls or links it, and it shares no code with the HIP kernels.
+
+Everything is plain NumPy in float64: a matrix product (`@`) is the only library primitive used
+as a step; there is no blocking, fusion or reordering beyond what the definitions state.
+
+Sources (cited by page title and section; the pages hold no code listing we follow line by line):
+  [API]      diffusers v0.43.0 model page "Krea2Transformer2DModel" (constructor signature and
+             parameter list; forward() parameters and return value).
+  [ARTICLE]  article "Diffusers 中的 Krea2Transformer2DModel：Krea 2 单流 MMDiT 流匹配 Transformer
+             架构全解", sections 一 (positioning) .. 八 (summary); §四.1..§四.6 are the module items
+             (1 TextFusion, 2 TransformerBlock, 3 Attention, 4 RMSNorm, 5 TimestepEmbedding,
+             6 FinalLayer) and the unnumbered "data flow" list that opens §四.
+  [PIPELINE] diffusers v0.43.0 pipeline page "Krea 2" (Krea2Pipeline, prepare_position_ids,
+             get_text_hidden_states, the guidance convention).
+
+Readings where the pages are silent or garbled (each restated where it is used):
+  R1  modulation = temb split in 6 chunks + per-block table; x -> (1 + scale) * norm(x) + shift;
+      h -> h + gate * branch (the article's block code lost its '=' and '+' signs).
+  R2  RMSNorm: x / sqrt(mean(x^2) + eps) * (1 + w); eps inside the root; w is zero-centred.
+  R3  softmax scale 1/sqrt(head_dim) (scaled-dot-product default).
+  R4  GQA: query head hq reads kv head hq // (num_heads / num_kv_heads) (repeat_interleave).
+  R5  mask: key padding only, text keys only; image keys always valid; no causal mask.
+  R6  sigmoid output gate: elementwise on the concatenated heads, computed from the attention
+      input, applied before the output projection.
+  R7  no bias in q/k/v/gate/out/SwiGLU projections; img_in, time MLP, time_mod_proj, txt_in and
+      the final projection carry biases.
+  R8  RoPE: interleaved adjacent pairs (2i, 2i+1); head dim split (t, h, w) in that order; pair i
+      of an axis with width d turns by pos * theta^(-2i/d); applied after the q/k norm.
+  R9  SwiGLU: down(silu(gate(x)) * up(x)).
+  R10 time path: s = 1000 t; emb = [cos(s f_k)] ++ [sin(s f_k)], f_k = 10000^(-k/half), k < half;
+      e = lin2(gelu_tanh(lin1(emb))); temb = mod_proj(gelu_tanh(e)).
+  R11 final layer: (scale, shift) = table[0] + e, table[1] + e (e: time embedding before the
+      GELU); out = proj((1 + scale) * RMSNorm(h_img) + shift); the norm has no weight by default.
+  R12 text fusion block: pre-norm block with the same attention (q/k norm, sigmoid gate), MHA,
+      no RoPE, no modulation; layer compressor Linear(num_layers, 1) without bias; txt_in is a
+      plain Linear with bias.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+F64 = np.float64
+
+
+def _f64(a):
+    return None if a is None else np.asarray(a, dtype=F64)
+
+
+# ----------------------------------------------------------------------------------------------
+# Elementwise pieces
+# ----------------------------------------------------------------------------------------------
+def rms_norm(x, weight, eps):
+    """Zero-centred RMSNorm, [ARTICLE] §四.4 (effective multiplier 1 + weight; statistics in
+    full precision) with eps inside the root (R2); the eps value is norm_eps of [API]."""
+    x = _f64(x)
+    y = x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    if weight is not None:
+        y = y * (1.0 + _f64(weight))
+    return y
+
+
+def sigmoid(x):
+    return 1.0 / (1.0 + np.exp(-x))
+
+
+def silu(x):
+    return x * sigmoid(x)
+
+
+def gelu_tanh(x):
+    """GELU with the tanh approximation ([ARTICLE] §四.5 names GELU-tanh for the time MLP)."""
+    return 0.5 * x * (1.0 + np.tanh(math.sqrt(2.0 / math.pi) * (x + 0.044715 * x ** 3)))
+
+
+# ----------------------------------------------------------------------------------------------
+# Rotary position embedding
+# ----------------------------------------------------------------------------------------------
+def rope_angles(position_ids, axes_dims, theta):
+    """Rotation angle of every (token, pair): [API] axes_dims_rope / rope_theta and the
+    position_ids parameter; [ARTICLE] §一 (3-axis RoPE of the Flux family) and §四.3 (R8).
+    Returns (L, sum(axes_dims) / 2)."""
+    pos = _f64(position_ids)
+    cols = []
+    for a, d in enumerate(axes_dims):
+        i = np.arange(d // 2, dtype=F64)
+        freq = float(theta) ** (-2.0 * i / d)
+        cols.append(pos[:, a:a + 1] * freq[None, :])
+    return np.concatenate(cols, axis=1)
+
+
+def apply_rope(x, angles):
+    """Rotate adjacent pairs (x[2i], x[2i+1]) by angles[..., i] (R8). x: (..., L, hd)."""
+    c, s = np.cos(angles), np.sin(angles)
+    x0, x1 = x[..., 0::2], x[..., 1::2]
+    out = np.empty_like(x)
+    out[..., 0::2] = x0 * c - x1 * s
+    out[..., 1::2] = x0 * s + x1 * c
+    return out
+
+
+# ----------------------------------------------------------------------------------------------
+# Attention
+# ----------------------------------------------------------------------------------------------
+def attention(q, k, v, key_valid):
+    """Softmax attention with GQA and a key mask, [ARTICLE] §四.3.
+    q: (B, nh, Lq, hd); k, v: (B, nkv, Lk, hd); key_valid: (B, Lk) bool or None.
+    K/V heads are repeated with repeat_interleave semantics (R4); scale 1/sqrt(hd) (R3)."""
+    nh, nkv, hd = q.shape[1], k.shape[1], q.shape[-1]
+    g = nh // nkv
+    k = np.repeat(k, g, axis=1)
+    v = np.repeat(v, g, axis=1)
+    s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(hd)
+    if key_valid is not None:
+        s = np.where(key_valid[:, None, None, :], s, -np.inf)
+    s = s - np.max(s, axis=-1, keepdims=True)
+    p = np.exp(s)
+    p = p / np.sum(p, axis=-1, keepdims=True)
+    return p @ v
+
+
+def key_valid_mask(B, L, T, mask):
+    """(B, L) key validity: text key j < T is valid iff mask[b, j]; image keys always (R5).
+    mask None means every text token is valid ([API] encoder_attention_mask)."""
+    kv = np.ones((B, L), dtype=bool)
+    if mask is not None:
+        kv[:, :T] = np.asarray(mask).astype(bool)
+    return kv
+
+
+# ----------------------------------------------------------------------------------------------
+# The single-stream block
+# ----------------------------------------------------------------------------------------------
+def modulation(temb, table):
+    """[ARTICLE] §四.2: temb (B, 6H) unflattened to (B, 6, H) plus the block's (6, H) table;
+    chunks are prescale, preshift, pregate, postscale, postshift, postgate (R1)."""
+    B = temb.shape[0]
+    H = table.shape[1]
+    return _f64(temb).reshape(B, 6, H) + _f64(table)[None]
+
+
+def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermediates=False):
+    """One Krea2TransformerBlock forward ([ARTICLE] §四.2 block, §四.3 attention, §四.4 norm).
+
+    h: (B, L, H) residual stream; temb: (B, 6H) or None (no modulation: text-fusion blocks);
+    position_ids: (L, 3) or None (no RoPE); mask: (B, T) or None; w: weight dict (nn.Linear
+    (out, in) layout); dims: BlockDims-like; T: text tokens at the start of the sequence.
+    rows: optional sorted sequence indices; only those output rows are computed (keys and
+    values still come from every row). Returns (B, len(rows) or L, H) float64.
+    """
+    h = _f64(h)
+    B, L, H = h.shape
+    nh, nkv, hd, eps = dims.num_heads, dims.num_kv_heads, dims.head_dim, dims.eps
+    rows = np.arange(L) if rows is None else np.asarray(rows)
+    R = rows.size
+    out = {}
+
+    if temb is not None:
+        mod = modulation(temb, w["scale_shift_table"])
+        ps, pt, pg, qs, qt, qg = (mod[:, i, None, :] for i in range(6))
+    else:
+        ps = pt = qs = qt = 0.0
+        pg = qg = 1.0
+
+    # (1 + prescale) * norm1(h) + preshift
+    x1 = (1.0 + ps) * rms_norm(h, w["norm1_w"], eps) + pt
+    out["x1"] = x1
+
+    # projections (R7: no bias); k and v for every row, q and gate for the requested rows
+    k = x1 @ _f64(w["to_k"]).T
+    v = x1 @ _f64(w["to_v"]).T
+    xr = x1[:, rows]
+    q = xr @ _f64(w["to_q"]).T
+    graw = xr @ _f64(w["to_gate"]).T
+
+    q = q.reshape(B, R, nh, hd).transpose(0, 2, 1, 3)
+    k = k.reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
+    v = v.reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
+
+    # per-head q/k RMSNorm over head_dim, then RoPE (R8)
+    q = rms_norm(q, w["norm_q_w"], eps)
+    k = rms_norm(k, w["norm_k_w"], eps)
+    if position_ids is not None:
+        ang = rope_angles(position_ids, dims.axes_dims, dims.rope_theta)
+        q = apply_rope(q, ang[rows][None, None])
+        k = apply_rope(k, ang[None, None])
+    out["q"], out["k"], out["v"], out["g"] = q, k, v, graw
+
+    o = attention(q, k, v, key_valid_mask(B, L, T, mask))
+    o = o.transpose(0, 2, 1, 3).reshape(B, R, nh * hd)
+    og = o * sigmoid(graw)                                   # R6
+    out["og"] = og
+
+    h1 = h[:, rows] + pg * (og @ _f64(w["to_out"]).T)
+    out["h1"] = h1
+    x2 = (1.0 + qs) * rms_norm(h1, w["norm2_w"], eps) + qt
+    out["x2"] = x2
+    a = silu(x2 @ _f64(w["ff_gate"]).T) * (x2 @ _f64(w["ff_up"]).T)   # R9
+    out["a"] = a
+    h2 = h1 + qg * (a @ _f64(w["ff_down"]).T)
+    out["out"] = h2
+    return (h2, out) if intermediates else h2
+
+
+# ----------------------------------------------------------------------------------------------
+# Time path
+# ----------------------------------------------------------------------------------------------
+def timestep_embedding(t, dim=256, max_period=10000.0, time_scale=1000.0):
+    """Cos-first sinusoidal embedding of 1000 t, width dim ([ARTICLE] §四.5; [API]
+    timestep_embed_dim; constants of R10)."""
+    t = _f64(t)
+    half = dim // 2
+    freqs = max_period ** (-np.arange(half, dtype=F64) / half)
+    arg = (time_scale * t)[:, None] * freqs[None, :]
+    return np.concatenate([np.cos(arg), np.sin(arg)], axis=1)
+
+
+def time_path(t, tw, dim=256):
+    """time_embed -> GELU -> time_mod_proj ([ARTICLE] data flow of §四; R10).
+    Returns (temb (B, 6H), e (B, H)) where e is time_embed's output (before the GELU)."""
+    emb = timestep_embedding(t, dim)
+    e = gelu_tanh(emb @ _f64(tw["lin1_w"]).T + _f64(tw["lin1_b"])) @ _f64(tw["lin2_w"]).T + _f64(tw["lin2_b"])
+    temb = gelu_tanh(e) @ _f64(tw["mod_w"]).T + _f64(tw["mod_b"])
+    return temb, e
+
+
+# ----------------------------------------------------------------------------------------------
+# Text fusion
+# ----------------------------------------------------------------------------------------------
+def text_fusion(enc, mask, tw, tdims):
+    """Krea2TextFusion ([ARTICLE] §四.1; R12): layerwise blocks over the layer axis of every
+    token, Linear(num_layers, 1) over the layer axis, refiner blocks over tokens with the mask.
+    enc: (B, T, num_layers, D). Returns (B, T, D)."""
+    enc = _f64(enc)
+    B, T, NL, D = enc.shape
+    x = enc.reshape(B * T, NL, D)
+    for bw in tw["layerwise"]:
+        x = block_forward(x, None, None, None, bw, tdims, T=0)
+    y = np.tensordot(x, _f64(tw["compress_w"]), axes=([1], [0])).reshape(B, T, D)
+    for bw in tw["refiner"]:
+        y = block_forward(y, None, None, mask, bw, tdims, T=T)
+    return y
+
+
+# ----------------------------------------------------------------------------------------------
+# Backbone
+# ----------------------------------------------------------------------------------------------
+def final_layer(h_img, e, table, norm_w, w, b, eps):
+    """Krea2FinalLayer ([ARTICLE] §四.6; R11)."""
+    scale = _f64(table)[0][None, None] + _f64(e)[:, None, :]
+    shift = _f64(table)[1][None, None] + _f64(e)[:, None, :]
+    x = (1.0 + scale) * rms_norm(h_img, norm_w, eps) + shift
+    return x @ _f64(w).T + _f64(b)
+
+
+def backbone_forward(x, enc, t, position_ids, mask, mw, dims, tdims, T, time_dim=256):
+    """Krea2Transformer2DModel.forward ([API] forward; [ARTICLE] data flow of §四):
+    time path, text fusion + txt_in, img_in, concat [text, image], blocks, image rows only,
+    final layer. Returns the velocity (B, N, in_channels)."""
+    temb, e = time_path(t, mw["time"], time_dim)
+    txt = text_fusion(enc, mask, mw["text"], tdims) @ _f64(mw["txt_in_w"]).T + _f64(mw["txt_in_b"])
+    img = _f64(x) @ _f64(mw["img_in_w"]).T + _f64(mw["img_in_b"])
+    h = np.concatenate([txt, img], axis=1)
+    for bw in mw["blocks"]:
+        h = block_forward(h, temb, position_ids, mask, bw, dims, T=T)
+    return final_layer(h[:, T:], e, mw["final_table"], mw.get("final_norm_w"), mw["final_w"],
+                       mw["final_b"], dims.eps)
+
+
+# ----------------------------------------------------------------------------------------------
+# Work accounting (used by the CPU baseline to express its throughput)
+# ----------------------------------------------------------------------------------------------
+def block_flops(dims, B, L, valid_keys, rows=None):
+    """Algorithmic FLOPs of one block: every GEMM over the computed rows; attention over valid
+    keys only; elementwise work not counted. valid_keys: per batch row, number of valid keys."""
+    H, nh, nkv, hd, I = dims.hidden, dims.num_heads, dims.num_kv_heads, dims.head_dim, dims.intermediate
+    R = L if rows is None else len(rows)
+    kv = 2 * B * L * H * (2 * nkv * hd)
+    per_row = 2 * H * (2 * nh * hd) + 2 * nh * hd * H + 3 * 2 * H * I
+    attn = sum(4 * hd * nh * R * vk for vk in valid_keys)
+    return kv + B * R * per_row + attn
