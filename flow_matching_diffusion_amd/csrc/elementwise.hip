@@ -1,0 +1,198 @@
+// Bandwidth-bound kernels of the block and backbone (gfx950).
+//
+//   modnorm        — (1 + scale_b) * RMSNorm(h; w) + shift_b, float32 statistics, one workgroup per row,
+//                    float4 loads and one pass over HBM (the row stays in registers between the
+//                    reduction and the write). Architecture article §四.2 (modulated pre-norms),
+//                    §四.4 (zero-centred RMSNorm computed in float32), §四.6 (final-layer norm).
+//   modulation     — temb chunks + per-block (6, H) table ([ARTICLE] §四.2), or e + (2, H) table for the
+//                    final layer (§四.6).
+//   rope_table     — cos/sin of the 3-axis rotary angles, once per forward ([ARTICLE] §四 data flow).
+//   time_embed     — cos-first sinusoid of 1000 t ([ARTICLE] §四.5).
+//   layer_compress — Linear(num_layers, 1, bias=False) over the text layer axis ([ARTICLE] §四.1).
+//   to_f32/from_f32 — operand dtype conversions.
+#include "k2_device.h"
+#include "k2_kernels.h"
+
+namespace k2 {
+
+template <typename TO> __device__ __forceinline__ void store4(TO* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void store4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+template <> __device__ __forceinline__ void store4<bf16>(bf16* p, float a, float b, float c, float d) {
+  bf16x4 v;
+  v[0] = (bf16)a; v[1] = (bf16)b; v[2] = (bf16)c; v[3] = (bf16)d;
+  *(bf16x4*)p = v;
+}
+
+__device__ __forceinline__ float block_sum256(float v, float* red) {
+  v = wave_sum(v);
+  const int w = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  const float s = red[0] + red[1] + red[2] + red[3];
+  __syncthreads();
+  return s;
+}
+
+template <typename TO>
+__global__ void __launch_bounds__(256) modnorm_kernel(ModnormArgs p) {
+  constexpr int CACHE = 8;  // float4 per thread kept in registers (rows up to 8192 wide)
+  __shared__ float red[4];
+  const int r = blockIdx.x;
+  const int b = r / p.rows_per_b, i = r - b * p.rows_per_b;
+  const float4* x = (const float4*)(p.in + ((size_t)b * p.in_rows_per_b + p.in_row_off + i) * p.H);
+  TO* y = (TO*)p.out + (size_t)r * p.H;
+  const int H4 = p.H >> 2;
+  float4 v[CACHE];
+  float ss = 0.0f;
+#pragma unroll
+  for (int u = 0; u < CACHE; ++u) {
+    const int c = threadIdx.x + u * 256;
+    if (c < H4) {
+      v[u] = x[c];
+      ss += v[u].x * v[u].x + v[u].y * v[u].y + v[u].z * v[u].z + v[u].w * v[u].w;
+    }
+  }
+  for (int c = threadIdx.x + CACHE * 256; c < H4; c += 256) {
+    const float4 t = x[c];
+    ss += t.x * t.x + t.y * t.y + t.z * t.z + t.w * t.w;
+  }
+  ss = block_sum256(ss, red);
+  const float inv = rsqrtf(ss / (float)p.H + p.eps);
+  const float4* w4 = (const float4*)p.w;
+  const float4* sc4 = p.scale ? (const float4*)(p.scale + (size_t)b * p.mod_stride) : nullptr;
+  const float4* sh4 = p.shift ? (const float4*)(p.shift + (size_t)b * p.mod_stride) : nullptr;
+  auto emit = [&](int c, float4 t) {
+    const float4 w = w4 ? w4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 sc = sc4 ? sc4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    const float4 sh = sh4 ? sh4[c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    store4<TO>(y + 4 * c, (1.0f + sc.x) * (t.x * inv * (1.0f + w.x)) + sh.x,
+               (1.0f + sc.y) * (t.y * inv * (1.0f + w.y)) + sh.y,
+               (1.0f + sc.z) * (t.z * inv * (1.0f + w.z)) + sh.z,
+               (1.0f + sc.w) * (t.w * inv * (1.0f + w.w)) + sh.w);
+  };
+#pragma unroll
+  for (int u = 0; u < CACHE; ++u) {
+    const int c = threadIdx.x + u * 256;
+    if (c < H4) emit(c, v[u]);
+  }
+  for (int c = threadIdx.x + CACHE * 256; c < H4; c += 256) emit(c, x[c]);
+}
+
+hipError_t modnorm(int dt, const ModnormArgs& p, hipStream_t s) {
+  if (p.rows <= 0) return hipSuccess;
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(modnorm_kernel<bf16>, dim3(p.rows), dim3(256), 0, s, p);
+  else
+    hipLaunchKernelGGL(modnorm_kernel<float>, dim3(p.rows), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
+
+__global__ void modulation_kernel(const float* temb, int temb_stride, int chunk_stride, const float* table,
+                                  float* mod, int B, int nchunks, int H) {
+  const size_t n = (size_t)B * nchunks * H;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (size_t)gridDim.x * blockDim.x) {
+    const int j = (int)(idx % H);
+    const int c = (int)((idx / H) % nchunks);
+    const int b = (int)(idx / ((size_t)H * nchunks));
+    mod[idx] = temb[(size_t)b * temb_stride + (size_t)c * chunk_stride + j] + (table ? table[(size_t)c * H + j] : 0.0f);
+  }
+}
+
+hipError_t modulation(const float* temb, int temb_stride, int chunk_stride, const float* table, float* mod, int B,
+                      int nchunks, int H, hipStream_t s) {
+  const size_t n = (size_t)B * nchunks * H;
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256 < 4096 ? (n + 255) / 256 : 4096);
+  hipLaunchKernelGGL(modulation_kernel, dim3(blocks), dim3(256), 0, s, temb, temb_stride, chunk_stride, table, mod, B,
+                     nchunks, H);
+  return hipGetLastError();
+}
+
+__global__ void rope_table_kernel(const float* pos, int L, int a0, int a1, int a2, float theta, float* co, float* si) {
+  const int half = (a0 + a1 + a2) / 2;
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= L * half) return;
+  const int l = idx / half, pi = idx - l * half;
+  int a, i, d;
+  if (pi < a0 / 2) { a = 0; i = pi; d = a0; }
+  else if (pi < (a0 + a1) / 2) { a = 1; i = pi - a0 / 2; d = a1; }
+  else { a = 2; i = pi - (a0 + a1) / 2; d = a2; }
+  const double ang = (double)pos[(size_t)l * 3 + a] * pow((double)theta, -2.0 * i / d);
+  co[idx] = (float)cos(ang);
+  si[idx] = (float)sin(ang);
+}
+
+hipError_t rope_table(const float* pos, int L, int a0, int a1, int a2, float theta, float* cos_out, float* sin_out,
+                      hipStream_t s) {
+  const int n = L * ((a0 + a1 + a2) / 2);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(rope_table_kernel, dim3((n + 255) / 256), dim3(256), 0, s, pos, L, a0, a1, a2, theta, cos_out,
+                     sin_out);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ void time_embed_kernel(const float* t, int B, int dim, T* out) {
+  const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= B * dim) return;
+  const int b = idx / dim, k = idx - b * dim, half = dim / 2;
+  const int kk = k < half ? k : k - half;
+  const double f = pow(10000.0, -(double)kk / half);
+  const double arg = 1000.0 * (double)t[b] * f;
+  out[idx] = to_t<T>((float)(k < half ? cos(arg) : sin(arg)));
+}
+
+hipError_t time_embed(int dt, const float* t, int B, int dim, void* out, hipStream_t s) {
+  const int n = B * dim;
+  if (n == 0) return hipSuccess;
+  if (dt == DT_BF16)
+    hipLaunchKernelGGL(time_embed_kernel<bf16>, dim3((n + 255) / 256), dim3(256), 0, s, t, B, dim, (bf16*)out);
+  else
+    hipLaunchKernelGGL(time_embed_kernel<float>, dim3((n + 255) / 256), dim3(256), 0, s, t, B, dim, (float*)out);
+  return hipGetLastError();
+}
+
+__global__ void layer_compress_kernel(const float* x, const float* c, float* y, int rows, int nl, int D) {
+  const size_t n = (size_t)rows * D;
+  for (size_t idx = (size_t)blockIdx.x * blockDim.x + threadIdx.x; idx < n; idx += (size_t)gridDim.x * blockDim.x) {
+    const size_t r = idx / D;
+    const int d = (int)(idx - r * D);
+    const float* src = x + r * nl * D + d;
+    float acc = 0.0f;
+    for (int l = 0; l < nl; ++l) acc += c[l] * src[(size_t)l * D];
+    y[idx] = acc;
+  }
+}
+
+hipError_t layer_compress(const float* x, const float* c, float* y, int rows, int nl, int D, hipStream_t s) {
+  const size_t n = (size_t)rows * D;
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+  hipLaunchKernelGGL(layer_compress_kernel, dim3(blocks), dim3(256), 0, s, x, c, y, rows, nl, D);
+  return hipGetLastError();
+}
+
+template <typename TI, typename TO>
+__global__ void convert_kernel(const TI* in, TO* out, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    out[i] = to_t<TO>(to_f(in[i]));
+}
+
+template <typename TI, typename TO>
+static hipError_t convert(const void* in, void* out, size_t n, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  const int blocks = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
+  hipLaunchKernelGGL((convert_kernel<TI, TO>), dim3(blocks), dim3(256), 0, s, (const TI*)in, (TO*)out, n);
+  return hipGetLastError();
+}
+
+hipError_t to_f32(int dt, const void* in, float* out, size_t n, hipStream_t s) {
+  return dt == DT_BF16 ? convert<bf16, float>(in, out, n, s) : convert<float, float>(in, out, n, s);
+}
+hipError_t from_f32(int dt, const float* in, void* out, size_t n, hipStream_t s) {
+  return dt == DT_BF16 ? convert<float, bf16>(in, out, n, s) : convert<float, float>(in, out, n, s);
+}
+
+}  // namespace k2

@@ -1,0 +1,643 @@
+// C ABI of libk2: argument validation, workspace carving and kernel sequencing.
+// Declarations and the contract of every entry point are in include/k2.h.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "k2.h"
+#include "k2_kernels.h"
+
+using namespace k2;
+
+namespace {
+
+// ---------------------------------------------------------------------------------------------
+// Errors
+// ---------------------------------------------------------------------------------------------
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Optional per-kernel event timing
+// ---------------------------------------------------------------------------------------------
+struct ProfEvent {
+  std::string name;
+  hipEvent_t a, b;
+};
+std::mutex g_pm;
+bool g_prof = false;
+std::vector<ProfEvent> g_pev;
+std::vector<hipEvent_t> g_pool;
+
+hipEvent_t take_event() {
+  if (!g_pool.empty()) {
+    hipEvent_t e = g_pool.back();
+    g_pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+template <class F>
+int run(const char* name, hipStream_t s, F f) {
+  hipEvent_t a = nullptr, b = nullptr;
+  if (g_prof) {
+    std::lock_guard<std::mutex> lk(g_pm);
+    a = take_event();
+    b = take_event();
+    if (a) (void)hipEventRecord(a, s);
+  }
+  hipError_t e = f();
+  if (a && b) {
+    (void)hipEventRecord(b, s);
+    std::lock_guard<std::mutex> lk(g_pm);
+    g_pev.push_back({name, a, b});
+  }
+  if (e != hipSuccess) return fail(K2_ERR_HIP, "%s: launch failed: %s", name, hipGetErrorString(e));
+  return K2_OK;
+}
+
+#define K2_RUN(name, s, expr)                               \
+  do {                                                      \
+    int run_rc__ = run(name, s, [&]() -> hipError_t { return expr; }); \
+    if (run_rc__ != K2_OK) return run_rc__;                 \
+  } while (0)
+
+// ---------------------------------------------------------------------------------------------
+// Validation
+// ---------------------------------------------------------------------------------------------
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_block_cfg(const k2_block_cfg* c, bool rope) {
+  if (!c) return fail(K2_ERR_NULL, "block config is NULL");
+  if (c->dtype != K2_F32 && c->dtype != K2_BF16) return fail(K2_ERR_DTYPE, "unknown dtype %d", c->dtype);
+  if (c->hidden <= 0 || c->num_heads <= 0 || c->num_kv_heads <= 0 || c->head_dim <= 0 || c->intermediate <= 0)
+    return fail(K2_ERR_CONFIG, "block dimensions must be positive");
+  if (c->hidden != c->num_heads * c->head_dim)
+    return fail(K2_ERR_CONFIG, "hidden (%d) must equal num_heads * head_dim (%d * %d)", c->hidden, c->num_heads,
+                c->head_dim);
+  if (c->num_heads % c->num_kv_heads != 0) return fail(K2_ERR_CONFIG, "num_heads must be a multiple of num_kv_heads");
+  const int G = c->num_heads / c->num_kv_heads;
+  if (G != 1 && G != 2 && G != 4) return fail(K2_ERR_CONFIG, "num_heads / num_kv_heads must be 1, 2 or 4 (got %d)", G);
+  if (c->head_dim != 64 && c->head_dim != 128) return fail(K2_ERR_CONFIG, "head_dim must be 64 or 128 (got %d)", c->head_dim);
+  if (c->hidden % 8 != 0 || c->intermediate % 8 != 0)
+    return fail(K2_ERR_CONFIG, "hidden and intermediate must be multiples of 8");
+  if (!(c->eps >= 0.0f)) return fail(K2_ERR_CONFIG, "eps must be >= 0");
+  if (rope) {
+    const int* a = c->axes_dims;
+    if (a[0] < 0 || a[1] < 0 || a[2] < 0 || a[0] % 2 || a[1] % 2 || a[2] % 2)
+      return fail(K2_ERR_CONFIG, "axes_dims must be even and non-negative");
+    if (a[0] + a[1] + a[2] != c->head_dim)
+      return fail(K2_ERR_CONFIG, "sum(axes_dims) (%d) must equal head_dim (%d)", a[0] + a[1] + a[2], c->head_dim);
+    if (!(c->rope_theta > 0.0f)) return fail(K2_ERR_CONFIG, "rope_theta must be > 0");
+  }
+  return K2_OK;
+}
+
+int check_block_weights(const k2_block_weights* w) {
+  if (!w) return fail(K2_ERR_NULL, "block weights are NULL");
+  if (!w->to_q || !w->to_k || !w->to_v || !w->to_gate || !w->to_out || !w->ff_gate || !w->ff_up || !w->ff_down)
+    return fail(K2_ERR_NULL, "a block projection weight is NULL");
+  return K2_OK;
+}
+
+int check_sizes(int B, int T, int N) {
+  if (B <= 0 || T < 0 || N < 0 || T + N <= 0) return fail(K2_ERR_SHAPE, "need B >= 1, T >= 0, N >= 0, T + N >= 1");
+  if (B > 65535) return fail(K2_ERR_SHAPE, "B must be <= 65535");
+  if ((long long)T + N > (1 << 24)) return fail(K2_ERR_SHAPE, "sequence too long");
+  return K2_OK;
+}
+
+int check_ws(const void* ws, size_t have, size_t need) {
+  if (need == 0) return K2_OK;
+  if (!ws) return fail(K2_ERR_NULL, "workspace is NULL");
+  if ((uintptr_t)ws % kAlign) return fail(K2_ERR_WORKSPACE, "workspace must be 256-byte aligned");
+  if (have < need) return fail(K2_ERR_WORKSPACE, "workspace too small: %zu < %zu bytes", have, need);
+  return K2_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Block workspace
+// ---------------------------------------------------------------------------------------------
+k2_block_workspace_layout block_layout(const k2_block_cfg* c, int B, int T, int N) {
+  k2_block_workspace_layout l = {};
+  const size_t es = dt_size(c->dtype);
+  const size_t L = (size_t)T + N, M = (size_t)B * L;
+  const size_t H = c->hidden, nq = (size_t)c->num_heads * c->head_dim, nk = (size_t)c->num_kv_heads * c->head_dim;
+  l.ldvt = (int)((L + 63) / 64 * 64);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  l.x1 = take(M * H * es);
+  l.q = take(M * nq * es);
+  l.k = take(M * nk * es);
+  l.vt = take((size_t)B * nk * l.ldvt * es);
+  l.g = take(M * nq * es);
+  l.og = take(M * nq * es);
+  l.x2 = take(M * H * es);
+  l.a = take(M * (size_t)c->intermediate * es);
+  l.rope = take(2 * L * (size_t)(c->head_dim / 2) * sizeof(float));
+  l.mod = take((size_t)B * 6 * H * sizeof(float));
+  l.kvalid = take(0);
+  l.total = off;
+  return l;
+}
+
+char* at(void* base, size_t off) { return (char*)base + off; }
+
+// One block forward; rope_cos/rope_sin precomputed by the caller when non-NULL.
+int block_run(const k2_block_cfg* c, const k2_block_weights* w, int B, int T, int N, const float* hin, float* hout,
+              const float* temb, const float* pos, const uint8_t* mask, void* ws, const float* rope_cos,
+              const float* rope_sin, hipStream_t s) {
+  const int dt = c->dtype;
+  const int H = c->hidden, hd = c->head_dim, nq = c->num_heads * hd, nk = c->num_kv_heads * hd, I = c->intermediate;
+  const int L = T + N, M = B * L;
+  const bool rope_inside = pos && !rope_cos;
+  const k2_block_workspace_layout lay = block_layout(c, B, T, N);
+  void* x1 = at(ws, lay.x1);
+  void* q = at(ws, lay.q);
+  void* k = at(ws, lay.k);
+  void* vt = at(ws, lay.vt);
+  void* g = at(ws, lay.g);
+  void* og = at(ws, lay.og);
+  void* x2 = at(ws, lay.x2);
+  void* a = at(ws, lay.a);
+  float* mod = (float*)at(ws, lay.mod);
+  const bool modulated = w->scale_shift_table != nullptr;
+
+  if (modulated) K2_RUN("modulation", s, modulation(temb, 6 * H, H, w->scale_shift_table, mod, B, 6, H, s));
+  if (rope_inside) {
+    rope_cos = (const float*)at(ws, lay.rope);
+    rope_sin = rope_cos + (size_t)L * (hd / 2);
+    K2_RUN("rope", s, rope_table(pos, L, c->axes_dims[0], c->axes_dims[1], c->axes_dims[2], c->rope_theta,
+                                 (float*)rope_cos, (float*)rope_sin, s));
+  }
+  if (!pos) rope_cos = rope_sin = nullptr;
+
+  ModnormArgs mn = {};
+  mn.in = hin; mn.out = x1; mn.rows = M; mn.H = H;
+  mn.rows_per_b = L; mn.in_rows_per_b = L; mn.in_row_off = 0;  // row r is batch r / L
+  mn.w = w->norm1_w;
+  mn.scale = modulated ? mod : nullptr;
+  mn.shift = modulated ? mod + H : nullptr;
+  mn.mod_stride = 6 * H;
+  mn.eps = c->eps;
+  K2_RUN("modnorm", s, modnorm(dt, mn, s));
+
+  QkvgArgs qa = {};
+  qa.wq = w->to_q; qa.wk = w->to_k; qa.wv = w->to_v; qa.wg = w->to_gate;
+  qa.nq = nq; qa.nk = nk; qa.hd = hd; qa.L = L;
+  qa.q = q; qa.k = k; qa.vt = vt; qa.g = g; qa.ldvt = lay.ldvt;
+  qa.wnq = w->norm_q_w; qa.wnk = w->norm_k_w;
+  qa.rope_cos = rope_cos; qa.rope_sin = rope_sin;
+  qa.eps = c->eps;
+  K2_RUN("gemm_qkvg", s, gemm_qkvg(dt, GemmA{x1, H, M, H}, qa, s));
+
+  AttnArgs at_ = {};
+  at_.q = q; at_.k = k; at_.vt = vt; at_.g = g; at_.og = og; at_.mask = mask;
+  at_.B = B; at_.L = L; at_.T = T; at_.nh = c->num_heads; at_.nkv = c->num_kv_heads; at_.hd = hd; at_.ldvt = lay.ldvt;
+  K2_RUN("attention", s, attention(dt, at_, s));
+
+  ResidArgs ro = {};
+  ro.w = w->to_out; ro.N = H; ro.hin = hin; ro.hout = hout;
+  ro.gate = modulated ? mod + 2 * H : nullptr; ro.gate_stride = 6 * H; ro.L = L;
+  K2_RUN("gemm_out", s, gemm_resid(dt, GemmA{og, nq, M, nq}, ro, s));
+
+  mn.in = hout; mn.out = x2; mn.w = w->norm2_w;
+  mn.scale = modulated ? mod + 3 * H : nullptr;
+  mn.shift = modulated ? mod + 4 * H : nullptr;
+  K2_RUN("modnorm", s, modnorm(dt, mn, s));
+
+  SwigluArgs sa = {};
+  sa.wgate = w->ff_gate; sa.wup = w->ff_up; sa.I = I; sa.a = a;
+  K2_RUN("gemm_swiglu", s, gemm_swiglu(dt, GemmA{x2, H, M, H}, sa, s));
+
+  ResidArgs rd = {};
+  rd.w = w->ff_down; rd.N = H; rd.hin = hout; rd.hout = hout;
+  rd.gate = modulated ? mod + 5 * H : nullptr; rd.gate_stride = 6 * H; rd.L = L;
+  K2_RUN("gemm_down", s, gemm_resid(dt, GemmA{a, I, M, I}, rd, s));
+  return K2_OK;
+}
+
+int validate_block_call(const k2_block_cfg* cfg, const k2_block_weights* w, int B, int T, int N, const void* hin,
+                        const void* hout, const float* temb, const float* pos, int pos_rows, int pos_cols) {
+  int rc;
+  if ((rc = check_block_cfg(cfg, pos != nullptr)) != K2_OK) return rc;
+  if ((rc = check_block_weights(w)) != K2_OK) return rc;
+  if ((rc = check_sizes(B, T, N)) != K2_OK) return rc;
+  if (!hin || !hout) return fail(K2_ERR_NULL, "hidden_in / hidden_out is NULL");
+  if (w->scale_shift_table && !temb) return fail(K2_ERR_NULL, "temb is NULL but the block has a scale_shift_table");
+  if (!w->scale_shift_table && temb) return fail(K2_ERR_CONFIG, "temb given for a block without scale_shift_table");
+  if (pos && (pos_rows != T + N || pos_cols != 3))
+    return fail(K2_ERR_SHAPE, "position_ids must be (T + N, 3) = (%d, 3), got (%d, %d)", T + N, pos_rows, pos_cols);
+  return K2_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Time path
+// ---------------------------------------------------------------------------------------------
+struct TimeLayout {
+  size_t emb, h1, ge, e, total;
+};
+TimeLayout time_layout(const k2_time_cfg* c, int B) {
+  TimeLayout l = {};
+  const size_t es = dt_size(c->dtype);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  l.emb = take((size_t)B * c->timestep_embed_dim * es);
+  l.h1 = take((size_t)B * c->hidden * es);
+  l.ge = take((size_t)B * c->hidden * es);
+  l.e = take((size_t)B * c->hidden * sizeof(float));
+  l.total = off;
+  return l;
+}
+
+int check_time(const k2_time_cfg* c, const k2_time_weights* w, int B) {
+  if (!c) return fail(K2_ERR_NULL, "time config is NULL");
+  if (!w) return fail(K2_ERR_NULL, "time weights are NULL");
+  if (c->dtype != K2_F32 && c->dtype != K2_BF16) return fail(K2_ERR_DTYPE, "unknown dtype %d", c->dtype);
+  if (c->hidden <= 0 || c->hidden % 8) return fail(K2_ERR_CONFIG, "time hidden must be a positive multiple of 8");
+  if (c->timestep_embed_dim <= 0 || c->timestep_embed_dim % 8)
+    return fail(K2_ERR_CONFIG, "timestep_embed_dim must be a positive multiple of 8");
+  if (!w->lin1_w || !w->lin2_w || !w->mod_w) return fail(K2_ERR_NULL, "a time-path weight is NULL");
+  if (B <= 0) return fail(K2_ERR_SHAPE, "B must be >= 1");
+  return K2_OK;
+}
+
+int time_run(const k2_time_cfg* c, const k2_time_weights* w, int B, const float* t, float* temb, float* emb_out,
+             void* ws, hipStream_t s) {
+  const int dt = c->dtype, H = c->hidden, D = c->timestep_embed_dim;
+  const TimeLayout l = time_layout(c, B);
+  void* emb = at(ws, l.emb);
+  void* h1 = at(ws, l.h1);
+  void* ge = at(ws, l.ge);
+  float* e = emb_out ? emb_out : (float*)at(ws, l.e);
+  K2_RUN("time_embed", s, time_embed(dt, t, B, D, emb, s));
+  PlainArgs p = {};
+  p.w = w->lin1_w; p.N = H; p.bias = w->lin1_b; p.outt = h1; p.ldt = H; p.act = 1;
+  p.rows_per_b = B; p.out_rows_per_b = B; p.out_row_off = 0;
+  K2_RUN("gemm_plain", s, gemm_plain(dt, GemmA{emb, D, B, D}, p, s));
+  p = PlainArgs{};
+  p.w = w->lin2_w; p.N = H; p.bias = w->lin2_b; p.outf = e; p.ldf = H; p.outt = ge; p.ldt = H; p.act = 1;
+  p.rows_per_b = B; p.out_rows_per_b = B; p.out_row_off = 0;
+  K2_RUN("gemm_plain", s, gemm_plain(dt, GemmA{h1, H, B, H}, p, s));
+  p = PlainArgs{};
+  p.w = w->mod_w; p.N = 6 * H; p.bias = w->mod_b; p.outf = temb; p.ldf = 6 * H;
+  p.rows_per_b = B; p.out_rows_per_b = B; p.out_row_off = 0;
+  K2_RUN("gemm_plain", s, gemm_plain(dt, GemmA{ge, H, B, H}, p, s));
+  return K2_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Text fusion
+// ---------------------------------------------------------------------------------------------
+struct TextLayout {
+  size_t xres, block, total;
+  size_t block_bytes;
+};
+TextLayout text_layout(const k2_text_cfg* c, int B, int T) {
+  TextLayout l = {};
+  const size_t D = c->block.hidden;
+  size_t off = 0;
+  l.xres = off;
+  off = align_up(off + (size_t)B * T * c->num_layers * D * sizeof(float));
+  const size_t lw = block_layout(&c->block, B * T, 0, c->num_layers).total;
+  const size_t rf = block_layout(&c->block, B, T, 0).total;
+  l.block_bytes = lw > rf ? lw : rf;
+  l.block = off;
+  off = align_up(off + l.block_bytes);
+  l.total = off;
+  return l;
+}
+
+int check_text(const k2_text_cfg* c, const k2_text_weights* w, int B, int T) {
+  if (!c) return fail(K2_ERR_NULL, "text config is NULL");
+  int rc;
+  if ((rc = check_block_cfg(&c->block, false)) != K2_OK) return rc;
+  if (c->num_layers <= 0 || c->num_layerwise_blocks < 0 || c->num_refiner_blocks < 0)
+    return fail(K2_ERR_CONFIG, "text fusion layer / block counts invalid");
+  if (!w) return fail(K2_ERR_NULL, "text weights are NULL");
+  if (!w->compress_w) return fail(K2_ERR_NULL, "compress_w is NULL");
+  if (c->num_layerwise_blocks && !w->layerwise) return fail(K2_ERR_NULL, "layerwise block weights are NULL");
+  if (c->num_refiner_blocks && !w->refiner) return fail(K2_ERR_NULL, "refiner block weights are NULL");
+  for (int i = 0; i < c->num_layerwise_blocks; ++i) {
+    if ((rc = check_block_weights(&w->layerwise[i])) != K2_OK) return rc;
+    if (w->layerwise[i].scale_shift_table) return fail(K2_ERR_CONFIG, "text-fusion blocks take no modulation table");
+  }
+  for (int i = 0; i < c->num_refiner_blocks; ++i) {
+    if ((rc = check_block_weights(&w->refiner[i])) != K2_OK) return rc;
+    if (w->refiner[i].scale_shift_table) return fail(K2_ERR_CONFIG, "text-fusion blocks take no modulation table");
+  }
+  if (B <= 0 || T <= 0) return fail(K2_ERR_SHAPE, "text fusion needs B >= 1 and T >= 1");
+  if ((long long)B * T > 65535) return fail(K2_ERR_SHAPE, "B * T must be <= 65535");
+  return K2_OK;
+}
+
+int text_run(const k2_text_cfg* c, const k2_text_weights* w, int B, int T, const void* enc, const uint8_t* mask,
+             float* out, void* ws, hipStream_t s) {
+  const TextLayout l = text_layout(c, B, T);
+  const int D = c->block.hidden, NL = c->num_layers;
+  float* xres = (float*)at(ws, l.xres);
+  void* bws = at(ws, l.block);
+  K2_RUN("convert", s, to_f32(c->block.dtype, enc, xres, (size_t)B * T * NL * D, s));
+  for (int i = 0; i < c->num_layerwise_blocks; ++i) {
+    int rc = block_run(&c->block, &w->layerwise[i], B * T, 0, NL, xres, xres, nullptr, nullptr, nullptr, bws, nullptr,
+                       nullptr, s);
+    if (rc != K2_OK) return rc;
+  }
+  K2_RUN("layer_compress", s, layer_compress(xres, w->compress_w, out, B * T, NL, D, s));
+  for (int i = 0; i < c->num_refiner_blocks; ++i) {
+    int rc = block_run(&c->block, &w->refiner[i], B, T, 0, out, out, nullptr, nullptr, mask, bws, nullptr, nullptr, s);
+    if (rc != K2_OK) return rc;
+  }
+  return K2_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Backbone
+// ---------------------------------------------------------------------------------------------
+struct ModelLayout {
+  size_t temb, e, time, txt, txt_t, text, h, rope, block, fmod, xf, total;
+};
+ModelLayout model_layout(const k2_model_cfg* c, int B, int T, int N) {
+  ModelLayout l = {};
+  const size_t es = dt_size(c->block.dtype);
+  const size_t H = c->block.hidden, L = (size_t)T + N, Dt = c->text.block.hidden;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  k2_time_cfg tc = {c->block.hidden, c->timestep_embed_dim, c->block.dtype};
+  l.temb = take((size_t)B * 6 * H * sizeof(float));
+  l.e = take((size_t)B * H * sizeof(float));
+  l.time = take(time_layout(&tc, B).total);
+  l.txt = take((size_t)B * T * Dt * sizeof(float));
+  l.txt_t = take((size_t)B * T * Dt * es);
+  l.text = take(T > 0 ? text_layout(&c->text, B, T).total : 0);
+  l.h = take((size_t)B * L * H * sizeof(float));
+  l.rope = take(2 * L * (size_t)(c->block.head_dim / 2) * sizeof(float));
+  l.block = take(block_layout(&c->block, B, T, N).total);
+  l.fmod = take((size_t)B * 2 * H * sizeof(float));
+  l.xf = take((size_t)B * N * H * es);
+  l.total = off;
+  return l;
+}
+
+int check_model(const k2_model_cfg* c, const k2_model_weights* w, int B, int T, int N) {
+  if (!c) return fail(K2_ERR_NULL, "model config is NULL");
+  int rc;
+  if ((rc = check_block_cfg(&c->block, true)) != K2_OK) return rc;
+  if (c->text.block.dtype != c->block.dtype) return fail(K2_ERR_DTYPE, "text and block dtypes differ");
+  if (c->num_layers < 0 || c->in_channels <= 0 || c->in_channels % 8 || c->timestep_embed_dim <= 0 ||
+      c->timestep_embed_dim % 8)
+    return fail(K2_ERR_CONFIG, "num_layers >= 0, in_channels and timestep_embed_dim positive multiples of 8");
+  if (c->text.block.hidden % 8) return fail(K2_ERR_CONFIG, "text hidden must be a multiple of 8");
+  if (!w) return fail(K2_ERR_NULL, "model weights are NULL");
+  if (!w->img_in_w || !w->txt_in_w || !w->final_w || !w->final_table)
+    return fail(K2_ERR_NULL, "img_in / txt_in / final weights are NULL");
+  if (c->num_layers && !w->blocks) return fail(K2_ERR_NULL, "block weights are NULL");
+  for (int i = 0; i < c->num_layers; ++i) {
+    if ((rc = check_block_weights(&w->blocks[i])) != K2_OK) return rc;
+    if (!w->blocks[i].scale_shift_table) return fail(K2_ERR_NULL, "block %d has no scale_shift_table", i);
+  }
+  k2_time_cfg tc = {c->block.hidden, c->timestep_embed_dim, c->block.dtype};
+  if ((rc = check_time(&tc, &w->time, B)) != K2_OK) return rc;
+  if ((rc = check_sizes(B, T, N)) != K2_OK) return rc;
+  if (N <= 0) return fail(K2_ERR_SHAPE, "the backbone needs N >= 1 image tokens");
+  if (T > 0 && (rc = check_text(&c->text, &w->text, B, T)) != K2_OK) return rc;
+  return K2_OK;
+}
+
+}  // namespace
+
+// =================================================================================================
+// Exported entry points
+// =================================================================================================
+extern "C" {
+
+void k2_block_cfg_default(k2_block_cfg* c) {
+  if (!c) return;
+  c->hidden = 6144;
+  c->num_heads = 48;
+  c->num_kv_heads = 12;
+  c->head_dim = 128;
+  c->intermediate = 16384;
+  c->axes_dims[0] = 32;
+  c->axes_dims[1] = 48;
+  c->axes_dims[2] = 48;
+  c->rope_theta = 1000.0f;
+  c->eps = 1e-5f;
+  c->dtype = K2_BF16;
+}
+
+void k2_text_cfg_default(k2_text_cfg* c) {
+  if (!c) return;
+  k2_block_cfg_default(&c->block);
+  c->block.hidden = 2560;
+  c->block.num_heads = 20;
+  c->block.num_kv_heads = 20;
+  c->block.head_dim = 128;
+  c->block.intermediate = 6912;
+  c->block.axes_dims[0] = c->block.axes_dims[1] = c->block.axes_dims[2] = 0;
+  c->num_layers = 12;
+  c->num_layerwise_blocks = 2;
+  c->num_refiner_blocks = 2;
+}
+
+void k2_model_cfg_default(k2_model_cfg* c) {
+  if (!c) return;
+  k2_block_cfg_default(&c->block);
+  k2_text_cfg_default(&c->text);
+  c->num_layers = 28;
+  c->in_channels = 64;
+  c->timestep_embed_dim = 256;
+}
+
+size_t k2_block_workspace_bytes(const k2_block_cfg* cfg, int B, int T, int N) {
+  if (!cfg || B < 0 || T < 0 || N < 0) return 0;
+  return block_layout(cfg, B, T, N).total;
+}
+
+int k2_block_workspace_layout_query(const k2_block_cfg* cfg, int B, int T, int N, k2_block_workspace_layout* out) {
+  if (!cfg || !out) return fail(K2_ERR_NULL, "config or output is NULL");
+  if (B < 0 || T < 0 || N < 0) return fail(K2_ERR_SHAPE, "negative size");
+  *out = block_layout(cfg, B, T, N);
+  return K2_OK;
+}
+
+int k2_block_forward(const k2_block_cfg* cfg, const k2_block_weights* w, int B, int T, int N, const float* hidden_in,
+                     float* hidden_out, const float* temb, const float* position_ids, int pos_rows, int pos_cols,
+                     const uint8_t* mask, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_block_call(cfg, w, B, T, N, hidden_in, hidden_out, temb, position_ids, pos_rows, pos_cols);
+  if (rc != K2_OK) return rc;
+  if ((rc = check_ws(workspace, workspace_bytes, k2_block_workspace_bytes(cfg, B, T, N))) != K2_OK) return rc;
+  g_err.clear();
+  return block_run(cfg, w, B, T, N, hidden_in, hidden_out, temb, position_ids, mask, workspace, nullptr, nullptr,
+                   (hipStream_t)stream);
+}
+
+size_t k2_timestep_modulation_workspace_bytes(const k2_time_cfg* cfg, int B) {
+  if (!cfg || B < 0) return 0;
+  return time_layout(cfg, B).total;
+}
+
+int k2_timestep_modulation_forward(const k2_time_cfg* cfg, const k2_time_weights* w, int B, const float* timestep,
+                                   float* temb, float* emb_out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_time(cfg, w, B);
+  if (rc != K2_OK) return rc;
+  if (!timestep || !temb) return fail(K2_ERR_NULL, "timestep / temb is NULL");
+  if ((rc = check_ws(workspace, workspace_bytes, time_layout(cfg, B).total)) != K2_OK) return rc;
+  g_err.clear();
+  return time_run(cfg, w, B, timestep, temb, emb_out, workspace, (hipStream_t)stream);
+}
+
+size_t k2_text_fusion_workspace_bytes(const k2_text_cfg* cfg, int B, int T) {
+  if (!cfg || B < 0 || T < 0) return 0;
+  return text_layout(cfg, B, T).total;
+}
+
+int k2_text_fusion_forward(const k2_text_cfg* cfg, const k2_text_weights* w, int B, int T, const void* enc,
+                           const uint8_t* mask, float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_text(cfg, w, B, T);
+  if (rc != K2_OK) return rc;
+  if (!enc || !out) return fail(K2_ERR_NULL, "encoder_hidden_states / out is NULL");
+  if ((rc = check_ws(workspace, workspace_bytes, text_layout(cfg, B, T).total)) != K2_OK) return rc;
+  g_err.clear();
+  return text_run(cfg, w, B, T, enc, mask, out, workspace, (hipStream_t)stream);
+}
+
+size_t k2_backbone_workspace_bytes(const k2_model_cfg* cfg, int B, int T, int N) {
+  if (!cfg || B < 0 || T < 0 || N < 0) return 0;
+  return model_layout(cfg, B, T, N).total;
+}
+
+int k2_backbone_forward(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N,
+                        const void* hidden_states, const void* enc, const float* timestep, const float* pos,
+                        int pos_rows, int pos_cols, const uint8_t* mask, float* out, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+  int rc = check_model(cfg, w, B, T, N);
+  if (rc != K2_OK) return rc;
+  if (!hidden_states || !timestep || !pos || !out || (T > 0 && !enc))
+    return fail(K2_ERR_NULL, "hidden_states / encoder_hidden_states / timestep / position_ids / out is NULL");
+  if (pos_rows != T + N || pos_cols != 3)
+    return fail(K2_ERR_SHAPE, "position_ids must be (T + N, 3) = (%d, 3), got (%d, %d)", T + N, pos_rows, pos_cols);
+  const ModelLayout l = model_layout(cfg, B, T, N);
+  if ((rc = check_ws(workspace, workspace_bytes, l.total)) != K2_OK) return rc;
+  g_err.clear();
+
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = cfg->block.dtype, H = cfg->block.hidden, hd = cfg->block.head_dim, L = T + N;
+  const int Dt = cfg->text.block.hidden, C = cfg->in_channels;
+  float* temb = (float*)at(workspace, l.temb);
+  float* e = (float*)at(workspace, l.e);
+  float* h = (float*)at(workspace, l.h);
+  float* rc_ = (float*)at(workspace, l.rope);
+  float* rs_ = rc_ + (size_t)L * (hd / 2);
+
+  // time path: temb (B, 6H) shared by all blocks, e (B, H) for the final layer
+  k2_time_cfg tc = {H, cfg->timestep_embed_dim, dt};
+  if ((rc = time_run(&tc, &w->time, B, timestep, temb, e, at(workspace, l.time), s)) != K2_OK) return rc;
+
+  // text path: text fusion -> txt_in into rows [0, T) of every batch row
+  if (T > 0) {
+    float* txt = (float*)at(workspace, l.txt);
+    void* txt_t = at(workspace, l.txt_t);
+    if ((rc = text_run(&cfg->text, &w->text, B, T, enc, mask, txt, at(workspace, l.text), s)) != K2_OK) return rc;
+    K2_RUN("convert", s, from_f32(dt, txt, txt_t, (size_t)B * T * Dt, s));
+    PlainArgs p = {};
+    p.w = w->txt_in_w; p.N = H; p.bias = w->txt_in_b; p.outf = h; p.ldf = H;
+    p.rows_per_b = T; p.out_rows_per_b = L; p.out_row_off = 0;
+    K2_RUN("gemm_plain", s, gemm_plain(dt, GemmA{txt_t, Dt, B * T, Dt}, p, s));
+  }
+  // image path: img_in into rows [T, L)
+  {
+    PlainArgs p = {};
+    p.w = w->img_in_w; p.N = H; p.bias = w->img_in_b; p.outf = h; p.ldf = H;
+    p.rows_per_b = N; p.out_rows_per_b = L; p.out_row_off = T;
+    K2_RUN("gemm_plain", s, gemm_plain(dt, GemmA{hidden_states, C, B * N, C}, p, s));
+  }
+  // rotary table once for all blocks
+  K2_RUN("rope", s, rope_table(pos, L, cfg->block.axes_dims[0], cfg->block.axes_dims[1], cfg->block.axes_dims[2],
+                               cfg->block.rope_theta, rc_, rs_, s));
+  void* bws = at(workspace, l.block);
+  for (int i = 0; i < cfg->num_layers; ++i) {
+    rc = block_run(&cfg->block, &w->blocks[i], B, T, N, h, h, temb, pos, mask, bws, rc_, rs_, s);
+    if (rc != K2_OK) return rc;
+  }
+  // final layer over the image rows only
+  float* fmod = (float*)at(workspace, l.fmod);
+  void* xf = at(workspace, l.xf);
+  K2_RUN("modulation", s, modulation(e, H, 0, w->final_table, fmod, B, 2, H, s));
+  ModnormArgs mn = {};
+  mn.in = h; mn.out = xf; mn.rows = B * N; mn.H = H;
+  mn.rows_per_b = N; mn.in_rows_per_b = L; mn.in_row_off = T;
+  mn.w = w->final_norm_w; mn.scale = fmod; mn.shift = fmod + H; mn.mod_stride = 2 * H; mn.eps = cfg->block.eps;
+  K2_RUN("modnorm", s, modnorm(dt, mn, s));
+  PlainArgs p = {};
+  p.w = w->final_w; p.N = C; p.bias = w->final_b; p.outf = out; p.ldf = C;
+  p.rows_per_b = B * N; p.out_rows_per_b = B * N; p.out_row_off = 0;
+  K2_RUN("gemm_plain", s, gemm_plain(dt, GemmA{xf, H, B * N, H}, p, s));
+  return K2_OK;
+}
+
+const char* k2_last_error(void) { return g_err.c_str(); }
+
+void k2_profile_enable(int enable) {
+  std::lock_guard<std::mutex> lk(g_pm);
+  g_prof = enable != 0;
+}
+
+void k2_profile_reset(void) {
+  std::lock_guard<std::mutex> lk(g_pm);
+  for (auto& ev : g_pev) {
+    g_pool.push_back(ev.a);
+    g_pool.push_back(ev.b);
+  }
+  g_pev.clear();
+}
+
+int k2_profile_query(const char* kernel, double* total_ms, int* launches) {
+  if (!kernel || !total_ms || !launches) return fail(K2_ERR_NULL, "NULL argument");
+  std::lock_guard<std::mutex> lk(g_pm);
+  double tot = 0.0;
+  int n = 0;
+  for (auto& ev : g_pev) {
+    if (ev.name != kernel) continue;
+    if (hipEventSynchronize(ev.b) != hipSuccess) return fail(K2_ERR_HIP, "event synchronize failed");
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, ev.a, ev.b) != hipSuccess) return fail(K2_ERR_HIP, "event elapsed time failed");
+    tot += ms;
+    ++n;
+  }
+  *total_ms = tot;
+  *launches = n;
+  return K2_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,94 @@
+// Device-side building blocks shared by the gfx950 kernels of libk2.
+//
+// Matrix-core convention used by every kernel here: a 16x16 output tile is accumulated with
+// mma16(acc, a, b), where each lane supplies an 8-element fragment of A and of B.
+//   A fragment: lane l holds row (l % 16), k slots 8*(l/16) .. 8*(l/16)+7 of a 32-wide k chunk
+//   B fragment: lane l holds column (l % 16), the same k slots
+//   acc (4 floats): lane l holds column (l % 16), rows 4*(l/16) + r, r = 0..3
+// For bf16 this is one v_mfma_f32_16x16x32_bf16. For fp32 it is eight v_mfma_f32_16x16x4_f32, the
+// i-th taking element i of each lane's fragment. Since A and B always use the same (lane group,
+// slot) -> k assignment, any permutation of k inside the chunk gives the same sum.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace k2 {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x8 __attribute__((ext_vector_type(8)));
+
+template <typename T> struct FragOf;
+template <> struct FragOf<bf16> { typedef bf16x8 type; };
+template <> struct FragOf<float> { typedef f32x8 type; };
+
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const bf16x8& a, const bf16x8& b) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mma16(f32x4 acc, const f32x8& a, const f32x8& b) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i], b[i], acc, 0, 0, 0);
+  return acc;
+}
+
+template <typename T> __device__ __forceinline__ T to_t(float x);
+template <> __device__ __forceinline__ float to_t<float>(float x) { return x; }
+template <> __device__ __forceinline__ bf16 to_t<bf16>(float x) { return (bf16)x; }  // RNE
+
+__device__ __forceinline__ float to_f(float x) { return x; }
+__device__ __forceinline__ float to_f(bf16 x) { return (float)x; }
+
+// Pack 8 floats into a fragment of T.
+__device__ __forceinline__ void pack8(bf16x8& f, const float* v) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = (bf16)v[i];
+}
+__device__ __forceinline__ void pack8(f32x8& f, const float* v) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f[i] = v[i];
+}
+
+__device__ __forceinline__ float sigmoidf_(float x) { return 1.0f / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float siluf_(float x) { return x / (1.0f + __expf(-x)); }
+__device__ __forceinline__ float gelu_tanhf_(float x) {
+  const float k0 = 0.7978845608028654f;  // sqrt(2/pi)
+  return 0.5f * x * (1.0f + tanhf(k0 * (x + 0.044715f * x * x * x)));
+}
+
+// Sum / max over the 16 lanes of a lane group (lanes with equal l/16).
+__device__ __forceinline__ float group16_sum(float v) {
+  v += __shfl_xor(v, 1);
+  v += __shfl_xor(v, 2);
+  v += __shfl_xor(v, 4);
+  v += __shfl_xor(v, 8);
+  return v;
+}
+// Over the 4 lane groups (lanes with equal l%16).
+__device__ __forceinline__ float across_groups_max(float v) {
+  v = fmaxf(v, __shfl_xor(v, 16));
+  v = fmaxf(v, __shfl_xor(v, 32));
+  return v;
+}
+__device__ __forceinline__ float across_groups_sum(float v) {
+  v += __shfl_xor(v, 16);
+  v += __shfl_xor(v, 32);
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// XOR swizzle of 16-byte chunk positions within 128-byte LDS rows (8 chunks): 16 consecutive rows
+// read at the same chunk land in 16 distinct 16-byte bank slots whether the LDS serves 128 or 256
+// bytes per cycle.
+__device__ __forceinline__ int swz8(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
+}  // namespace k2

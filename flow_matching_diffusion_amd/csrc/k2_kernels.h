@@ -1,0 +1,120 @@
+// Internal launcher interface between the C ABI (k2_api.cpp) and the kernel translation units.
+// Plain structs of device pointers and sizes; each launcher enqueues one kernel on `s` and returns
+// the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace k2 {
+
+enum Dt { DT_F32 = 0, DT_BF16 = 1 };
+
+inline size_t dt_size(int dt) { return dt == DT_BF16 ? 2 : 4; }
+
+// ---------------------------------------------------------------------------------------------
+// GEMM: C[m, n] = sum_k A[m, k] * Bw[n, k]  (A row-major M x K, weights nn.Linear (N, K) layout)
+// ---------------------------------------------------------------------------------------------
+struct GemmA {
+  const void* A;
+  int lda;
+  int M, K;
+};
+
+// q/k/v/gate projection of the block: B rows are the concatenation [to_q; to_k; to_v; to_gate].
+// Epilogue: per-head RMSNorm (1 + w) on q and k, then RoPE; v stored transposed per (batch, kv head);
+// gate stored as is.
+struct QkvgArgs {
+  const void* wq; const void* wk; const void* wv; const void* wg;  // (nq, K), (nk, K), (nk, K), (nq, K)
+  int nq, nk;                   // nh*hd, nkv*hd
+  int hd, L;                    // head dim, tokens per batch row
+  void* q; void* k; void* vt; void* g;
+  int ldvt;                     // row stride of vt (B, nkv, hd, ldvt)
+  const float* wnq; const float* wnk;  // (hd) zero-centred, may be NULL
+  const float* rope_cos; const float* rope_sin;  // (L, hd/2) or NULL (no RoPE)
+  float eps;
+};
+
+// SwiGLU up projection: a = silu(x Wgate^T) * (x Wup^T), a: (M, I).
+struct SwigluArgs {
+  const void* wgate; const void* wup;
+  int I;
+  void* a;
+};
+
+// Residual projection: hout[m, n] = hin[m, n] + gate[m / L, n] * (A Bw^T)[m, n]; gate NULL = 1.
+struct ResidArgs {
+  const void* w;
+  int N;
+  const float* hin; float* hout;
+  const float* gate; int gate_stride;  // gate row b at gate + b * gate_stride
+  int L;
+};
+
+// Plain projection with bias and optional outputs; output row for input row m is
+// (m / rows_per_b) * out_rows_per_b + out_row_off + (m % rows_per_b).
+struct PlainArgs {
+  const void* w;
+  int N;
+  const float* bias;            // (N) or NULL
+  float* outf; int ldf;         // acc + bias (float), or NULL
+  void* outt; int ldt;          // act(acc + bias) in the operand dtype, or NULL
+  int act;                      // 0 = identity, 1 = gelu_tanh (applies to outt only)
+  int rows_per_b, out_rows_per_b, out_row_off;
+};
+
+hipError_t gemm_qkvg(int dt, const GemmA& a, const QkvgArgs& p, hipStream_t s);
+hipError_t gemm_swiglu(int dt, const GemmA& a, const SwigluArgs& p, hipStream_t s);
+hipError_t gemm_resid(int dt, const GemmA& a, const ResidArgs& p, hipStream_t s);
+hipError_t gemm_plain(int dt, const GemmA& a, const PlainArgs& p, hipStream_t s);
+
+// ---------------------------------------------------------------------------------------------
+// Attention: og[m, h*hd + d] = softmax-attention output * sigmoid(g[m, h*hd + d])
+// ---------------------------------------------------------------------------------------------
+struct AttnArgs {
+  const void* q; const void* k; const void* vt; const void* g;
+  void* og;
+  const uint8_t* mask;  // (B, T) or NULL
+  int B, L, T;
+  int nh, nkv, hd;
+  int ldvt;
+};
+hipError_t attention(int dt, const AttnArgs& p, hipStream_t s);
+
+// ---------------------------------------------------------------------------------------------
+// Row kernels
+// ---------------------------------------------------------------------------------------------
+// out[r] = (1 + scale_b) * RMSNorm(in[src_row(r)]; w) + shift_b in the operand dtype, where
+// r = b * rows_per_b + i reads input row b * in_rows_per_b + in_row_off + i and
+// scale_b = scale + b * mod_stride (NULL = 0), shift_b likewise.
+struct ModnormArgs {
+  const float* in; void* out;
+  int rows, H;
+  int rows_per_b, in_rows_per_b, in_row_off;
+  const float* w;
+  const float* scale; const float* shift; int mod_stride;
+  float eps;
+};
+hipError_t modnorm(int dt, const ModnormArgs& p, hipStream_t s);
+
+// mod[b, c, j] = temb[b * temb_stride + c * chunk_stride + j] + table[c, j] for c < nchunks
+// (table may be NULL). chunk_stride = H splits temb into chunks; 0 adds the same vector to every row.
+hipError_t modulation(const float* temb, int temb_stride, int chunk_stride, const float* table, float* mod,
+                      int B, int nchunks, int H, hipStream_t s);
+
+// cos/sin (L, hd/2) of the 3-axis rotary angles pos[l, a] * theta^(-2i/d_a).
+hipError_t rope_table(const float* pos, int L, int a0, int a1, int a2, float theta, float* cos_out,
+                      float* sin_out, hipStream_t s);
+
+// Sinusoidal time embedding [cos(1000 t f_k)] ++ [sin(1000 t f_k)] in the operand dtype.
+hipError_t time_embed(int dt, const float* t, int B, int dim, void* out, hipStream_t s);
+
+// y[n, d] = sum_l c[l] * x[n, l, d] (float32).
+hipError_t layer_compress(const float* x, const float* c, float* y, int rows, int nl, int D, hipStream_t s);
+
+// Element conversion between float32 and the operand dtype.
+hipError_t to_f32(int dt, const void* in, float* out, size_t n, hipStream_t s);
+hipError_t from_f32(int dt, const float* in, void* out, size_t n, hipStream_t s);
+
+}  // namespace k2

@@ -1,0 +1,64 @@
+"""Helpers shared by the GPU parity tests (inputs from synth, expected values from the oracle)."""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+
+from flow_matching_diffusion_amd import synth as S
+
+
+def device():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def rel_err(got, ref):
+    """max |got - ref| / rms(ref), the parity metric; also returns the rms error ratio."""
+    got = np.asarray(got, np.float64)
+    ref = np.asarray(ref, np.float64)
+    rms = np.sqrt(np.mean(ref * ref))
+    d = np.abs(got - ref)
+    return d.max() / rms, np.sqrt(np.mean(d * d)) / rms
+
+
+TOL = {"f32": 1e-4, "bf16": 2e-2}
+
+
+def temb_for(wl, inp):
+    """float32 temb fed to both sides: the workload's own N(0,1) vector, or the oracle time path of t."""
+    from oracle import k2_oracle as O
+    if "temb" in inp:
+        return inp["temb"]
+    temb, _ = O.time_path(inp["timestep"], inp["time_weights"], wl.timestep_embed_dim)
+    return temb.astype(np.float32)
+
+
+def gpu_block(wl, inp, temb, h=None, mask="default", dev=None, keep_ws=False):
+    """Run k2_block_forward on the workload's inputs; returns the output (and workspace)."""
+    import torch
+    import flow_matching_diffusion_amd as k2
+    dev = dev or device()
+    cfg = k2.block_cfg(wl.dims, wl.dtype)
+    w = k2.upload(inp["weights"], wl.dtype, dev)
+    h = inp["h"] if h is None else h
+    m = inp["mask"] if isinstance(mask, str) else mask
+    ht = torch.from_numpy(np.ascontiguousarray(h)).to(dev)
+    tt = None if temb is None else torch.from_numpy(np.ascontiguousarray(temb, dtype=np.float32)).to(dev)
+    pt = None if inp["position_ids"] is None else torch.from_numpy(inp["position_ids"]).to(dev)
+    mt = None if m is None else torch.from_numpy(np.ascontiguousarray(m)).to(dev)
+    B, L, _ = h.shape
+    ws = torch.empty(k2.load().k2_block_workspace_bytes(__import__("ctypes").byref(cfg), B, wl.T, L - wl.T),
+                     dtype=torch.uint8, device=dev)
+    out = k2.block_forward(cfg, w, ht, tt, pt, mt, wl.T, workspace=ws)
+    torch.cuda.synchronize()
+    res = out.cpu().numpy()
+    if keep_ws:
+        return res, ws, cfg
+    return res
+
+
+def workload(name, **kw):
+    wl = S.WORKLOADS[name]
+    return S.replace(wl, **kw) if kw else wl
