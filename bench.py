@@ -1,0 +1,249 @@
+#!/usr/bin/env python3
+"""Benchmark of the Krea 2 single-stream block forward on one MI355X.
+
+A step is one k2_block_forward (all stages: modulation, modulated RMSNorm, q/k/v/gate projection
+with q/k norm + RoPE, masked GQA attention with the sigmoid gate, output projection + gated
+residual, modulated RMSNorm, SwiGLU, down projection + gated residual) over the 1024^2 CFG pair
+(B=2, 512 text tokens with 300 / 16 valid + a 64x64 latent grid, L = 4608, full-size dims), with
+weights and activations resident in HBM; temb is computed once before timing (the backbone
+computes it once for all 28 blocks). value = algorithmic block TFLOP/s (GEMMs over every row,
+attention over valid keys only). Also reported: the 28-block backbone with text fusion at the
+same resolution as denoise steps/s (one call = one CFG step), per-kernel times, the roofline of
+the dominant kernel, and the CPU oracle on a bounded sample.
+
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-backbone] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "Krea2 block TFLOP/s & % bf16 MFMA peak; denoise steps/s at 1024², B=2"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
+PEAK_HBM_GBS = 8000.0
+KERNELS = ("modulation", "modnorm", "gemm_qkvg", "attention", "gemm_out", "gemm_swiglu", "gemm_down", "rope")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "flow_matching_diffusion_amd", "csrc", f) for f in
+                  ("gemm.hip", "k2_device.h", "attention.hip", "elementwise.hip")]
+
+
+def block_flops(d, B, L, valid_keys):
+    """GEMMs over all B*L rows + attention over valid keys (4 hd nh per query-key pair)."""
+    H, nh, nkv, hd, I = d.hidden, d.num_heads, d.num_kv_heads, d.head_dim, d.intermediate
+    per_row = 2 * H * (2 * nh * hd + 2 * nkv * hd) + 2 * nh * hd * H + 6 * H * I
+    return B * L * per_row + sum(4 * hd * nh * L * v for v in valid_keys)
+
+
+def kernel_flops(d, M, name):
+    H, nh, nkv, hd, I = d.hidden, d.num_heads, d.num_kv_heads, d.head_dim, d.intermediate
+    return {"gemm_qkvg": 2 * M * H * (2 * nh * hd + 2 * nkv * hd), "gemm_out": 2 * M * nh * hd * H,
+            "gemm_swiglu": 4 * M * H * I, "gemm_down": 2 * M * I * H}.get(name)
+
+
+def source_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        h.update(open(p, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_for(key):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if the kernels have not
+    changed since it was taken (else None)."""
+    try:
+        t = json.load(open(TRAFFIC_FILE))
+    except (OSError, ValueError):
+        return None
+    e = t.get(key)
+    if not e or e.get("source_sha") != source_hash():
+        return None
+    return e["fetch_bytes"] + e["write_bytes"]
+
+
+def cpu_baseline(wl, rows):
+    """The CPU oracle as it stands on a bounded sample of the same workload: batch row 0, keys and
+    values for all of its rows, the whole block for `rows` sampled query rows."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    from flow_matching_diffusion_amd import synth as S
+    from oracle import k2_oracle as O
+
+    wl1 = S.replace(wl, B=1, valid=None if wl.valid is None else wl.valid[:1],
+                    t=None if wl.t is None else wl.t[:1])
+    inp = S.block_inputs(wl1)
+    if "temb" in inp:
+        temb = inp["temb"]
+    else:
+        temb = O.time_path(inp["timestep"], inp["time_weights"], wl.timestep_embed_dim)[0].astype(np.float32)
+    sel = S.sample_rows(wl1, rows)
+    t0 = time.perf_counter()
+    O.block_forward(inp["h"], temb, inp["position_ids"], inp["mask"], inp["weights"], wl.dims, wl.T, rows=sel)
+    dt = time.perf_counter() - t0
+    d = wl.dims
+    L = wl.L
+    valid = L if wl.valid is None else wl.N + wl.valid[0]
+    per_row = 2 * d.hidden * (2 * d.num_heads * d.head_dim) + 2 * d.num_heads * d.head_dim * d.hidden + \
+        6 * d.hidden * d.intermediate
+    flops = 2 * L * d.hidden * 2 * d.num_kv_heads * d.head_dim + len(sel) * per_row + \
+        4 * d.head_dim * d.num_heads * len(sel) * valid
+    threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+    return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": max(threads) if threads else 1,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"{wl.name} batch row 0: keys/values for all {L} rows + the whole block for {len(sel)} "
+                      f"seeded query rows ({flops / 1e12:.3f} TFLOP), float64 NumPy"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="block1024")
+    ap.add_argument("--backbone-steps", type=int, default=5)
+    ap.add_argument("--no-backbone", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=256)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py: this build runs on one GPU only; --gpus must be 1 (no multi-GPU path is built)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import flow_matching_diffusion_amd as k2
+    from flow_matching_diffusion_amd import synth as S
+
+    dev = torch.device("cuda:0")
+    k2.load()
+    wl = S.WORKLOADS[args.workload]
+    d = wl.dims
+    B, T, N, L = wl.B, wl.T, wl.N, wl.L
+    f32 = torch.float32
+
+    w = S.device_block_weights(wl.seed, "block.", d, wl.dtype, dev)
+    h = S.device_normal(wl.seed, "hidden", (B, L, d.hidden), 1.0, f32, dev)
+    if wl.t is not None:
+        tw = S.device_model_weights(wl.seed, S.replace(wl, num_layers=0), dev)["time"]
+        temb, _ = k2.timestep_modulation_forward(d.hidden, wl.timestep_embed_dim, wl.dtype, tw,
+                                                 torch.tensor(wl.t, dtype=f32, device=dev))
+    else:
+        temb = S.device_normal(wl.seed, "temb", (B, 6 * d.hidden), 1.0, f32, dev)
+    pos = torch.from_numpy(S.position_ids(T, *wl.grid)).to(dev)
+    m = S.text_mask(B, T, wl.valid)
+    mask = None if m is None else torch.from_numpy(m).to(dev)
+    cfg = k2.block_cfg(d, wl.dtype)
+    out = torch.empty_like(h)
+    import ctypes
+    ws = torch.empty(k2.load().k2_block_workspace_bytes(ctypes.byref(cfg), B, T, N), dtype=torch.uint8, device=dev)
+
+    def step():
+        k2.block_forward(cfg, w, h, temb, pos, mask, T, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    k2.profile_reset()
+    k2.profile_enable(True)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    k2.profile_enable(False)
+    wall_ms = (t1 - t0) * 1e3 / args.steps
+    ev_ms = e0.elapsed_time(e1) / args.steps
+    ms = max(wall_ms, ev_ms)
+    valid_keys = [L if wl.valid is None else N + v for v in (wl.valid or [L] * B)]
+    flops = block_flops(d, B, L, valid_keys)
+    tflops = flops / (ms * 1e-3) / 1e12
+    M = B * L
+    kernels = {}
+    for name in KERNELS:
+        tot, n = k2.profile_query(name)
+        if n:
+            kernels[name] = {"avg_ms": round(tot / n, 4), "launches_per_step": n // args.steps}
+            kf = kernel_flops(d, M, name)
+            if kf:
+                kernels[name]["tflops"] = round(kf / (tot / n * 1e-3) / 1e12, 1)
+    attn_flops = sum(4 * d.head_dim * d.num_heads * L * v for v in valid_keys)
+    if "attention" in kernels:
+        kernels["attention"]["tflops"] = round(attn_flops / (kernels["attention"]["avg_ms"] * 1e-3) / 1e12, 1)
+    if "modnorm" in kernels:
+        nbytes = M * d.hidden * (4 + (2 if wl.dtype == "bf16" else 4))
+        kernels["modnorm"]["gbs"] = round(nbytes / (kernels["modnorm"]["avg_ms"] * 1e-3) / 1e9, 1)
+
+    dom = "gemm_swiglu"
+    dom_flops = kernel_flops(d, M, dom)
+    dom_ms = kernels[dom]["avg_ms"]
+    achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1), "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_for(f"{dom}@{wl.name}"),
+                "algorithmic_per_launch": f"{dom_flops:.4e} FLOP (2*M*2I*H, M={M}, I={d.intermediate}, H={d.hidden})"}
+
+    result = {
+        "metric": METRIC, "value": round(tflops, 2), "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": wl.dtype, "data": "synthetic (seeded, device-generated N(0,1) activations, "
+                                                           "N(0,0.02) weights)",
+        "config": {"workload": wl.name, "B": B, "text_tokens": T, "valid_text": list(wl.valid or []),
+                   "grid": list(wl.grid), "L": L, "hidden": d.hidden, "heads": d.num_heads, "kv_heads": d.num_kv_heads,
+                   "head_dim": d.head_dim, "intermediate": d.intermediate, "timestep": list(wl.t or [])},
+        "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "block_gflop": round(flops / 1e9, 1),
+        "kernels": kernels,
+        "roofline": roofline,
+    }
+    del w, h, out, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_backbone:
+        bwl = S.WORKLOADS["backbone1024"]
+        mw = S.device_model_weights(bwl.seed, bwl, dev)
+        x = S.device_normal(bwl.seed, "latents", (bwl.B, bwl.N, bwl.in_channels), 1.0,
+                            torch.bfloat16 if bwl.dtype == "bf16" else f32, dev)
+        enc = S.device_normal(bwl.seed, "encoder_hidden_states", (bwl.B, bwl.T, bwl.text.num_layers, bwl.text.hidden),
+                              1.0, torch.bfloat16 if bwl.dtype == "bf16" else f32, dev)
+        tt = torch.tensor(bwl.t, dtype=f32, device=dev)
+        bpos = torch.from_numpy(S.position_ids(bwl.T, *bwl.grid)).to(dev)
+        bm = torch.from_numpy(S.text_mask(bwl.B, bwl.T, bwl.valid)).to(dev)
+        mcfg = k2.model_cfg(bwl.dims, bwl.text, bwl.num_layers, bwl.in_channels, bwl.timestep_embed_dim, bwl.dtype)
+        bws = torch.empty(k2.backbone_workspace_bytes(mcfg, bwl.B, bwl.T, bwl.N), dtype=torch.uint8, device=dev)
+        for _ in range(2):
+            k2.backbone_forward(mcfg, mw, x, enc, tt, bpos, bm, workspace=bws)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.backbone_steps):
+            v = k2.backbone_forward(mcfg, mw, x, enc, tt, bpos, bm, workspace=bws)
+        torch.cuda.synchronize()
+        bms = (time.perf_counter() - t0) * 1e3 / args.backbone_steps
+        assert bool(torch.isfinite(v).all())
+        bflops = bwl.num_layers * flops  # blocks only; text fusion and projections are extra work
+        result["denoise_steps_per_s"] = round(1e3 / bms, 3)
+        result["backbone"] = {"workload": bwl.name, "ms_per_step": round(bms, 2), "layers": bwl.num_layers,
+                              "block_tflops_in_backbone": round(bflops / (bms * 1e-3) / 1e12, 1),
+                              "base_image_s_28_steps": round(28 * bms / 1e3, 2)}
+        del mw, bws, x, enc
+        torch.cuda.empty_cache()
+
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(wl, args.cpu_rows)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

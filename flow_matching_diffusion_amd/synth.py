@@ -300,3 +300,68 @@ def sample_rows(wl: Workload, count: int, seed: int | None = None) -> np.ndarray
 
 def replace(wl: Workload, **kw) -> Workload:
     return dataclasses.replace(wl, **kw)
+
+
+# ----------------------------------------------------------------------------------------------
+# Device-side generation (bench workloads: same shapes and distributions, drawn on the GPU)
+# ----------------------------------------------------------------------------------------------
+def device_normal(seed: int, name: str, shape, sigma: float, dtype, device):
+    """Seeded N(0, sigma^2) tensor drawn on the device (torch's generator), cast to dtype."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed((seed << 32) ^ zlib.crc32(name.encode()))
+    t = torch.randn(tuple(shape), generator=g, device=device, dtype=torch.float32)
+    if sigma != 1.0:
+        t.mul_(sigma)
+    return t.to(dtype)
+
+
+def device_block_weights(seed: int, prefix: str, d: BlockDims, dtype: str, device, modulated: bool = True) -> dict:
+    import torch
+    td = torch.bfloat16 if dtype == "bf16" else torch.float32
+    H, nh, nkv, hd, I = d.hidden, d.num_heads, d.num_kv_heads, d.head_dim, d.intermediate
+    s = WEIGHT_SIGMA
+    w = {}
+    if modulated:
+        w["scale_shift_table"] = device_normal(seed, prefix + "scale_shift_table", (6, H), s, torch.float32, device)
+    for n, shp in (("norm1_w", (H,)), ("norm2_w", (H,)), ("norm_q_w", (hd,)), ("norm_k_w", (hd,))):
+        w[n] = device_normal(seed, prefix + n, shp, s, torch.float32, device)
+    shapes = {"to_q": (nh * hd, H), "to_k": (nkv * hd, H), "to_v": (nkv * hd, H), "to_gate": (nh * hd, H),
+              "to_out": (H, nh * hd), "ff_gate": (I, H), "ff_up": (I, H), "ff_down": (H, I)}
+    for n, shp in shapes.items():
+        w[n] = device_normal(seed, prefix + n, shp, s, td, device)
+    return w
+
+
+def device_model_weights(seed: int, wl: Workload, device) -> dict:
+    import torch
+    td = torch.bfloat16 if wl.dtype == "bf16" else torch.float32
+    f32 = torch.float32
+    d, t = wl.dims, (wl.text or TextDims())
+    H, s = d.hidden, WEIGHT_SIGMA
+    tb = text_block_dims(t)
+    return {
+        "img_in_w": device_normal(seed, "img_in_w", (H, wl.in_channels), s, td, device),
+        "img_in_b": device_normal(seed, "img_in_b", (H,), s, f32, device),
+        "txt_in_w": device_normal(seed, "txt_in_w", (H, t.hidden), s, td, device),
+        "txt_in_b": device_normal(seed, "txt_in_b", (H,), s, f32, device),
+        "time": {
+            "lin1_w": device_normal(seed, "time.lin1_w", (H, wl.timestep_embed_dim), s, td, device),
+            "lin1_b": device_normal(seed, "time.lin1_b", (H,), s, f32, device),
+            "lin2_w": device_normal(seed, "time.lin2_w", (H, H), s, td, device),
+            "lin2_b": device_normal(seed, "time.lin2_b", (H,), s, f32, device),
+            "mod_w": device_normal(seed, "time.mod_w", (6 * H, H), s, td, device),
+            "mod_b": device_normal(seed, "time.mod_b", (6 * H,), s, f32, device),
+        },
+        "text": {
+            "layerwise": [device_block_weights(seed, f"text.layerwise{i}.", tb, wl.dtype, device, modulated=False)
+                          for i in range(t.num_layerwise_blocks)],
+            "compress_w": device_normal(seed, "text.compress_w", (t.num_layers,), s, f32, device),
+            "refiner": [device_block_weights(seed, f"text.refiner{i}.", tb, wl.dtype, device, modulated=False)
+                        for i in range(t.num_refiner_blocks)],
+        },
+        "blocks": [device_block_weights(seed, f"blocks{i}.", d, wl.dtype, device) for i in range(wl.num_layers)],
+        "final_table": device_normal(seed, "final_table", (2, H), s, f32, device),
+        "final_w": device_normal(seed, "final_w", (wl.in_channels, H), s, td, device),
+        "final_b": device_normal(seed, "final_b", (wl.in_channels,), s, f32, device),
+    }

@@ -38,6 +38,14 @@ Readings where the pages are silent or garbled (each restated where it is used):
   R12 text fusion block: pre-norm block with the same attention (q/k norm, sigmoid gate), MHA,
       no RoPE, no modulation; layer compressor Linear(num_layers, 1) without bias; txt_in is a
       plain Linear with bias.
+  R13 bf16 operands: the model runs in bfloat16 ([PIPELINE] examples load it with
+      torch_dtype=bfloat16) and RMSNorm computes in float32 and casts back to the model dtype
+      ([ARTICLE] §四.4). With `rnd=bf16_round` the oracle rounds to bf16 exactly where the bf16
+      model hands a matrix product a bf16 operand: the modulated norm outputs, the q/k (after norm
+      and RoPE), v and gate projections, the gated attention output, the SwiGLU activation, the
+      time-MLP inputs, the fused text before txt_in and the final-layer norm output. Everything
+      else (residual stream, statistics, softmax, accumulation) stays float64. rnd=None is the
+      exact function.
 """
 from __future__ import annotations
 
@@ -50,6 +58,20 @@ F64 = np.float64
 
 def _f64(a):
     return None if a is None else np.asarray(a, dtype=F64)
+
+
+def _id(x):
+    return x
+
+
+def bf16_round(x):
+    """Round to the nearest bfloat16 (ties to even) via float32; returns float64 (R13).
+    A bfloat16 is the upper 16 bits of a float32, so rounding adds half of the dropped range
+    (0x7FFF, plus 1 when the kept lsb is odd) and clears the low 16 bits."""
+    f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
+    u = f.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
+    return u.astype(np.uint32).view(np.float32).astype(F64)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -144,15 +166,17 @@ def modulation(temb, table):
     return _f64(temb).reshape(B, 6, H) + _f64(table)[None]
 
 
-def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermediates=False):
+def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermediates=False, rnd=None):
     """One Krea2TransformerBlock forward ([ARTICLE] §四.2 block, §四.3 attention, §四.4 norm).
 
     h: (B, L, H) residual stream; temb: (B, 6H) or None (no modulation: text-fusion blocks);
     position_ids: (L, 3) or None (no RoPE); mask: (B, T) or None; w: weight dict (nn.Linear
     (out, in) layout); dims: BlockDims-like; T: text tokens at the start of the sequence.
     rows: optional sorted sequence indices; only those output rows are computed (keys and
-    values still come from every row). Returns (B, len(rows) or L, H) float64.
+    values still come from every row). rnd: operand rounding of R13 (None = exact).
+    Returns (B, len(rows) or L, H) float64.
     """
+    rnd = rnd or _id
     h = _f64(h)
     B, L, H = h.shape
     nh, nkv, hd, eps = dims.num_heads, dims.num_kv_heads, dims.head_dim, dims.eps
@@ -168,15 +192,15 @@ def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermedia
         pg = qg = 1.0
 
     # (1 + prescale) * norm1(h) + preshift
-    x1 = (1.0 + ps) * rms_norm(h, w["norm1_w"], eps) + pt
+    x1 = rnd((1.0 + ps) * rms_norm(h, w["norm1_w"], eps) + pt)
     out["x1"] = x1
 
     # projections (R7: no bias); k and v for every row, q and gate for the requested rows
     k = x1 @ _f64(w["to_k"]).T
-    v = x1 @ _f64(w["to_v"]).T
+    v = rnd(x1 @ _f64(w["to_v"]).T)
     xr = x1[:, rows]
     q = xr @ _f64(w["to_q"]).T
-    graw = xr @ _f64(w["to_gate"]).T
+    graw = rnd(xr @ _f64(w["to_gate"]).T)
 
     q = q.reshape(B, R, nh, hd).transpose(0, 2, 1, 3)
     k = k.reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
@@ -189,18 +213,19 @@ def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermedia
         ang = rope_angles(position_ids, dims.axes_dims, dims.rope_theta)
         q = apply_rope(q, ang[rows][None, None])
         k = apply_rope(k, ang[None, None])
+    q, k = rnd(q), rnd(k)
     out["q"], out["k"], out["v"], out["g"] = q, k, v, graw
 
     o = attention(q, k, v, key_valid_mask(B, L, T, mask))
     o = o.transpose(0, 2, 1, 3).reshape(B, R, nh * hd)
-    og = o * sigmoid(graw)                                   # R6
+    og = rnd(o * sigmoid(graw))                              # R6
     out["og"] = og
 
     h1 = h[:, rows] + pg * (og @ _f64(w["to_out"]).T)
     out["h1"] = h1
-    x2 = (1.0 + qs) * rms_norm(h1, w["norm2_w"], eps) + qt
+    x2 = rnd((1.0 + qs) * rms_norm(h1, w["norm2_w"], eps) + qt)
     out["x2"] = x2
-    a = silu(x2 @ _f64(w["ff_gate"]).T) * (x2 @ _f64(w["ff_up"]).T)   # R9
+    a = rnd(silu(x2 @ _f64(w["ff_gate"]).T) * (x2 @ _f64(w["ff_up"]).T))   # R9
     out["a"] = a
     h2 = h1 + qg * (a @ _f64(w["ff_down"]).T)
     out["out"] = h2
@@ -220,19 +245,21 @@ def timestep_embedding(t, dim=256, max_period=10000.0, time_scale=1000.0):
     return np.concatenate([np.cos(arg), np.sin(arg)], axis=1)
 
 
-def time_path(t, tw, dim=256):
-    """time_embed -> GELU -> time_mod_proj ([ARTICLE] data flow of §四; R10).
+def time_path(t, tw, dim=256, rnd=None):
+    """time_embed -> GELU -> time_mod_proj ([ARTICLE] data flow of §四; R10; rnd: R13).
     Returns (temb (B, 6H), e (B, H)) where e is time_embed's output (before the GELU)."""
-    emb = timestep_embedding(t, dim)
-    e = gelu_tanh(emb @ _f64(tw["lin1_w"]).T + _f64(tw["lin1_b"])) @ _f64(tw["lin2_w"]).T + _f64(tw["lin2_b"])
-    temb = gelu_tanh(e) @ _f64(tw["mod_w"]).T + _f64(tw["mod_b"])
+    rnd = rnd or _id
+    emb = rnd(timestep_embedding(t, dim))
+    h1 = rnd(gelu_tanh(emb @ _f64(tw["lin1_w"]).T + _f64(tw["lin1_b"])))
+    e = h1 @ _f64(tw["lin2_w"]).T + _f64(tw["lin2_b"])
+    temb = rnd(gelu_tanh(e)) @ _f64(tw["mod_w"]).T + _f64(tw["mod_b"])
     return temb, e
 
 
 # ----------------------------------------------------------------------------------------------
 # Text fusion
 # ----------------------------------------------------------------------------------------------
-def text_fusion(enc, mask, tw, tdims):
+def text_fusion(enc, mask, tw, tdims, rnd=None):
     """Krea2TextFusion ([ARTICLE] §四.1; R12): layerwise blocks over the layer axis of every
     token, Linear(num_layers, 1) over the layer axis, refiner blocks over tokens with the mask.
     enc: (B, T, num_layers, D). Returns (B, T, D)."""
@@ -240,36 +267,38 @@ def text_fusion(enc, mask, tw, tdims):
     B, T, NL, D = enc.shape
     x = enc.reshape(B * T, NL, D)
     for bw in tw["layerwise"]:
-        x = block_forward(x, None, None, None, bw, tdims, T=0)
+        x = block_forward(x, None, None, None, bw, tdims, T=0, rnd=rnd)
     y = np.tensordot(x, _f64(tw["compress_w"]), axes=([1], [0])).reshape(B, T, D)
     for bw in tw["refiner"]:
-        y = block_forward(y, None, None, mask, bw, tdims, T=T)
+        y = block_forward(y, None, None, mask, bw, tdims, T=T, rnd=rnd)
     return y
 
 
 # ----------------------------------------------------------------------------------------------
 # Backbone
 # ----------------------------------------------------------------------------------------------
-def final_layer(h_img, e, table, norm_w, w, b, eps):
+def final_layer(h_img, e, table, norm_w, w, b, eps, rnd=None):
     """Krea2FinalLayer ([ARTICLE] §四.6; R11)."""
+    rnd = rnd or _id
     scale = _f64(table)[0][None, None] + _f64(e)[:, None, :]
     shift = _f64(table)[1][None, None] + _f64(e)[:, None, :]
-    x = (1.0 + scale) * rms_norm(h_img, norm_w, eps) + shift
+    x = rnd((1.0 + scale) * rms_norm(h_img, norm_w, eps) + shift)
     return x @ _f64(w).T + _f64(b)
 
 
-def backbone_forward(x, enc, t, position_ids, mask, mw, dims, tdims, T, time_dim=256):
+def backbone_forward(x, enc, t, position_ids, mask, mw, dims, tdims, T, time_dim=256, rnd=None):
     """Krea2Transformer2DModel.forward ([API] forward; [ARTICLE] data flow of §四):
     time path, text fusion + txt_in, img_in, concat [text, image], blocks, image rows only,
     final layer. Returns the velocity (B, N, in_channels)."""
-    temb, e = time_path(t, mw["time"], time_dim)
-    txt = text_fusion(enc, mask, mw["text"], tdims) @ _f64(mw["txt_in_w"]).T + _f64(mw["txt_in_b"])
+    r = rnd or _id
+    temb, e = time_path(t, mw["time"], time_dim, rnd=rnd)
+    txt = r(text_fusion(enc, mask, mw["text"], tdims, rnd=rnd)) @ _f64(mw["txt_in_w"]).T + _f64(mw["txt_in_b"])
     img = _f64(x) @ _f64(mw["img_in_w"]).T + _f64(mw["img_in_b"])
     h = np.concatenate([txt, img], axis=1)
     for bw in mw["blocks"]:
-        h = block_forward(h, temb, position_ids, mask, bw, dims, T=T)
+        h = block_forward(h, temb, position_ids, mask, bw, dims, T=T, rnd=rnd)
     return final_layer(h[:, T:], e, mw["final_table"], mw.get("final_norm_w"), mw["final_w"],
-                       mw["final_b"], dims.eps)
+                       mw["final_b"], dims.eps, rnd=rnd)
 
 
 # ----------------------------------------------------------------------------------------------

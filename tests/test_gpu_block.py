@@ -3,14 +3,16 @@
 Sizes: the tiny fp32 block and micro shapes with ragged tails are compared element by element;
 the full-size 512^2 block in full; the 1024^2 pair and the 2048^2 long block on seeded row samples
 (keys and values of every row enter each sampled row's attention, so the sample still checks the
-whole key range). Tolerances: max|gpu - oracle| / rms(oracle) <= 1e-4 (fp32) and <= 2e-2 (bf16).
+whole key range). Tolerances on max|gpu - oracle| / rms(oracle): fp32 <= 1e-4 against the exact
+oracle; bf16 <= 2e-2 against the oracle with bf16 operands, and against the exact oracle no worse
+than that oracle's own bf16-vs-exact deviation (tests/k2_testutil.parity).
 """
 import numpy as np
 import pytest
 
 from flow_matching_diffusion_amd import synth as S
 from oracle import k2_oracle as O
-from tests.k2_testutil import TOL, device, gpu_block, rel_err, temb_for, workload
+from tests.k2_testutil import gpu_block, parity, rel_err, temb_for, workload
 
 pytestmark = pytest.mark.gpu
 
@@ -18,13 +20,11 @@ pytestmark = pytest.mark.gpu
 def _check(wl, inp, rows=None, tag=""):
     temb = temb_for(wl, inp)
     got = gpu_block(wl, inp, temb)
-    ref = O.block_forward(inp["h"], temb, inp["position_ids"], inp["mask"], inp["weights"], wl.dims, wl.T, rows=rows)
     if rows is not None:
         got = got[:, rows]
-    err, rms = rel_err(got, ref)
-    print(f"{tag or wl.name}: max rel err {err:.3e}, rms rel err {rms:.3e}", flush=True)
-    assert np.all(np.isfinite(got))
-    assert err <= TOL[wl.dtype], f"{tag or wl.name}: {err:.3e} > {TOL[wl.dtype]}"
+    fn = lambda rnd: O.block_forward(inp["h"], temb, inp["position_ids"], inp["mask"], inp["weights"], wl.dims, wl.T,
+                                     rows=rows, rnd=rnd)
+    parity(tag or wl.name, wl.dtype, got, fn)
     return got
 
 

@@ -586,3 +586,41 @@ def test_block_flops_full_size():
     wl = S.WORKLOADS["block1024"]
     f = O.block_flops(d, wl.B, wl.L, [wl.N + v for v in wl.valid])
     assert abs(f - 8.9650e12) / 8.9650e12 < 1e-4
+
+
+# ----------------------------------------------------------------------------------------------
+# bf16 operand rounding (the bf16 model's operand precision)
+# ----------------------------------------------------------------------------------------------
+def test_bf16_round_known_values():
+    # bf16 keeps 7 mantissa bits: spacing 2^-7 at 1.0; halfway cases go to the even mantissa
+    v = np.array([1.0, 1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -12, -2.5, 3.0e38, 1e-40, 0.0])
+    r = O.bf16_round(v)
+    np.testing.assert_array_equal(r[:4], [1.0, 1.0, 1 + 2 ** -6, 1 + 2 ** -7])
+    assert r[4] == -2.5 and r[7] == 0.0
+
+
+def test_bf16_round_matches_library_conversion():
+    x = np.random.default_rng(2).standard_normal(100000).astype(np.float32) * 37
+    ref = torch.from_numpy(x).to(torch.bfloat16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(O.bf16_round(x), ref)
+
+
+def test_block_bf16_operand_mode():
+    wl, inp = micro_inputs(seed=61)
+    args = (inp["h"], inp["temb"], inp["position_ids"], inp["mask"], inp["weights"], MICRO, wl.T)
+    exact = O.block_forward(*args)
+    np.testing.assert_array_equal(O.block_forward(*args, rnd=lambda x: x), exact)
+    b = O.block_forward(*args, rnd=O.bf16_round)
+    rel = np.abs(b - exact).max() / np.sqrt(np.mean(exact ** 2))
+    assert 1e-5 < rel < 5e-2
+    # rounding every operand point to bf16 equals rounding the same inputs of the exact steps:
+    # with weights, h and temb already bf16-representable, zero gates still give the identity
+    w = dict(inp["weights"])
+    H = MICRO.hidden
+    tab = w["scale_shift_table"].astype(np.float64).copy()
+    tab[2] = -inp["temb"][0, 2 * H:3 * H]
+    tab[5] = -inp["temb"][0, 5 * H:6 * H]
+    w["scale_shift_table"] = tab
+    got = O.block_forward(inp["h"][:1], inp["temb"][:1], inp["position_ids"], inp["mask"][:1], w, MICRO, wl.T,
+                          rnd=O.bf16_round)
+    np.testing.assert_array_equal(got, inp["h"][:1].astype(np.float64))
