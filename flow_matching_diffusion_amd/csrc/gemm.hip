@@ -28,7 +28,9 @@
 namespace k2 {
 
 // ---------------------------------------------------------------------------------------------
-// Weight-row maps: global row n of the (virtual) weight matrix -> pointer to its K elements
+// Weight-row maps. The loader moves weight rows in aligned groups of G rows (G divides 64); every
+// group lies inside one weight matrix, so group(n) returns that matrix's pointer at virtual row n
+// and how many of the group's rows exist there (rows past the end read as zero).
 // ---------------------------------------------------------------------------------------------
 template <typename T>
 struct BSegs {
@@ -36,12 +38,12 @@ struct BSegs {
   int start[5];
   int nseg;
   int ldb;
-  __device__ __forceinline__ const T* row(int n) const {
-    if (n >= start[nseg]) return nullptr;
+  __device__ __forceinline__ const T* group(int n, int& nvalid) const {
     int s = 0;
 #pragma unroll
     for (int i = 1; i < 4; ++i)
       if (i < nseg && n >= start[i]) s = i;
+    nvalid = start[s + 1] - n;
     return p[s] + (size_t)(n - start[s]) * ldb;
   }
 };
@@ -52,13 +54,13 @@ struct BSwiglu {
   const T* up;
   int I;
   int ldb;
-  __device__ __forceinline__ const T* row(int n) const {
+  __device__ __forceinline__ const T* group(int n, int& nvalid) const {
     constexpr int HALF = WN / 2;
     const int per = n / WN, jj = n - per * WN;
     const bool is_up = jj >= HALF;
     const int col = per * HALF + (is_up ? jj - HALF : jj);
-    if (col >= I) return nullptr;
-    return (is_up ? up : gate) + (size_t)col * ldb;
+    nvalid = I - col;
+    return (is_up ? up : gate) + (size_t)(col < I ? col : 0) * ldb;
   }
 };
 
@@ -251,6 +253,18 @@ __device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_m, int ti
 // ---------------------------------------------------------------------------------------------
 // Main loop
 // ---------------------------------------------------------------------------------------------
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;  // offset past every resource: the load returns zeros
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, size_t bytes) {
+  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 template <typename T, int BM, int BN, int WM, int WN, class BMap, class Epi>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap, Epi epi) {
@@ -260,9 +274,9 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
   constexpr int BK = CPR * EPC;        // bf16: 64, fp32: 32
   constexpr int FC = 8 / EPC;          // chunks per 8-element fragment
   constexpr int KS = BK / 32;          // 32-wide k chunks per slab
-  constexpr int RSTEP = NT / CPR;      // LDS rows covered by one pass of the workgroup
+  constexpr int RSTEP = NT / CPR;      // rows moved by one load instruction of the workgroup
   constexpr int A_LD = BM / RSTEP, B_LD = BN / RSTEP;
-  static_assert(BM % RSTEP == 0 && BN % RSTEP == 0, "tile/thread mismatch");
+  static_assert(BM % RSTEP == 0 && BN % RSTEP == 0 && 64 % RSTEP == 0, "tile/thread mismatch");
   constexpr int MI = WM / 16, NJ = WN / 16;
   typedef typename FragOf<T>::type Frag;
 
@@ -275,22 +289,30 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
   tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
-  // Every chunk this thread moves sits in column c of rows rbase + i * RSTEP.
-  const int c = tid & (CPR - 1), rbase = tid / CPR;
-  const T* a_src[A_LD];
-  const T* b_src[B_LD];
+  // Thread tid moves chunk column c of rows r + i * RSTEP (i < A_LD / B_LD) of each slab.
+  const int c = tid & (CPR - 1), r = tid / CPR;
+  const rsrc_t ra_src = make_rsrc(A + (size_t)m0 * lda, (size_t)(M - m0) * lda * sizeof(T));
+  rsrc_t rb_src[B_LD];
+#pragma unroll
+  for (int i = 0; i < B_LD; ++i) {
+    const int n = n0 + i * RSTEP;
+    int nvalid = 0;
+    const T* base = n < Ntot ? bmap.group(n, nvalid) : A;
+    nvalid = n < Ntot ? (nvalid < 0 ? 0 : (nvalid > RSTEP ? RSTEP : nvalid)) : 0;
+    rb_src[i] = make_rsrc(base, (size_t)nvalid * bmap.ldb * sizeof(T));
+  }
+  uint32_t a_off[A_LD], b_off;
   int a_dst[A_LD], b_dst[B_LD];
 #pragma unroll
   for (int i = 0; i < A_LD; ++i) {
-    const int row = rbase + i * RSTEP, gm = m0 + row;
-    a_src[i] = gm < M ? A + (size_t)gm * lda + c * EPC : nullptr;
+    const int row = r + i * RSTEP;
+    a_off[i] = (uint32_t)(row * lda + c * EPC) * sizeof(T);
     a_dst[i] = row * CPR + (c ^ swz8(row));
   }
+  b_off = (uint32_t)(r * bmap.ldb + c * EPC) * sizeof(T);
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
-    const int row = rbase + i * RSTEP, gn = n0 + row;
-    const T* p = gn < Ntot ? bmap.row(gn) : nullptr;
-    b_src[i] = p ? p + c * EPC : nullptr;
+    const int row = r + i * RSTEP;
     b_dst[i] = (BM + row) * CPR + (c ^ swz8(row));
   }
 
@@ -301,24 +323,29 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
     for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   uint4 ra[A_LD], rb[B_LD];
-  const uint4 zero = {0u, 0u, 0u, 0u};
   const int nk = (K + BK - 1) / BK;
 
-  auto gload = [&](int kt) {
-    const int k0 = kt * BK;
-    const bool kin = k0 + c * EPC < K;
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) ra[i] = (a_src[i] && kin) ? *(const uint4*)(a_src[i] + k0) : zero;
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) rb[i] = (b_src[i] && kin) ? *(const uint4*)(b_src[i] + k0) : zero;
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_LD; ++i) smem[buf][a_dst[i]] = ra[i];
-#pragma unroll
-    for (int i = 0; i < B_LD; ++i) smem[buf][b_dst[i]] = rb[i];
-  };
-  auto compute = [&](int buf) {
+#define K2_GLOAD(kt)                                                                         \
+  do {                                                                                       \
+    const int k0_ = (kt) * BK;                                                               \
+    const bool kin_ = k0_ + c * EPC < K;                                                     \
+    const uint32_t kb_ = (uint32_t)k0_ * sizeof(T);                                          \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) ra[i] = bload(ra_src, kin_ ? a_off[i] + kb_ : kOOB); \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) rb[i] = bload(rb_src[i], kin_ ? b_off + kb_ : kOOB); \
+  } while (0)
+
+#define K2_SSTORE(buf)                                                        \
+  do {                                                                        \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) smem[buf][a_dst[i]] = ra[i]; \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) smem[buf][b_dst[i]] = rb[i]; \
+  } while (0)
+
+  K2_GLOAD(0);
+  K2_SSTORE(0);
+  __syncthreads();
+  for (int kt = 0; kt < nk; ++kt) {
+    const int buf = kt & 1;
+    if (kt + 1 < nk) K2_GLOAD(kt + 1);
     const uint4* sA = smem[buf];
     const uint4* sB = smem[buf] + BM * CPR;
 #pragma unroll
@@ -342,17 +369,11 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
 #pragma unroll
         for (int j = 0; j < NJ; ++j) acc[i][j] = mma16(acc[i][j], af[i], bfr[j]);
     }
-  };
-
-  gload(0);
-  sstore(0);
-  __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kt + 1);
-    compute(kt & 1);
-    if (kt + 1 < nk) sstore((kt + 1) & 1);
+    if (kt + 1 < nk) K2_SSTORE(buf ^ 1);
     __syncthreads();
   }
+#undef K2_GLOAD
+#undef K2_SSTORE
   epi.template apply<MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M);
 }
 
