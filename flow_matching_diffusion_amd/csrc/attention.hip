@@ -8,38 +8,82 @@
 //
 // One workgroup = (batch row, kv head, block of query rows). Its 4 waves cover the G query heads
 // that share the kv head, 64 query rows each, so every K/V tile staged in LDS serves all G heads.
-// Per 64-key tile a wave computes S^T = K Q^T (keys along MFMA rows, queries along columns): the
+// Per key tile a wave computes S^T = K Q^T (keys along MFMA rows, queries along columns): the
 // online-softmax statistics of a query then live in one lane column and need only two cross-group
 // shuffles. K rows are fed to the MFMA in a permuted order such that the lane group that ends up
-// holding S^T rows 4g..4g+3 of two adjacent 16-key blocks holds 8 consecutive keys; those 8
+// holding S^T rows 4g..4g+3 of the tile's two 16-key blocks holds 8 consecutive keys; those 8
 // probabilities are exactly the B fragment of O^T += V^T P^T, so P never leaves registers. V comes
 // in transposed (written that way by the projection epilogue) so V^T fragments are contiguous.
-// Tiles whose keys are all padding are skipped.
+//
+// Keys come in tiles of 32. Key validity of the text tiles is computed once per workgroup into
+// LDS; tiles whose keys are all padding are skipped, and only tiles holding padding or the sequence
+// end pay for masking.
+// The running maximum is rescaled lazily: O and the row sums are only rescaled when some query's
+// maximum grew by more than 2^8 since the last rescale (exp2 of scores up to 2^8 stays exact in
+// the float32 sum and the bf16 P operand), which the final division by the row sum undoes exactly.
 #include "k2_device.h"
 #include "k2_kernels.h"
 
 namespace k2 {
 
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+
+__device__ __forceinline__ rsrc_t attn_rsrc(const void* p, size_t bytes) {
+  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+__device__ __forceinline__ uint4 attn_bload(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
 // 16 keys read together by a lane group (key = 32c + 8(r/4) + 4e + r%4) -> distinct chunk slots.
 __device__ __forceinline__ int swz_key(int key) { return (key & 3) | ((key >> 1) & 12); }
+
+constexpr int kMaxTextTiles = 512;  // 32-key text tiles: text tokens up to 16384
+
+// Keep the first n (0 < n < EPC) elements of a 16-byte chunk of EPC elements, zero the rest.
+template <int EPC>
+__device__ __forceinline__ uint4 keep_first(uint4 v, int n) {
+  constexpr int BITS = 128 / EPC;  // bits per element: 16 (bf16) or 32 (fp32)
+  uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int e = 0; e < 32 / BITS; ++e)
+      if (i * (32 / BITS) + e < n) m |= (BITS == 32 ? 0xFFFFFFFFu : (0xFFFFu << (e * BITS)));
+    w[i] &= m;
+  }
+  return uint4{w[0], w[1], w[2], w[3]};
+}
+
+// V^T tile rows hold the 32 keys of a tile: 64 bytes (bf16, 4 chunks) or 128 bytes (fp32, 8 chunks).
+// 16 consecutive rows read at one chunk land in distinct bank slots (128- or 256-byte LDS cycles).
+template <int CPR>
+__device__ __forceinline__ int swz_v(int d) {
+  return CPR == 4 ? (((d >> 2) ^ (d >> 1)) & 3) : (swz8(d) & (CPR - 1));
+}
 
 template <typename T, int HD, int G>
 __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2) {
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int FC = 8 / EPC;          // chunks per 8-element fragment
-  constexpr int KT = 64;               // keys per tile
+  constexpr int KT = 32;               // keys per tile
   constexpr int CPRK = HD / EPC;       // chunks per key row of the K tile
   constexpr int CPRV = KT / EPC;       // chunks per head-dim row of the V^T tile
   constexpr int K_CH = KT * CPRK, V_CH = HD * CPRV;
   constexpr int K_LD = K_CH / 256, V_LD = V_CH / 256;
+  static_assert(K_CH % 256 == 0 && V_CH % 256 == 0, "tile/thread mismatch");
   constexpr int WPH = 4 / G;           // waves per query head
   constexpr int BQ = 64 * WPH;         // query rows per workgroup
   constexpr int NHB = HD / 16;
   constexpr int NKS = HD / 32;
+  constexpr float kRescale = 8.0f;     // log2 growth of the maximum that forces a rescale
   typedef typename FragOf<T>::type Frag;
 
   __shared__ uint4 sK[2][K_CH];
   __shared__ uint4 sV[2][V_CH];
+  __shared__ uint32_t sBits[kMaxTextTiles];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -47,13 +91,23 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
   const int q0 = blockIdx.x * BQ + (wave / G) * 64;
   const int L = p.L, T_ = p.T;
   const int ldq = p.nh * HD, ldk = p.nkv * HD;
-  const T* qp = (const T*)p.q;
-  const T* kp = (const T*)p.k;
-  const T* vp = (const T*)p.vt + (size_t)(b * p.nkv + kvh) * HD * p.ldvt;
-  const uint8_t* mrow = p.mask ? p.mask + (size_t)b * T_ : nullptr;
   const uint4 zero = {0u, 0u, 0u, 0u};
 
+  // Validity bits of the 32-key tiles that hold text keys (bit j: key t*32 + j is a valid key);
+  // one wave ballot covers two tiles.
+  const int ntt = (T_ + KT - 1) / KT;
+  for (int u = wave; 2 * u < ntt; u += 4) {
+    const int key = u * 64 + lane;
+    const bool ok = key < L && (key >= T_ || !p.mask || p.mask[(size_t)b * T_ + key] != 0);
+    const uint64_t bits = __ballot(ok);
+    if (lane == 0) {
+      sBits[2 * u] = (uint32_t)bits;
+      if (2 * u + 1 < ntt) sBits[2 * u + 1] = (uint32_t)(bits >> 32);
+    }
+  }
+
   // Q^T fragments stay in registers for the whole key loop.
+  const T* qp = (const T*)p.q;
   Frag qf[4][NKS];
 #pragma unroll
   for (int qb = 0; qb < 4; ++qb) {
@@ -68,48 +122,39 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
       }
   }
 
-  auto key_ok = [&](int key) -> bool { return key < L && (key >= T_ || !mrow || mrow[key] != 0); };
-  const int nt = (L + KT - 1) / KT;
-  auto next_needed = [&](int t) -> int {  // wave-uniform; identical in every wave
-    for (; t < nt; ++t)
-      if (__ballot(key_ok(t * KT + lane))) break;
-    return t;
-  };
+  // K rows of this (batch, kv head); V^T rows (head dims) of length ldvt.
+  const rsrc_t kr = attn_rsrc((const T*)p.k + ((size_t)b * L * ldk + kvh * HD),
+                              ((size_t)(L - 1) * ldk + HD) * sizeof(T));
+  const T* vbase = (const T*)p.vt + (size_t)(b * p.nkv + kvh) * HD * p.ldvt;
+  const rsrc_t vr = attn_rsrc(vbase, (size_t)HD * p.ldvt * sizeof(T));
+  const int kc = tid % CPRK, krow = tid / CPRK;  // K: rows krow + i * KSTEP
+  const int vc = tid % CPRV, vrow = tid / CPRV;  // V^T: rows vrow + i * VSTEP
+  constexpr int KSTEP = 256 / CPRK, VSTEP = 256 / CPRV;
 
   uint4 rk[K_LD], rv[V_LD];
-  auto gload = [&](int t) {
-    const int t0 = t * KT;
-#pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int qc = tid + i * 256, key = qc / CPRK, c = qc % CPRK, gk = t0 + key;
-      rk[i] = gk < L ? *(const uint4*)(kp + (size_t)(b * L + gk) * ldk + kvh * HD + c * EPC) : zero;
-    }
-#pragma unroll
-    for (int i = 0; i < V_LD; ++i) {
-      const int qc = tid + i * 256, d = qc / CPRV, c = qc % CPRV, k0 = t0 + c * EPC;
-      const T* src = vp + (size_t)d * p.ldvt + k0;
-      if (k0 + EPC <= L) {
-        rv[i] = *(const uint4*)src;
-      } else {
-        T tmp[EPC];
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) tmp[e] = (k0 + e < L) ? src[e] : to_t<T>(0.0f);
-        rv[i] = *(const uint4*)tmp;
-      }
-    }
-  };
-  auto sstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < K_LD; ++i) {
-      const int qc = tid + i * 256, key = qc / CPRK, c = qc % CPRK;
-      sK[buf][key * CPRK + (c ^ (swz_key(key) & (CPRK - 1)))] = rk[i];
-    }
-#pragma unroll
-    for (int i = 0; i < V_LD; ++i) {
-      const int qc = tid + i * 256, d = qc / CPRV, c = qc % CPRV;
-      sV[buf][d * CPRV + (c ^ (swz8(d) & (CPRV - 1)))] = rv[i];
-    }
-  };
+#define K2_ATT_GLOAD(t)                                                                            \
+  do {                                                                                             \
+    const int t0_ = (t) * KT;                                                                      \
+    _Pragma("unroll") for (int i = 0; i < K_LD; ++i)                                               \
+      rk[i] = attn_bload(kr, (uint32_t)(((t0_ + krow + i * KSTEP) * ldk + kc * EPC) * sizeof(T))); \
+    const int k0_ = t0_ + vc * EPC;                                                                \
+    _Pragma("unroll") for (int i = 0; i < V_LD; ++i) {                                             \
+      const uint32_t off_ = k0_ < L ? (uint32_t)(((vrow + i * VSTEP) * p.ldvt + k0_) * sizeof(T)) : 0x80000000u; \
+      rv[i] = attn_bload(vr, off_);                                                                \
+      if (k0_ + EPC > L && k0_ < L) rv[i] = keep_first<EPC>(rv[i], L - k0_);                        \
+    }                                                                                              \
+  } while (0)
+#define K2_ATT_SSTORE(buf)                                                                         \
+  do {                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < K_LD; ++i) {                                             \
+      const int key_ = krow + i * KSTEP;                                                           \
+      sK[buf][key_ * CPRK + (kc ^ (swz_key(key_) & (CPRK - 1)))] = rk[i];                          \
+    }                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < V_LD; ++i) {                                             \
+      const int d_ = vrow + i * VSTEP;                                                             \
+      sV[buf][d_ * CPRV + (vc ^ swz_v<CPRV>(d_))] = rv[i];                                         \
+    }                                                                                              \
+  } while (0)
 
   f32x4 o[NHB][4];
 #pragma unroll
@@ -123,19 +168,34 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
     l_i[qb] = 0.0f;
   }
 
-  auto compute = [&](int buf, int t) {
-    // S^T = K Q^T over this tile
-    f32x4 s[4][4];
+  __syncthreads();  // sBits ready
+  const int nt = (L + KT - 1) / KT;
+  int t = 0;
+  while (t < nt && t < ntt && sBits[t] == 0) ++t;
+  if (t < nt) {
+    K2_ATT_GLOAD(t);
+    K2_ATT_SSTORE(0);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (t < nt) {
+    int tn = t + 1;
+    while (tn < nt && tn < ntt && sBits[tn] == 0) ++tn;  // skip tiles of padding only
+    if (tn < nt) K2_ATT_GLOAD(tn);
+    const int t0 = t * KT;
+
+    // S^T = K Q^T over this tile: block kb, lane row 4g + r holds key 8g + 4kb + r
+    f32x4 s[2][4];
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) s[kb][qb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < NKS; ++ks) {
-      Frag kf[4];
+      Frag kf[2];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const int key = 32 * (kb >> 1) + 8 * (col >> 2) + 4 * (kb & 1) + (col & 3);
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = 8 * (col >> 2) + 4 * kb + (col & 3);
 #pragma unroll
         for (int f = 0; f < FC; ++f) {
           const int ch = ks * 4 * FC + grp * FC + f;
@@ -143,92 +203,91 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
         }
       }
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int qb = 0; qb < 4; ++qb) s[kb][qb] = mma16(s[kb][qb], kf[kb], qf[qb][ks]);
     }
 
-    // key validity of this tile, one bit per key
-    const int t0 = t * KT;
-    const uint64_t vbits = __ballot(key_ok(t0 + lane));
+    // scale to base 2; mask only tiles with padding or the sequence end
+    const uint32_t vbits = t < ntt ? sBits[t] : (t0 + KT <= L ? ~0u : ((1u << (L - t0)) - 1u));
+    if (vbits == ~0u) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int qb = 0; qb < 4; ++qb) s[kb][qb] *= scale_log2;
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const bool ok = (vbits >> (8 * grp + 4 * kb + r)) & 1u;
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb) s[kb][qb][r] = ok ? s[kb][qb][r] * scale_log2 : -INFINITY;
+        }
+    }
 
-    // online softmax (base 2), per query column
+    // online softmax with lazy rescaling
+    float mt[4];
+    bool grow = false;
 #pragma unroll
     for (int qb = 0; qb < 4; ++qb) {
       float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int kk = 32 * (kb >> 1) + 8 * grp + 4 * (kb & 1) + r;
-          const float v = ((vbits >> kk) & 1) ? s[kb][qb][r] * scale_log2 : -INFINITY;
-          s[kb][qb][r] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = across_groups_max(mx);
-      const float mnew = fmaxf(m_i[qb], mx);
-      const float base = mnew == -INFINITY ? 0.0f : mnew;
-      const float alpha = exp2f(m_i[qb] - base);
-      float rs = 0.0f;
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const float pv = exp2f(s[kb][qb][r] - base);
-          s[kb][qb][r] = pv;
-          rs += pv;
-        }
-      l_i[qb] = l_i[qb] * alpha + rs;
-      m_i[qb] = mnew;
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) o[hb][qb] *= alpha;
+        for (int r = 0; r < 4; ++r) mx = fmaxf(mx, s[kb][qb][r]);
+      mt[qb] = across_groups_max(mx);
+      grow |= mt[qb] > m_i[qb] + kRescale;
     }
-
-    // O^T += V^T P^T
-#pragma unroll
-    for (int c2 = 0; c2 < 2; ++c2) {
-      Frag pf[4];
+    if (__any(grow)) {
 #pragma unroll
       for (int qb = 0; qb < 4; ++qb) {
-        float tmp[8];
+        const float mnew = fmaxf(m_i[qb], mt[qb]);
+        const float alpha = m_i[qb] == -INFINITY ? 0.0f : exp2f(m_i[qb] - mnew);
+        l_i[qb] *= alpha;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          tmp[r] = s[2 * c2][qb][r];
-          tmp[4 + r] = s[2 * c2 + 1][qb][r];
-        }
-        pack8(pf[qb], tmp);
-      }
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) {
-        Frag vf;
-        const int d = hb * 16 + col;
-#pragma unroll
-        for (int f = 0; f < FC; ++f) {
-          const int ch = (c2 * 32 + 8 * grp) / EPC + f;
-          ((uint4*)&vf)[f] = sV[buf][d * CPRV + (ch ^ (swz8(d) & (CPRV - 1)))];
-        }
-#pragma unroll
-        for (int qb = 0; qb < 4; ++qb) o[hb][qb] = mma16(o[hb][qb], vf, pf[qb]);
+        for (int hb = 0; hb < NHB; ++hb) o[hb][qb] *= alpha;
+        m_i[qb] = mnew;
       }
     }
-  };
+    Frag pf[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const float base = m_i[qb] == -INFINITY ? 0.0f : m_i[qb];
+      float pv[8];
+      float rs = 0.0f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          pv[4 * kb + r] = exp2f(s[kb][qb][r] - base);
+          rs += pv[4 * kb + r];
+        }
+      l_i[qb] += rs;
+      pack8(pf[qb], pv);
+    }
 
-  int t = next_needed(0);
-  if (t < nt) {
-    gload(t);
-    sstore(0);
-  }
-  __syncthreads();
-  int buf = 0;
-  while (t < nt) {
-    const int tn = next_needed(t + 1);
-    if (tn < nt) gload(tn);
-    compute(buf, t);
-    if (tn < nt) sstore(buf ^ 1);
+    // O^T += V^T P^T: A = V^T rows (head dims), k slots = the lane group's 8 consecutive keys
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      Frag vf;
+      const int d = hb * 16 + col;
+#pragma unroll
+      for (int f = 0; f < FC; ++f) {
+        const int ch = grp * FC + f;
+        ((uint4*)&vf)[f] = sV[buf][d * CPRV + (ch ^ swz_v<CPRV>(d))];
+      }
+#pragma unroll
+      for (int qb = 0; qb < 4; ++qb) o[hb][qb] = mma16(o[hb][qb], vf, pf[qb]);
+    }
+
+    if (tn < nt) K2_ATT_SSTORE(buf ^ 1);
     __syncthreads();
     buf ^= 1;
     t = tn;
   }
+#undef K2_ATT_GLOAD
+#undef K2_ATT_SSTORE
 
   // normalise, gate, store: lane holds 4 consecutive head-dim values of one query row
   const T* gp = (const T*)p.g;
@@ -256,6 +315,7 @@ template <typename T, int HD, int G>
 static hipError_t launch_attn(const AttnArgs& p, hipStream_t s) {
   constexpr int BQ = 64 * (4 / G);
   if (p.L <= 0 || p.B <= 0) return hipSuccess;
+  if (p.T > kMaxTextTiles * 32) return hipErrorInvalidValue;
   dim3 grid((p.L + BQ - 1) / BQ, p.nkv, p.B);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
   hipLaunchKernelGGL((attn_kernel<T, HD, G>), grid, dim3(256), 0, s, p, scale_log2);

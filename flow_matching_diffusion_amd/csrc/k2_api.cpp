@@ -122,6 +122,7 @@ int check_sizes(int B, int T, int N) {
   if (B <= 0 || T < 0 || N < 0 || T + N <= 0) return fail(K2_ERR_SHAPE, "need B >= 1, T >= 0, N >= 0, T + N >= 1");
   if (B > 65535) return fail(K2_ERR_SHAPE, "B must be <= 65535");
   if ((long long)T + N > (1 << 24)) return fail(K2_ERR_SHAPE, "sequence too long");
+  if (T > 16384) return fail(K2_ERR_SHAPE, "at most 16384 text tokens (got %d)", T);
   return K2_OK;
 }
 
@@ -354,6 +355,7 @@ int check_text(const k2_text_cfg* c, const k2_text_weights* w, int B, int T) {
   }
   if (B <= 0 || T <= 0) return fail(K2_ERR_SHAPE, "text fusion needs B >= 1 and T >= 1");
   if ((long long)B * T > 65535) return fail(K2_ERR_SHAPE, "B * T must be <= 65535");
+  if (T > 16384) return fail(K2_ERR_SHAPE, "at most 16384 text tokens (got %d)", T);
   return K2_OK;
 }
 

@@ -53,7 +53,7 @@ typedef enum { K2_F32 = 0, K2_BF16 = 1 } k2_dtype;
  * Requirements checked by k2_block_forward: hidden == num_heads * head_dim ([API]: hidden size is
  * head dim times heads); num_heads % num_kv_heads == 0 with num_heads / num_kv_heads in {1, 2, 4};
  * head_dim in {64, 128}; axes_dims even and summing to head_dim ([ARTICLE] §三); hidden and
- * intermediate multiples of 64.
+ * intermediate multiples of 8; B <= 65535; T <= 16384 text tokens.
  * --------------------------------------------------------------------------------------------- */
 typedef struct {
   int hidden;        /* 6144 */
