@@ -9,7 +9,8 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libk2.so")
 
 K2_F32, K2_BF16 = 0, 1
 STATUS = {0: "K2_OK", -1: "K2_ERR_NULL", -2: "K2_ERR_SHAPE", -3: "K2_ERR_CONFIG", -4: "K2_ERR_DTYPE",
-          -5: "K2_ERR_WORKSPACE", -6: "K2_ERR_HIP"}
+          -5: "K2_ERR_WORKSPACE", -6: "K2_ERR_HIP",
+          -7: "K2_ERR_ALIGN"}
 
 BLOCK_WEIGHT_FIELDS = ("scale_shift_table", "norm1_w", "norm2_w", "norm_q_w", "norm_k_w", "to_q", "to_k", "to_v",
                        "to_gate", "to_out", "ff_gate", "ff_up", "ff_down")

@@ -65,35 +65,85 @@ struct BSwiglu {
 };
 
 // ---------------------------------------------------------------------------------------------
-// Epilogues. acc[i][j][r] holds C[row0 + 16 i + 4 (lane / 16) + r][col0 + 16 j + lane % 16].
+// Accumulator layouts. Both main loops feed the matrix cores with the weight fragment as the first
+// operand and the activation fragment as the second, so the instruction computes a block of C^T and
+// each lane ends up holding ONE output row and runs of 4 consecutive output columns:
+//   16x16 (fp32 path, v_mfma_f32_16x16x4f32):   lane holds row lane%16, columns 4*(lane/16) + e
+//   32x32 (bf16 path, v_mfma_f32_32x32x16_bf16): lane holds row lane%32, columns 8*q + 4*(lane/32) + e
+// with e < 4 and q < NQ. A wave's tile is MI x NJ blocks of BS x BS, and
+//   acc[i][j][4*q + e] = C[row0 + row(i, lane)][col0 + col(j, q, lane) + e].
+// rowsum() adds over the lanes holding the same row.
 // ---------------------------------------------------------------------------------------------
+template <int BS> struct Lay;
+template <> struct Lay<16> {
+  typedef f32x4 F;
+  static constexpr int NQ = 1;
+  __device__ static __forceinline__ int row(int i, int lane) { return 16 * i + (lane & 15); }
+  __device__ static __forceinline__ int col(int j, int q, int lane) { return 16 * j + 4 * (lane >> 4); }
+  __device__ static __forceinline__ float rowsum(float v) {
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+  }
+};
+template <> struct Lay<32> {
+  typedef f32x16 F;
+  static constexpr int NQ = 4;
+  __device__ static __forceinline__ int row(int i, int lane) { return 32 * i + (lane & 31); }
+  __device__ static __forceinline__ int col(int j, int q, int lane) { return 32 * j + 8 * q + 4 * (lane >> 5); }
+  __device__ static __forceinline__ float rowsum(float v) { return v + __shfl_xor(v, 32); }
+};
+
+template <class F>
+__device__ __forceinline__ float4 quad(const F& a, int q) {
+  return make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+}
+__device__ __forceinline__ float4 ld4(const float* p) { return *reinterpret_cast<const float4*>(p); }
+__device__ __forceinline__ void st4(float* p, float4 v) { *reinterpret_cast<float4*>(p) = v; }
+__device__ __forceinline__ void st4(bf16* p, float4 v) {
+  bf16x4 t;
+  t[0] = (bf16)v.x; t[1] = (bf16)v.y; t[2] = (bf16)v.z; t[3] = (bf16)v.w;
+  *reinterpret_cast<bf16x4*>(p) = t;
+}
+__device__ __forceinline__ float4 fma4(float4 g, float4 a, float4 h) {
+  return make_float4(h.x + g.x * a.x, h.y + g.y * a.y, h.z + g.z * a.z, h.w + g.w * a.w);
+}
+
+// ---------------------------------------------------------------------------------------------
+// Epilogues: every access moves 4 consecutive columns (N, I, ld* and all column offsets are
+// multiples of 4; the entry points require 16-byte aligned activation, bias and output pointers).
+// ---------------------------------------------------------------------------------------------
+// hout = hin + gate[batch] * acc (gated residual; gate NULL means 1). hin may alias hout.
 template <typename T>
 struct EpiResid {
   const float* hin;
   float* hout;
   const float* gate;
   int gate_stride, L, N;
-  template <int MI, int NJ>
-  __device__ __forceinline__ void apply(const f32x4 (&acc)[MI][NJ], int row0, int col0, int lane, int M) const {
+  template <class LY, int MI, int NJ>
+  __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
+                                        int M) const {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int m = row0 + LY::row(i, lane);
+      if (m >= M) continue;
+      const float* gb = gate ? gate + (size_t)(m / L) * gate_stride : nullptr;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = row0 + i * 16 + (lane >> 4) * 4 + r;
-        if (m >= M) continue;
-        const float* gb = gate ? gate + (size_t)(m / L) * gate_stride : nullptr;
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int n = col0 + j * 16 + (lane & 15);
+        for (int q = 0; q < LY::NQ; ++q) {
+          const int n = col0 + LY::col(j, q, lane);
           if (n >= N) continue;
           const size_t idx = (size_t)m * N + n;
-          const float gv = gb ? gb[n] : 1.0f;
-          hout[idx] = hin[idx] + gv * acc[i][j][r];
+          const float4 g = gb ? ld4(gb + n) : make_float4(1.f, 1.f, 1.f, 1.f);
+          st4(hout + idx, fma4(g, quad(acc[i][j], q), ld4(hin + idx)));
         }
-      }
+    }
   }
 };
 
+// acc + bias into a float output and/or act(acc + bias) into an operand-dtype output, with input
+// row m written to output row (m / rpb) * orpb + ooff + m % rpb.
 template <typename T>
 struct EpiPlain {
   const float* bias;
@@ -101,51 +151,66 @@ struct EpiPlain {
   int ldf;
   T* outt;
   int ldt, act, N, rpb, orpb, ooff;
-  template <int MI, int NJ>
-  __device__ __forceinline__ void apply(const f32x4 (&acc)[MI][NJ], int row0, int col0, int lane, int M) const {
+  template <class LY, int MI, int NJ>
+  __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
+                                        int M) const {
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int m = row0 + LY::row(i, lane);
+      if (m >= M) continue;
+      const size_t orow = (size_t)(m / rpb) * orpb + ooff + (m % rpb);
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = row0 + i * 16 + (lane >> 4) * 4 + r;
-        if (m >= M) continue;
-        const size_t orow = (size_t)(m / rpb) * orpb + ooff + (m % rpb);
+      for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int j = 0; j < NJ; ++j) {
-          const int n = col0 + j * 16 + (lane & 15);
+        for (int q = 0; q < LY::NQ; ++q) {
+          const int n = col0 + LY::col(j, q, lane);
           if (n >= N) continue;
-          const float v = acc[i][j][r] + (bias ? bias[n] : 0.0f);
-          if (outf) outf[orow * ldf + n] = v;
-          if (outt) outt[orow * ldt + n] = to_t<T>(act ? gelu_tanhf_(v) : v);
+          float4 v = quad(acc[i][j], q);
+          if (bias) {
+            const float4 b4 = ld4(bias + n);
+            v.x += b4.x; v.y += b4.y; v.z += b4.z; v.w += b4.w;
+          }
+          if (outf) st4(outf + orow * ldf + n, v);
+          if (outt) {
+            if (act) v = make_float4(gelu_tanhf_(v.x), gelu_tanhf_(v.y), gelu_tanhf_(v.z), gelu_tanhf_(v.w));
+            st4(outt + orow * ldt + n, v);
+          }
         }
-      }
+    }
   }
 };
 
+// a = silu(gate) * up; the wave's first WN/2 columns are gate, the last WN/2 the matching up columns.
 template <typename T, int WN>
 struct EpiSwiglu {
   T* a;
   int I;
-  template <int MI, int NJ>
-  __device__ __forceinline__ void apply(const f32x4 (&acc)[MI][NJ], int row0, int col0, int lane, int M) const {
-    static_assert(NJ * 16 == WN, "wave width");
+  template <class LY, int MI, int NJ>
+  __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
+                                        int M) const {
+    static_assert(NJ * (LY::NQ == 1 ? 16 : 32) == WN, "wave width");
     const int cbase = (col0 / WN) * (WN / 2);
 #pragma unroll
-    for (int i = 0; i < MI; ++i)
+    for (int i = 0; i < MI; ++i) {
+      const int m = row0 + LY::row(i, lane);
+      if (m >= M) continue;
 #pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int m = row0 + i * 16 + (lane >> 4) * 4 + r;
-        if (m >= M) continue;
+      for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
-        for (int j = 0; j < NJ / 2; ++j) {
-          const int col = cbase + j * 16 + (lane & 15);
-          if (col >= I) continue;
-          a[(size_t)m * I + col] = to_t<T>(siluf_(acc[i][j][r]) * acc[i][j + NJ / 2][r]);
+        for (int q = 0; q < LY::NQ; ++q) {
+          const int c = cbase + LY::col(j, q, lane);
+          if (c >= I) continue;
+          const float4 g = quad(acc[i][j], q), u = quad(acc[i][j + NJ / 2], q);
+          st4(a + (size_t)m * I + c, make_float4(siluf_(g.x) * u.x, siluf_(g.y) * u.y, siluf_(g.z) * u.z,
+                                                 siluf_(g.w) * u.w));
         }
-      }
+    }
   }
 };
 
+// Fused QKV + output-gate projection: per head of q and k, RMSNorm over the head's HD columns
+// (weight 1 + w) then rotary embedding on interleaved pairs (2c, 2c+1); v goes out transposed
+// (vt[b][kv head][d][token], leading dimension ldvt); the gate projection goes out as is.
 template <typename T, int HD>
 struct EpiQkvg {
   T* q;
@@ -158,14 +223,16 @@ struct EpiQkvg {
   const float* rs;
   int nq, nk, L, ldvt;
   float eps;
-  template <int MI, int NJ>
-  __device__ __forceinline__ void apply(const f32x4 (&acc)[MI][NJ], int row0, int col0, int lane, int M) const {
-    constexpr int HB = HD / 16;  // 16-column blocks per head
+  template <class LY, int MI, int NJ>
+  __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
+                                        int M) const {
+    constexpr int BS = LY::NQ == 1 ? 16 : 32;
+    constexpr int HB = HD / BS;  // column blocks per head
     static_assert(NJ % HB == 0, "a wave covers whole heads");
     const int ntot = 2 * nq + 2 * nk;
 #pragma unroll
     for (int h0 = 0; h0 < NJ; h0 += HB) {
-      const int nh0 = col0 + h0 * 16;  // first column of this head (wave-uniform)
+      const int nh0 = col0 + h0 * BS;  // first column of this head (wave-uniform)
       if (nh0 >= ntot) break;
       const int seg = nh0 < nq ? 0 : nh0 < nq + nk ? 1 : nh0 < nq + 2 * nk ? 2 : 3;
       if (seg <= 1) {
@@ -173,63 +240,65 @@ struct EpiQkvg {
         const int ld = seg == 0 ? nq : nk;
         const int cb = seg == 0 ? nh0 : nh0 - nq;
         const float* wn = seg == 0 ? wnq : wnk;
-        float wmul[HB];
 #pragma unroll
-        for (int jj = 0; jj < HB; ++jj) wmul[jj] = 1.0f + (wn ? wn[jj * 16 + (lane & 15)] : 0.0f);
+        for (int i = 0; i < MI; ++i) {
+          const int m = row0 + LY::row(i, lane);  // every lane sharing this row takes the same branches
+          float ss = 0.0f;
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+          for (int jj = 0; jj < HB; ++jj)
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = row0 + i * 16 + (lane >> 4) * 4 + r;
-            float ss = 0.0f;
+            for (int r = 0; r < 4 * LY::NQ; ++r) ss += acc[i][h0 + jj][r] * acc[i][h0 + jj][r];
+          ss = LY::rowsum(ss);
+          const float inv = rsqrtf(ss * (1.0f / HD) + eps);
+          const int l = (m < M ? m : 0) % L;
 #pragma unroll
-            for (int jj = 0; jj < HB; ++jj) ss += acc[i][h0 + jj][r] * acc[i][h0 + jj][r];
-            ss = group16_sum(ss);
-            const float inv = rsqrtf(ss * (1.0f / HD) + eps);
-            const int l = (m < M ? m : 0) % L;
+          for (int jj = 0; jj < HB; ++jj)
 #pragma unroll
-            for (int jj = 0; jj < HB; ++jj) {
-              const int d = jj * 16 + (lane & 15);
-              float y = acc[i][h0 + jj][r] * inv * wmul[jj];
-              const float partner = __shfl_xor(y, 1);
+            for (int qq = 0; qq < LY::NQ; ++qq) {
+              const int d = LY::col(jj, qq, lane);
+              float4 y = quad(acc[i][h0 + jj], qq);
+              float4 w4 = wn ? ld4(wn + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+              y.x *= inv * (1.0f + w4.x); y.y *= inv * (1.0f + w4.y);
+              y.z *= inv * (1.0f + w4.z); y.w *= inv * (1.0f + w4.w);
               if (rc) {
-                const float c = rc[(size_t)l * (HD / 2) + (d >> 1)];
-                const float s = rs[(size_t)l * (HD / 2) + (d >> 1)];
-                y = (d & 1) ? partner * s + y * c : y * c - partner * s;
+                const float2 c2 = *reinterpret_cast<const float2*>(rc + (size_t)l * (HD / 2) + (d >> 1));
+                const float2 s2 = *reinterpret_cast<const float2*>(rs + (size_t)l * (HD / 2) + (d >> 1));
+                y = make_float4(y.x * c2.x - y.y * s2.x, y.y * c2.x + y.x * s2.x,
+                                y.z * c2.y - y.w * s2.y, y.w * c2.y + y.z * s2.y);
               }
-              if (m < M) dst[(size_t)m * ld + cb + d] = to_t<T>(y);
+              if (m < M) st4(dst + (size_t)m * ld + cb + d, y);
             }
-          }
+        }
       } else if (seg == 2) {
         const int kvh = (nh0 - nq - nk) / HD;
         const int nkvh = nk / HD;
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i) {
+          const int m = row0 + LY::row(i, lane);
+          if (m >= M) continue;
+          const int b = m / L, l = m - b * L;
+          T* base = vt + (size_t)(b * nkvh + kvh) * HD * ldvt + l;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = row0 + i * 16 + (lane >> 4) * 4 + r;
-            if (m >= M) continue;
-            const int b = m / L, l = m - b * L;
+          for (int jj = 0; jj < HB; ++jj)
 #pragma unroll
-            for (int jj = 0; jj < HB; ++jj) {
-              const int d = jj * 16 + (lane & 15);
-              vt[((size_t)(b * nkvh + kvh) * HD + d) * ldvt + l] = to_t<T>(acc[i][h0 + jj][r]);
+            for (int qq = 0; qq < LY::NQ; ++qq) {
+              const int d = LY::col(jj, qq, lane);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) base[(size_t)(d + e) * ldvt] = to_t<T>(acc[i][h0 + jj][4 * qq + e]);
             }
-          }
+        }
       } else {
         const int cb = nh0 - nq - 2 * nk;
 #pragma unroll
-        for (int i = 0; i < MI; ++i)
+        for (int i = 0; i < MI; ++i) {
+          const int m = row0 + LY::row(i, lane);
+          if (m >= M) continue;
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int m = row0 + i * 16 + (lane >> 4) * 4 + r;
-            if (m >= M) continue;
+          for (int jj = 0; jj < HB; ++jj)
 #pragma unroll
-            for (int jj = 0; jj < HB; ++jj) {
-              const int d = jj * 16 + (lane & 15);
-              g[(size_t)m * nq + cb + d] = to_t<T>(acc[i][h0 + jj][r]);
-            }
-          }
+            for (int qq = 0; qq < LY::NQ; ++qq)
+              st4(g + (size_t)m * nq + cb + LY::col(jj, qq, lane), quad(acc[i][h0 + jj], qq));
+        }
       }
     }
   }
@@ -238,10 +307,19 @@ struct EpiQkvg {
 // ---------------------------------------------------------------------------------------------
 // Tile order
 // ---------------------------------------------------------------------------------------------
+#ifndef K2_TILE_GROUP
+#define K2_TILE_GROUP 8
+#endif
+#ifndef K2_TILE_XCD
+#define K2_TILE_XCD 1
+#endif
 __device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_m, int tiles_n, int& tm, int& tn) {
-  const int per = nb >> 3, rem = nb & 7, xcd = bid & 7, loc = bid >> 3;
-  const int logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
-  constexpr int GM = 8;
+  int logical = bid;
+  if (K2_TILE_XCD) {
+    const int per = nb >> 3, rem = nb & 7, xcd = bid & 7, loc = bid >> 3;
+    logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
+  }
+  constexpr int GM = K2_TILE_GROUP;
   const int group_size = GM * tiles_n;
   const int group = logical / group_size, first_m = group * GM;
   const int gm = min(tiles_m - first_m, GM);
@@ -265,6 +343,11 @@ __device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
+// 128-byte LDS rows, 32 consecutive rows read at 2 consecutive chunks (the 32x32x16 fragment
+// pattern) and 8 rows x 8 chunks written at once: conflict-free on gfx950 (measured with the LDS
+// bank-conflict counter).
+__device__ __forceinline__ int swz128(int row) { return (row >> 1) & 7; }
+
 template <typename T, int BM, int BN, int WM, int WN, class BMap, class Epi>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap, Epi epi) {
@@ -277,8 +360,14 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
   constexpr int RSTEP = NT / CPR;      // rows moved by one load instruction of the workgroup
   constexpr int A_LD = BM / RSTEP, B_LD = BN / RSTEP;
   static_assert(BM % RSTEP == 0 && BN % RSTEP == 0 && 64 % RSTEP == 0, "tile/thread mismatch");
-  constexpr int MI = WM / 16, NJ = WN / 16;
+  // bf16 accumulates 32x32 blocks with v_mfma_f32_32x32x16_bf16 (about twice the rate of the
+  // 16x16x32 form on this part); fp32 keeps 16x16 blocks.
+  constexpr bool W32 = sizeof(T) == 2;
+  constexpr int BS = W32 ? 32 : 16;
+  constexpr int MI = WM / BS, NJ = WN / BS;
   typedef typename FragOf<T>::type Frag;
+  typedef typename std::conditional<W32, f32x16, f32x4>::type Acc;
+  auto swz = [](int row) { return W32 ? swz128(row) : swz8(row); };
 
   __shared__ uint4 smem[2][(BM + BN) * CPR];
 
@@ -307,92 +396,325 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
   for (int i = 0; i < A_LD; ++i) {
     const int row = r + i * RSTEP;
     a_off[i] = (uint32_t)(row * lda + c * EPC) * sizeof(T);
-    a_dst[i] = row * CPR + (c ^ swz8(row));
+    a_dst[i] = row * CPR + (c ^ swz(row));
   }
   b_off = (uint32_t)(r * bmap.ldb + c * EPC) * sizeof(T);
 #pragma unroll
   for (int i = 0; i < B_LD; ++i) {
     const int row = r + i * RSTEP;
-    b_dst[i] = (BM + row) * CPR + (c ^ swz8(row));
+    b_dst[i] = (BM + row) * CPR + (c ^ swz(row));
   }
 
-  f32x4 acc[MI][NJ];
+  Acc acc[MI][NJ];
 #pragma unroll
   for (int i = 0; i < MI; ++i)
 #pragma unroll
-    for (int j = 0; j < NJ; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < (int)(sizeof(Acc) / 4); ++r) acc[i][j][r] = 0.0f;
 
-  uint4 ra[A_LD], rb[B_LD];
+  uint4 ra0[A_LD], rb0[B_LD], ra1[A_LD], rb1[B_LD];
   const int nk = (K + BK - 1) / BK;
+  const int nk2 = (nk + 1) & ~1;  // slabs past K load zeros, so the loop runs in pairs of slabs
 
-#define K2_GLOAD(kt)                                                                         \
+#define K2_GLOAD(RA, RB, kt)                                                                 \
   do {                                                                                       \
     const int k0_ = (kt) * BK;                                                               \
     const bool kin_ = k0_ + c * EPC < K;                                                     \
     const uint32_t kb_ = (uint32_t)k0_ * sizeof(T);                                          \
-    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) ra[i] = bload(ra_src, kin_ ? a_off[i] + kb_ : kOOB); \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) rb[i] = bload(rb_src[i], kin_ ? b_off + kb_ : kOOB); \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) RA[i] = bload(ra_src, kin_ ? a_off[i] + kb_ : kOOB); \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) RB[i] = bload(rb_src[i], kin_ ? b_off + kb_ : kOOB); \
+    __builtin_amdgcn_sched_barrier(0); /* keep the loads ahead of the slab's matrix-core work */ \
   } while (0)
 
-#define K2_SSTORE(buf)                                                        \
+#define K2_SSTORE(RA, RB, buf)                                                \
   do {                                                                        \
-    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) smem[buf][a_dst[i]] = ra[i]; \
-    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) smem[buf][b_dst[i]] = rb[i]; \
+    _Pragma("unroll") for (int i = 0; i < A_LD; ++i) smem[buf][a_dst[i]] = RA[i]; \
+    _Pragma("unroll") for (int i = 0; i < B_LD; ++i) smem[buf][b_dst[i]] = RB[i]; \
   } while (0)
 
-  K2_GLOAD(0);
-  K2_SSTORE(0);
+  // One slab from LDS stage `buf`. 32x32x16 (bf16): lane l supplies row/column l%32 and k slots
+  // 8*(l/32)..+7 of a 16-wide k step, i.e. chunk 2s + l/32 of the 128-byte row for step s.
+  // 16x16 (fp32): lane l supplies row/column l%16 and fragment chunks of lane group l/16.
+#define K2_COMPUTE(buf)                                                                          \
+  do {                                                                                           \
+    const uint4* sA = smem[buf];                                                                 \
+    const uint4* sB = smem[buf] + BM * CPR;                                                      \
+    if constexpr (W32) {                                                                         \
+      _Pragma("unroll") for (int s = 0; s < BK / 16; ++s) {                                      \
+        bf16x8 fa[MI], fb[NJ];                                                                   \
+        const int ch = 2 * s + (lane >> 5);                                                      \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
+          const int row = wm * WM + i * 32 + (lane & 31);                                        \
+          fa[i] = __builtin_bit_cast(bf16x8, sA[row * CPR + (ch ^ swz128(row))]);                \
+        }                                                                                        \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                         \
+          const int row = wn * WN + j * 32 + (lane & 31);                                        \
+          fb[j] = __builtin_bit_cast(bf16x8, sB[row * CPR + (ch ^ swz128(row))]);                \
+        }                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
+          _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                         \
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fb[j], fa[i], acc[i][j], 0, 0, 0); \
+      }                                                                                          \
+    } else {                                                                                     \
+      _Pragma("unroll") for (int ks = 0; ks < KS; ++ks) {                                        \
+        Frag af[MI], bfr[NJ];                                                                    \
+        const int cb = ks * 4 * FC + (lane >> 4) * FC;                                           \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i) {                                         \
+          const int row = wm * WM + i * 16 + (lane & 15);                                        \
+          _Pragma("unroll") for (int f = 0; f < FC; ++f)                                         \
+            ((uint4*)&af[i])[f] = sA[row * CPR + ((cb + f) ^ swz8(row))];                        \
+        }                                                                                        \
+        _Pragma("unroll") for (int j = 0; j < NJ; ++j) {                                         \
+          const int row = wn * WN + j * 16 + (lane & 15);                                        \
+          _Pragma("unroll") for (int f = 0; f < FC; ++f)                                         \
+            ((uint4*)&bfr[j])[f] = sB[row * CPR + ((cb + f) ^ swz8(row))];                       \
+        }                                                                                        \
+        _Pragma("unroll") for (int i = 0; i < MI; ++i)                                           \
+          _Pragma("unroll") for (int j = 0; j < NJ; ++j) acc[i][j] = mma16(acc[i][j], bfr[j], af[i]); \
+      }                                                                                          \
+    }                                                                                            \
+  } while (0)
+
+  // Slab j is loaded into registers during step j-2 and written to LDS at the end of step j-1, so
+  // its global loads have about two slabs of matrix-core work to land.
+  K2_GLOAD(ra0, rb0, 0);
+  K2_GLOAD(ra1, rb1, 1);
+  K2_SSTORE(ra0, rb0, 0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) K2_GLOAD(kt + 1);
-    const uint4* sA = smem[buf];
-    const uint4* sB = smem[buf] + BM * CPR;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      Frag af[MI], bfr[NJ];
-      const int cb = ks * 4 * FC + (lane >> 4) * FC;
-#pragma unroll
-      for (int i = 0; i < MI; ++i) {
-        const int row = wm * WM + i * 16 + (lane & 15);
-#pragma unroll
-        for (int f = 0; f < FC; ++f) ((uint4*)&af[i])[f] = sA[row * CPR + ((cb + f) ^ swz8(row))];
-      }
-#pragma unroll
-      for (int j = 0; j < NJ; ++j) {
-        const int row = wn * WN + j * 16 + (lane & 15);
-#pragma unroll
-        for (int f = 0; f < FC; ++f) ((uint4*)&bfr[j])[f] = sB[row * CPR + ((cb + f) ^ swz8(row))];
-      }
-#pragma unroll
-      for (int i = 0; i < MI; ++i)
-#pragma unroll
-        for (int j = 0; j < NJ; ++j) acc[i][j] = mma16(acc[i][j], af[i], bfr[j]);
-    }
-    if (kt + 1 < nk) K2_SSTORE(buf ^ 1);
+  for (int kt = 0; kt < nk2; kt += 2) {
+    K2_GLOAD(ra0, rb0, kt + 2);  // LDS[0] holds slab kt; slab kt+1 is in flight in ra1/rb1
+    K2_COMPUTE(0);
+    K2_SSTORE(ra1, rb1, 1);
+    __syncthreads();
+    K2_GLOAD(ra1, rb1, kt + 3);  // LDS[1] holds slab kt+1; slab kt+2 is in flight in ra0/rb0
+    K2_COMPUTE(1);
+    K2_SSTORE(ra0, rb0, 0);
     __syncthreads();
   }
+#undef K2_COMPUTE
 #undef K2_GLOAD
 #undef K2_SSTORE
-  epi.template apply<MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M);
+  epi.template apply<Lay<BS>, MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M);
+}
+
+// ---------------------------------------------------------------------------------------------
+// bf16 main loop: 256x256 workgroup tile, 4 waves (one per SIMD), each owning a 128x128 sub-tile
+// of 4x4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
+//
+// K advances in 64-wide slabs; a slab is 512 LDS rows (256 of A, 256 of B) of one 128-byte line
+// each, streamed by buffer->LDS DMA into one of two 64 KB stages. A DMA instruction moves 1 KB =
+// 8 rows: lane i writes row i/8 at chunk position i%8, so it fetches global chunk (i%8) ^
+// swz128(row), which is how the XOR swizzle is applied. Rows past M or past a weight matrix's end
+// and chunks past K are out of the buffer's range and read as zero.
+//
+// Inside a slab the wave runs 4 k16 sub-steps; fragments are double-buffered in registers, so the
+// LDS reads of sub-step s+1 are in flight while the matrix cores work on sub-step s. One barrier
+// per slab, after sub-step 2: by then every wave has read the stage's last fragments and has seen
+// its own DMA of the next slab land, so the stage can be refilled with slab k+2 and the next slab's
+// first fragments read during sub-step 3.
+// ---------------------------------------------------------------------------------------------
+// 16-byte-per-lane DMA from a buffer into LDS at lds + 16 * lane. The builtin exists for the device
+// pass only; the host pass (which only needs the kernel's launch stub) sees an empty body.
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+#endif
+}
+
+template <class BMap, class Epi>
+__global__ void __launch_bounds__(256)
+gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap, Epi epi) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, BK = 64;
+  constexpr int MI = WM / 32, NJ = WN / 32;
+  constexpr uint32_t OOB = 0x80000000u;
+
+  __shared__ uint4 st0[(BM + BN) * 8];
+  __shared__ uint4 st1[(BM + BN) * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: resources live in SGPRs
+  const int wm = wave >> 1, wn = wave & 1;
+  const int tiles_m = (M + BM - 1) / BM, tiles_n = (Ntot + BN - 1) / BN;
+  int tm, tn;
+  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  const int m0 = tm * BM, n0 = tn * BN;
+
+  // DMA duties: wave w moves A rows 64w .. 64w+63 and B rows 64w .. 64w+63 of the tile, 8 blocks of
+  // 8 rows each. Block j's rows are 8j .. 8j+7 past the wave's first row; swz128 of its rows depends
+  // only on j's parity, so two chunk choices cover all blocks.
+  const int pos = lane & 7, lr = lane >> 3;
+  const int cc[2] = {pos ^ ((lr >> 1) & 7), pos ^ ((4 + (lr >> 1)) & 7)};
+  const rsrc_t ra = make_rsrc(A + (size_t)m0 * lda, (size_t)(M - m0) * lda * sizeof(bf16));
+  uint32_t avo[2], bvo[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    avo[p] = (uint32_t)((64 * wave + lr) * lda + cc[p] * 8) * sizeof(bf16);
+    bvo[p] = (uint32_t)(lr * bmap.ldb + cc[p] * 8) * sizeof(bf16);
+  }
+  const uint32_t arow8 = (uint32_t)(8 * lda) * sizeof(bf16);  // byte distance of consecutive A blocks
+  rsrc_t rb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const int n = n0 + 64 * wave + 8 * j;
+    int nvalid = 0;
+    const bf16* base = n < Ntot ? bmap.group(n, nvalid) : A;
+    nvalid = n < Ntot ? (nvalid < 0 ? 0 : (nvalid > 8 ? 8 : nvalid)) : 0;
+    rb[j] = make_rsrc(base, (size_t)nvalid * bmap.ldb * sizeof(bf16));
+  }
+
+#define K2_ISSUE(ST, kt)                                                                         \
+  do {                                                                                           \
+    const int k0_ = (kt) * BK;                                                                   \
+    const uint32_t kb_ = (uint32_t)k0_ * sizeof(bf16);                                           \
+    const bool in0_ = k0_ + cc[0] * 8 < K, in1_ = k0_ + cc[1] * 8 < K;                           \
+    const uint32_t a0_ = in0_ ? avo[0] + kb_ : OOB, a1_ = in1_ ? avo[1] + kb_ : OOB;             \
+    const uint32_t b0_ = in0_ ? bvo[0] + kb_ : OOB, b1_ = in1_ ? bvo[1] + kb_ : OOB;             \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                \
+      dma16(ra, (ST) + (64 * wave + 8 * j) * 8, (j & 1) ? a1_ + j * arow8 : a0_ + j * arow8);    \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                \
+      dma16(rb[j], (ST) + (BM + 64 * wave + 8 * j) * 8, (j & 1) ? b1_ : b0_);                     \
+  } while (0)
+
+  f32x16 acc[MI][NJ];
+#pragma unroll
+  for (int i = 0; i < MI; ++i)
+#pragma unroll
+    for (int j = 0; j < NJ; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+  // Fragment reads: lane l supplies row/column l%32 and k slots 8*(l/32)..+7 of a k16 sub-step,
+  // i.e. chunk 2s + l/32 of the 128-byte row. The rows a lane reads all have the same swz128.
+  const int fsw = ((lane & 31) >> 1) & 7, hh = lane >> 5;
+  const int arow = (wm * WM + (lane & 31)) * 8, brow = (BM + wn * WN + (lane & 31)) * 8;
+  bf16x8 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
+#define K2_READ(FA, FB, ST, s)                                                                   \
+  do {                                                                                           \
+    const int ch_ = (2 * (s) + hh) ^ fsw;                                                        \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                               \
+      FA[i] = __builtin_bit_cast(bf16x8, (ST)[arow + i * 32 * 8 + ch_]);                         \
+    _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                               \
+      FB[j] = __builtin_bit_cast(bf16x8, (ST)[brow + j * 32 * 8 + ch_]);                         \
+  } while (0)
+#define K2_MMA(FA, FB)                                                                           \
+  do {                                                                                           \
+    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                               \
+      _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                             \
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[j], FA[i], acc[i][j], 0, 0, 0);    \
+  } while (0)
+  // vmcnt(n) with expcnt and lgkmcnt left unconstrained (gfx9 s_waitcnt encoding)
+#define K2_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define K2_FENCE() __builtin_amdgcn_sched_barrier(0)
+#define K2_BARRIER()                   \
+  do {                                 \
+    asm volatile("" ::: "memory");     \
+    K2_FENCE();                        \
+    __builtin_amdgcn_s_barrier();      \
+    K2_FENCE();                        \
+    asm volatile("" ::: "memory");     \
+  } while (0)
+  // Scheduling groups (mask, count): the next sub-step's 8 fragment reads go out before this
+  // sub-step's 16 matrix-core instructions; in the sub-step after the barrier the 16 DMA
+  // instructions of slab k+2 alternate with them.
+#define K2_ORDER()                                      \
+  do {                                                  \
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  \
+    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0); \
+    K2_FENCE();                                         \
+  } while (0)
+#define K2_ORDER_DMA()                                                             \
+  do {                                                                             \
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                             \
+    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           \
+      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                           \
+    }                                                                              \
+    K2_FENCE();                                                                    \
+  } while (0)
+  // The loop turns at the slab barrier. Entering K2_TURN, sub-steps 0..2 of slab k (stage CUR) are
+  // issued and slab k's last fragments are being read into fa1/fb1; slab k+1 is streaming into NXT.
+  // K2_TURN finishes slab k, refills CUR with slab k+2 and runs sub-steps 0..2 of slab k+1.
+#define K2_TURN(CUR, NXT, k)                                                                  \
+  do {                                                                                        \
+    K2_WAIT_VM(0);                                                                            \
+    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): every read of CUR has landed */        \
+    K2_BARRIER();                                                                             \
+    K2_ISSUE(CUR, (k) + 2);                                                                   \
+    K2_READ(fa0, fb0, NXT, 0);                                                                \
+    K2_MMA(fa1, fb1);                                                                         \
+    K2_ORDER_DMA();                                                                           \
+    K2_READ(fa1, fb1, NXT, 1);                                                                \
+    K2_MMA(fa0, fb0);                                                                         \
+    K2_ORDER();                                                                               \
+    K2_READ(fa0, fb0, NXT, 2);                                                                \
+    K2_MMA(fa1, fb1);                                                                         \
+    K2_ORDER();                                                                               \
+    K2_READ(fa1, fb1, NXT, 3);                                                                \
+    K2_MMA(fa0, fb0);                                                                         \
+    K2_ORDER();                                                                               \
+  } while (0)
+
+  const int nk = (K + BK - 1) / BK;
+  const int nk2 = nk < 2 ? 2 : (nk + 1) & ~1;  // slabs past K read zeros: the loop runs in pairs
+  K2_ISSUE(st0, 0);
+  K2_ISSUE(st1, 1);
+  K2_WAIT_VM(16);  // this wave's DMA of slab 0 landed; slab 1's 16 may still be in flight
+  K2_BARRIER();
+  K2_READ(fa0, fb0, st0, 0);
+  K2_READ(fa1, fb1, st0, 1);
+  K2_MMA(fa0, fb0);
+  K2_ORDER();
+  K2_READ(fa0, fb0, st0, 2);
+  K2_MMA(fa1, fb1);
+  K2_ORDER();
+  K2_READ(fa1, fb1, st0, 3);
+  K2_MMA(fa0, fb0);
+  K2_ORDER();
+  for (int kt = 0; kt < nk2 - 2; kt += 2) {
+    K2_TURN(st0, st1, kt);
+    K2_TURN(st1, st0, kt + 1);
+  }
+  K2_TURN(st0, st1, nk2 - 2);
+  __builtin_amdgcn_s_waitcnt(0xC07F);
+  K2_MMA(fa1, fb1);  // last sub-step of slab nk2 - 1
+  K2_WAIT_VM(0);     // no DMA may still write LDS when the workgroup retires
+#undef K2_TURN
+#undef K2_ORDER
+#undef K2_ORDER_DMA
+#undef K2_BARRIER
+#undef K2_FENCE
+#undef K2_WAIT_VM
+#undef K2_MMA
+#undef K2_READ
+#undef K2_ISSUE
+  epi.template apply<Lay<32>, MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M);
 }
 
 // ---------------------------------------------------------------------------------------------
 // Launch configurations
 // ---------------------------------------------------------------------------------------------
 template <typename T> struct Cfg;
-template <> struct Cfg<bf16> { static constexpr int BM = 256, BN = 256, WM = 64, WN = 128; };
-template <> struct Cfg<float> { static constexpr int BM = 64, BN = 128, WM = 32, WN = 128; };
+template <> struct Cfg<bf16> { static constexpr int BM = 256, BN = 256, WM = 128, WN = 128; static constexpr bool DMA = true; };
+template <> struct Cfg<float> { static constexpr int BM = 64, BN = 128, WM = 32, WN = 128; static constexpr bool DMA = false; };
 
-template <typename T, class BMap, class Epi>
-static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& epi, hipStream_t s) {
-  typedef Cfg<T> C;
+template <typename T, class C, class BMap, class Epi>
+static hipError_t launch_cfg(const GemmA& a, int Ntot, const BMap& bmap, const Epi& epi, hipStream_t s) {
   constexpr int NT = (C::BM / C::WM) * (C::BN / C::WN) * 64;
   if (a.M <= 0 || Ntot <= 0) return hipSuccess;
   const int tiles = ((a.M + C::BM - 1) / C::BM) * ((Ntot + C::BN - 1) / C::BN);
-  hipLaunchKernelGGL((gemm_kernel<T, C::BM, C::BN, C::WM, C::WN, BMap, Epi>), dim3(tiles), dim3(NT), 0, s,
-                     (const T*)a.A, a.lda, a.M, a.K, Ntot, bmap, epi);
+  if constexpr (sizeof(T) == 2 && C::DMA)
+    hipLaunchKernelGGL((gemm_bf16_kernel<BMap, Epi>), dim3(tiles), dim3(256), 0, s, (const bf16*)a.A, a.lda, a.M,
+                       a.K, Ntot, bmap, epi);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, C::BM, C::BN, C::WM, C::WN, BMap, Epi>), dim3(tiles), dim3(NT), 0, s,
+                       (const T*)a.A, a.lda, a.M, a.K, Ntot, bmap, epi);
   return hipGetLastError();
+}
+
+template <typename T, class BMap, class Epi>
+static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& epi, hipStream_t s) {
+  return launch_cfg<T, Cfg<T>>(a, Ntot, bmap, epi, s);
 }
 
 template <typename T, int HD>
@@ -413,6 +735,8 @@ static hipError_t qkvg_t(const GemmA& a, const QkvgArgs& p, hipStream_t s) {
 template <typename T>
 static hipError_t swiglu_t(const GemmA& a, const SwigluArgs& p, hipStream_t s) {
   constexpr int WN = Cfg<T>::WN;
+  constexpr int RSTEP = (Cfg<T>::BM / Cfg<T>::WM) * (Cfg<T>::BN / Cfg<T>::WN) * 64 / 8;
+  static_assert((WN / 2) % RSTEP == 0, "a load group must not straddle gate and up rows");
   BSwiglu<T, WN> bm;
   bm.gate = (const T*)p.wgate; bm.up = (const T*)p.wup; bm.I = p.I; bm.ldb = a.K;
   EpiSwiglu<T, WN> e;

@@ -6,6 +6,7 @@
 #include <cstdio>
 #include <cstring>
 #include <mutex>
+#include <initializer_list>
 #include <string>
 #include <vector>
 
@@ -111,11 +112,19 @@ int check_block_cfg(const k2_block_cfg* c, bool rope) {
   return K2_OK;
 }
 
+// Device pointers other than the workspace must be 16-byte aligned (NULL passes).
+int check_align(const char* what, std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if ((uintptr_t)p & 15) return fail(K2_ERR_ALIGN, "%s: device pointer %p is not 16-byte aligned", what, p);
+  return K2_OK;
+}
+
 int check_block_weights(const k2_block_weights* w) {
   if (!w) return fail(K2_ERR_NULL, "block weights are NULL");
   if (!w->to_q || !w->to_k || !w->to_v || !w->to_gate || !w->to_out || !w->ff_gate || !w->ff_up || !w->ff_down)
     return fail(K2_ERR_NULL, "a block projection weight is NULL");
-  return K2_OK;
+  return check_align("block weights", {w->scale_shift_table, w->norm1_w, w->norm2_w, w->norm_q_w, w->norm_k_w, w->to_q,
+                                       w->to_k, w->to_v, w->to_gate, w->to_out, w->ff_gate, w->ff_up, w->ff_down});
 }
 
 int check_sizes(int B, int T, int N) {
@@ -251,7 +260,7 @@ int validate_block_call(const k2_block_cfg* cfg, const k2_block_weights* w, int 
   if (!w->scale_shift_table && temb) return fail(K2_ERR_CONFIG, "temb given for a block without scale_shift_table");
   if (pos && (pos_rows != T + N || pos_cols != 3))
     return fail(K2_ERR_SHAPE, "position_ids must be (T + N, 3) = (%d, 3), got (%d, %d)", T + N, pos_rows, pos_cols);
-  return K2_OK;
+  return check_align("hidden_in / hidden_out / temb", {hin, hout, temb});
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -286,7 +295,7 @@ int check_time(const k2_time_cfg* c, const k2_time_weights* w, int B) {
     return fail(K2_ERR_CONFIG, "timestep_embed_dim must be a positive multiple of 8");
   if (!w->lin1_w || !w->lin2_w || !w->mod_w) return fail(K2_ERR_NULL, "a time-path weight is NULL");
   if (B <= 0) return fail(K2_ERR_SHAPE, "B must be >= 1");
-  return K2_OK;
+  return check_align("time-path weights", {w->lin1_w, w->lin1_b, w->lin2_w, w->lin2_b, w->mod_w, w->mod_b});
 }
 
 int time_run(const k2_time_cfg* c, const k2_time_weights* w, int B, const float* t, float* temb, float* emb_out,
@@ -423,6 +432,10 @@ int check_model(const k2_model_cfg* c, const k2_model_weights* w, int B, int T, 
   if (!w) return fail(K2_ERR_NULL, "model weights are NULL");
   if (!w->img_in_w || !w->txt_in_w || !w->final_w || !w->final_table)
     return fail(K2_ERR_NULL, "img_in / txt_in / final weights are NULL");
+  if ((rc = check_align("img_in / txt_in / final weights", {w->img_in_w, w->img_in_b, w->txt_in_w, w->txt_in_b,
+                                                            w->final_w, w->final_b, w->final_norm_w,
+                                                            w->final_table})) != K2_OK)
+    return rc;
   if (c->num_layers && !w->blocks) return fail(K2_ERR_NULL, "block weights are NULL");
   for (int i = 0; i < c->num_layers; ++i) {
     if ((rc = check_block_weights(&w->blocks[i])) != K2_OK) return rc;
@@ -514,6 +527,7 @@ int k2_timestep_modulation_forward(const k2_time_cfg* cfg, const k2_time_weights
   int rc = check_time(cfg, w, B);
   if (rc != K2_OK) return rc;
   if (!timestep || !temb) return fail(K2_ERR_NULL, "timestep / temb is NULL");
+  if ((rc = check_align("temb / emb_out", {temb, emb_out})) != K2_OK) return rc;
   if ((rc = check_ws(workspace, workspace_bytes, time_layout(cfg, B).total)) != K2_OK) return rc;
   g_err.clear();
   return time_run(cfg, w, B, timestep, temb, emb_out, workspace, (hipStream_t)stream);
@@ -529,6 +543,7 @@ int k2_text_fusion_forward(const k2_text_cfg* cfg, const k2_text_weights* w, int
   int rc = check_text(cfg, w, B, T);
   if (rc != K2_OK) return rc;
   if (!enc || !out) return fail(K2_ERR_NULL, "encoder_hidden_states / out is NULL");
+  if ((rc = check_align("encoder_hidden_states / out", {enc, out})) != K2_OK) return rc;
   if ((rc = check_ws(workspace, workspace_bytes, text_layout(cfg, B, T).total)) != K2_OK) return rc;
   g_err.clear();
   return text_run(cfg, w, B, T, enc, mask, out, workspace, (hipStream_t)stream);
@@ -547,6 +562,7 @@ int k2_backbone_forward(const k2_model_cfg* cfg, const k2_model_weights* w, int 
   if (rc != K2_OK) return rc;
   if (!hidden_states || !timestep || !pos || !out || (T > 0 && !enc))
     return fail(K2_ERR_NULL, "hidden_states / encoder_hidden_states / timestep / position_ids / out is NULL");
+  if ((rc = check_align("hidden_states / encoder_hidden_states / out", {hidden_states, enc, out})) != K2_OK) return rc;
   if (pos_rows != T + N || pos_cols != 3)
     return fail(K2_ERR_SHAPE, "position_ids must be (T + N, 3) = (%d, 3), got (%d, %d)", T + N, pos_rows, pos_cols);
   const ModelLayout l = model_layout(cfg, B, T, N);

@@ -25,6 +25,8 @@
  *     A launch failure returns K2_ERR_HIP; a fault inside a kernel surfaces at the caller's next sync.
  *   - Workspace: at least *_workspace_bytes() bytes of device memory, 256-byte aligned. Its contents
  *     on entry are ignored; it is clobbered.
+ *   - Every other device pointer (weights, biases, norm weights, tables, activations, outputs) must be
+ *     16-byte aligned: the kernels move 16 bytes per lane. Violations return K2_ERR_ALIGN.
  */
 #ifndef K2_H
 #define K2_H
@@ -43,7 +45,8 @@ typedef enum {
   K2_ERR_CONFIG = -3,    /* unsupported or inconsistent configuration */
   K2_ERR_DTYPE = -4,     /* unknown dtype */
   K2_ERR_WORKSPACE = -5, /* workspace too small or misaligned */
-  K2_ERR_HIP = -6        /* a HIP launch failed */
+  K2_ERR_HIP = -6,       /* a HIP launch failed */
+  K2_ERR_ALIGN = -7      /* a device pointer is not 16-byte aligned */
 } k2_status;
 
 typedef enum { K2_F32 = 0, K2_BF16 = 1 } k2_dtype;

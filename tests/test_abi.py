@@ -15,7 +15,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "k2.h")
 GOLDEN = os.path.join(ROOT, "tests", "golden", "krea2_defaults.json")
 
-OK, ENULL, ESHAPE, ECONFIG, EDTYPE, EWS = 0, -1, -2, -3, -4, -5
+OK, ENULL, ESHAPE, ECONFIG, EDTYPE, EWS, EALIGN = 0, -1, -2, -3, -4, -5, -7
 
 
 def declared_functions():
@@ -124,6 +124,14 @@ def test_block_validation_codes():
     assert call_block(ws_bytes=need - 1) == EWS
     assert call_block(ws=FAKE + 8, ws_bytes=need) == EWS
     assert call_block(ws=None, ws_bytes=need) == ENULL
+    # every other device pointer must be 16-byte aligned (the kernels move 16 bytes per lane)
+    assert call_block(hin=FAKE + 4) == EALIGN and b"16-byte" in lib.k2_last_error()
+    assert call_block(hout=FAKE + 8) == EALIGN
+    assert call_block(temb=FAKE + 12) == EALIGN
+    w = good_weights(); w.norm_q_w = FAKE + 0x100004
+    assert call_block(w=w) == EALIGN
+    w = good_weights(); w.ff_down = FAKE + 0x100002
+    assert call_block(w=w) == EALIGN
 
 
 def test_workspace_layout_is_ordered_and_aligned():
