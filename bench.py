@@ -12,6 +12,9 @@ same resolution as denoise steps/s (one call = one CFG step), per-kernel times, 
 the dominant kernel, and the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-backbone] [--no-cpu-baseline]
+                       [--cpu-rows R] [--copy-calibration]
+--copy-calibration first runs a plain elementwise copy (negation) of 1 GiB float32, a kernel of known
+HBM traffic against which the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled.
 """
 from __future__ import annotations
 
@@ -28,6 +31,7 @@ sys.path.insert(0, ROOT)
 METRIC = "Krea2 block TFLOP/s & % bf16 MFMA peak; denoise steps/s at 1024², B=2"
 PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (256 CU x 2.4 GHz x 4096 FLOP/clk)
 PEAK_HBM_GBS = 8000.0
+COPY_BYTES = 1 << 30
 KERNELS = ("modulation", "modnorm", "gemm_qkvg", "attention", "gemm_out", "gemm_swiglu", "gemm_down", "rope")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "flow_matching_diffusion_amd", "csrc", f) for f in
@@ -110,7 +114,8 @@ def main():
     ap.add_argument("--backbone-steps", type=int, default=5)
     ap.add_argument("--no-backbone", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=256)
+    ap.add_argument("--cpu-rows", type=int, default=4608)
+    ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: this build runs on one GPU only; --gpus must be 1 (no multi-GPU path is built)",
@@ -125,6 +130,13 @@ def main():
 
     dev = torch.device("cuda:0")
     k2.load()
+    if args.copy_calibration:
+        src = torch.zeros(COPY_BYTES // 4, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(2):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     wl = S.WORKLOADS[args.workload]
     d = wl.dims
     B, T, N, L = wl.B, wl.T, wl.N, wl.L
