@@ -6,7 +6,10 @@
 // marks it padding; image keys are always valid; the output is multiplied elementwise by
 // sigmoid(gate) before the output projection.
 //
-// One workgroup = (batch row, kv head, block of query rows). Its 4 waves cover the G query heads
+// Two kernels: attn_bf16_kernel (32x32x16 bf16 matrix cores, the production path) and attn_kernel
+// (16x16 blocks, used for float32 operands).
+//
+// attn_kernel: one workgroup = (batch row, kv head, block of query rows). Its 4 waves cover the G query heads
 // that share the kv head, 64 query rows each, so every K/V tile staged in LDS serves all G heads.
 // Per key tile a wave computes S^T = K Q^T (keys along MFMA rows, queries along columns): the
 // online-softmax statistics of a query then live in one lane column and need only two cross-group
@@ -26,15 +29,6 @@
 
 namespace k2 {
 
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-
-__device__ __forceinline__ rsrc_t attn_rsrc(const void* p, size_t bytes) {
-  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
-}
-__device__ __forceinline__ uint4 attn_bload(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
 
 // 16 keys read together by a lane group (key = 32c + 8(r/4) + 4e + r%4) -> distinct chunk slots.
 __device__ __forceinline__ int swz_key(int key) { return (key & 3) | ((key >> 1) & 12); }
@@ -123,10 +117,10 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
   }
 
   // K rows of this (batch, kv head); V^T rows (head dims) of length ldvt.
-  const rsrc_t kr = attn_rsrc((const T*)p.k + ((size_t)b * L * ldk + kvh * HD),
+  const rsrc_t kr = make_rsrc((const T*)p.k + ((size_t)b * L * ldk + kvh * HD),
                               ((size_t)(L - 1) * ldk + HD) * sizeof(T));
   const T* vbase = (const T*)p.vt + (size_t)(b * p.nkv + kvh) * HD * p.ldvt;
-  const rsrc_t vr = attn_rsrc(vbase, (size_t)HD * p.ldvt * sizeof(T));
+  const rsrc_t vr = make_rsrc(vbase, (size_t)HD * p.ldvt * sizeof(T));
   const int kc = tid % CPRK, krow = tid / CPRK;  // K: rows krow + i * KSTEP
   const int vc = tid % CPRV, vrow = tid / CPRV;  // V^T: rows vrow + i * VSTEP
   constexpr int KSTEP = 256 / CPRK, VSTEP = 256 / CPRV;
@@ -136,11 +130,11 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
   do {                                                                                             \
     const int t0_ = (t) * KT;                                                                      \
     _Pragma("unroll") for (int i = 0; i < K_LD; ++i)                                               \
-      rk[i] = attn_bload(kr, (uint32_t)(((t0_ + krow + i * KSTEP) * ldk + kc * EPC) * sizeof(T))); \
+      rk[i] = bload(kr, (uint32_t)(((t0_ + krow + i * KSTEP) * ldk + kc * EPC) * sizeof(T))); \
     const int k0_ = t0_ + vc * EPC;                                                                \
     _Pragma("unroll") for (int i = 0; i < V_LD; ++i) {                                             \
       const uint32_t off_ = k0_ < L ? (uint32_t)(((vrow + i * VSTEP) * p.ldvt + k0_) * sizeof(T)) : 0x80000000u; \
-      rv[i] = attn_bload(vr, off_);                                                                \
+      rv[i] = bload(vr, off_);                                                                \
       if (k0_ + EPC > L && k0_ < L) rv[i] = keep_first<EPC>(rv[i], L - k0_);                        \
     }                                                                                              \
   } while (0)
@@ -311,6 +305,254 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// attn_bf16_kernel: one workgroup = (batch row, kv head, block of query rows); each of its 4 waves
+// owns 32 query rows of one of the G query heads that share the kv head, so every K / V^T tile
+// staged in LDS serves all of them. A wave needs under 256 registers, so two workgroups share a
+// compute unit and one's softmax overlaps the other's matrix-core work.
+//
+// Keys come in tiles of 64, streamed by buffer->LDS DMA into two stages. Per tile and 32-key
+// block, S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys along rows, the wave's 32 queries along
+// columns): a lane holds one query's scores, and the lane 32 apart holds the rest of that query's
+// keys, so the row max is an in-lane max plus one exchange. K rows enter the MFMA in a permuted
+// order (bits 2 and 3 of the row index swapped) so that accumulator entries 8s'..8s'+7 of lane l are
+// keys 16s' + 8(l/32) + 0..7: packed to bf16 they are exactly the B operand (P^T) of
+// O^T += V^T P^T for k-step s', and P never leaves registers. V^T (written transposed by the
+// projection epilogue) gives contiguous A fragments.
+//
+// LDS: K rows are 256 bytes (16 chunks) stored at chunk c ^ (row & 15); V^T rows are 128 bytes (8
+// chunks) at chunk c ^ swz128(d). Both make the fragment reads (32 rows x 2 chunks) and the DMA
+// writes conflict-free.
+// Softmax runs in base 2: p = exp2(s * log2(e)/sqrt(hd) - m), one fused multiply-add before exp2.
+// The running maximum is rescaled lazily (see above). Text-key validity is kept per 64-key tile.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int swz_k256(int row) { return row & 15; }
+__device__ __forceinline__ int swz_v128(int d) { return (d >> 1) & 7; }
+// accumulator row -> key of a 32-key block (bits 2 and 3 swapped; an involution)
+__device__ __forceinline__ int kperm(int rho) { return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1); }
+
+constexpr int kMaxTextTiles64 = 256;  // 64-key text tiles: text tokens up to 16384
+
+template <int HD, int G>
+__global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float scale_log2) {
+  constexpr int KT = 64;              // keys per tile
+  constexpr int KCH = HD / 8;         // 16-byte chunks per K row
+  constexpr int VCH = KT / 8;         // chunks per V^T row
+  constexpr int NS = HD / 16;         // k16 steps over head_dim
+  constexpr int NHB = HD / 32;        // 32-row head-dim blocks of O^T
+  constexpr int WPH = 4 / G;          // waves per query head
+  constexpr int BQ = 32 * WPH;        // query rows per workgroup
+  constexpr int K_DMA = KT * KCH / 256;  // 1 KB DMA instructions per wave for the K tile
+  constexpr int V_DMA = HD * VCH / 256;  // ... and for the V^T tile
+  constexpr float kRescale = 8.0f;
+  static_assert(KCH == 16 || KCH == 8, "head_dim 128 or 64");
+
+  __shared__ uint4 sK[2][KT * KCH];
+  __shared__ uint4 sV[2][HD * VCH];
+  __shared__ uint64_t sBits[kMaxTextTiles64];
+
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int head = kvh * G + wave % G;
+  const int q0 = blockIdx.x * BQ + (wave / G) * 32;
+  const int L = p.L, T_ = p.T;
+  const int ldq = p.nh * HD, ldk = p.nkv * HD;
+  const int h32 = lane >> 5, c32 = lane & 31;
+
+  // validity bits of the text tiles (bit j: key 64t + j is a valid key)
+  const int ntt = (T_ + KT - 1) / KT;
+  for (int u = wave; u < ntt; u += 4) {
+    const int key = u * KT + lane;
+    const bool ok = key < L && (key >= T_ || !p.mask || p.mask[(size_t)b * T_ + key] != 0);
+    const uint64_t bits = __ballot(ok);
+    if (lane == 0) sBits[u] = bits;
+  }
+
+  // Q^T fragments (B operand of S^T = K Q^T): lane l holds query q0 + l%32, head dims 16s + 8(l/32)..+7
+  bf16x8 qf[NS];
+  {
+    const int row = q0 + c32;
+    const bf16* src = (const bf16*)p.q + (size_t)(b * L + (row < L ? row : 0)) * ldq + head * HD;
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+      qf[s] = row < L ? *(const bf16x8*)(src + 16 * s + 8 * h32) : bf16x8{};
+  }
+
+  // DMA duties. K: wave w moves tile rows 16w.. (hd 128: 4 blocks of 4 rows; hd 64: 2 blocks of 8).
+  // V^T: wave w moves head-dim rows HD/4*w .. (blocks of 8 rows).
+  constexpr int KRB = 1024 / (KCH * 16);  // K rows per DMA block
+  const rsrc_t kr = make_rsrc((const bf16*)p.k + ((size_t)b * L * ldk + kvh * HD),
+                              ((size_t)(L - 1) * ldk + HD) * sizeof(bf16));
+  const rsrc_t vr = make_rsrc((const bf16*)p.vt + (size_t)(b * p.nkv + kvh) * HD * p.ldvt,
+                              (size_t)HD * p.ldvt * sizeof(bf16));
+  uint32_t kvo[K_DMA], vvo[V_DMA];
+#pragma unroll
+  for (int j = 0; j < K_DMA; ++j) {
+    const int row = (wave * K_DMA + j) * KRB + lane / KCH, pc = lane % KCH;
+    kvo[j] = (uint32_t)(row * ldk + (pc ^ (swz_k256(row) & (KCH - 1))) * 8) * sizeof(bf16);
+  }
+#pragma unroll
+  for (int j = 0; j < V_DMA; ++j) {
+    const int d = (wave * V_DMA + j) * 8 + lane / 8, pc = lane % 8;
+    vvo[j] = (uint32_t)(d * p.ldvt + (pc ^ swz_v128(d)) * 8) * sizeof(bf16);
+  }
+  auto issue = [&](int st, int t) {
+    const uint32_t kt0 = (uint32_t)(t * KT * ldk) * sizeof(bf16), vt0 = (uint32_t)(t * KT) * sizeof(bf16);
+#pragma unroll
+    for (int j = 0; j < K_DMA; ++j) dma16(kr, &sK[st][(wave * K_DMA + j) * 64], kvo[j] + kt0);
+#pragma unroll
+    for (int j = 0; j < V_DMA; ++j) dma16(vr, &sV[st][(wave * V_DMA + j) * 64], vvo[j] + vt0);
+  };
+  // keys past L in the last tile: V^T columns there hold whatever the workspace held; zero them
+  auto zero_tail = [&](int st, int t) {
+    const int valid = L - t * KT;  // 0 < valid < KT
+    for (int i = tid; i < HD * VCH; i += 256) {
+      const int d = i / VCH, pc = i % VCH, k0 = (pc ^ swz_v128(d)) * 8;
+      if (k0 + 8 > valid) {
+        uint4 v = sV[st][i];
+        uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          if (k0 + e >= valid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
+        sV[st][i] = uint4{w[0], w[1], w[2], w[3]};
+      }
+    }
+  };
+
+  f32x16 o[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[hb][r] = 0.0f;
+  float m_i = -INFINITY, l_i = 0.0f;
+
+  // fragment read offsets (uint4 units): K row kperm(l%32) of a 32-key block, V^T row d = l%32
+  const int krow = kperm(c32), ksw = swz_k256(krow) & (KCH - 1);
+  const int vsw = swz_v128(c32);
+
+  __syncthreads();  // sBits
+  const int nt = (L + KT - 1) / KT;
+  auto next_tile = [&](int t) {
+    while (t < nt && t < ntt && sBits[t] == 0) ++t;
+    return t;
+  };
+  int t = next_tile(0);
+  if (t < nt) issue(0, t);
+  K2_WAIT_VM(0);
+  __syncthreads();
+  if (t < nt && t * KT + KT > L) {
+    zero_tail(0, t);
+    __syncthreads();
+  }
+  int st = 0;
+  while (t < nt) {
+    const int tn = next_tile(t + 1);
+    if (tn < nt) issue(st ^ 1, tn);
+    const uint4* sk = sK[st];
+    const uint4* sv = sV[st];
+
+    // S^T for the two 32-key blocks
+    f32x16 sc[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.0f;
+#pragma unroll
+      for (int s = 0; s < NS; ++s) {
+        const bf16x8 kf = __builtin_bit_cast(bf16x8, sk[(32 * kb + krow) * KCH + ((2 * s + h32) ^ ksw)]);
+        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[kb], 0, 0, 0);
+      }
+    }
+
+    // mask (tiles holding padding or the sequence end only), max, lazy rescale
+    const int t0 = t * KT;
+    const uint64_t vb = t < ntt ? sBits[t] : (t0 + KT <= L ? ~0ull : ((1ull << (L - t0)) - 1ull));
+    if (vb != ~0ull) {
+      // entry r of block kb is key 32kb + 16(r/8) + 8(l/32) + r%8: bytes 4kb + l/32 and 4kb + 2 + l/32
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t lb = (uint32_t)((vb >> (8 * (4 * kb + h32))) & 0xFFu) |
+                            ((uint32_t)((vb >> (8 * (4 * kb + 2 + h32))) & 0xFFu) << 8);
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((lb >> r) & 1u)) sc[kb][r] = -INFINITY;
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+    if (__any(mx > m_i + kRescale)) {
+      const float mnew = fmaxf(m_i, mx);
+      const float alpha = m_i == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_i - mnew);
+      l_i *= alpha;
+#pragma unroll
+      for (int hb = 0; hb < NHB; ++hb) o[hb] *= alpha;
+      m_i = mnew;
+    }
+    const float base = m_i == -INFINITY ? 0.0f : m_i;
+
+    // P^T fragments and the row-sum partial of this lane's keys
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          // v_exp_f32: results below 2^-126 flush to zero, which a probability can afford
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * h + e], scale_log2, -base));
+          l_i += pv[e];
+        }
+        pack8(pf[2 * kb + h], pv);
+      }
+
+    // O^T += V^T P^T: step (kb, h) covers keys 32kb + 16h .. +15; lane group l/32 supplies 8 of them
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d = 32 * hb + c32;
+        const bf16x8 vf = __builtin_bit_cast(bf16x8, sv[d * VCH + ((2 * j + h32) ^ vsw)]);
+        o[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j], o[hb], 0, 0, 0);
+      }
+
+    K2_WAIT_VM(0);
+    __syncthreads();
+    if (tn < nt && tn * KT + KT > L) {
+      zero_tail(st ^ 1, tn);
+      __syncthreads();
+    }
+    st ^= 1;
+    t = tn;
+  }
+
+  // normalise, gate, store: lane holds query q0 + l%32 and head dims 32hb + 8j + 4(l/32) + 0..3
+  const float lsum = l_i + __shfl_xor(l_i, 32);
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  const int row = q0 + c32;
+  if (row < L) {
+    const size_t base = (size_t)(b * L + row) * ldq + head * HD;
+    const bf16* gp = (const bf16*)p.g + base;
+    bf16* op = (bf16*)p.og + base;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * hb + 8 * j + 4 * h32;
+        const bf16x4 gv = *(const bf16x4*)(gp + d0);
+        bf16x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (bf16)(o[hb][4 * j + e] * inv * sigmoidf_((float)gv[e]));
+        *(bf16x4*)(op + d0) = out;
+      }
+  }
+}
+
 template <typename T, int HD, int G>
 static hipError_t launch_attn(const AttnArgs& p, hipStream_t s) {
   constexpr int BQ = 64 * (4 / G);
@@ -322,12 +564,29 @@ static hipError_t launch_attn(const AttnArgs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+template <int HD, int G>
+static hipError_t launch_attn_bf16(const AttnArgs& p, hipStream_t s) {
+  constexpr int BQ = 32 * (4 / G);
+  if (p.L <= 0 || p.B <= 0) return hipSuccess;
+  if (p.T > kMaxTextTiles64 * 64 || p.ldvt % 64 != 0) return hipErrorInvalidValue;
+  dim3 grid((p.L + BQ - 1) / BQ, p.nkv, p.B);
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
+  hipLaunchKernelGGL((attn_bf16_kernel<HD, G>), grid, dim3(256), 0, s, p, scale_log2);
+  return hipGetLastError();
+}
+
 template <typename T, int HD>
 static hipError_t attn_hd(const AttnArgs& p, hipStream_t s) {
   const int G = p.nh / p.nkv;
-  if (G == 4) return launch_attn<T, HD, 4>(p, s);
-  if (G == 2) return launch_attn<T, HD, 2>(p, s);
-  if (G == 1) return launch_attn<T, HD, 1>(p, s);
+  if constexpr (sizeof(T) == 2) {
+    if (G == 4) return launch_attn_bf16<HD, 4>(p, s);
+    if (G == 2) return launch_attn_bf16<HD, 2>(p, s);
+    if (G == 1) return launch_attn_bf16<HD, 1>(p, s);
+  } else {
+    if (G == 4) return launch_attn<T, HD, 4>(p, s);
+    if (G == 2) return launch_attn<T, HD, 2>(p, s);
+    if (G == 1) return launch_attn<T, HD, 1>(p, s);
+  }
   return hipErrorInvalidValue;
 }
 

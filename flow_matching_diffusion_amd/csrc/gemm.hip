@@ -331,17 +331,6 @@ __device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_m, int ti
 // ---------------------------------------------------------------------------------------------
 // Main loop
 // ---------------------------------------------------------------------------------------------
-typedef __amdgpu_buffer_rsrc_t rsrc_t;
-constexpr uint32_t kOOB = 0x80000000u;  // offset past every resource: the load returns zeros
-
-__device__ __forceinline__ rsrc_t make_rsrc(const void* p, size_t bytes) {
-  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
-}
-
-__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
-  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
-}
 
 // 128-byte LDS rows, 32 consecutive rows read at 2 consecutive chunks (the 32x32x16 fragment
 // pattern) and 8 rows x 8 chunks written at once: conflict-free on gfx950 (measured with the LDS
@@ -514,13 +503,6 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
 // its own DMA of the next slab land, so the stage can be refilled with slab k+2 and the next slab's
 // first fragments read during sub-step 3.
 // ---------------------------------------------------------------------------------------------
-// 16-byte-per-lane DMA from a buffer into LDS at lds + 16 * lane. The builtin exists for the device
-// pass only; the host pass (which only needs the kernel's launch stub) sees an empty body.
-__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t off) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
-#endif
-}
 
 template <class BMap, class Epi>
 __global__ void __launch_bounds__(256)
@@ -603,8 +585,6 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BM
       _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                             \
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[j], FA[i], acc[i][j], 0, 0, 0);    \
   } while (0)
-  // vmcnt(n) with expcnt and lgkmcnt left unconstrained (gfx9 s_waitcnt encoding)
-#define K2_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
 #define K2_FENCE() __builtin_amdgcn_sched_barrier(0)
 #define K2_BARRIER()                   \
   do {                                 \
@@ -638,7 +618,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BM
 #define K2_TURN(CUR, NXT, k)                                                                  \
   do {                                                                                        \
     K2_WAIT_VM(0);                                                                            \
-    __builtin_amdgcn_s_waitcnt(0xC07F); /* lgkmcnt(0): every read of CUR has landed */        \
+    K2_WAIT_LGKM0(); /* every read of CUR has landed */                                       \
     K2_BARRIER();                                                                             \
     K2_ISSUE(CUR, (k) + 2);                                                                   \
     K2_READ(fa0, fb0, NXT, 0);                                                                \
@@ -676,7 +656,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BM
     K2_TURN(st1, st0, kt + 1);
   }
   K2_TURN(st0, st1, nk2 - 2);
-  __builtin_amdgcn_s_waitcnt(0xC07F);
+  K2_WAIT_LGKM0();
   K2_MMA(fa1, fb1);  // last sub-step of slab nk2 - 1
   K2_WAIT_VM(0);     // no DMA may still write LDS when the workgroup retires
 #undef K2_TURN
@@ -684,7 +664,6 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BM
 #undef K2_ORDER_DMA
 #undef K2_BARRIER
 #undef K2_FENCE
-#undef K2_WAIT_VM
 #undef K2_MMA
 #undef K2_READ
 #undef K2_ISSUE

@@ -87,6 +87,33 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Buffer resources (raw, 32-bit offsets). A load whose offset lies past the resource's byte size
+// returns zeros; kOOB is an offset past every resource, used to switch a lane's load off.
+typedef __amdgpu_buffer_rsrc_t rsrc_t;
+constexpr uint32_t kOOB = 0x80000000u;
+
+__device__ __forceinline__ rsrc_t make_rsrc(const void* p, size_t bytes) {
+  const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);
+}
+
+__device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+
+// 16-byte-per-lane DMA from a buffer into LDS at lds + 16 * lane (lds must be wave-uniform). The
+// builtin exists for the device pass only; the host pass (which only needs kernels' launch stubs)
+// sees an empty body.
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t off) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+#endif
+}
+
+// vmcnt(n) with expcnt and lgkmcnt left unconstrained, and lgkmcnt(0) alone (gfx9 s_waitcnt fields).
+#define K2_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 15) | (((n) >> 4) << 14) | (7 << 4) | (15 << 8))
+#define K2_WAIT_LGKM0() __builtin_amdgcn_s_waitcnt(0xC07F)
+
 // XOR swizzle of 16-byte chunk positions within 128-byte LDS rows (8 chunks). Measured on gfx950
 // with the LDS bank-conflict counter: ds_read_b128 of 16 consecutive rows x 4 consecutive chunks
 // (the MFMA fragment pattern) and ds_write_b128 of 8 rows x 8 chunks both run conflict-free (4 LDS
