@@ -489,7 +489,7 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
 
 // ---------------------------------------------------------------------------------------------
 // bf16 main loop: 256x256 workgroup tile, 4 waves (one per SIMD), each owning a 128x128 sub-tile
-// of 4x4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane).
+// of 4x4 blocks of v_mfma_f32_32x32x16_bf16 (256 fp32 accumulators per lane, in AGPRs).
 //
 // K advances in 64-wide slabs; a slab is 512 LDS rows (256 of A, 256 of B) of one 128-byte line
 // each, streamed by buffer->LDS DMA into one of two 64 KB stages. A DMA instruction moves 1 KB =
@@ -497,22 +497,33 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
 // swz128(row), which is how the XOR swizzle is applied. Rows past M or past a weight matrix's end
 // and chunks past K are out of the buffer's range and read as zero.
 //
-// Inside a slab the wave runs 4 k16 sub-steps; fragments are double-buffered in registers, so the
-// LDS reads of sub-step s+1 are in flight while the matrix cores work on sub-step s. One barrier
-// per slab, after sub-step 2: by then every wave has read the stage's last fragments and has seen
-// its own DMA of the next slab land, so the stage can be refilled with slab k+2 and the next slab's
-// first fragments read during sub-step 3.
+// Inside a slab the wave runs 4 k16 sub-steps of 16 matrix-core instructions; fragments are
+// double-buffered in registers, each of the next sub-step's 8 fragment reads issued right after
+// one of this sub-step's matrix-core instructions. The instruction order is spelled out and
+// pinned with scheduling fences. One barrier per slab, before its last sub-step: by then every
+// wave has read the slab's last fragments and has seen its own DMA of the next slab land, so the
+// stage is refilled with slab k+2, and the next slab's first fragments are read during the last
+// sub-step.
+//
+// SPREAD picks where the 16 DMA instructions of slab k+2 go. 0: all right after the barrier,
+// which gives them the whole slab to land (best when the weights exceed the 256 MB last-level
+// cache and come from HBM). 2: interleaved with the matrix-core instructions of the two sub-steps
+// after the barrier, which keeps them from stalling the wave in a burst (measured 10-15% faster
+// when the operands stay cache-resident).
 // ---------------------------------------------------------------------------------------------
-
-template <class BMap, class Epi>
+template <int SPREAD, class BMap, class Epi>
 __global__ void __launch_bounds__(256)
 gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap, Epi epi) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, BK = 64;
   constexpr int MI = WM / 32, NJ = WN / 32;
-  constexpr uint32_t OOB = 0x80000000u;
+  constexpr int NRD = MI + NJ, NMF = MI * NJ;  // fragment reads / matrix-core ops per sub-step
+  constexpr int NBW = 8;                       // 1 KB DMA blocks per wave and operand per slab
+  constexpr int DPW = 2 * NBW;                 // DMA instructions per wave per slab
+  constexpr int STAGE = (BM + BN) * 8;         // uint4 per stage
+  static_assert(SPREAD == 0 || SPREAD == 2, "DMA schedule");
 
-  __shared__ uint4 st0[(BM + BN) * 8];
-  __shared__ uint4 st1[(BM + BN) * 8];
+  __shared__ uint4 st0[STAGE];
+  __shared__ uint4 st1[STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: resources live in SGPRs
@@ -535,27 +546,26 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BM
     bvo[p] = (uint32_t)(lr * bmap.ldb + cc[p] * 8) * sizeof(bf16);
   }
   const uint32_t arow8 = (uint32_t)(8 * lda) * sizeof(bf16);  // byte distance of consecutive A blocks
-  rsrc_t rb[8];
+  rsrc_t rb[NBW];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < NBW; ++j) {
     const int n = n0 + 64 * wave + 8 * j;
     int nvalid = 0;
     const bf16* base = n < Ntot ? bmap.group(n, nvalid) : A;
     nvalid = n < Ntot ? (nvalid < 0 ? 0 : (nvalid > 8 ? 8 : nvalid)) : 0;
     rb[j] = make_rsrc(base, (size_t)nvalid * bmap.ldb * sizeof(bf16));
   }
-
-#define K2_ISSUE(ST, kt)                                                                         \
+  // DMA instruction d (0..15) of slab kt into stage ST: A blocks first, then B blocks
+#define K2_DMA1(ST, kt, d)                                                                       \
   do {                                                                                           \
-    const int k0_ = (kt) * BK;                                                                   \
-    const uint32_t kb_ = (uint32_t)k0_ * sizeof(bf16);                                           \
-    const bool in0_ = k0_ + cc[0] * 8 < K, in1_ = k0_ + cc[1] * 8 < K;                           \
-    const uint32_t a0_ = in0_ ? avo[0] + kb_ : OOB, a1_ = in1_ ? avo[1] + kb_ : OOB;             \
-    const uint32_t b0_ = in0_ ? bvo[0] + kb_ : OOB, b1_ = in1_ ? bvo[1] + kb_ : OOB;             \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                \
-      dma16(ra, (ST) + (64 * wave + 8 * j) * 8, (j & 1) ? a1_ + j * arow8 : a0_ + j * arow8);    \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j)                                                \
-      dma16(rb[j], (ST) + (BM + 64 * wave + 8 * j) * 8, (j & 1) ? b1_ : b0_);                     \
+    const int k0_ = (kt) * BK, j_ = (d) % NBW;                                                   \
+    const bool in_ = k0_ + cc[j_ & 1] * 8 < K;                                                   \
+    if ((d) < NBW)                                                                               \
+      dma16(ra, (ST) + (64 * wave + 8 * j_) * 8,                                                 \
+            in_ ? avo[j_ & 1] + j_ * arow8 + (uint32_t)k0_ * sizeof(bf16) : kOOB);               \
+    else                                                                                         \
+      dma16(rb[j_], (ST) + (BM + 64 * wave + 8 * j_) * 8,                                        \
+            in_ ? bvo[j_ & 1] + (uint32_t)k0_ * sizeof(bf16) : kOOB);                            \
   } while (0)
 
   f32x16 acc[MI][NJ];
@@ -571,21 +581,28 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BM
   const int fsw = ((lane & 31) >> 1) & 7, hh = lane >> 5;
   const int arow = (wm * WM + (lane & 31)) * 8, brow = (BM + wn * WN + (lane & 31)) * 8;
   bf16x8 fa0[MI], fb0[NJ], fa1[MI], fb1[NJ];
-#define K2_READ(FA, FB, ST, s)                                                                   \
+#define K2_FENCE() __builtin_amdgcn_sched_barrier(0)
+  // fragment q of sub-step s from stage ST: A blocks 0..MI-1, then B blocks 0..NJ-1
+#define K2_READ1(FA, FB, ST, s, q)                                                               \
   do {                                                                                           \
     const int ch_ = (2 * (s) + hh) ^ fsw;                                                        \
-    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                               \
-      FA[i] = __builtin_bit_cast(bf16x8, (ST)[arow + i * 32 * 8 + ch_]);                         \
-    _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                               \
-      FB[j] = __builtin_bit_cast(bf16x8, (ST)[brow + j * 32 * 8 + ch_]);                         \
+    if ((q) < MI) FA[(q) % MI] = __builtin_bit_cast(bf16x8, (ST)[arow + ((q) % MI) * 256 + ch_]); \
+    else FB[((q) - MI) % NJ] = __builtin_bit_cast(bf16x8, (ST)[brow + (((q) - MI) % NJ) * 256 + ch_]); \
   } while (0)
-#define K2_MMA(FA, FB)                                                                           \
+  // one sub-step: the matrix-core work of (FA, FB); after instruction q, fragment q of sub-step RS
+  // of stage RST into (GA, GB) (q < NRD, RS >= 0) and, every NMF/ND instructions, DMA D0 + q/(NMF/ND)
+  // of slab DK into DST
+#define K2_STEP(FA, FB, GA, GB, RST, RS, DST, DK, D0, ND)                                        \
   do {                                                                                           \
-    _Pragma("unroll") for (int i = 0; i < MI; ++i)                                               \
-      _Pragma("unroll") for (int j = 0; j < NJ; ++j)                                             \
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[j], FA[i], acc[i][j], 0, 0, 0);    \
+    _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                            \
+      acc[q / NJ][q % NJ] =                                                                      \
+          __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[q % NJ], FA[q / NJ], acc[q / NJ][q % NJ], 0, 0, 0); \
+      if ((RS) >= 0 && q < NRD) K2_READ1(GA, GB, RST, RS, q);                                    \
+      if ((ND) > 0 && q % (NMF / ((ND) > 0 ? (ND) : 1)) == 0)                                    \
+        K2_DMA1(DST, DK, (D0) + q / (NMF / ((ND) > 0 ? (ND) : 1)));                              \
+      K2_FENCE();                                                                                \
+    }                                                                                            \
   } while (0)
-#define K2_FENCE() __builtin_amdgcn_sched_barrier(0)
 #define K2_BARRIER()                   \
   do {                                 \
     asm volatile("" ::: "memory");     \
@@ -594,79 +611,51 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BM
     K2_FENCE();                        \
     asm volatile("" ::: "memory");     \
   } while (0)
-  // Scheduling groups (mask, count): the next sub-step's 8 fragment reads go out before this
-  // sub-step's 16 matrix-core instructions; in the sub-step after the barrier the 16 DMA
-  // instructions of slab k+2 alternate with them.
-#define K2_ORDER()                                      \
-  do {                                                  \
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  \
-    __builtin_amdgcn_sched_group_barrier(0x008, 16, 0); \
-    K2_FENCE();                                         \
-  } while (0)
-#define K2_ORDER_DMA()                                                             \
-  do {                                                                             \
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                             \
-    _Pragma("unroll") for (int q_ = 0; q_ < 16; ++q_) {                            \
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                           \
-      __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                           \
-    }                                                                              \
-    K2_FENCE();                                                                    \
-  } while (0)
-  // The loop turns at the slab barrier. Entering K2_TURN, sub-steps 0..2 of slab k (stage CUR) are
-  // issued and slab k's last fragments are being read into fa1/fb1; slab k+1 is streaming into NXT.
-  // K2_TURN finishes slab k, refills CUR with slab k+2 and runs sub-steps 0..2 of slab k+1.
-#define K2_TURN(CUR, NXT, k)                                                                  \
-  do {                                                                                        \
-    K2_WAIT_VM(0);                                                                            \
-    K2_WAIT_LGKM0(); /* every read of CUR has landed */                                       \
-    K2_BARRIER();                                                                             \
-    K2_ISSUE(CUR, (k) + 2);                                                                   \
-    K2_READ(fa0, fb0, NXT, 0);                                                                \
-    K2_MMA(fa1, fb1);                                                                         \
-    K2_ORDER_DMA();                                                                           \
-    K2_READ(fa1, fb1, NXT, 1);                                                                \
-    K2_MMA(fa0, fb0);                                                                         \
-    K2_ORDER();                                                                               \
-    K2_READ(fa0, fb0, NXT, 2);                                                                \
-    K2_MMA(fa1, fb1);                                                                         \
-    K2_ORDER();                                                                               \
-    K2_READ(fa1, fb1, NXT, 3);                                                                \
-    K2_MMA(fa0, fb0);                                                                         \
-    K2_ORDER();                                                                               \
+  // The loop turns at the slab barrier. Entering, sub-steps 0..2 of slab k (stage CUR) are issued
+  // and its last fragments are being read into fa1/fb1; slab k+1 is streaming into NXT. The turn
+  // waits for slab k+1, refills CUR with slab k+2, finishes slab k and runs sub-steps 0..2 of k+1.
+#define K2_TURN(CUR, NXT, k)                                                                     \
+  do {                                                                                           \
+    K2_WAIT_VM(0);                                                                               \
+    K2_WAIT_LGKM0(); /* every read of CUR has landed */                                          \
+    K2_BARRIER();                                                                                \
+    if (SPREAD == 0) {                                                                           \
+      _Pragma("unroll") for (int d_ = 0; d_ < DPW; ++d_) K2_DMA1(CUR, (k) + 2, d_);              \
+      K2_FENCE();                                                                                \
+    }                                                                                            \
+    K2_STEP(fa1, fb1, fa0, fb0, NXT, 0, CUR, (k) + 2, 0, SPREAD ? DPW / 2 : 0);                  \
+    K2_STEP(fa0, fb0, fa1, fb1, NXT, 1, CUR, (k) + 2, DPW / 2, SPREAD ? DPW / 2 : 0);            \
+    K2_STEP(fa1, fb1, fa0, fb0, NXT, 2, CUR, (k) + 2, 0, 0);                                     \
+    K2_STEP(fa0, fb0, fa1, fb1, NXT, 3, CUR, (k) + 2, 0, 0);                                     \
   } while (0)
 
   const int nk = (K + BK - 1) / BK;
   const int nk2 = nk < 2 ? 2 : (nk + 1) & ~1;  // slabs past K read zeros: the loop runs in pairs
-  K2_ISSUE(st0, 0);
-  K2_ISSUE(st1, 1);
-  K2_WAIT_VM(16);  // this wave's DMA of slab 0 landed; slab 1's 16 may still be in flight
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) K2_DMA1(st0, 0, d);
+#pragma unroll
+  for (int d = 0; d < DPW; ++d) K2_DMA1(st1, 1, d);
+  K2_WAIT_VM(DPW);  // this wave's DMA of slab 0 landed; slab 1's may still be in flight
   K2_BARRIER();
-  K2_READ(fa0, fb0, st0, 0);
-  K2_READ(fa1, fb1, st0, 1);
-  K2_MMA(fa0, fb0);
-  K2_ORDER();
-  K2_READ(fa0, fb0, st0, 2);
-  K2_MMA(fa1, fb1);
-  K2_ORDER();
-  K2_READ(fa1, fb1, st0, 3);
-  K2_MMA(fa0, fb0);
-  K2_ORDER();
+#pragma unroll
+  for (int q = 0; q < NRD; ++q) K2_READ1(fa0, fb0, st0, 0, q);
+  K2_STEP(fa0, fb0, fa1, fb1, st0, 1, st0, 0, 0, 0);
+  K2_STEP(fa1, fb1, fa0, fb0, st0, 2, st0, 0, 0, 0);
+  K2_STEP(fa0, fb0, fa1, fb1, st0, 3, st0, 0, 0, 0);
   for (int kt = 0; kt < nk2 - 2; kt += 2) {
     K2_TURN(st0, st1, kt);
     K2_TURN(st1, st0, kt + 1);
   }
   K2_TURN(st0, st1, nk2 - 2);
   K2_WAIT_LGKM0();
-  K2_MMA(fa1, fb1);  // last sub-step of slab nk2 - 1
-  K2_WAIT_VM(0);     // no DMA may still write LDS when the workgroup retires
+  K2_STEP(fa1, fb1, fa0, fb0, st0, -1, st0, 0, 0, 0);  // last sub-step of slab nk2 - 1
+  K2_WAIT_VM(0);  // no DMA may still write LDS when the workgroup retires
 #undef K2_TURN
-#undef K2_ORDER
-#undef K2_ORDER_DMA
 #undef K2_BARRIER
+#undef K2_STEP
+#undef K2_READ1
 #undef K2_FENCE
-#undef K2_MMA
-#undef K2_READ
-#undef K2_ISSUE
+#undef K2_DMA1
   epi.template apply<Lay<32>, MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M);
 }
 
@@ -674,26 +663,39 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BM
 // Launch configurations
 // ---------------------------------------------------------------------------------------------
 template <typename T> struct Cfg;
-template <> struct Cfg<bf16> { static constexpr int BM = 256, BN = 256, WM = 128, WN = 128; static constexpr bool DMA = true; };
+template <> struct Cfg<bf16> {
+  static constexpr int BM = 256, BN = 256, WM = 128, WN = 128;
+  static constexpr bool DMA = true;
+};
 template <> struct Cfg<float> { static constexpr int BM = 64, BN = 128, WM = 32, WN = 128; static constexpr bool DMA = false; };
 
-template <typename T, class C, class BMap, class Epi>
+template <typename T, class C, class BMap, class Epi, int SPREAD = 2>
 static hipError_t launch_cfg(const GemmA& a, int Ntot, const BMap& bmap, const Epi& epi, hipStream_t s) {
   constexpr int NT = (C::BM / C::WM) * (C::BN / C::WN) * 64;
   if (a.M <= 0 || Ntot <= 0) return hipSuccess;
   const int tiles = ((a.M + C::BM - 1) / C::BM) * ((Ntot + C::BN - 1) / C::BN);
   if constexpr (sizeof(T) == 2 && C::DMA)
-    hipLaunchKernelGGL((gemm_bf16_kernel<BMap, Epi>), dim3(tiles), dim3(256), 0, s, (const bf16*)a.A, a.lda, a.M,
-                       a.K, Ntot, bmap, epi);
+    hipLaunchKernelGGL((gemm_bf16_kernel<SPREAD, BMap, Epi>), dim3(tiles), dim3(256), 0, s, (const bf16*)a.A, a.lda,
+                       a.M, a.K, Ntot, bmap, epi);
   else
     hipLaunchKernelGGL((gemm_kernel<T, C::BM, C::BN, C::WM, C::WN, BMap, Epi>), dim3(tiles), dim3(NT), 0, s,
                        (const T*)a.A, a.lda, a.M, a.K, Ntot, bmap, epi);
   return hipGetLastError();
 }
 
+// bf16: the DMA schedule follows the weight matrix's size. Weights larger than the 256 MB
+// last-level cache are re-read from HBM by every group of M tiles, and their slabs need the whole
+// slab period to land (DMA right after the barrier); cache-resident weights do better with the
+// DMA spread among the matrix-core instructions (measured on the block's four GEMM shapes).
+constexpr size_t kLastLevelCacheBytes = size_t(256) << 20;
+
 template <typename T, class BMap, class Epi>
 static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& epi, hipStream_t s) {
-  return launch_cfg<T, Cfg<T>>(a, Ntot, bmap, epi, s);
+  if constexpr (sizeof(T) == 2) {
+    if ((size_t)Ntot * a.K * sizeof(T) > kLastLevelCacheBytes)
+      return launch_cfg<T, Cfg<T>, BMap, Epi, 0>(a, Ntot, bmap, epi, s);
+  }
+  return launch_cfg<T, Cfg<T>, BMap, Epi, 2>(a, Ntot, bmap, epi, s);
 }
 
 template <typename T, int HD>
