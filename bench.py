@@ -35,7 +35,7 @@ COPY_BYTES = 1 << 30
 KERNELS = ("modulation", "modnorm", "gemm_qkvg", "attention", "gemm_out", "gemm_swiglu", "gemm_down", "rope")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "flow_matching_diffusion_amd", "csrc", f) for f in
-                  ("gemm.hip", "k2_device.h", "attention.hip", "elementwise.hip")]
+                  ("gemm.hip", "k2_device.h", "k2_tiles.h", "attention.hip", "elementwise.hip")]
 
 
 def block_flops(d, B, L, valid_keys):

@@ -24,6 +24,7 @@
 //            (used for img_in / txt_in / final layer / the time MLP).
 #include "k2_device.h"
 #include "k2_kernels.h"
+#include "k2_tiles.h"
 
 namespace k2 {
 
@@ -307,26 +308,6 @@ struct EpiQkvg {
 // ---------------------------------------------------------------------------------------------
 // Tile order
 // ---------------------------------------------------------------------------------------------
-#ifndef K2_TILE_GROUP
-#define K2_TILE_GROUP 8
-#endif
-#ifndef K2_TILE_XCD
-#define K2_TILE_XCD 1
-#endif
-__device__ __forceinline__ void tile_coords(int bid, int nb, int tiles_m, int tiles_n, int& tm, int& tn) {
-  int logical = bid;
-  if (K2_TILE_XCD) {
-    const int per = nb >> 3, rem = nb & 7, xcd = bid & 7, loc = bid >> 3;
-    logical = (xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per) + loc;
-  }
-  constexpr int GM = K2_TILE_GROUP;
-  const int group_size = GM * tiles_n;
-  const int group = logical / group_size, first_m = group * GM;
-  const int gm = min(tiles_m - first_m, GM);
-  const int r = logical - group * group_size;
-  tm = first_m + r % gm;
-  tn = r / gm;
-}
 
 // ---------------------------------------------------------------------------------------------
 // Main loop
@@ -339,7 +320,7 @@ __device__ __forceinline__ int swz128(int row) { return (row >> 1) & 7; }
 
 template <typename T, int BM, int BN, int WM, int WN, class BMap, class Epi>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
-gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap, Epi epi) {
+gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, int scn, BMap bmap, Epi epi) {
   constexpr int NWN = BN / WN, NW = (BM / WM) * NWN, NT = NW * 64;
   constexpr int EPC = 16 / sizeof(T);  // elements per 16-byte chunk
   constexpr int CPR = 8;               // chunks per 128-byte LDS row
@@ -364,7 +345,7 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
   const int wm = wave / NWN, wn = wave % NWN;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (Ntot + BN - 1) / BN;
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_coords(blockIdx.x, tiles_m, tiles_n, scn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // Thread tid moves chunk column c of rows r + i * RSTEP (i < A_LD / B_LD) of each slab.
@@ -513,7 +494,7 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap,
 // ---------------------------------------------------------------------------------------------
 template <int SPREAD, class BMap, class Epi>
 __global__ void __launch_bounds__(256)
-gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BMap bmap, Epi epi) {
+gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int scn, BMap bmap, Epi epi) {
   constexpr int BM = 256, BN = 256, WM = 128, WN = 128, BK = 64;
   constexpr int MI = WM / 32, NJ = WN / 32;
   constexpr int NRD = MI + NJ, NMF = MI * NJ;  // fragment reads / matrix-core ops per sub-step
@@ -530,7 +511,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, BM
   const int wm = wave >> 1, wn = wave & 1;
   const int tiles_m = (M + BM - 1) / BM, tiles_n = (Ntot + BN - 1) / BN;
   int tm, tn;
-  tile_coords(blockIdx.x, gridDim.x, tiles_m, tiles_n, tm, tn);
+  tile_coords(blockIdx.x, tiles_m, tiles_n, scn, tm, tn);
   const int m0 = tm * BM, n0 = tn * BN;
 
   // DMA duties: wave w moves A rows 64w .. 64w+63 and B rows 64w .. 64w+63 of the tile, 8 blocks of
@@ -669,33 +650,39 @@ template <> struct Cfg<bf16> {
 };
 template <> struct Cfg<float> { static constexpr int BM = 64, BN = 128, WM = 32, WN = 128; static constexpr bool DMA = false; };
 
-template <typename T, class C, class BMap, class Epi, int SPREAD = 2>
-static hipError_t launch_cfg(const GemmA& a, int Ntot, const BMap& bmap, const Epi& epi, hipStream_t s) {
+template <typename T, class C, class BMap, class Epi, int SPREAD>
+static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap, const Epi& epi, hipStream_t s) {
   constexpr int NT = (C::BM / C::WM) * (C::BN / C::WN) * 64;
-  if (a.M <= 0 || Ntot <= 0) return hipSuccess;
   const int tiles = ((a.M + C::BM - 1) / C::BM) * ((Ntot + C::BN - 1) / C::BN);
   if constexpr (sizeof(T) == 2 && C::DMA)
     hipLaunchKernelGGL((gemm_bf16_kernel<SPREAD, BMap, Epi>), dim3(tiles), dim3(256), 0, s, (const bf16*)a.A, a.lda,
-                       a.M, a.K, Ntot, bmap, epi);
+                       a.M, a.K, Ntot, scn, bmap, epi);
   else
     hipLaunchKernelGGL((gemm_kernel<T, C::BM, C::BN, C::WM, C::WN, BMap, Epi>), dim3(tiles), dim3(NT), 0, s,
-                       (const T*)a.A, a.lda, a.M, a.K, Ntot, bmap, epi);
+                       (const T*)a.A, a.lda, a.M, a.K, Ntot, scn, bmap, epi);
   return hipGetLastError();
 }
 
-// bf16: the DMA schedule follows the weight matrix's size. Weights larger than the 256 MB
-// last-level cache are re-read from HBM by every group of M tiles, and their slabs need the whole
-// slab period to land (DMA right after the barrier); cache-resident weights do better with the
-// DMA spread among the matrix-core instructions (measured on the block's four GEMM shapes).
+// Launch policy, from measurements on the block's GEMM shapes:
+//  - tile order: super-columns (see tile_coords) when the weights are the larger operand; when the
+//    activations are larger, their re-reads per super-column cost more than they save;
+//  - bf16 DMA schedule: spread among the matrix-core instructions, unless the weight rows in use at
+//    once exceed the 256 MB last-level cache, in which case their slabs come from HBM and need the
+//    whole slab period to land (DMA right after the barrier).
 constexpr size_t kLastLevelCacheBytes = size_t(256) << 20;
 
 template <typename T, class BMap, class Epi>
 static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& epi, hipStream_t s) {
+  typedef Cfg<T> C;
+  if (a.M <= 0 || Ntot <= 0) return hipSuccess;
+  const int tiles_n = (Ntot + C::BN - 1) / C::BN;
+  const size_t a_bytes = (size_t)a.M * a.K * sizeof(T), b_bytes = (size_t)Ntot * a.K * sizeof(T);
+  const int scn = b_bytes >= a_bytes ? super_cols(tiles_n, C::BN, a.K, sizeof(T)) : tiles_n;
   if constexpr (sizeof(T) == 2) {
-    if ((size_t)Ntot * a.K * sizeof(T) > kLastLevelCacheBytes)
-      return launch_cfg<T, Cfg<T>, BMap, Epi, 0>(a, Ntot, bmap, epi, s);
+    if ((size_t)scn * C::BN * a.K * sizeof(T) > kLastLevelCacheBytes)
+      return launch_cfg<T, C, BMap, Epi, 0>(a, Ntot, scn, bmap, epi, s);
   }
-  return launch_cfg<T, Cfg<T>, BMap, Epi, 2>(a, Ntot, bmap, epi, s);
+  return launch_cfg<T, C, BMap, Epi, 2>(a, Ntot, scn, bmap, epi, s);
 }
 
 template <typename T, int HD>
