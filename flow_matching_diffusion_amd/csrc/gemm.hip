@@ -492,31 +492,25 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, int scn, B
 // after the barrier, which keeps them from stalling the wave in a burst (measured 10-15% faster
 // when the operands stay cache-resident).
 // ---------------------------------------------------------------------------------------------
-template <int SPREAD, class BMap, class Epi>
-__global__ void __launch_bounds__(256)
-gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int scn, BMap bmap, Epi epi) {
-  constexpr int BM = 256, BN = 256, WM = 128, WN = 128, BK = 64;
-  constexpr int MI = WM / 32, NJ = WN / 32;
+//
+// NJ picks the wave's N width (32 * NJ): 4 gives the 256x256 tile; 2 a 256x128 half tile, used to
+// split the last partial round of tiles so that it takes half as long (see gemm_bf16_kernel).
+template <int SPREAD, int NJ, class BMap, class Epi>
+__device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int m0, int n0,
+                                          const BMap& bmap, const Epi& epi, uint4* st0, uint4* st1) {
+  constexpr int BM = 256, BN = 64 * NJ, WM = 128, WN = 32 * NJ, BK = 64;
+  constexpr int MI = WM / 32;
   constexpr int NRD = MI + NJ, NMF = MI * NJ;  // fragment reads / matrix-core ops per sub-step
-  constexpr int NBW = 8;                       // 1 KB DMA blocks per wave and operand per slab
-  constexpr int DPW = 2 * NBW;                 // DMA instructions per wave per slab
-  constexpr int STAGE = (BM + BN) * 8;         // uint4 per stage
-  static_assert(SPREAD == 0 || SPREAD == 2, "DMA schedule");
-
-  __shared__ uint4 st0[STAGE];
-  __shared__ uint4 st1[STAGE];
+  constexpr int NBA = 8, NBB = BN / 32;        // 1 KB DMA blocks (8 rows) per wave per slab: A, B
+  constexpr int DPW = NBA + NBB;               // DMA instructions per wave per slab
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: resources live in SGPRs
   const int wm = wave >> 1, wn = wave & 1;
-  const int tiles_m = (M + BM - 1) / BM, tiles_n = (Ntot + BN - 1) / BN;
-  int tm, tn;
-  tile_coords(blockIdx.x, tiles_m, tiles_n, scn, tm, tn);
-  const int m0 = tm * BM, n0 = tn * BN;
 
-  // DMA duties: wave w moves A rows 64w .. 64w+63 and B rows 64w .. 64w+63 of the tile, 8 blocks of
-  // 8 rows each. Block j's rows are 8j .. 8j+7 past the wave's first row; swz128 of its rows depends
-  // only on j's parity, so two chunk choices cover all blocks.
+  // DMA duties: wave w moves A rows 64w .. 64w+63 and B rows 8*NBB*w .. of the tile, in blocks of
+  // 8 rows. Block j's rows are 8j .. 8j+7 past the wave's first row; swz128 of its rows depends only
+  // on j's parity, so two chunk choices cover all blocks.
   const int pos = lane & 7, lr = lane >> 3;
   const int cc[2] = {pos ^ ((lr >> 1) & 7), pos ^ ((4 + (lr >> 1)) & 7)};
   const rsrc_t ra = make_rsrc(A + (size_t)m0 * lda, (size_t)(M - m0) * lda * sizeof(bf16));
@@ -527,26 +521,28 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, in
     bvo[p] = (uint32_t)(lr * bmap.ldb + cc[p] * 8) * sizeof(bf16);
   }
   const uint32_t arow8 = (uint32_t)(8 * lda) * sizeof(bf16);  // byte distance of consecutive A blocks
-  rsrc_t rb[NBW];
+  rsrc_t rb[NBB];
 #pragma unroll
-  for (int j = 0; j < NBW; ++j) {
-    const int n = n0 + 64 * wave + 8 * j;
+  for (int j = 0; j < NBB; ++j) {
+    const int n = n0 + 8 * NBB * wave + 8 * j;
     int nvalid = 0;
     const bf16* base = n < Ntot ? bmap.group(n, nvalid) : A;
     nvalid = n < Ntot ? (nvalid < 0 ? 0 : (nvalid > 8 ? 8 : nvalid)) : 0;
     rb[j] = make_rsrc(base, (size_t)nvalid * bmap.ldb * sizeof(bf16));
   }
-  // DMA instruction d (0..15) of slab kt into stage ST: A blocks first, then B blocks
+  // DMA instruction d (0 .. DPW-1) of slab kt into stage ST: A blocks first, then B blocks
 #define K2_DMA1(ST, kt, d)                                                                       \
   do {                                                                                           \
-    const int k0_ = (kt) * BK, j_ = (d) % NBW;                                                   \
-    const bool in_ = k0_ + cc[j_ & 1] * 8 < K;                                                   \
-    if ((d) < NBW)                                                                               \
+    const int k0_ = (kt) * BK;                                                                   \
+    if ((d) < NBA) {                                                                             \
+      const int j_ = (d) % NBA;                                                                  \
       dma16(ra, (ST) + (64 * wave + 8 * j_) * 8,                                                 \
-            in_ ? avo[j_ & 1] + j_ * arow8 + (uint32_t)k0_ * sizeof(bf16) : kOOB);               \
-    else                                                                                         \
-      dma16(rb[j_], (ST) + (BM + 64 * wave + 8 * j_) * 8,                                        \
-            in_ ? bvo[j_ & 1] + (uint32_t)k0_ * sizeof(bf16) : kOOB);                            \
+            k0_ + cc[j_ & 1] * 8 < K ? avo[j_ & 1] + j_ * arow8 + (uint32_t)k0_ * sizeof(bf16) : kOOB); \
+    } else {                                                                                     \
+      const int j_ = ((d) - NBA) % NBB;                                                          \
+      dma16(rb[j_], (ST) + (BM + 8 * NBB * wave + 8 * j_) * 8,                                   \
+            k0_ + cc[j_ & 1] * 8 < K ? bvo[j_ & 1] + (uint32_t)k0_ * sizeof(bf16) : kOOB);       \
+    }                                                                                            \
   } while (0)
 
   f32x16 acc[MI][NJ];
@@ -571,16 +567,16 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, in
     else FB[((q) - MI) % NJ] = __builtin_bit_cast(bf16x8, (ST)[brow + (((q) - MI) % NJ) * 256 + ch_]); \
   } while (0)
   // one sub-step: the matrix-core work of (FA, FB); after instruction q, fragment q of sub-step RS
-  // of stage RST into (GA, GB) (q < NRD, RS >= 0) and, every NMF/ND instructions, DMA D0 + q/(NMF/ND)
-  // of slab DK into DST
+  // of stage RST into (GA, GB) (q < NRD, RS >= 0) and DMA instructions D0 + [ceil(q ND / NMF),
+  // ceil((q+1) ND / NMF)) of slab DK into DST (ND spread evenly over the NMF instructions)
 #define K2_STEP(FA, FB, GA, GB, RST, RS, DST, DK, D0, ND)                                        \
   do {                                                                                           \
     _Pragma("unroll") for (int q = 0; q < NMF; ++q) {                                            \
       acc[q / NJ][q % NJ] =                                                                      \
           __builtin_amdgcn_mfma_f32_32x32x16_bf16(FB[q % NJ], FA[q / NJ], acc[q / NJ][q % NJ], 0, 0, 0); \
       if ((RS) >= 0 && q < NRD) K2_READ1(GA, GB, RST, RS, q);                                    \
-      if ((ND) > 0 && q % (NMF / ((ND) > 0 ? (ND) : 1)) == 0)                                    \
-        K2_DMA1(DST, DK, (D0) + q / (NMF / ((ND) > 0 ? (ND) : 1)));                              \
+      _Pragma("unroll") for (int d_ = (q * (ND) + NMF - 1) / NMF; d_ < ((q + 1) * (ND) + NMF - 1) / NMF; ++d_) \
+        K2_DMA1(DST, DK, (D0) + d_);                                                             \
       K2_FENCE();                                                                                \
     }                                                                                            \
   } while (0)
@@ -595,6 +591,7 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, in
   // The loop turns at the slab barrier. Entering, sub-steps 0..2 of slab k (stage CUR) are issued
   // and its last fragments are being read into fa1/fb1; slab k+1 is streaming into NXT. The turn
   // waits for slab k+1, refills CUR with slab k+2, finishes slab k and runs sub-steps 0..2 of k+1.
+  constexpr int DH = DPW / 2;
 #define K2_TURN(CUR, NXT, k)                                                                     \
   do {                                                                                           \
     K2_WAIT_VM(0);                                                                               \
@@ -604,8 +601,8 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, in
       _Pragma("unroll") for (int d_ = 0; d_ < DPW; ++d_) K2_DMA1(CUR, (k) + 2, d_);              \
       K2_FENCE();                                                                                \
     }                                                                                            \
-    K2_STEP(fa1, fb1, fa0, fb0, NXT, 0, CUR, (k) + 2, 0, SPREAD ? DPW / 2 : 0);                  \
-    K2_STEP(fa0, fb0, fa1, fb1, NXT, 1, CUR, (k) + 2, DPW / 2, SPREAD ? DPW / 2 : 0);            \
+    K2_STEP(fa1, fb1, fa0, fb0, NXT, 0, CUR, (k) + 2, 0, SPREAD ? DH : 0);                       \
+    K2_STEP(fa0, fb0, fa1, fb1, NXT, 1, CUR, (k) + 2, DH, SPREAD ? DPW - DH : 0);                \
     K2_STEP(fa1, fb1, fa0, fb0, NXT, 2, CUR, (k) + 2, 0, 0);                                     \
     K2_STEP(fa0, fb0, fa1, fb1, NXT, 3, CUR, (k) + 2, 0, 0);                                     \
   } while (0)
@@ -640,6 +637,29 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, in
   epi.template apply<Lay<32>, MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M);
 }
 
+// Workgroups 0 .. nmain-1 each compute a 256x256 tile (tile order: tile_coords). With TAIL, the
+// tiles_total - nmain tiles of the last partial round are split in two 256x128 halves run by
+// workgroups nmain + 2u and nmain + 2u + 1 (u: tail tile index), so that round takes about half as
+// long; TAIL is used when the halves fit in one round.
+template <int SPREAD, bool TAIL, class BMap, class Epi>
+__global__ void __launch_bounds__(256)
+gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int scn, int nmain, BMap bmap,
+                 Epi epi) {
+  __shared__ uint4 st0[(256 + 256) * 8];
+  __shared__ uint4 st1[(256 + 256) * 8];
+  const int tiles_m = (M + 255) / 256, tiles_n = (Ntot + 255) / 256;
+  const int bid = blockIdx.x;
+  int tm, tn;
+  if (!TAIL || bid < nmain) {
+    tile_coords(bid, tiles_m, tiles_n, scn, tm, tn);
+    gemm_tile<SPREAD, 4>(A, lda, M, K, Ntot, tm * 256, tn * 256, bmap, epi, st0, st1);
+  } else if constexpr (TAIL) {
+    const int u = bid - nmain;
+    tile_coords(nmain + (u >> 1), tiles_m, tiles_n, scn, tm, tn);
+    gemm_tile<SPREAD, 2>(A, lda, M, K, Ntot, tm * 256, tn * 256 + (u & 1) * 128, bmap, epi, st0, st1);
+  }
+}
+
 // ---------------------------------------------------------------------------------------------
 // Launch configurations
 // ---------------------------------------------------------------------------------------------
@@ -650,16 +670,40 @@ template <> struct Cfg<bf16> {
 };
 template <> struct Cfg<float> { static constexpr int BM = 64, BN = 128, WM = 32, WN = 128; static constexpr bool DMA = false; };
 
-template <typename T, class C, class BMap, class Epi, int SPREAD>
+// Compute units of the current device (one bf16 GEMM workgroup runs per compute unit).
+static int compute_units() {
+  static thread_local int dev_cached = -1, cu_cached = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != dev_cached) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    dev_cached = dev;
+    cu_cached = n;
+  }
+  return cu_cached;
+}
+
+template <typename T, class C, class BMap, class Epi, int SPREAD, bool TAIL>
 static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap, const Epi& epi, hipStream_t s) {
   constexpr int NT = (C::BM / C::WM) * (C::BN / C::WN) * 64;
   const int tiles = ((a.M + C::BM - 1) / C::BM) * ((Ntot + C::BN - 1) / C::BN);
-  if constexpr (sizeof(T) == 2 && C::DMA)
-    hipLaunchKernelGGL((gemm_bf16_kernel<SPREAD, BMap, Epi>), dim3(tiles), dim3(256), 0, s, (const bf16*)a.A, a.lda,
-                       a.M, a.K, Ntot, scn, bmap, epi);
-  else
+  if constexpr (sizeof(T) == 2 && C::DMA) {
+    int nmain = tiles, grid = tiles;
+    if constexpr (TAIL) {
+      const int ncu = compute_units();
+      const int tail = tiles % ncu;
+      if (tiles > ncu && tail > 0 && 2 * tail <= ncu) {
+        nmain = tiles - tail;
+        grid = nmain + 2 * tail;
+      }
+    }
+    hipLaunchKernelGGL((gemm_bf16_kernel<SPREAD, TAIL, BMap, Epi>), dim3(grid), dim3(256), 0, s, (const bf16*)a.A,
+                       a.lda, a.M, a.K, Ntot, scn, nmain, bmap, epi);
+  } else {
     hipLaunchKernelGGL((gemm_kernel<T, C::BM, C::BN, C::WM, C::WN, BMap, Epi>), dim3(tiles), dim3(NT), 0, s,
                        (const T*)a.A, a.lda, a.M, a.K, Ntot, scn, bmap, epi);
+  }
   return hipGetLastError();
 }
 
@@ -671,7 +715,7 @@ static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap
 //    whole slab period to land (DMA right after the barrier).
 constexpr size_t kLastLevelCacheBytes = size_t(256) << 20;
 
-template <typename T, class BMap, class Epi>
+template <typename T, class BMap, class Epi, bool TAIL = false>
 static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& epi, hipStream_t s) {
   typedef Cfg<T> C;
   if (a.M <= 0 || Ntot <= 0) return hipSuccess;
@@ -680,9 +724,9 @@ static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& 
   const int scn = b_bytes >= a_bytes ? super_cols(tiles_n, C::BN, a.K, sizeof(T)) : tiles_n;
   if constexpr (sizeof(T) == 2) {
     if ((size_t)scn * C::BN * a.K * sizeof(T) > kLastLevelCacheBytes)
-      return launch_cfg<T, C, BMap, Epi, 0>(a, Ntot, scn, bmap, epi, s);
+      return launch_cfg<T, C, BMap, Epi, 0, TAIL>(a, Ntot, scn, bmap, epi, s);
   }
-  return launch_cfg<T, C, BMap, Epi, 2>(a, Ntot, scn, bmap, epi, s);
+  return launch_cfg<T, C, BMap, Epi, 2, TAIL>(a, Ntot, scn, bmap, epi, s);
 }
 
 template <typename T, int HD>
@@ -719,7 +763,7 @@ static hipError_t resid_t(const GemmA& a, const ResidArgs& p, hipStream_t s) {
   bm.p[0] = (const T*)p.w; bm.start[0] = 0; bm.start[1] = p.N; bm.nseg = 1; bm.ldb = a.K;
   EpiResid<T> e;
   e.hin = p.hin; e.hout = p.hout; e.gate = p.gate; e.gate_stride = p.gate_stride; e.L = p.L; e.N = p.N;
-  return launch<T>(a, p.N, bm, e, s);
+  return launch<T, BSegs<T>, EpiResid<T>, true>(a, p.N, bm, e, s);
 }
 
 template <typename T>
@@ -729,7 +773,7 @@ static hipError_t plain_t(const GemmA& a, const PlainArgs& p, hipStream_t s) {
   EpiPlain<T> e;
   e.bias = p.bias; e.outf = p.outf; e.ldf = p.ldf; e.outt = (T*)p.outt; e.ldt = p.ldt; e.act = p.act;
   e.N = p.N; e.rpb = p.rows_per_b; e.orpb = p.out_rows_per_b; e.ooff = p.out_row_off;
-  return launch<T>(a, p.N, bm, e, s);
+  return launch<T, BSegs<T>, EpiPlain<T>, true>(a, p.N, bm, e, s);
 }
 
 hipError_t gemm_qkvg(int dt, const GemmA& a, const QkvgArgs& p, hipStream_t s) {
