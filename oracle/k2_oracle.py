@@ -46,6 +46,17 @@ Readings where the pages are silent or garbled (each restated where it is used):
       time-MLP inputs, the fused text before txt_in and the final-layer norm output. Everything
       else (residual stream, statistics, softmax, accumulation) stays float64. rnd=None is the
       exact function.
+  R14 sampler shift ([PIPELINE] Krea2Pipeline, scheduler and is_distilled parameters): mu is the
+      straight line through (base_image_seq_len, base_shift) = (256, 0.5) and
+      (max_image_seq_len, max_shift) = (6400, 1.15) evaluated at the image token count; the
+      distilled checkpoint uses mu = 1.15. The named "exponential time shift" is taken as
+      sigma -> e^mu / (e^mu + (1/sigma - 1)), which fixes sigma = 1 and is the identity at mu = 0.
+  R15 sigma grid ([PIPELINE] __call__, sigmas parameter): linspace(1, 1/N, N), shifted, then a
+      terminal 0 appended (N + 1 values); the transformer is called at timestep t = sigma_i (its
+      time path multiplies by 1000, R10).
+  R16 update ([PIPELINE] __call__, guidance_scale parameter): v = cond + g (cond - uncond), with the
+      uncond pass skipped when g <= 0; the Euler step is x <- x + (sigma_{i+1} - sigma_i) v. The
+      latent state is kept in float32 between steps.
 """
 from __future__ import annotations
 
@@ -299,6 +310,69 @@ def backbone_forward(x, enc, t, position_ids, mask, mw, dims, tdims, T, time_dim
         h = block_forward(h, temb, position_ids, mask, bw, dims, T=T, rnd=rnd)
     return final_layer(h[:, T:], e, mw["final_table"], mw.get("final_norm_w"), mw["final_w"],
                        mw["final_b"], dims.eps, rnd=rnd)
+
+
+# ----------------------------------------------------------------------------------------------
+# Sampler: flow-match Euler with the resolution-aware shift and CFG (R14 - R16)
+# ----------------------------------------------------------------------------------------------
+SHIFT_DEFAULTS = dict(base_shift=0.5, max_shift=1.15, base_image_seq_len=256, max_image_seq_len=6400,
+                      distilled_mu=1.15)
+
+
+def shift_mu(image_seq_len, distilled=False, base_shift=0.5, max_shift=1.15, base_image_seq_len=256,
+             max_image_seq_len=6400, distilled_mu=1.15):
+    """mu for an image of image_seq_len tokens: the line through the two (length, shift) points (R14)."""
+    if distilled:
+        return float(distilled_mu)
+    slope = (max_shift - base_shift) / (max_image_seq_len - base_image_seq_len)
+    return float(base_shift + slope * (image_seq_len - base_image_seq_len))
+
+
+def time_shift(mu, sigma):
+    """Exponential time shift e^mu / (e^mu + (1/sigma - 1)) (R14); sigma in (0, 1]."""
+    sigma = np.asarray(sigma, dtype=F64)
+    return math.exp(mu) / (math.exp(mu) + (1.0 / sigma - 1.0))
+
+
+def flow_sigmas(num_steps, image_seq_len, distilled=False, **shift):
+    """The N + 1 noise levels of the sampler (R15): shifted linspace(1, 1/N, N) then 0."""
+    base = np.linspace(1.0, 1.0 / num_steps, num_steps, dtype=F64)
+    mu = shift_mu(image_seq_len, distilled, **shift)
+    return np.concatenate([time_shift(mu, base), [0.0]])
+
+
+def cfg_velocity(v_cond, v_uncond, guidance):
+    """Krea 2's guidance convention: cond + g (cond - uncond); cond alone when g <= 0 (R16)."""
+    v_cond = _f64(v_cond)
+    if guidance <= 0:
+        return v_cond
+    return v_cond + guidance * (v_cond - _f64(v_uncond))
+
+
+def euler_step(x, v, sigma, sigma_next):
+    """x + (sigma_next - sigma) v (R16)."""
+    return _f64(x) + (float(sigma_next) - float(sigma)) * _f64(v)
+
+
+def denoise_step(x, enc, enc_neg, mask, mask_neg, position_ids, mw, dims, tdims, T, sigma, sigma_next, guidance,
+                 time_dim=256, rnd=None):
+    """One sampler step on a single image: the transformer on the (cond, uncond) pair at t = sigma
+    (cond only when guidance <= 0), the guidance combine and the Euler update. x: (1, N, C) latents;
+    enc / enc_neg: (1, T, layers, D) prompt and negative-prompt stacks; masks (1, T) or None.
+    The transformer input is x in the operand precision (rnd), the state stays float64."""
+    r = rnd or _id
+    xin = r(_f64(x))
+    if guidance > 0:
+        xb = np.concatenate([xin, xin], axis=0)
+        eb = np.concatenate([_f64(enc), _f64(enc_neg)], axis=0)
+        mb = None if mask is None else np.concatenate([mask, mask_neg], axis=0)
+        t = np.array([sigma, sigma], dtype=F64)
+        v = backbone_forward(xb, eb, t, position_ids, mb, mw, dims, tdims, T, time_dim=time_dim, rnd=rnd)
+        vel = cfg_velocity(v[:1], v[1:], guidance)
+    else:
+        t = np.array([sigma], dtype=F64)
+        vel = backbone_forward(xin, enc, t, position_ids, mask, mw, dims, tdims, T, time_dim=time_dim, rnd=rnd)
+    return euler_step(x, vel, sigma, sigma_next)
 
 
 # ----------------------------------------------------------------------------------------------
