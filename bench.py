@@ -8,8 +8,9 @@ residual, modulated RMSNorm, SwiGLU, down projection + gated residual) over the 
 weights and activations resident in HBM; temb is computed once before timing (the backbone
 computes it once for all 28 blocks). value = algorithmic block TFLOP/s (GEMMs over every row,
 attention over valid keys only). Also reported: the 28-block backbone with text fusion at the
-same resolution as denoise steps/s (one call = one CFG step), per-kernel times, the roofline of
-the dominant kernel, and the CPU oracle on a bounded sample.
+same resolution as denoise steps/s (one call = one CFG step), the sampler (k2_denoise_step on one image,
+with guidance as the base checkpoint's 28 steps and without as the distilled 8 steps) as time per
+image, per-kernel times, the roofline of the dominant kernel, and the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-backbone] [--no-cpu-baseline]
                        [--cpu-rows R] [--copy-calibration]
@@ -112,6 +113,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="block1024")
     ap.add_argument("--backbone-steps", type=int, default=5)
+    ap.add_argument("--sampler-steps", type=int, default=3)
     ap.add_argument("--no-backbone", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4608)
@@ -247,9 +249,30 @@ def main():
         bflops = bwl.num_layers * flops  # blocks only; text fusion and projections are extra work
         result["denoise_steps_per_s"] = round(1e3 / bms, 3)
         result["backbone"] = {"workload": bwl.name, "ms_per_step": round(bms, 2), "layers": bwl.num_layers,
-                              "block_tflops_in_backbone": round(bflops / (bms * 1e-3) / 1e12, 1),
-                              "base_image_s_28_steps": round(28 * bms / 1e3, 2)}
-        del mw, bws, x, enc
+                              "block_tflops_in_backbone": round(bflops / (bms * 1e-3) / 1e12, 1)}
+        # the sampler on one image: k2_denoise_step (transformer on the prompt / negative-prompt pair,
+        # guidance 4.5, as the base checkpoint's 28-step schedule) and without guidance (distilled, 8 steps)
+        del bws
+        lat = S.device_normal(bwl.seed, "latents", (1, bwl.N, bwl.in_channels), 1.0, f32, dev)
+        sig = k2.flow_sigmas(28, bwl.N)
+        sampler = {}
+        for name, g, steps, G in (("base", 4.5, 28, 2), ("distilled", 0.0, 8, 1)):
+            dws = torch.empty(k2.denoise_workspace_bytes(mcfg, bwl.T, bwl.N, g > 0), dtype=torch.uint8, device=dev)
+            e, mk = enc[:G].contiguous(), bm[:G].contiguous()
+            k2.denoise_step(mcfg, mw, lat, e, bpos, mk, float(sig[0]), float(sig[1]), g, workspace=dws)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(args.sampler_steps):
+                k2.denoise_step(mcfg, mw, lat, e, bpos, mk, float(sig[i]), float(sig[i + 1]), g, workspace=dws)
+            torch.cuda.synchronize()
+            sms = (time.perf_counter() - t0) * 1e3 / args.sampler_steps
+            sampler[name] = {"guidance": g, "transformer_batch": G, "ms_per_step": round(sms, 2),
+                             "image_s": round(steps * sms / 1e3, 2), "steps": steps,
+                             "timed_steps": args.sampler_steps}
+            del dws
+        assert bool(torch.isfinite(lat).all())
+        result["sampler"] = sampler
+        del mw, x, enc, lat
         torch.cuda.empty_cache()
 
     if not args.no_cpu_baseline:

@@ -267,6 +267,64 @@ def backbone_workspace_bytes(cfg, B: int, T: int, N: int) -> int:
     return load().k2_backbone_workspace_bytes(ctypes.byref(cfg), B, T, N)
 
 
+# ------------------------------------------------------------------------------------------------
+# Sampler
+# ------------------------------------------------------------------------------------------------
+def shift_cfg(**kw) -> _abi.ShiftCfg:
+    """k2_shift_cfg with the defaults of k2_shift_cfg_default, fields overridden by keyword."""
+    c = _abi.ShiftCfg()
+    load().k2_shift_cfg_default(ctypes.byref(c))
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def flow_sigmas(num_steps: int, image_seq_len: int, distilled: bool = False, cfg=None):
+    """k2_flow_sigmas (host): the num_steps + 1 noise levels as a float32 NumPy array."""
+    import numpy as np
+    out = (ctypes.c_float * (num_steps + 1))()
+    check(load().k2_flow_sigmas(None if cfg is None else ctypes.byref(cfg), num_steps, image_seq_len,
+                                1 if distilled else 0, out))
+    return np.frombuffer(out, dtype=np.float32).copy()
+
+
+def cfg_euler_update(x, v_cond, v_uncond, guidance: float, sigma: float, sigma_next: float, out=None, stream=None):
+    """k2_cfg_euler_update on float32 device tensors of equal size; returns x_out (x itself if out is x)."""
+    torch = _torch()
+    _dev_tensor(x, "x", torch.float32)
+    _dev_tensor(v_cond, "v_cond", torch.float32)
+    if v_uncond is not None:
+        _dev_tensor(v_uncond, "v_uncond", torch.float32)
+    out = torch.empty_like(x) if out is None else out
+    check(load().k2_cfg_euler_update(_ptr(x), _ptr(out), _ptr(v_cond), _ptr(v_uncond), x.numel(), guidance, sigma,
+                                     sigma_next, _stream(stream)))
+    return out
+
+
+def denoise_workspace_bytes(cfg, T: int, N: int, guided: bool) -> int:
+    return load().k2_denoise_workspace_bytes(ctypes.byref(cfg), T, N, 1 if guided else 0)
+
+
+def denoise_step(cfg, weights: dict, latents, enc, position_ids, mask, sigma: float, sigma_next: float,
+                 guidance: float, workspace=None, stream=None):
+    """k2_denoise_step: latents (1, N, in_channels) float32, updated in place; enc (G, T, layers, D) in the
+    operand dtype with G = 2 (prompt, negative prompt) when guidance > 0, else 1; mask (G, T) or None."""
+    torch = _torch()
+    lib = load()
+    _dev_tensor(latents, "latents", torch.float32)
+    _, N, _ = latents.shape
+    T = enc.shape[1] if enc is not None else 0
+    mask = _mask_u8(mask)
+    mw, keep = _model_weights(weights)
+    ws = _workspace(lib.k2_denoise_workspace_bytes(ctypes.byref(cfg), T, N, 1 if guidance > 0 else 0),
+                    latents.device, workspace)
+    check(lib.k2_denoise_step(ctypes.byref(cfg), ctypes.byref(mw), T, N, _ptr(latents), _ptr(enc), _ptr(mask),
+                              _ptr(position_ids), position_ids.shape[0], position_ids.shape[1], sigma, sigma_next,
+                              guidance, _ptr(ws), ws.numel(), _stream(stream)))
+    del keep
+    return latents
+
+
 def profile_enable(on: bool = True):
     load().k2_profile_enable(1 if on else 0)
 

@@ -60,6 +60,11 @@ class ModelWeights(ctypes.Structure):
                 ("final_table", c_void_p), ("final_norm_w", c_void_p), ("final_w", c_void_p), ("final_b", c_void_p)]
 
 
+class ShiftCfg(ctypes.Structure):
+    _fields_ = [("base_shift", c_float), ("max_shift", c_float), ("base_image_seq_len", c_int),
+                ("max_image_seq_len", c_int), ("distilled_mu", c_float)]
+
+
 # name -> (restype, argtypes): every function declared in include/k2.h
 SIGNATURES = {
     "k2_block_cfg_default": (None, [POINTER(BlockCfg)]),
@@ -79,6 +84,13 @@ SIGNATURES = {
     "k2_backbone_forward": (c_int, [POINTER(ModelCfg), POINTER(ModelWeights), c_int, c_int, c_int, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_size_t,
                                     c_void_p]),
+    "k2_shift_cfg_default": (None, [POINTER(ShiftCfg)]),
+    "k2_flow_sigmas": (c_int, [POINTER(ShiftCfg), c_int, c_int, c_int, POINTER(c_float)]),
+    "k2_cfg_euler_update": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_float, c_float, c_float,
+                                    c_void_p]),
+    "k2_denoise_workspace_bytes": (c_size_t, [POINTER(ModelCfg), c_int, c_int, c_int]),
+    "k2_denoise_step": (c_int, [POINTER(ModelCfg), POINTER(ModelWeights), c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                c_void_p, c_int, c_int, c_float, c_float, c_float, c_void_p, c_size_t, c_void_p]),
     "k2_last_error": (c_char_p, []),
     "k2_profile_enable": (None, [c_int]),
     "k2_profile_reset": (None, []),

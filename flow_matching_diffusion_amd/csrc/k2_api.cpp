@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/k2.h.
 #include <hip/hip_runtime.h>
 
+#include <cmath>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
@@ -554,6 +555,10 @@ size_t k2_backbone_workspace_bytes(const k2_model_cfg* cfg, int B, int T, int N)
   return model_layout(cfg, B, T, N).total;
 }
 
+int backbone_run(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N, const void* hidden_states,
+                 const void* enc, const float* timestep, const float* pos, const uint8_t* mask, float* out,
+                 void* workspace, hipStream_t s);
+
 int k2_backbone_forward(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N,
                         const void* hidden_states, const void* enc, const float* timestep, const float* pos,
                         int pos_rows, int pos_cols, const uint8_t* mask, float* out, void* workspace,
@@ -568,8 +573,15 @@ int k2_backbone_forward(const k2_model_cfg* cfg, const k2_model_weights* w, int 
   const ModelLayout l = model_layout(cfg, B, T, N);
   if ((rc = check_ws(workspace, workspace_bytes, l.total)) != K2_OK) return rc;
   g_err.clear();
+  return backbone_run(cfg, w, B, T, N, hidden_states, enc, timestep, pos, mask, out, workspace, (hipStream_t)stream);
+}
 
-  hipStream_t s = (hipStream_t)stream;
+// The backbone after validation (also the transformer call of k2_denoise_step).
+int backbone_run(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N, const void* hidden_states,
+                 const void* enc, const float* timestep, const float* pos, const uint8_t* mask, float* out,
+                 void* workspace, hipStream_t s) {
+  int rc;
+  const ModelLayout l = model_layout(cfg, B, T, N);
   const int dt = cfg->block.dtype, H = cfg->block.hidden, hd = cfg->block.head_dim, L = T + N;
   const int Dt = cfg->text.block.hidden, C = cfg->in_channels;
   float* temb = (float*)at(workspace, l.temb);
@@ -621,6 +633,118 @@ int k2_backbone_forward(const k2_model_cfg* cfg, const k2_model_weights* w, int 
   p.w = w->final_w; p.N = C; p.bias = w->final_b; p.outf = out; p.ldf = C;
   p.rows_per_b = B * N; p.out_rows_per_b = B * N; p.out_row_off = 0;
   K2_RUN("gemm_plain", s, gemm_plain(dt, GemmA{xf, H, B * N, H}, p, s));
+  return K2_OK;
+}
+
+// ---------------------------------------------------------------------------------------------
+// Sampler: flow-match Euler with the resolution-aware exponential time shift and guidance
+// ([PIPELINE] Krea2Pipeline scheduler / is_distilled parameters, __call__ sigmas / guidance_scale)
+// ---------------------------------------------------------------------------------------------
+void k2_shift_cfg_default(k2_shift_cfg* c) {
+  if (!c) return;
+  c->base_shift = 0.5f;
+  c->max_shift = 1.15f;
+  c->base_image_seq_len = 256;
+  c->max_image_seq_len = 6400;
+  c->distilled_mu = 1.15f;
+}
+
+int k2_flow_sigmas(const k2_shift_cfg* cfg, int num_steps, int image_seq_len, int distilled, float* sigmas_out) {
+  k2_shift_cfg d;
+  k2_shift_cfg_default(&d);
+  const k2_shift_cfg* c = cfg ? cfg : &d;
+  if (!sigmas_out) return fail(K2_ERR_NULL, "sigmas_out is NULL");
+  if (num_steps <= 0) return fail(K2_ERR_SHAPE, "num_steps must be >= 1");
+  if (image_seq_len <= 0) return fail(K2_ERR_SHAPE, "image_seq_len must be >= 1");
+  if (c->max_image_seq_len == c->base_image_seq_len)
+    return fail(K2_ERR_CONFIG, "base_image_seq_len and max_image_seq_len must differ");
+  double mu;
+  if (distilled) {
+    mu = c->distilled_mu;
+  } else {
+    const double slope = ((double)c->max_shift - c->base_shift) / ((double)c->max_image_seq_len - c->base_image_seq_len);
+    mu = c->base_shift + slope * ((double)image_seq_len - c->base_image_seq_len);
+  }
+  const double em = std::exp(mu);
+  for (int i = 0; i < num_steps; ++i) {
+    // linspace(1, 1/N, N)
+    const double sig = num_steps == 1 ? 1.0 : 1.0 + (1.0 / num_steps - 1.0) * i / (num_steps - 1);
+    sigmas_out[i] = (float)(em / (em + (1.0 / sig - 1.0)));
+  }
+  sigmas_out[num_steps] = 0.0f;
+  g_err.clear();
+  return K2_OK;
+}
+
+int k2_cfg_euler_update(const float* x, float* x_out, const float* v_cond, const float* v_uncond, size_t n,
+                        float guidance, float sigma, float sigma_next, void* stream) {
+  if (n == 0) return K2_OK;
+  if (!x || !x_out || !v_cond || (guidance > 0.0f && !v_uncond))
+    return fail(K2_ERR_NULL, "x / x_out / v_cond (/ v_uncond when guidance > 0) is NULL");
+  int rc;
+  if ((rc = check_align("x / x_out / v_cond / v_uncond", {x, x_out, v_cond, v_uncond})) != K2_OK) return rc;
+  if (!std::isfinite(guidance) || !std::isfinite(sigma) || !std::isfinite(sigma_next))
+    return fail(K2_ERR_SHAPE, "guidance and sigmas must be finite");
+  g_err.clear();
+  hipStream_t s = (hipStream_t)stream;
+  K2_RUN("cfg_euler", s, cfg_euler(x, x_out, v_cond, guidance > 0.0f ? v_uncond : nullptr, n, guidance,
+                                   sigma_next - sigma, s));
+  return K2_OK;
+}
+
+struct DenoiseLayout {
+  size_t xin, v, t, model, total;
+};
+DenoiseLayout denoise_layout(const k2_model_cfg* c, int T, int N, int guided) {
+  DenoiseLayout l = {};
+  const int B = guided ? 2 : 1;
+  const size_t nc = (size_t)N * c->in_channels;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  l.xin = take(B * nc * dt_size(c->block.dtype));
+  l.v = take(B * nc * sizeof(float));
+  l.t = take(B * sizeof(float));
+  l.model = take(model_layout(c, B, T, N).total);
+  l.total = off;
+  return l;
+}
+
+size_t k2_denoise_workspace_bytes(const k2_model_cfg* cfg, int T, int N, int guided) {
+  if (!cfg || T < 0 || N < 0) return 0;
+  return denoise_layout(cfg, T, N, guided != 0).total;
+}
+
+int k2_denoise_step(const k2_model_cfg* cfg, const k2_model_weights* w, int T, int N, float* latents, const void* enc,
+                    const uint8_t* mask, const float* pos, int pos_rows, int pos_cols, float sigma, float sigma_next,
+                    float guidance, void* workspace, size_t workspace_bytes, void* stream) {
+  const int guided = guidance > 0.0f, B = guided ? 2 : 1;
+  int rc = check_model(cfg, w, B, T, N);
+  if (rc != K2_OK) return rc;
+  if (!latents || !pos || (T > 0 && !enc)) return fail(K2_ERR_NULL, "latents / encoder_hidden_states / position_ids is NULL");
+  if ((rc = check_align("latents / encoder_hidden_states", {latents, enc})) != K2_OK) return rc;
+  if (pos_rows != T + N || pos_cols != 3)
+    return fail(K2_ERR_SHAPE, "position_ids must be (T + N, 3) = (%d, 3), got (%d, %d)", T + N, pos_rows, pos_cols);
+  if (!std::isfinite(guidance) || !std::isfinite(sigma) || !std::isfinite(sigma_next))
+    return fail(K2_ERR_SHAPE, "guidance and sigmas must be finite");
+  const DenoiseLayout l = denoise_layout(cfg, T, N, guided);
+  if ((rc = check_ws(workspace, workspace_bytes, l.total)) != K2_OK) return rc;
+  g_err.clear();
+
+  hipStream_t s = (hipStream_t)stream;
+  const int dt = cfg->block.dtype;
+  const size_t nc = (size_t)N * cfg->in_channels, es = dt_size(dt);
+  char* xin = at(workspace, l.xin);
+  float* v = (float*)at(workspace, l.v);
+  float* t = (float*)at(workspace, l.t);
+  // the transformer input: the latents in the operand dtype, once per guidance branch
+  for (int b = 0; b < B; ++b) K2_RUN("convert", s, from_f32(dt, latents, xin + b * nc * es, nc, s));
+  K2_RUN("fill", s, fill_f32(t, B, sigma, s));
+  if ((rc = backbone_run(cfg, w, B, T, N, xin, enc, t, pos, mask, v, at(workspace, l.model), s)) != K2_OK) return rc;
+  K2_RUN("cfg_euler", s, cfg_euler(latents, latents, v, guided ? v + nc : nullptr, nc, guidance, sigma_next - sigma, s));
   return K2_OK;
 }
 

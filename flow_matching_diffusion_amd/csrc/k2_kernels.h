@@ -117,4 +117,10 @@ hipError_t layer_compress(const float* x, const float* c, float* y, int rows, in
 hipError_t to_f32(int dt, const void* in, float* out, size_t n, hipStream_t s);
 hipError_t from_f32(int dt, const float* in, void* out, size_t n, hipStream_t s);
 
+// x_out = x + dsigma * (vc + g (vc - vu)) over n floats (vc alone when vu is NULL); x_out may alias x.
+hipError_t cfg_euler(const float* x, float* x_out, const float* vc, const float* vu, size_t n, float g, float dsigma,
+                     hipStream_t s);
+// out[i] = v for i < n
+hipError_t fill_f32(float* out, int n, float v, hipStream_t s);
+
 }  // namespace k2

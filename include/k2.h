@@ -9,6 +9,8 @@
  *              架构全解": §二 (I/O contract and its ValueErrors), §三 (defaults and the axes check),
  *              §四 data flow, §四.1 TextFusion, §四.2 TransformerBlock, §四.3 Attention, §四.4 RMSNorm,
  *              §四.5 TimestepEmbedding, §四.6 FinalLayer.
+ *   [PIPELINE] diffusers v0.43.0 pipeline page "Krea 2": Krea2Pipeline parameters (scheduler,
+ *              is_distilled) and __call__ parameters (num_inference_steps, sigmas, guidance_scale).
  *
  * Conventions shared by every entry point
  *   - Pointers named *_w, *_b, tables, activations, outputs and workspace are DEVICE pointers owned by
@@ -213,6 +215,46 @@ int k2_backbone_forward(const k2_model_cfg* cfg, const k2_model_weights* w, int 
                         void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
+ * Sampler ([PIPELINE] Krea2Pipeline: FlowMatchEulerDiscreteScheduler with dynamic shifting and
+ * Krea 2's shift parameters, is_distilled; __call__: sigmas, guidance_scale, num_inference_steps).
+ *   sigma grid: linspace(1, 1/N, N) under the exponential time shift e^mu / (e^mu + 1/sigma - 1),
+ *   mu on the line through (base_image_seq_len, base_shift) and (max_image_seq_len, max_shift) at
+ *   the image token count (distilled checkpoint: mu = distilled_mu), then a terminal 0;
+ *   velocity v = cond + g (cond - uncond), the unconditional pass skipped when g <= 0;
+ *   Euler update x <- x + (sigma_next - sigma) v; the transformer runs at timestep t = sigma.
+ * The latent state is float32 between steps.
+ * --------------------------------------------------------------------------------------------- */
+typedef struct {
+  float base_shift;       /* 0.5 */
+  float max_shift;        /* 1.15 */
+  int base_image_seq_len; /* 256 */
+  int max_image_seq_len;  /* 6400 */
+  float distilled_mu;     /* 1.15 */
+} k2_shift_cfg;
+void k2_shift_cfg_default(k2_shift_cfg* cfg);
+
+/* HOST function (no device work): the num_steps + 1 noise levels into the host array sigmas_out.
+   cfg NULL = the defaults above. K2_ERR_SHAPE if num_steps < 1 or image_seq_len < 1. */
+int k2_flow_sigmas(const k2_shift_cfg* cfg, int num_steps, int image_seq_len, int distilled, float* sigmas_out);
+
+/* x_out = x + (sigma_next - sigma) * (v_cond + guidance (v_cond - v_uncond)) over n device floats
+   (v_uncond unused, may be NULL, when guidance <= 0). x_out may alias x. One fused kernel. */
+int k2_cfg_euler_update(const float* x, float* x_out, const float* v_cond, const float* v_uncond, size_t n,
+                        float guidance, float sigma, float sigma_next, void* stream);
+
+/* One sampler step of ONE image: the transformer (k2_backbone_forward semantics) on the batch
+   (prompt, negative prompt) when guidance > 0, else on the prompt alone, at timestep sigma; then the
+   guidance combine and Euler update into `latents`.
+   latents: (1, N, in_channels) float32, read and updated in place.
+   enc: (G, T, text layers, text hidden) in dtype, G = 2 (prompt, then negative prompt) when
+   guidance > 0, else 1; mask: (G, T) or NULL; position_ids: (T + N, 3) float32.
+   Workspace: k2_denoise_workspace_bytes(cfg, T, N, guidance > 0). */
+size_t k2_denoise_workspace_bytes(const k2_model_cfg* cfg, int T, int N, int guided);
+int k2_denoise_step(const k2_model_cfg* cfg, const k2_model_weights* w, int T, int N, float* latents, const void* enc,
+                    const uint8_t* mask, const float* position_ids, int pos_rows, int pos_cols, float sigma,
+                    float sigma_next, float guidance, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------------------------------
  * Diagnostics
  * --------------------------------------------------------------------------------------------- */
 /* Message for the last non-OK status returned on this thread ("" if none). */
@@ -222,7 +264,8 @@ const char* k2_last_error(void);
    launches while enabled. k2_profile_query synchronises on the recorded events and returns the
    total milliseconds and launch count of kernels whose name equals `kernel` (names: "modnorm",
    "gemm_qkvg", "attention", "gemm_out", "gemm_swiglu", "gemm_down", "rope", "modulation",
-   "gemm_plain", "time_embed", "layer_compress", "scatter", ...). Returns K2_OK or K2_ERR_HIP. */
+   "gemm_plain", "time_embed", "layer_compress", "convert", "fill", "cfg_euler", ...). Returns K2_OK or
+   K2_ERR_HIP. */
 void k2_profile_enable(int enable);
 void k2_profile_reset(void);
 int k2_profile_query(const char* kernel, double* total_ms, int* launches);
