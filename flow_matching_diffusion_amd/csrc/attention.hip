@@ -345,6 +345,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
   constexpr int K_DMA = KT * KCH / 256;  // 1 KB DMA instructions per wave for the K tile
   constexpr int V_DMA = HD * VCH / 256;  // ... and for the V^T tile
   constexpr float kRescale = 8.0f;
+  constexpr int RA = 4;               // fragment read-ahead (matrix-core instructions)
   static_assert(KCH == 16 || KCH == 8, "head_dim 128 or 64");
 
   __shared__ uint4 sK[2][KT * KCH];
@@ -452,18 +453,31 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
     const uint4* sk = sK[st];
     const uint4* sv = sV[st];
 
-    // S^T for the two 32-key blocks
+    // S^T for the two 32-key blocks, their chains interleaved: item i is (k-step i/2, block i%2).
+    // Fragments run through a ring of RA + 1 registers, each read RA items before its use; the
+    // order is pinned with scheduling fences.
+#define K2_KFRAG(i) __builtin_bit_cast(bf16x8, sk[(32 * ((i) & 1) + krow) * KCH + ((2 * ((i) >> 1) + h32) ^ ksw)])
+#define K2_VFRAG(i) __builtin_bit_cast(bf16x8, sv[(32 * ((i) % NHB) + c32) * VCH + ((2 * ((i) / NHB) + h32) ^ vsw)])
     f32x16 sc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) sc[kb][r] = 0.0f;
+    bf16x8 ring[RA + 1];
 #pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        const bf16x8 kf = __builtin_bit_cast(bf16x8, sk[(32 * kb + krow) * KCH + ((2 * s + h32) ^ ksw)]);
-        sc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[s], sc[kb], 0, 0, 0);
-      }
+    for (int i = 0; i < RA; ++i) ring[i] = K2_KFRAG(i);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 2 * NS; ++i) {
+      if (i + RA < 2 * NS) ring[(i + RA) % (RA + 1)] = K2_KFRAG(i + RA);
+      sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % (RA + 1)], qf[i >> 1], sc[i & 1], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
     }
+    // the first V^T fragments of the PV product go out now and land during the softmax
+    bf16x8 vring[RA + 1];
+#pragma unroll
+    for (int i = 0; i < RA; ++i) vring[i] = K2_VFRAG(i);
+    __builtin_amdgcn_sched_barrier(0);
 
     // mask (tiles holding padding or the sequence end only), max, lazy rescale
     const int t0 = t * KT;
@@ -511,15 +525,17 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
         pack8(pf[2 * kb + h], pv);
       }
 
-    // O^T += V^T P^T: step (kb, h) covers keys 32kb + 16h .. +15; lane group l/32 supplies 8 of them
+    // O^T += V^T P^T: step j = (kb, h) covers keys 32kb + 16h .. +15, lane group l/32 supplies 8 of
+    // them; item i is (step i / NHB, head-dim block i % NHB), so the NHB chains interleave.
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d = 32 * hb + c32;
-        const bf16x8 vf = __builtin_bit_cast(bf16x8, sv[d * VCH + ((2 * j + h32) ^ vsw)]);
-        o[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[j], o[hb], 0, 0, 0);
-      }
+    for (int i = 0; i < 4 * NHB; ++i) {
+      if (i + RA < 4 * NHB) vring[(i + RA) % (RA + 1)] = K2_VFRAG(i + RA);
+      o[i % NHB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vring[i % (RA + 1)], pf[i / NHB], o[i % NHB], 0, 0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+#undef K2_KFRAG
+#undef K2_VFRAG
 
     K2_WAIT_VM(0);
     __syncthreads();
