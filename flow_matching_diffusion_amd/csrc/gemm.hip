@@ -493,9 +493,13 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, int scn, B
 //
 // SPREAD picks where the DMA instructions of a turn go. 0: all right after the barrier, which
 // gives them the whole slab to land (best when the weights exceed the 256 MB last-level cache and
-// come from HBM). 2: interleaved with the matrix-core instructions of the two sub-steps after the
-// barrier, which keeps them from stalling the wave in a burst (measured 10-15% faster when the
-// operands stay cache-resident).
+// come from HBM). 2 or 4: interleaved evenly with the matrix-core instructions of the first 2 or
+// all 4 sub-steps after the barrier, which keeps them from stalling the wave in a burst (measured
+// 10-15% faster than 0 when the operands stay cache-resident).
+//
+// KFULL (K a multiple of 64): every slab is whole, so a DMA's lane offsets are fixed and the slab's
+// K offset goes in the instruction's scalar offset; slabs past K (fetched ahead, never read) reload
+// slab 0. Otherwise each lane checks its chunk against K and chunks past it read as zero.
 //
 // NJ picks the wave's N width (32 * NJ): 4 gives the 256x256 tile; 2 a 256x128 half tile, used to
 // split the last partial round of tiles so that it takes half as long (see gemm_bf16_kernel).
@@ -509,7 +513,7 @@ struct Rings {
   static constexpr int units(int NJ) { return (RA * 256 + RB * 64 * NJ) * 8; }
 };
 
-template <int SPREAD, int NJ, int RA, int RB, class BMap, class Epi>
+template <int SPREAD, bool KFULL, int NJ, int RA, int RB, class BMap, class Epi>
 __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int m0, int n0,
                                           const BMap& bmap, const Epi& epi, uint4* lds) {
   typedef Rings<RA, RB> R;
@@ -557,14 +561,22 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
 #define K2_DMA_A(ST, kt, j)                                                                      \
   do {                                                                                           \
     const int k0_ = (kt) * BK;                                                                   \
-    dma16(ra, (ST) + (64 * wave + 8 * (j)) * 8,                                                  \
-          k0_ + cc[(j) & 1] * 8 < K ? avo[(j) & 1] + (j) * arow8 + (uint32_t)k0_ * sizeof(bf16) : kOOB); \
+    if (KFULL)                                                                                   \
+      dma16(ra, (ST) + (64 * wave + 8 * (j)) * 8, avo[(j) & 1] + (j) * arow8,                    \
+            (uint32_t)(k0_ < K ? k0_ : 0) * sizeof(bf16));                                       \
+    else                                                                                         \
+      dma16(ra, (ST) + (64 * wave + 8 * (j)) * 8,                                                \
+            k0_ + cc[(j) & 1] * 8 < K ? avo[(j) & 1] + (j) * arow8 + (uint32_t)k0_ * sizeof(bf16) : kOOB, 0); \
   } while (0)
 #define K2_DMA_B(ST, kt, j)                                                                      \
   do {                                                                                           \
     const int k0_ = (kt) * BK;                                                                   \
-    dma16(rb[j], (ST) + (8 * NBB * wave + 8 * (j)) * 8,                                          \
-          k0_ + cc[(j) & 1] * 8 < K ? bvo[(j) & 1] + (uint32_t)k0_ * sizeof(bf16) : kOOB);       \
+    if (KFULL)                                                                                   \
+      dma16(rb[j], (ST) + (8 * NBB * wave + 8 * (j)) * 8, bvo[(j) & 1],                          \
+            (uint32_t)(k0_ < K ? k0_ : 0) * sizeof(bf16));                                       \
+    else                                                                                         \
+      dma16(rb[j], (ST) + (8 * NBB * wave + 8 * (j)) * 8,                                        \
+            k0_ + cc[(j) & 1] * 8 < K ? bvo[(j) & 1] + (uint32_t)k0_ * sizeof(bf16) : kOOB, 0);  \
   } while (0)
   // DMA instruction d (0 .. DPW-1) of a turn: A slab kA into STA, B slab kB into STB, shorter ring first
 #define K2_DMA1(d, STA, kA, STB, kB)                                                             \
@@ -654,7 +666,10 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
   }
   // Turn kt: wait for slab kt+1, refill slab kt's stages (A with slab kt+RA, B with kt+RB), finish
   // slab kt and run sub-steps 0..2 of slab kt+1.
-  constexpr int DH = DPW / 2;
+  // DMA instructions of a turn: step i of the SPREAD first steps issues [DS(i), DS(i+1))
+  constexpr int NS = SPREAD > 0 ? SPREAD : 1;
+#define K2_DS(i) ((i) < NS ? (i) * DPW / NS : DPW)
+#define K2_DN(i) (SPREAD > 0 ? K2_DS((i) + 1) - K2_DS(i) : 0)
   const int nk = (K + BK - 1) / BK;
   int sa = 0, sb = 0;  // ring stages of slab kt
   for (int kt = 0; kt < nk - 1; ++kt) {
@@ -671,10 +686,10 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
       for (int d = 0; d < DPW; ++d) K2_DMA1(d, wA, kt + RA, wB, kt + RB);
       K2_FENCE();
     }
-    K2_STEP(fa1, fb1, fa0, fb0, rA, rB, 0, 0, SPREAD ? DH : 0);
-    K2_STEP(fa0, fb0, fa1, fb1, rA, rB, 1, DH, SPREAD ? DPW - DH : 0);
-    K2_STEP(fa1, fb1, fa0, fb0, rA, rB, 2, 0, 0);
-    K2_STEP(fa0, fb0, fa1, fb1, rA, rB, 3, 0, 0);
+    K2_STEP(fa1, fb1, fa0, fb0, rA, rB, 0, K2_DS(0), K2_DN(0));
+    K2_STEP(fa0, fb0, fa1, fb1, rA, rB, 1, K2_DS(1), K2_DN(1));
+    K2_STEP(fa1, fb1, fa0, fb0, rA, rB, 2, K2_DS(2), K2_DN(2));
+    K2_STEP(fa0, fb0, fa1, fb1, rA, rB, 3, K2_DS(3), K2_DN(3));
     sa = sa1;
     sb = sb1;
   }
@@ -686,6 +701,8 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
     K2_STEP(fa1, fb1, fa0, fb0, ringA, ringB, -1, 0, 0);  // last sub-step of slab nk - 1
   }
   K2_WAIT_VM(0);  // no DMA may still write LDS when the workgroup retires
+#undef K2_DN
+#undef K2_DS
 #undef K2_BARRIER
 #undef K2_STEP
 #undef K2_READ1
@@ -700,7 +717,7 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
 // tiles_total - nmain tiles of the last partial round are split in two 256x128 halves run by
 // workgroups nmain + 2u and nmain + 2u + 1 (u: tail tile index), so that round takes about half as
 // long; TAIL is used when the halves fit in one round.
-template <int SPREAD, int RA, int RB, bool TAIL, class BMap, class Epi>
+template <int SPREAD, bool KFULL, int RA, int RB, bool TAIL, class BMap, class Epi>
 __global__ void __launch_bounds__(256)
 gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int scn, int nmain, BMap bmap,
                  Epi epi) {
@@ -710,11 +727,11 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, in
   int tm, tn;
   if (!TAIL || bid < nmain) {
     tile_coords(bid, tiles_m, tiles_n, scn, tm, tn);
-    gemm_tile<SPREAD, 4, RA, RB>(A, lda, M, K, Ntot, tm * 256, tn * 256, bmap, epi, lds);
+    gemm_tile<SPREAD, KFULL, 4, RA, RB>(A, lda, M, K, Ntot, tm * 256, tn * 256, bmap, epi, lds);
   } else if constexpr (TAIL) {
     const int u = bid - nmain;
     tile_coords(nmain + (u >> 1), tiles_m, tiles_n, scn, tm, tn);
-    gemm_tile<SPREAD, 2, RA, RB>(A, lda, M, K, Ntot, tm * 256, tn * 256 + (u & 1) * 128, bmap, epi, lds);
+    gemm_tile<SPREAD, KFULL, 2, RA, RB>(A, lda, M, K, Ntot, tm * 256, tn * 256 + (u & 1) * 128, bmap, epi, lds);
   }
 }
 
@@ -747,7 +764,7 @@ static int compute_units() {
 // projection unchanged; 3 + 2 loses on SwiGLU. The weights' slabs are the ones that arrive late:
 // each super-column starts on weight rows that are still in HBM.
 constexpr int kRingA = 2, kRingB = 3;
-template <typename T, class C, class BMap, class Epi, int SPREAD, bool TAIL>
+template <typename T, class C, class BMap, class Epi, int SPREAD, bool KFULL, bool TAIL>
 static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap, const Epi& epi, hipStream_t s) {
   constexpr int NT = (C::BM / C::WM) * (C::BN / C::WN) * 64;
   const int tiles = ((a.M + C::BM - 1) / C::BM) * ((Ntot + C::BN - 1) / C::BN);
@@ -761,7 +778,7 @@ static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap
         grid = nmain + 2 * tail;
       }
     }
-    hipLaunchKernelGGL((gemm_bf16_kernel<SPREAD, kRingA, kRingB, TAIL, BMap, Epi>), dim3(grid), dim3(256), 0, s, (const bf16*)a.A,
+    hipLaunchKernelGGL((gemm_bf16_kernel<SPREAD, KFULL, kRingA, kRingB, TAIL, BMap, Epi>), dim3(grid), dim3(256), 0, s, (const bf16*)a.A,
                        a.lda, a.M, a.K, Ntot, scn, nmain, bmap, epi);
   } else {
     hipLaunchKernelGGL((gemm_kernel<T, C::BM, C::BN, C::WM, C::WN, BMap, Epi>), dim3(tiles), dim3(NT), 0, s,
@@ -773,12 +790,14 @@ static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap
 // Launch policy, from measurements on the block's GEMM shapes:
 //  - tile order: super-columns (see tile_coords) when the weights are the larger operand; when the
 //    activations are larger, their re-reads per super-column cost more than they save;
-//  - bf16 DMA schedule: spread among the matrix-core instructions, unless the weight rows in use at
-//    once exceed the 256 MB last-level cache, in which case their slabs come from HBM and need the
-//    whole slab period to land (DMA right after the barrier).
+//  - bf16 DMA schedule: spread among the matrix-core instructions (over SPREAD_CACHED sub-steps:
+//    the SwiGLU projection runs best with 2, the other projections with 4), unless the weight rows
+//    in use at once exceed the 256 MB last-level cache, in which case their slabs come from HBM
+//    and need the whole slab period to land (DMA right after the barrier);
+//  - K a multiple of 64 takes the scalar-offset DMA (2-5 % faster than per-lane K checks).
 constexpr size_t kLastLevelCacheBytes = size_t(256) << 20;
 
-template <typename T, class BMap, class Epi, bool TAIL = false>
+template <typename T, class BMap, class Epi, bool TAIL = false, int SPREAD_CACHED = 4>
 static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& epi, hipStream_t s) {
   typedef Cfg<T> C;
   if (a.M <= 0 || Ntot <= 0) return hipSuccess;
@@ -786,10 +805,13 @@ static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& 
   const size_t a_bytes = (size_t)a.M * a.K * sizeof(T), b_bytes = (size_t)Ntot * a.K * sizeof(T);
   const int scn = b_bytes >= a_bytes ? super_cols(tiles_n, C::BN, a.K, sizeof(T)) : tiles_n;
   if constexpr (sizeof(T) == 2) {
+    if (a.K % 64 != 0) return launch_cfg<T, C, BMap, Epi, 2, false, TAIL>(a, Ntot, scn, bmap, epi, s);
     if ((size_t)scn * C::BN * a.K * sizeof(T) > kLastLevelCacheBytes)
-      return launch_cfg<T, C, BMap, Epi, 0, TAIL>(a, Ntot, scn, bmap, epi, s);
+      return launch_cfg<T, C, BMap, Epi, 0, true, TAIL>(a, Ntot, scn, bmap, epi, s);
+    return launch_cfg<T, C, BMap, Epi, SPREAD_CACHED, true, TAIL>(a, Ntot, scn, bmap, epi, s);
+  } else {
+    return launch_cfg<T, C, BMap, Epi, 0, false, TAIL>(a, Ntot, scn, bmap, epi, s);
   }
-  return launch_cfg<T, C, BMap, Epi, 2, TAIL>(a, Ntot, scn, bmap, epi, s);
 }
 
 template <typename T, int HD>
@@ -817,7 +839,7 @@ static hipError_t swiglu_t(const GemmA& a, const SwigluArgs& p, hipStream_t s) {
   EpiSwiglu<T, WN> e;
   e.a = (T*)p.a; e.I = p.I;
   const int ntot = ((p.I + WN / 2 - 1) / (WN / 2)) * WN;
-  return launch<T>(a, ntot, bm, e, s);
+  return launch<T, BSwiglu<T, WN>, EpiSwiglu<T, WN>, false, 2>(a, ntot, bm, e, s);
 }
 
 template <typename T>

@@ -101,12 +101,13 @@ __device__ __forceinline__ uint4 bload(rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
 
-// 16-byte-per-lane DMA from a buffer into LDS at lds + 16 * lane (lds must be wave-uniform). The
-// builtin exists for the device pass only; the host pass (which only needs kernels' launch stubs)
-// sees an empty body.
-__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t off) {
+// 16-byte-per-lane DMA from a buffer into LDS at lds + 16 * lane (lds must be wave-uniform), from
+// byte offset off (per lane) + soff (wave-uniform, scalar offset field). The builtin exists for the
+// device pass only; the host pass (which only needs kernels' launch stubs) sees an empty body.
+__device__ __forceinline__ void dma16(rsrc_t r, void* lds, uint32_t off, uint32_t soff = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, (int)off, (int)soff,
+                                           0, 0);
 #endif
 }
 
