@@ -114,16 +114,24 @@ __device__ __forceinline__ float4 fma4(float4 g, float4 a, float4 h) {
 // Epilogues: every access moves 4 consecutive columns (N, I, ld* and all column offsets are
 // multiples of 4; the entry points require 16-byte aligned activation, bias and output pointers).
 // ---------------------------------------------------------------------------------------------
+// Epilogues that read nothing beyond their own arguments stage nothing in LDS.
+struct EpiNoStage {
+  static constexpr bool kStaged = false;
+  static constexpr int stage_floats() { return 0; }
+  __device__ bool wants_stage(int) const { return false; }
+  __device__ void stage(float*, int, int, int, int) const {}
+};
+
 // hout = hin + gate[batch] * acc (gated residual; gate NULL means 1). hin may alias hout.
 template <typename T>
-struct EpiResid {
+struct EpiResid : EpiNoStage {
   const float* hin;
   float* hout;
   const float* gate;
   int gate_stride, L, N;
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
-                                        int M) const {
+                                        int M, const float* stg = nullptr) const {
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = row0 + LY::row(i, lane);
@@ -146,7 +154,7 @@ struct EpiResid {
 // acc + bias into a float output and/or act(acc + bias) into an operand-dtype output, with input
 // row m written to output row (m / rpb) * orpb + ooff + m % rpb.
 template <typename T>
-struct EpiPlain {
+struct EpiPlain : EpiNoStage {
   const float* bias;
   float* outf;
   int ldf;
@@ -154,7 +162,7 @@ struct EpiPlain {
   int ldt, act, N, rpb, orpb, ooff;
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
-                                        int M) const {
+                                        int M, const float* stg = nullptr) const {
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = row0 + LY::row(i, lane);
@@ -183,12 +191,12 @@ struct EpiPlain {
 
 // a = silu(gate) * up; the wave's first WN/2 columns are gate, the last WN/2 the matching up columns.
 template <typename T, int WN>
-struct EpiSwiglu {
+struct EpiSwiglu : EpiNoStage {
   T* a;
   int I;
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
-                                        int M) const {
+                                        int M, const float* stg = nullptr) const {
     static_assert(NJ * (LY::NQ == 1 ? 16 : 32) == WN, "wave width");
     const int cbase = (col0 / WN) * (WN / 2);
 #pragma unroll
@@ -224,9 +232,40 @@ struct EpiQkvg {
   const float* rs;
   int nq, nk, L, ldvt;
   float eps;
+
+  // The bf16 kernel stages in LDS, after its main loop and for tiles holding q or k heads: the
+  // multipliers 1 + w of the q and k norms (HD floats each), then for each of the tile's 256 rows
+  // the RoPE (cos, sin) of pair p at float 2 HD + r kStgRow + 2p. Rows are padded to kStgRow floats
+  // so that the 16 rows a quarter-wave reads fall in different banks. Reading the table from
+  // global memory inside the epilogue, between its stores, made q and k tiles' epilogues several
+  // times longer than the others'.
+  static constexpr bool kStaged = true;
+  static constexpr int kStgRow = HD + 4;
+  static constexpr int stage_floats() { return 2 * HD + 256 * kStgRow; }
+  __device__ bool wants_stage(int n0) const { return n0 < nq + nk; }
+  __device__ void stage(float* st, int m0, int M, int tid, int nthr) const {
+    for (int i = tid; i < 2 * HD; i += nthr) {
+      const float* w = i < HD ? wnq : wnk;
+      st[i] = 1.0f + (w ? w[i % HD] : 0.0f);
+    }
+    if (!rc) return;
+    constexpr int P4 = HD / 8;  // float4s of cos (or sin) per row: HD / 2 pairs
+    float* t = st + 2 * HD;
+#pragma unroll 4
+    for (int i = tid; i < 256 * P4; i += nthr) {
+      const int r = i / P4, c4 = i - r * P4;
+      const int m = m0 + r;
+      const int l = (m < M ? m : 0) % L;
+      const float4 c = ld4(rc + (size_t)l * (HD / 2) + 4 * c4), sn = ld4(rs + (size_t)l * (HD / 2) + 4 * c4);
+      float* d = t + r * kStgRow + 8 * c4;
+      st4(d, make_float4(c.x, sn.x, c.y, sn.y));
+      st4(d + 4, make_float4(c.z, sn.z, c.w, sn.w));
+    }
+  }
+
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
-                                        int M) const {
+                                        int M, const float* stg = nullptr) const {
     constexpr int BS = LY::NQ == 1 ? 16 : 32;
     constexpr int HB = HD / BS;  // column blocks per head
     static_assert(NJ % HB == 0, "a wave covers whole heads");
@@ -258,14 +297,24 @@ struct EpiQkvg {
             for (int qq = 0; qq < LY::NQ; ++qq) {
               const int d = LY::col(jj, qq, lane);
               float4 y = quad(acc[i][h0 + jj], qq);
-              float4 w4 = wn ? ld4(wn + d) : make_float4(0.f, 0.f, 0.f, 0.f);
-              y.x *= inv * (1.0f + w4.x); y.y *= inv * (1.0f + w4.y);
-              y.z *= inv * (1.0f + w4.z); y.w *= inv * (1.0f + w4.w);
-              if (rc) {
-                const float2 c2 = *reinterpret_cast<const float2*>(rc + (size_t)l * (HD / 2) + (d >> 1));
-                const float2 s2 = *reinterpret_cast<const float2*>(rs + (size_t)l * (HD / 2) + (d >> 1));
-                y = make_float4(y.x * c2.x - y.y * s2.x, y.y * c2.x + y.x * s2.x,
-                                y.z * c2.y - y.w * s2.y, y.w * c2.y + y.z * s2.y);
+              if (stg) {  // staged multipliers and (cos, sin) pairs
+                const float4 w4 = ld4(stg + (seg == 0 ? 0 : HD) + d);
+                y.x *= inv * w4.x; y.y *= inv * w4.y; y.z *= inv * w4.z; y.w *= inv * w4.w;
+                if (rc) {
+                  const float4 cs = ld4(stg + 2 * HD + ((row0 & 255) + LY::row(i, lane)) * kStgRow + d);
+                  y = make_float4(y.x * cs.x - y.y * cs.y, y.y * cs.x + y.x * cs.y,
+                                  y.z * cs.z - y.w * cs.w, y.w * cs.z + y.z * cs.w);
+                }
+              } else {
+                const float4 w4 = wn ? ld4(wn + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+                y.x *= inv * (1.0f + w4.x); y.y *= inv * (1.0f + w4.y);
+                y.z *= inv * (1.0f + w4.z); y.w *= inv * (1.0f + w4.w);
+                if (rc) {
+                  const float2 c2 = *reinterpret_cast<const float2*>(rc + (size_t)l * (HD / 2) + (d >> 1));
+                  const float2 s2 = *reinterpret_cast<const float2*>(rs + (size_t)l * (HD / 2) + (d >> 1));
+                  y = make_float4(y.x * c2.x - y.y * s2.x, y.y * c2.x + y.x * s2.x,
+                                  y.z * c2.y - y.w * s2.y, y.w * c2.y + y.z * s2.y);
+                }
               }
               if (m < M) st4(dst + (size_t)m * ld + cb + d, y);
             }
@@ -701,6 +750,16 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
     K2_STEP(fa1, fb1, fa0, fb0, ringA, ringB, -1, 0, 0);  // last sub-step of slab nk - 1
   }
   K2_WAIT_VM(0);  // no DMA may still write LDS when the workgroup retires
+  const float* stg = nullptr;
+  if constexpr (Epi::kStaged) {
+    static_assert(Epi::stage_floats() * sizeof(float) <= Rings<RA, RB>::units(4) * sizeof(uint4), "LDS staging");
+    if (epi.wants_stage(n0)) {  // tile-uniform
+      __syncthreads();  // every wave is done with the rings
+      epi.stage(reinterpret_cast<float*>(lds), m0, M, tid, 256);
+      __syncthreads();
+      stg = reinterpret_cast<const float*>(lds);
+    }
+  }
 #undef K2_DN
 #undef K2_DS
 #undef K2_BARRIER
@@ -710,7 +769,7 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
 #undef K2_DMA1
 #undef K2_DMA_B
 #undef K2_DMA_A
-  epi.template apply<Lay<32>, MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M);
+  epi.template apply<Lay<32>, MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M, stg);
 }
 
 // Workgroups 0 .. nmain-1 each compute a 256x256 tile (tile order: tile_coords). With TAIL, the
