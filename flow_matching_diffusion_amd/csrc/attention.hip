@@ -330,6 +330,12 @@ __device__ __forceinline__ int swz_k256(int row) { return row & 15; }
 __device__ __forceinline__ int swz_v128(int d) { return (d >> 1) & 7; }
 // accumulator row -> key of a 32-key block (bits 2 and 3 swapped; an involution)
 __device__ __forceinline__ int kperm(int rho) { return (rho & ~12) | ((rho & 4) << 1) | ((rho & 8) >> 1); }
+// max over lanes l and l ^ 32: v_permlane32_swap of two copies hands every lane both halves'
+// values, with no LDS traffic (a shuffle would wait on the fragment reads in flight)
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
 
 constexpr int kMaxTextTiles64 = 256;  // 64-key text tiles: text tokens up to 16384
 
@@ -348,9 +354,13 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
   constexpr int RA = 4;               // fragment read-ahead (matrix-core instructions)
   static_assert(KCH == 16 || KCH == 8, "head_dim 128 or 64");
 
-  __shared__ uint4 sK[2][KT * KCH];
-  __shared__ uint4 sV[2][HD * VCH];
+  // two stages each of K and V^T, as separate arrays: the compiler then sees that a DMA into one
+  // stage cannot alias reads of the other and does not wait for the DMA before those reads
+  __shared__ uint4 sK0[KT * KCH], sK1[KT * KCH];
+  __shared__ uint4 sV0[HD * VCH], sV1[HD * VCH];
   __shared__ uint64_t sBits[kMaxTextTiles64];
+#define K2_SK(st) ((st) ? sK1 : sK0)
+#define K2_SV(st) ((st) ? sV1 : sV0)
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -398,12 +408,13 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
     const int d = (wave * V_DMA + j) * 8 + lane / 8, pc = lane % 8;
     vvo[j] = (uint32_t)(d * p.ldvt + (pc ^ swz_v128(d)) * 8) * sizeof(bf16);
   }
-  auto issue = [&](int st, int t) {
-    const uint32_t kt0 = (uint32_t)(t * KT * ldk) * sizeof(bf16), vt0 = (uint32_t)(t * KT) * sizeof(bf16);
-#pragma unroll
-    for (int j = 0; j < K_DMA; ++j) dma16(kr, &sK[st][(wave * K_DMA + j) * 64], kvo[j] + kt0);
-#pragma unroll
-    for (int j = 0; j < V_DMA; ++j) dma16(vr, &sV[st][(wave * V_DMA + j) * 64], vvo[j] + vt0);
+  // DMA of tile t's K rows / V^T columns into stage st (a t past the last tile reads zeros or
+  // in-range padding and is never used)
+  auto issue_k = [&](int st, int t, int j) {
+    dma16(kr, K2_SK(st) + (wave * K_DMA + j) * 64, kvo[j] + (uint32_t)(t * KT * ldk) * sizeof(bf16));
+  };
+  auto issue_v = [&](int st, int t, int j) {
+    dma16(vr, K2_SV(st) + (wave * V_DMA + j) * 64, vvo[j] + (uint32_t)(t * KT) * sizeof(bf16));
   };
   // keys past L in the last tile: V^T columns there hold whatever the workspace held; zero them
   auto zero_tail = [&](int st, int t) {
@@ -411,12 +422,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
     for (int i = tid; i < HD * VCH; i += 256) {
       const int d = i / VCH, pc = i % VCH, k0 = (pc ^ swz_v128(d)) * 8;
       if (k0 + 8 > valid) {
-        uint4 v = sV[st][i];
+        uint4 v = K2_SV(st)[i];
         uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int e = 0; e < 8; ++e)
           if (k0 + e >= valid) w[e >> 1] &= (e & 1) ? 0x0000FFFFu : 0xFFFF0000u;
-        sV[st][i] = uint4{w[0], w[1], w[2], w[3]};
+        K2_SV(st)[i] = uint4{w[0], w[1], w[2], w[3]};
       }
     }
   };
@@ -431,6 +442,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
   // fragment read offsets (uint4 units): K row kperm(l%32) of a 32-key block, V^T row d = l%32
   const int krow = kperm(c32), ksw = swz_k256(krow) & (KCH - 1);
   const int vsw = swz_v128(c32);
+#define K2_KFRAG(sk, i) __builtin_bit_cast(bf16x8, (sk)[(32 * ((i) & 1) + krow) * KCH + ((2 * ((i) >> 1) + h32) ^ ksw)])
+#define K2_VFRAG(sv, i) __builtin_bit_cast(bf16x8, (sv)[(32 * ((i) % NHB) + c32) * VCH + ((2 * ((i) / NHB) + h32) ^ vsw)])
+#define K2_FENCE() __builtin_amdgcn_sched_barrier(0)
 
   __syncthreads();  // sBits
   const int nt = (L + KT - 1) / KT;
@@ -438,115 +452,142 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
     while (t < nt && t < ntt && sBits[t] == 0) ++t;
     return t;
   };
+  // Software pipeline over the valid key tiles t_0, t_1, ...: iteration i computes S of t_{i+1}
+  // (K in stage (i+1)&1) while running the softmax of t_i, then O^T += V^T P^T for t_i (V in stage
+  // i&1) while packing P and summing it; the matrix-core work of each phase is interleaved with
+  // the other phase's vector work so that the two overlap. DMA during iteration i: K of t_{i+2}
+  // into stage i&1 and V of t_{i+1} into stage (i+1)&1; one barrier per iteration.
   int t = next_tile(0);
-  if (t < nt) issue(0, t);
-  K2_WAIT_VM(0);
-  __syncthreads();
-  if (t < nt && t * KT + KT > L) {
-    zero_tail(0, t);
-    __syncthreads();
-  }
-  int st = 0;
-  while (t < nt) {
-    const int tn = next_tile(t + 1);
-    if (tn < nt) issue(st ^ 1, tn);
-    const uint4* sk = sK[st];
-    const uint4* sv = sV[st];
-
-    // S^T for the two 32-key blocks, their chains interleaved: item i is (k-step i/2, block i%2).
-    // Fragments run through a ring of RA + 1 registers, each read RA items before its use; the
-    // order is pinned with scheduling fences.
-#define K2_KFRAG(i) __builtin_bit_cast(bf16x8, sk[(32 * ((i) & 1) + krow) * KCH + ((2 * ((i) >> 1) + h32) ^ ksw)])
-#define K2_VFRAG(i) __builtin_bit_cast(bf16x8, sv[(32 * ((i) % NHB) + c32) * VCH + ((2 * ((i) / NHB) + h32) ^ vsw)])
-    f32x16 sc[2];
+  if (t >= nt) {  // no valid key at all: the output is zero
+    m_i = 0.0f;
+  } else {
+    int tn = next_tile(t + 1);
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int j = 0; j < K_DMA; ++j) issue_k(0, t, j);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) sc[kb][r] = 0.0f;
-    bf16x8 ring[RA + 1];
+    for (int j = 0; j < V_DMA; ++j) issue_v(0, t, j);
 #pragma unroll
-    for (int i = 0; i < RA; ++i) ring[i] = K2_KFRAG(i);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 2 * NS; ++i) {
-      if (i + RA < 2 * NS) ring[(i + RA) % (RA + 1)] = K2_KFRAG(i + RA);
-      sc[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % (RA + 1)], qf[i >> 1], sc[i & 1], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-    // the first V^T fragments of the PV product go out now and land during the softmax
-    bf16x8 vring[RA + 1];
-#pragma unroll
-    for (int i = 0; i < RA; ++i) vring[i] = K2_VFRAG(i);
-    __builtin_amdgcn_sched_barrier(0);
-
-    // mask (tiles holding padding or the sequence end only), max, lazy rescale
-    const int t0 = t * KT;
-    const uint64_t vb = t < ntt ? sBits[t] : (t0 + KT <= L ? ~0ull : ((1ull << (L - t0)) - 1ull));
-    if (vb != ~0ull) {
-      // entry r of block kb is key 32kb + 16(r/8) + 8(l/32) + r%8: bytes 4kb + l/32 and 4kb + 2 + l/32
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const uint32_t lb = (uint32_t)((vb >> (8 * (4 * kb + h32))) & 0xFFu) |
-                            ((uint32_t)((vb >> (8 * (4 * kb + 2 + h32))) & 0xFFu) << 8);
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((lb >> r) & 1u)) sc[kb][r] = -INFINITY;
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-    if (__any(mx > m_i + kRescale)) {
-      const float mnew = fmaxf(m_i, mx);
-      const float alpha = m_i == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_i - mnew);
-      l_i *= alpha;
-#pragma unroll
-      for (int hb = 0; hb < NHB; ++hb) o[hb] *= alpha;
-      m_i = mnew;
-    }
-    const float base = m_i == -INFINITY ? 0.0f : m_i;
-
-    // P^T fragments and the row-sum partial of this lane's keys
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        float pv[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          // v_exp_f32: results below 2^-126 flush to zero, which a probability can afford
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[kb][8 * h + e], scale_log2, -base));
-          l_i += pv[e];
-        }
-        pack8(pf[2 * kb + h], pv);
-      }
-
-    // O^T += V^T P^T: step j = (kb, h) covers keys 32kb + 16h .. +15, lane group l/32 supplies 8 of
-    // them; item i is (step i / NHB, head-dim block i % NHB), so the NHB chains interleave.
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 4 * NHB; ++i) {
-      if (i + RA < 4 * NHB) vring[(i + RA) % (RA + 1)] = K2_VFRAG(i + RA);
-      o[i % NHB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vring[i % (RA + 1)], pf[i / NHB], o[i % NHB], 0, 0, 0);
-      __builtin_amdgcn_sched_barrier(0);
-    }
-#undef K2_KFRAG
-#undef K2_VFRAG
-
+    for (int j = 0; j < K_DMA; ++j) issue_k(1, tn, j);
     K2_WAIT_VM(0);
     __syncthreads();
-    if (tn < nt && tn * KT + KT > L) {
-      zero_tail(st ^ 1, tn);
+    if (t * KT + KT > L) {
+      zero_tail(0, t);
       __syncthreads();
     }
-    st ^= 1;
-    t = tn;
-  }
+    f32x16 sa[2], sb[2];  // scores of the tile being finished / the next tile, by 32-key block
+    {
+      const uint4* sk = sK0;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sa[kb][r] = 0.0f;
+      bf16x8 ring[RA + 1];
+#pragma unroll
+      for (int i = 0; i < RA; ++i) ring[i] = K2_KFRAG(sk, i);
+      K2_FENCE();
+#pragma unroll
+      for (int i = 0; i < 2 * NS; ++i) {
+        if (i + RA < 2 * NS) ring[(i + RA) % (RA + 1)] = K2_KFRAG(sk, i + RA);
+        sa[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % (RA + 1)], qf[i >> 1], sa[i & 1], 0, 0, 0);
+        K2_FENCE();
+      }
+    }
+    __syncthreads();  // every wave has read K stage 0
 
+    // One iteration: SC holds tile t's raw scores, SN receives tile tn's; st = i & 1.
+#define K2_ATT_ITER(SC, SN, st)                                                                    \
+    do {                                                                                           \
+      const int tnn = tn < nt ? next_tile(tn + 1) : nt;                                            \
+      const uint4* skn = K2_SK((st) ^ 1);                                                          \
+      const uint4* svc = K2_SV(st);                                                                \
+      /* mask tile t (tiles holding padding or the sequence end only): entry r of block kb is */   \
+      /* key 32kb + 16(r/8) + 8(l/32) + r%8, i.e. bytes 4kb + l/32 and 4kb + 2 + l/32 */           \
+      const int t0 = t * KT;                                                                       \
+      const uint64_t vb = t < ntt ? sBits[t] : (t0 + KT <= L ? ~0ull : ((1ull << (L - t0)) - 1ull)); \
+      if (vb != ~0ull) {                                                                           \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb) {                                         \
+          const uint32_t lb = (uint32_t)((vb >> (8 * (4 * kb + h32))) & 0xFFu) |                   \
+                              ((uint32_t)((vb >> (8 * (4 * kb + 2 + h32))) & 0xFFu) << 8);         \
+          _Pragma("unroll") for (int r = 0; r < 16; ++r) if (!((lb >> r) & 1u)) SC[kb][r] = -INFINITY; \
+        }                                                                                          \
+      }                                                                                            \
+      /* phase A: S of tile tn, interleaved with tile t's max, rescale and exponentials */         \
+      _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                             \
+        _Pragma("unroll") for (int r = 0; r < 16; ++r) SN[kb][r] = 0.0f;                           \
+      bf16x8 ring[RA + 1];                                                                         \
+      _Pragma("unroll") for (int i = 0; i < RA; ++i) ring[i] = K2_KFRAG(skn, i);                   \
+      K2_FENCE();                                                                                  \
+      float mx = -INFINITY, base = 0.0f;                                                           \
+      _Pragma("unroll") for (int i = 0; i < 2 * NS; ++i) {                                         \
+        if (i + RA < 2 * NS) ring[(i + RA) % (RA + 1)] = K2_KFRAG(skn, i + RA);                    \
+        SN[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ring[i % (RA + 1)], qf[i >> 1], SN[i & 1], 0, 0, 0); \
+        if (i < K_DMA) issue_k(st, tnn, i);                                                        \
+        else if (i < K_DMA + V_DMA) issue_v((st) ^ 1, tn, i - K_DMA);                              \
+        if (i < 4) {                                                                               \
+          _Pragma("unroll") for (int e = 0; e < 8; ++e) mx = fmaxf(mx, SC[i >> 1][8 * (i & 1) + e]); \
+        } else if (i == 4) {                                                                       \
+          mx = max_xor32(mx) * scale_log2;                                                         \
+          if (__any(mx > m_i + kRescale)) {                                                        \
+            const float mnew = fmaxf(m_i, mx);                                                     \
+            const float alpha = m_i == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(m_i - mnew);      \
+            l_i *= alpha;                                                                          \
+            _Pragma("unroll") for (int hb = 0; hb < NHB; ++hb) o[hb] *= alpha;                     \
+            m_i = mnew;                                                                            \
+          }                                                                                        \
+          base = m_i == -INFINITY ? 0.0f : m_i;                                                    \
+        } else {                                                                                   \
+          /* 32 exponentials over the remaining 2 NS - 5 instructions */                            \
+          constexpr int NX = 2 * NS - 5;                                                           \
+          _Pragma("unroll") for (int x = ((i - 5) * 32) / NX; x < ((i - 4) * 32) / NX; ++x)         \
+            SC[x >> 4][x & 15] = __builtin_amdgcn_exp2f(fmaf(SC[x >> 4][x & 15], scale_log2, -base)); \
+        }                                                                                          \
+        K2_FENCE();                                                                                \
+      }                                                                                            \
+      /* phase B: O^T += V^T P^T for tile t; step j = (kb, h) covers keys 32kb + 16h .. +15, */    \
+      /* packed just before its first instruction; the row sum runs alongside */                   \
+      bf16x8 vring[RA + 1];                                                                        \
+      _Pragma("unroll") for (int i = 0; i < RA; ++i) vring[i] = K2_VFRAG(svc, i);                  \
+      K2_FENCE();                                                                                  \
+      bf16x8 pf;                                                                                   \
+      float ls0 = 0.0f, ls1 = 0.0f;                                                                \
+      _Pragma("unroll") for (int i = 0; i < 4 * NHB; ++i) {                                        \
+        const int j = i / NHB;                                                                     \
+        if (i % NHB == 0) {                                                                        \
+          float pv[8];                                                                             \
+          _Pragma("unroll") for (int e = 0; e < 8; ++e) pv[e] = SC[j >> 1][8 * (j & 1) + e];        \
+          pack8(pf, pv);                                                                           \
+        }                                                                                          \
+        if (i + RA < 4 * NHB) vring[(i + RA) % (RA + 1)] = K2_VFRAG(svc, i + RA);                  \
+        o[i % NHB] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vring[i % (RA + 1)], pf, o[i % NHB], 0, 0, 0); \
+        /* row sum: 32 values over the 4 NHB instructions */                                       \
+        _Pragma("unroll") for (int x = (i * 32) / (4 * NHB); x < ((i + 1) * 32) / (4 * NHB); ++x) { \
+          if (x & 1) ls1 += SC[x >> 4][x & 15]; else ls0 += SC[x >> 4][x & 15];                    \
+        }                                                                                          \
+        K2_FENCE();                                                                                \
+      }                                                                                            \
+      l_i += ls0 + ls1;                                                                            \
+      K2_WAIT_VM(0);                                                                               \
+      __syncthreads();                                                                             \
+      if (tn < nt && tn * KT + KT > L) {                                                           \
+        zero_tail((st) ^ 1, tn);                                                                   \
+        __syncthreads();                                                                           \
+      }                                                                                            \
+      t = tn;                                                                                      \
+      tn = tnn;                                                                                    \
+    } while (0)
+    for (;;) {
+      K2_ATT_ITER(sa, sb, 0);
+      if (t >= nt) break;
+      K2_ATT_ITER(sb, sa, 1);
+      if (t >= nt) break;
+    }
+#undef K2_ATT_ITER
+  }
+#undef K2_FENCE
+#undef K2_KFRAG
+#undef K2_VFRAG
+#undef K2_SK
+#undef K2_SV
   // normalise, gate, store: lane holds query q0 + l%32 and head dims 32hb + 8j + 4(l/32) + 0..3
   const float lsum = l_i + __shfl_xor(l_i, 32);
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
