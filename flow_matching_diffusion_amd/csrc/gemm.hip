@@ -106,6 +106,10 @@ __device__ __forceinline__ void st4(bf16* p, float4 v) {
   t[0] = (bf16)v.x; t[1] = (bf16)v.y; t[2] = (bf16)v.z; t[3] = (bf16)v.w;
   *reinterpret_cast<bf16x4*>(p) = t;
 }
+// two floats rounded to bf16 (nearest even) and packed, the first in the low half
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return (uint32_t)__builtin_bit_cast(uint16_t, (bf16)lo) | ((uint32_t)__builtin_bit_cast(uint16_t, (bf16)hi) << 16);
+}
 __device__ __forceinline__ float4 fma4(float4 g, float4 a, float4 h) {
   return make_float4(h.x + g.x * a.x, h.y + g.y * a.y, h.z + g.z * a.z, h.w + g.w * a.w);
 }
@@ -117,6 +121,8 @@ __device__ __forceinline__ float4 fma4(float4 g, float4 a, float4 h) {
 // Epilogues that read nothing beyond their own arguments stage nothing in LDS.
 struct EpiNoStage {
   static constexpr bool kStaged = false;
+  static constexpr bool kLdsOut = false;  // the epilogue writes its output through a per-wave LDS area
+  static constexpr int kLdsOutFloats = 0;
   static constexpr int stage_floats() { return 0; }
   __device__ bool wants_stage(int) const { return false; }
   __device__ void stage(float*, int, int, int, int) const {}
@@ -131,7 +137,7 @@ struct EpiResid : EpiNoStage {
   int gate_stride, L, N;
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
-                                        int M, const float* stg = nullptr) const {
+                                        int M, float* stg = nullptr) const {
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = row0 + LY::row(i, lane);
@@ -162,7 +168,7 @@ struct EpiPlain : EpiNoStage {
   int ldt, act, N, rpb, orpb, ooff;
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
-                                        int M, const float* stg = nullptr) const {
+                                        int M, float* stg = nullptr) const {
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
       const int m = row0 + LY::row(i, lane);
@@ -192,27 +198,70 @@ struct EpiPlain : EpiNoStage {
 // a = silu(gate) * up; the wave's first WN/2 columns are gate, the last WN/2 the matching up columns.
 template <typename T, int WN>
 struct EpiSwiglu : EpiNoStage {
+  // bf16: each 32-row block of the wave's output (32 rows x WN/2 columns) is written to the wave's
+  // LDS area in the accumulator layout, then read back row-major, 8 lanes per 128-byte row, so
+  // every global store writes whole 128-byte lines. Stored straight from the accumulator layout,
+  // an instruction wrote 16 bytes into each of 32 rows 32 KiB apart, and the kernel wrote 2.6x its
+  // output to memory (partial lines).
+  static constexpr bool kLdsOut = sizeof(T) == 2;
+  static constexpr int kPitch = 144;  // bytes per staged row: 128 + 16 of padding
+  static constexpr int kLdsOutFloats = sizeof(T) == 2 ? 128 * kPitch / 4 : 0;  // 128 rows per wave
   T* a;
   int I;
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
-                                        int M, const float* stg = nullptr) const {
+                                        int M, float* stg = nullptr) const {
     static_assert(NJ * (LY::NQ == 1 ? 16 : 32) == WN, "wave width");
     const int cbase = (col0 / WN) * (WN / 2);
+    if constexpr (kLdsOut) {
+      static_assert(LY::NQ == 4 && WN == 128 && MI * 32 <= 128, "staged layout: 32x32 blocks, 64 bf16 per row");
+      char* const sm = reinterpret_cast<char*>(stg);
+      const int hi = lane >> 5, r = lane & 31;  // writer: row r, columns 8 q + 4 hi of each block
+      const int rr = lane >> 3, ch = lane & 7;  // reader: row 8 k + rr, columns 8 ch .. 8 ch + 7
+      const int c = cbase + 8 * ch;
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int m = row0 + LY::row(i, lane);
-      if (m >= M) continue;
+      for (int i = 0; i < MI; ++i) {
+        char* const blk = sm + i * 32 * kPitch;  // blocks do not share LDS: no wait between them
 #pragma unroll
-      for (int j = 0; j < NJ / 2; ++j)
+        for (int j = 0; j < NJ / 2; ++j)
 #pragma unroll
-        for (int q = 0; q < LY::NQ; ++q) {
-          const int c = cbase + LY::col(j, q, lane);
-          if (c >= I) continue;
-          const float4 g = quad(acc[i][j], q), u = quad(acc[i][j + NJ / 2], q);
-          st4(a + (size_t)m * I + c, make_float4(siluf_(g.x) * u.x, siluf_(g.y) * u.y, siluf_(g.z) * u.z,
-                                                 siluf_(g.w) * u.w));
+          for (int q = 0; q < 4; ++q) {
+            const float4 g = quad(acc[i][j], q), u = quad(acc[i][j + NJ / 2], q);
+            *reinterpret_cast<uint2*>(blk + r * kPitch + 64 * j + 16 * q + 8 * hi) =
+                make_uint2(pack_bf16x2(siluf_(g.x) * u.x, siluf_(g.y) * u.y),
+                           pack_bf16x2(siluf_(g.z) * u.z, siluf_(g.w) * u.w));
+          }
+        // a wave's LDS accesses complete in order, so the reads below see the writes above
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const int row = 8 * k + rr;
+          const uint4 v = *reinterpret_cast<const uint4*>(blk + row * kPitch + 16 * ch);
+          const int m = row0 + 32 * i + row;
+          if (m < M && c < I) {
+            T* p = a + (size_t)m * I + c;
+            if (c + 8 <= I)
+              *reinterpret_cast<uint4*>(p) = v;
+            else  // I is a multiple of 4: the last chunk holds 4 columns
+              *reinterpret_cast<uint2*>(p) = make_uint2(v.x, v.y);
+          }
         }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int m = row0 + LY::row(i, lane);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < NJ / 2; ++j)
+#pragma unroll
+          for (int q = 0; q < LY::NQ; ++q) {
+            const int c = cbase + LY::col(j, q, lane);
+            if (c >= I) continue;
+            const float4 g = quad(acc[i][j], q), u = quad(acc[i][j + NJ / 2], q);
+            st4(a + (size_t)m * I + c, make_float4(siluf_(g.x) * u.x, siluf_(g.y) * u.y, siluf_(g.z) * u.z,
+                                                   siluf_(g.w) * u.w));
+          }
+      }
     }
   }
 };
@@ -240,6 +289,8 @@ struct EpiQkvg {
   // global memory inside the epilogue, between its stores, made q and k tiles' epilogues several
   // times longer than the others'.
   static constexpr bool kStaged = true;
+  static constexpr bool kLdsOut = false;
+  static constexpr int kLdsOutFloats = 0;
   static constexpr int kStgRow = HD + 4;
   static constexpr int stage_floats() { return 2 * HD + 256 * kStgRow; }
   __device__ bool wants_stage(int n0) const { return n0 < nq + nk; }
@@ -265,7 +316,7 @@ struct EpiQkvg {
 
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
-                                        int M, const float* stg = nullptr) const {
+                                        int M, float* stg = nullptr) const {
     constexpr int BS = LY::NQ == 1 ? 16 : 32;
     constexpr int HB = HD / BS;  // column blocks per head
     static_assert(NJ % HB == 0, "a wave covers whole heads");
@@ -750,14 +801,19 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
     K2_STEP(fa1, fb1, fa0, fb0, ringA, ringB, -1, 0, 0);  // last sub-step of slab nk - 1
   }
   K2_WAIT_VM(0);  // no DMA may still write LDS when the workgroup retires
-  const float* stg = nullptr;
+  float* stg = nullptr;
+  if constexpr (Epi::kLdsOut) {
+    static_assert(4 * Epi::kLdsOutFloats * sizeof(float) <= Rings<RA, RB>::units(4) * sizeof(uint4), "LDS output");
+    __syncthreads();  // every wave is done with the rings
+    stg = reinterpret_cast<float*>(lds) + wave * Epi::kLdsOutFloats;
+  }
   if constexpr (Epi::kStaged) {
     static_assert(Epi::stage_floats() * sizeof(float) <= Rings<RA, RB>::units(4) * sizeof(uint4), "LDS staging");
     if (epi.wants_stage(n0)) {  // tile-uniform
       __syncthreads();  // every wave is done with the rings
       epi.stage(reinterpret_cast<float*>(lds), m0, M, tid, 256);
       __syncthreads();
-      stg = reinterpret_cast<const float*>(lds);
+      stg = reinterpret_cast<float*>(lds);
     }
   }
 #undef K2_DN
