@@ -610,6 +610,130 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
   }
 }
 
+// ---------------------------------------------------------------------------------------------
+// Short sequences (L <= 32: the layerwise text-fusion stage runs attention over the 12 hidden
+// layers of every token, B = batch x tokens sequences). One wave per (batch row, query head), four
+// per workgroup, no LDS: the wave loads its Q^T and permuted K fragments straight from memory,
+// computes S^T = K Q^T in HD/16 matrix-core steps, takes the softmax in registers (each lane holds
+// one query's scores; lanes l and l + 32 split the keys) and forms O^T = V^T P^T with one step per
+// 16 keys. Same masking, GQA head map, scale and gate as the tiled kernel.
+// ---------------------------------------------------------------------------------------------
+constexpr int kShortL = 32;
+
+template <int HD>
+__global__ void __launch_bounds__(256) attn_short_kernel(AttnArgs p, float scale_log2) {
+  constexpr int NS = HD / 16;   // k16 steps over head_dim
+  constexpr int NHB = HD / 32;  // 32-row head-dim blocks of O^T
+  const int lane = threadIdx.x & 63;
+  const int pair = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (pair >= p.B * p.nh) return;  // no barriers below
+  const int b = pair / p.nh, head = pair - b * p.nh;
+  const int kvh = head / (p.nh / p.nkv);
+  const int L = p.L, T_ = p.T;
+  const int ldq = p.nh * HD, ldk = p.nkv * HD;
+  const int h32 = lane >> 5, c32 = lane & 31;
+
+  // Q^T (B operand): lane l holds query l%32, head dims 16s + 8(l/32)..+7. K (A operand): lane l
+  // holds key kperm(l%32), so that the probabilities a lane ends up with are the P^T operand.
+  const int key_l = kperm(c32);
+  const bf16* qsrc = (const bf16*)p.q + (size_t)(b * L + (c32 < L ? c32 : 0)) * ldq + head * HD + 8 * h32;
+  const bf16* ksrc = (const bf16*)p.k + (size_t)(b * L + (key_l < L ? key_l : 0)) * ldk + kvh * HD + 8 * h32;
+  bf16x8 qf[NS], kf[NS];
+#pragma unroll
+  for (int st = 0; st < NS; ++st) {
+    qf[st] = c32 < L ? *(const bf16x8*)(qsrc + 16 * st) : bf16x8{};
+    kf[st] = key_l < L ? *(const bf16x8*)(ksrc + 16 * st) : bf16x8{};
+  }
+  // V^T (A operand of O^T += V^T P^T): lane l holds head dim 32hb + l%32, keys 16c + 8(l/32)..+7;
+  // keys at or past L read as zero (the workspace there holds anything)
+  const int nch = (L + 15) / 16;
+  const bf16* vsrc = (const bf16*)p.vt + ((size_t)(b * p.nkv + kvh) * HD + c32) * p.ldvt + 8 * h32;
+  bf16x8 vf[2][NHB];
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    const int k0 = 16 * c + 8 * h32;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) {
+      uint4 v = uint4{0u, 0u, 0u, 0u};
+      if (c < nch && k0 < L) {
+        v = *(const uint4*)(vsrc + (size_t)32 * hb * p.ldvt + 16 * c);
+        if (k0 + 8 > L) v = keep_first<8>(v, L - k0);
+      }
+      vf[c][hb] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+
+  f32x16 sacc;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) sacc[r] = 0.0f;
+#pragma unroll
+  for (int st = 0; st < NS; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sacc, 0, 0, 0);
+
+  // softmax over keys (base 2): register r holds key kperm(8(r/4) + 4(l/32) + r%4)
+  float sc[16];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    const int key = kperm(8 * (r >> 2) + 4 * h32 + (r & 3));
+    const bool ok = key < L && (key >= T_ || !p.mask || p.mask[(size_t)b * T_ + key] != 0);
+    sc[r] = ok ? sacc[r] * scale_log2 : -INFINITY;
+    mx = fmaxf(mx, sc[r]);
+  }
+  mx = max_xor32(mx);
+  if (mx == -INFINITY) mx = 0.0f;  // no valid key: every probability is 0 and the output 0
+  float ls = 0.0f;
+  float pv[16];
+#pragma unroll
+  for (int r = 0; r < 16; ++r) {
+    pv[r] = exp2f(sc[r] - mx);
+    ls += pv[r];
+  }
+  f32x16 o[NHB];
+#pragma unroll
+  for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[hb][r] = 0.0f;
+#pragma unroll
+  for (int c = 0; c < 2; ++c) {
+    if (c >= nch) break;  // wave-uniform
+    bf16x8 pf;
+    pack8(pf, pv + 8 * c);
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb) o[hb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf[c][hb], pf, o[hb], 0, 0, 0);
+  }
+
+  // normalise, gate, store: lane holds query l%32 and head dims 32hb + 8j + 4(l/32) + 0..3
+  const float lsum = ls + __shfl_xor(ls, 32);
+  const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  if (c32 < L) {
+    const size_t base = (size_t)(b * L + c32) * ldq + head * HD;
+    const bf16* gp = (const bf16*)p.g + base;
+    bf16* op = (bf16*)p.og + base;
+#pragma unroll
+    for (int hb = 0; hb < NHB; ++hb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int d0 = 32 * hb + 8 * j + 4 * h32;
+        const bf16x4 gv = *(const bf16x4*)(gp + d0);
+        bf16x4 out;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) out[e] = (bf16)(o[hb][4 * j + e] * inv * sigmoidf_((float)gv[e]));
+        *(bf16x4*)(op + d0) = out;
+      }
+  }
+}
+
+template <int HD>
+static hipError_t launch_attn_short(const AttnArgs& p, hipStream_t s) {
+  if (p.L <= 0 || p.B <= 0) return hipSuccess;
+  // V^T rows must hold the 32 key slots the fragments read, 16-byte aligned
+  if (p.L > kShortL || p.ldvt < kShortL || p.ldvt % 8 != 0) return hipErrorInvalidValue;
+  const long pairs = (long)p.B * p.nh;
+  const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
+  hipLaunchKernelGGL((attn_short_kernel<HD>), dim3((unsigned)((pairs + 3) / 4)), dim3(256), 0, s, p, scale_log2);
+  return hipGetLastError();
+}
+
 template <typename T, int HD, int G>
 static hipError_t launch_attn(const AttnArgs& p, hipStream_t s) {
   constexpr int BQ = 64 * (4 / G);
@@ -636,6 +760,7 @@ template <typename T, int HD>
 static hipError_t attn_hd(const AttnArgs& p, hipStream_t s) {
   const int G = p.nh / p.nkv;
   if constexpr (sizeof(T) == 2) {
+    if (p.L <= kShortL) return launch_attn_short<HD>(p, s);
     if (G == 4) return launch_attn_bf16<HD, 4>(p, s);
     if (G == 2) return launch_attn_bf16<HD, 2>(p, s);
     if (G == 1) return launch_attn_bf16<HD, 1>(p, s);

@@ -152,7 +152,8 @@ k2_block_workspace_layout block_layout(const k2_block_cfg* c, int B, int T, int 
   const size_t es = dt_size(c->dtype);
   const size_t L = (size_t)T + N, M = (size_t)B * L;
   const size_t H = c->hidden, nq = (size_t)c->num_heads * c->head_dim, nk = (size_t)c->num_kv_heads * c->head_dim;
-  l.ldvt = (int)((L + 63) / 64 * 64);
+  // V^T rows: 64-key tiles for the tiled attention kernel, 32 key slots for short sequences
+  l.ldvt = L <= 32 ? 32 : (int)((L + 63) / 64 * 64);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t o = off;

@@ -98,9 +98,10 @@ size_t k2_block_workspace_bytes(const k2_block_cfg* cfg, int B, int T, int N);
 
 /* Byte offsets of the intermediate tensors inside the block workspace (valid after a call on the
    same sizes): x1/x2 (B*L, hidden) modulated norms, q (B*L, nh*hd) and k (B*L, nkv*hd) after q/k norm
-   and RoPE, vt (B, nkv, hd, ldvt) values transposed, g (B*L, nh*hd) raw gate, og (B*L, nh*hd) gated
-   attention output, a (B*L, intermediate) SwiGLU activation — all of element type dtype — and mod
-   (B, 6, hidden) float32 modulation. Intended for tests and debugging. */
+   and RoPE, vt (B, nkv, hd, ldvt) values transposed (ldvt = 32 when L <= 32, else L rounded up to
+   64), g (B*L, nh*hd) raw gate, og (B*L, nh*hd) gated attention output, a (B*L, intermediate)
+   SwiGLU activation — all of element type dtype — and mod (B, 6, hidden) float32 modulation.
+   Intended for tests and debugging. */
 typedef struct {
   size_t x1, q, k, vt, g, og, x2, a, rope, mod, kvalid, total;
   int ldvt;

@@ -141,6 +141,9 @@ def test_workspace_layout_is_ordered_and_aligned():
     assert offs == sorted(offs) and all(o % 256 == 0 for o in offs)
     assert lay.total == lib.k2_block_workspace_bytes(ctypes.byref(good_cfg()), 2, 512, 4096)
     assert lay.ldvt % 64 == 0 and lay.ldvt >= 4608
+    # short sequences (the layerwise text-fusion stage): 32 key slots per V^T row
+    assert k2.block_workspace_layout(good_cfg(), 1024, 0, 12).ldvt == 32
+    assert k2.block_workspace_layout(good_cfg(), 2, 0, 33).ldvt == 64
 
 
 def test_time_and_text_and_backbone_validation():

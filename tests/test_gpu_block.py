@@ -47,6 +47,17 @@ MICRO = {
                                   axes_dims=(32, 48, 48)), "bf16", 2, 140, (12, 11), (70, 3)),
     "g4_hd128_f32": (S.BlockDims(hidden=512, num_heads=4, num_kv_heads=1, head_dim=128, intermediate=1024,
                                  axes_dims=(32, 48, 48)), "f32", 2, 140, (12, 11), (70, 3)),
+    # short sequences (L <= 32, the layerwise text-fusion shape): many batch rows, one key chunk
+    # (L = 12, no text, no mask), masked text with one row all padding (L = 16), two key chunks at
+    # the limit (L = 32), and L = 5 where half the lanes hold no key
+    "short12_g1_hd128_bf16": (S.BlockDims(hidden=256, num_heads=2, num_kv_heads=2, head_dim=128, intermediate=320,
+                                          axes_dims=(32, 48, 48)), "bf16", 40, 0, (3, 4), None),
+    "short16_g4_hd64_bf16": (S.BlockDims(hidden=256, num_heads=4, num_kv_heads=1, head_dim=64, intermediate=200,
+                                         axes_dims=(16, 24, 24)), "bf16", 5, 6, (2, 5), (4, 0, 6, 1, 3)),
+    "short32_g2_hd128_bf16": (S.BlockDims(hidden=512, num_heads=4, num_kv_heads=2, head_dim=128, intermediate=256,
+                                          axes_dims=(32, 48, 48)), "bf16", 3, 7, (5, 5), (7, 2, 0)),
+    "short5_g4_hd128_bf16": (S.BlockDims(hidden=512, num_heads=4, num_kv_heads=1, head_dim=128, intermediate=256,
+                                         axes_dims=(32, 48, 48)), "bf16", 7, 2, (1, 3), (1, 2, 0, 2, 1, 1, 2)),
 }
 
 
