@@ -8,9 +8,10 @@ residual, modulated RMSNorm, SwiGLU, down projection + gated residual) over the 
 weights and activations resident in HBM; temb is computed once before timing (the backbone
 computes it once for all 28 blocks). value = algorithmic block TFLOP/s (GEMMs over every row,
 attention over valid keys only). Also reported: the 28-block backbone with text fusion at the
-same resolution as denoise steps/s (one call = one CFG step), the sampler (k2_denoise_step on one image,
-with guidance as the base checkpoint's 28 steps and without as the distilled 8 steps) as time per
-image, per-kernel times, the roofline of the dominant kernel, and the CPU oracle on a bounded sample.
+same resolution as denoise steps/s (one call = one CFG step), the sampler on one image (with guidance
+as the base checkpoint's 28 steps and without as the distilled 8 steps) as time per image, both with
+the text rows computed once per prompt pair (k2_text_embed, then k2_denoise_step_cached) and with
+the text path run at every step (k2_denoise_step), per-kernel times, the roofline of the dominant kernel, and the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-backbone] [--no-cpu-baseline]
                        [--cpu-rows R] [--copy-calibration]
@@ -266,10 +267,30 @@ def main():
                 k2.denoise_step(mcfg, mw, lat, e, bpos, mk, float(sig[i]), float(sig[i + 1]), g, workspace=dws)
             torch.cuda.synchronize()
             sms = (time.perf_counter() - t0) * 1e3 / args.sampler_steps
-            sampler[name] = {"guidance": g, "transformer_batch": G, "ms_per_step": round(sms, 2),
-                             "image_s": round(steps * sms / 1e3, 2), "steps": steps,
-                             "timed_steps": args.sampler_steps}
             del dws
+            # the text rows once per prompt pair (k2_text_embed), then steps that reuse them
+            tws = torch.empty(k2.text_embed_workspace_bytes(mcfg, G, bwl.T), dtype=torch.uint8, device=dev)
+            cws = torch.empty(k2.denoise_cached_workspace_bytes(mcfg, bwl.T, bwl.N, g > 0), dtype=torch.uint8,
+                              device=dev)
+            txt = k2.text_embed(mcfg, mw, e, mk, workspace=tws)
+            k2.denoise_step_cached(mcfg, mw, lat, txt, bpos, mk, float(sig[0]), float(sig[1]), g, workspace=cws)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            txt = k2.text_embed(mcfg, mw, e, mk, workspace=tws)
+            torch.cuda.synchronize()
+            tms = (time.perf_counter() - t0) * 1e3
+            t0 = time.perf_counter()
+            for i in range(args.sampler_steps):
+                k2.denoise_step_cached(mcfg, mw, lat, txt, bpos, mk, float(sig[i]), float(sig[i + 1]), g,
+                                       workspace=cws)
+            torch.cuda.synchronize()
+            cms = (time.perf_counter() - t0) * 1e3 / args.sampler_steps
+            sampler[name] = {"guidance": g, "transformer_batch": G, "steps": steps, "timed_steps": args.sampler_steps,
+                             "text_cached": {"text_embed_ms": round(tms, 2), "ms_per_step": round(cms, 2),
+                                             "image_s": round((tms + steps * cms) / 1e3, 3)},
+                             "text_every_step": {"ms_per_step": round(sms, 2),
+                                                 "image_s": round(steps * sms / 1e3, 3)}}
+            del tws, cws, txt
         assert bool(torch.isfinite(lat).all())
         result["sampler"] = sampler
         del mw, x, enc, lat

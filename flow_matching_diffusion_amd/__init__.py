@@ -267,6 +267,55 @@ def backbone_workspace_bytes(cfg, B: int, T: int, N: int) -> int:
     return load().k2_backbone_workspace_bytes(ctypes.byref(cfg), B, T, N)
 
 
+def text_embed_workspace_bytes(cfg, B: int, T: int) -> int:
+    return load().k2_text_embed_workspace_bytes(ctypes.byref(cfg), B, T)
+
+
+def text_embed(cfg, weights: dict, enc, mask, workspace=None, stream=None):
+    """k2_text_embed: txt_in(text_fusion(enc)) for the backbone's text rows, (B, T, hidden) float32.
+    enc (B, T, layers, D) in the operand dtype; mask (B, T) or None."""
+    torch = _torch()
+    lib = load()
+    _dev_tensor(enc, "encoder_hidden_states")
+    B, T = enc.shape[0], enc.shape[1]
+    mask = _mask_u8(mask)
+    out = torch.empty(B, T, cfg.block.hidden, dtype=torch.float32, device=enc.device)
+    mw, keep = _model_weights(weights)
+    ws = _workspace(lib.k2_text_embed_workspace_bytes(ctypes.byref(cfg), B, T), enc.device, workspace)
+    check(lib.k2_text_embed(ctypes.byref(cfg), ctypes.byref(mw), B, T, _ptr(enc), _ptr(mask), _ptr(out), _ptr(ws),
+                            ws.numel(), _stream(stream)))
+    del keep
+    return out
+
+
+def backbone_cached_workspace_bytes(cfg, B: int, T: int, N: int) -> int:
+    return load().k2_backbone_cached_workspace_bytes(ctypes.byref(cfg), B, T, N)
+
+
+def backbone_forward_cached(cfg, weights: dict, x, txt_h, timestep, position_ids, mask, workspace=None, stream=None):
+    """k2_backbone_forward_cached: the backbone with its text rows from text_embed (txt_h (B, T, hidden)
+    float32, or None when T = 0). Returns the velocity (B, N, in_channels) float32."""
+    torch = _torch()
+    lib = load()
+    _dev_tensor(x, "hidden_states")
+    _dev_tensor(timestep, "timestep", torch.float32)
+    B, N, C = x.shape
+    T = 0
+    if txt_h is not None:
+        _dev_tensor(txt_h, "txt_h", torch.float32)
+        T = txt_h.shape[1]
+    mask = _mask_u8(mask)
+    out = torch.empty(B, N, C, dtype=torch.float32, device=x.device)
+    mw, keep = _model_weights(weights)
+    ws = _workspace(lib.k2_backbone_cached_workspace_bytes(ctypes.byref(cfg), B, T, N), x.device, workspace)
+    check(lib.k2_backbone_forward_cached(ctypes.byref(cfg), ctypes.byref(mw), B, T, N, _ptr(x), _ptr(txt_h),
+                                         _ptr(timestep), _ptr(position_ids), position_ids.shape[0],
+                                         position_ids.shape[1], _ptr(mask), _ptr(out), _ptr(ws), ws.numel(),
+                                         _stream(stream)))
+    del keep
+    return out
+
+
 # ------------------------------------------------------------------------------------------------
 # Sampler
 # ------------------------------------------------------------------------------------------------
@@ -321,6 +370,33 @@ def denoise_step(cfg, weights: dict, latents, enc, position_ids, mask, sigma: fl
     check(lib.k2_denoise_step(ctypes.byref(cfg), ctypes.byref(mw), T, N, _ptr(latents), _ptr(enc), _ptr(mask),
                               _ptr(position_ids), position_ids.shape[0], position_ids.shape[1], sigma, sigma_next,
                               guidance, _ptr(ws), ws.numel(), _stream(stream)))
+    del keep
+    return latents
+
+
+def denoise_cached_workspace_bytes(cfg, T: int, N: int, guided: bool) -> int:
+    return load().k2_denoise_cached_workspace_bytes(ctypes.byref(cfg), T, N, 1 if guided else 0)
+
+
+def denoise_step_cached(cfg, weights: dict, latents, txt_h, position_ids, mask, sigma: float, sigma_next: float,
+                        guidance: float, workspace=None, stream=None):
+    """k2_denoise_step_cached: denoise_step with the text rows txt_h (G, T, hidden) float32 from text_embed
+    (computed once per prompt pair), or None when T = 0."""
+    torch = _torch()
+    lib = load()
+    _dev_tensor(latents, "latents", torch.float32)
+    _, N, _ = latents.shape
+    T = 0
+    if txt_h is not None:
+        _dev_tensor(txt_h, "txt_h", torch.float32)
+        T = txt_h.shape[1]
+    mask = _mask_u8(mask)
+    mw, keep = _model_weights(weights)
+    ws = _workspace(lib.k2_denoise_cached_workspace_bytes(ctypes.byref(cfg), T, N, 1 if guidance > 0 else 0),
+                    latents.device, workspace)
+    check(lib.k2_denoise_step_cached(ctypes.byref(cfg), ctypes.byref(mw), T, N, _ptr(latents), _ptr(txt_h),
+                                     _ptr(mask), _ptr(position_ids), position_ids.shape[0], position_ids.shape[1],
+                                     sigma, sigma_next, guidance, _ptr(ws), ws.numel(), _stream(stream)))
     del keep
     return latents
 

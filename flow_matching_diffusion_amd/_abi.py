@@ -84,6 +84,13 @@ SIGNATURES = {
     "k2_backbone_forward": (c_int, [POINTER(ModelCfg), POINTER(ModelWeights), c_int, c_int, c_int, c_void_p, c_void_p,
                                     c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_size_t,
                                     c_void_p]),
+    "k2_text_embed_workspace_bytes": (c_size_t, [POINTER(ModelCfg), c_int, c_int]),
+    "k2_text_embed": (c_int, [POINTER(ModelCfg), POINTER(ModelWeights), c_int, c_int, c_void_p, c_void_p, c_void_p,
+                              c_void_p, c_size_t, c_void_p]),
+    "k2_backbone_cached_workspace_bytes": (c_size_t, [POINTER(ModelCfg), c_int, c_int, c_int]),
+    "k2_backbone_forward_cached": (c_int, [POINTER(ModelCfg), POINTER(ModelWeights), c_int, c_int, c_int, c_void_p,
+                                           c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p,
+                                           c_size_t, c_void_p]),
     "k2_shift_cfg_default": (None, [POINTER(ShiftCfg)]),
     "k2_flow_sigmas": (c_int, [POINTER(ShiftCfg), c_int, c_int, c_int, POINTER(c_float)]),
     "k2_cfg_euler_update": (c_int, [c_void_p, c_void_p, c_void_p, c_void_p, c_size_t, c_float, c_float, c_float,
@@ -91,6 +98,10 @@ SIGNATURES = {
     "k2_denoise_workspace_bytes": (c_size_t, [POINTER(ModelCfg), c_int, c_int, c_int]),
     "k2_denoise_step": (c_int, [POINTER(ModelCfg), POINTER(ModelWeights), c_int, c_int, c_void_p, c_void_p, c_void_p,
                                 c_void_p, c_int, c_int, c_float, c_float, c_float, c_void_p, c_size_t, c_void_p]),
+    "k2_denoise_cached_workspace_bytes": (c_size_t, [POINTER(ModelCfg), c_int, c_int, c_int]),
+    "k2_denoise_step_cached": (c_int, [POINTER(ModelCfg), POINTER(ModelWeights), c_int, c_int, c_void_p, c_void_p,
+                                       c_void_p, c_void_p, c_int, c_int, c_float, c_float, c_float, c_void_p, c_size_t,
+                                       c_void_p]),
     "k2_last_error": (c_char_p, []),
     "k2_profile_enable": (None, [c_int]),
     "k2_profile_reset": (None, []),

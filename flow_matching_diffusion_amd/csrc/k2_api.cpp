@@ -396,7 +396,8 @@ int text_run(const k2_text_cfg* c, const k2_text_weights* w, int B, int T, const
 struct ModelLayout {
   size_t temb, e, time, txt, txt_t, text, h, rope, block, fmod, xf, total;
 };
-ModelLayout model_layout(const k2_model_cfg* c, int B, int T, int N) {
+// text: whether the call runs the text path itself (false: the caller passes its cached output)
+ModelLayout model_layout(const k2_model_cfg* c, int B, int T, int N, bool text = true) {
   ModelLayout l = {};
   const size_t es = dt_size(c->block.dtype);
   const size_t H = c->block.hidden, L = (size_t)T + N, Dt = c->text.block.hidden;
@@ -410,9 +411,10 @@ ModelLayout model_layout(const k2_model_cfg* c, int B, int T, int N) {
   l.temb = take((size_t)B * 6 * H * sizeof(float));
   l.e = take((size_t)B * H * sizeof(float));
   l.time = take(time_layout(&tc, B).total);
-  l.txt = take((size_t)B * T * Dt * sizeof(float));
-  l.txt_t = take((size_t)B * T * Dt * es);
-  l.text = take(T > 0 ? text_layout(&c->text, B, T).total : 0);
+  const size_t Tt = text ? (size_t)T : 0;
+  l.txt = take((size_t)B * Tt * Dt * sizeof(float));
+  l.txt_t = take((size_t)B * Tt * Dt * es);
+  l.text = take(Tt > 0 ? text_layout(&c->text, B, T).total : 0);
   l.h = take((size_t)B * L * H * sizeof(float));
   l.rope = take(2 * L * (size_t)(c->block.head_dim / 2) * sizeof(float));
   l.block = take(block_layout(&c->block, B, T, N).total);
@@ -422,7 +424,7 @@ ModelLayout model_layout(const k2_model_cfg* c, int B, int T, int N) {
   return l;
 }
 
-int check_model(const k2_model_cfg* c, const k2_model_weights* w, int B, int T, int N) {
+int check_model(const k2_model_cfg* c, const k2_model_weights* w, int B, int T, int N, bool text = true) {
   if (!c) return fail(K2_ERR_NULL, "model config is NULL");
   int rc;
   if ((rc = check_block_cfg(&c->block, true)) != K2_OK) return rc;
@@ -432,7 +434,7 @@ int check_model(const k2_model_cfg* c, const k2_model_weights* w, int B, int T, 
     return fail(K2_ERR_CONFIG, "num_layers >= 0, in_channels and timestep_embed_dim positive multiples of 8");
   if (c->text.block.hidden % 8) return fail(K2_ERR_CONFIG, "text hidden must be a multiple of 8");
   if (!w) return fail(K2_ERR_NULL, "model weights are NULL");
-  if (!w->img_in_w || !w->txt_in_w || !w->final_w || !w->final_table)
+  if (!w->img_in_w || (text && !w->txt_in_w) || !w->final_w || !w->final_table)
     return fail(K2_ERR_NULL, "img_in / txt_in / final weights are NULL");
   if ((rc = check_align("img_in / txt_in / final weights", {w->img_in_w, w->img_in_b, w->txt_in_w, w->txt_in_b,
                                                             w->final_w, w->final_b, w->final_norm_w,
@@ -447,7 +449,45 @@ int check_model(const k2_model_cfg* c, const k2_model_weights* w, int B, int T, 
   if ((rc = check_time(&tc, &w->time, B)) != K2_OK) return rc;
   if ((rc = check_sizes(B, T, N)) != K2_OK) return rc;
   if (N <= 0) return fail(K2_ERR_SHAPE, "the backbone needs N >= 1 image tokens");
-  if (T > 0 && (rc = check_text(&c->text, &w->text, B, T)) != K2_OK) return rc;
+  if (text && T > 0 && (rc = check_text(&c->text, &w->text, B, T)) != K2_OK) return rc;
+  return K2_OK;
+}
+
+// txt_in(text_fusion(enc)) into rows [0, T) of every batch row of out (out_rows_per_b rows per batch
+// row, width hidden, float32). ws: text_embed_layout(c, B, T).total bytes.
+struct TextEmbedLayout {
+  size_t txt, txt_t, text, total;
+};
+TextEmbedLayout text_embed_layout(const k2_model_cfg* c, int B, int T) {
+  TextEmbedLayout l = {};
+  const size_t es = dt_size(c->block.dtype), Dt = c->text.block.hidden;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  l.txt = take((size_t)B * T * Dt * sizeof(float));
+  l.txt_t = take((size_t)B * T * Dt * es);
+  l.text = take(T > 0 ? text_layout(&c->text, B, T).total : 0);
+  l.total = off;
+  return l;
+}
+
+int text_embed_run(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, const void* enc,
+                   const uint8_t* mask, float* out, int out_rows_per_b, void* ws, hipStream_t s) {
+  if (T <= 0) return K2_OK;
+  const TextEmbedLayout l = text_embed_layout(cfg, B, T);
+  const int dt = cfg->block.dtype, H = cfg->block.hidden, Dt = cfg->text.block.hidden;
+  float* txt = (float*)at(ws, l.txt);
+  void* txt_t = at(ws, l.txt_t);
+  int rc;
+  if ((rc = text_run(&cfg->text, &w->text, B, T, enc, mask, txt, at(ws, l.text), s)) != K2_OK) return rc;
+  K2_RUN("convert", s, from_f32(dt, txt, txt_t, (size_t)B * T * Dt, s));
+  PlainArgs p = {};
+  p.w = w->txt_in_w; p.N = H; p.bias = w->txt_in_b; p.outf = out; p.ldf = H;
+  p.rows_per_b = T; p.out_rows_per_b = out_rows_per_b; p.out_row_off = 0;
+  K2_RUN("gemm_plain", s, gemm_plain(dt, GemmA{txt_t, Dt, B * T, Dt}, p, s));
   return K2_OK;
 }
 
@@ -556,35 +596,92 @@ size_t k2_backbone_workspace_bytes(const k2_model_cfg* cfg, int B, int T, int N)
   return model_layout(cfg, B, T, N).total;
 }
 
+size_t k2_backbone_cached_workspace_bytes(const k2_model_cfg* cfg, int B, int T, int N) {
+  if (!cfg || B < 0 || T < 0 || N < 0) return 0;
+  return model_layout(cfg, B, T, N, false).total;
+}
+
+size_t k2_text_embed_workspace_bytes(const k2_model_cfg* cfg, int B, int T) {
+  if (!cfg || B < 0 || T < 0) return 0;
+  return text_embed_layout(cfg, B, T).total;
+}
+
+int k2_text_embed(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, const void* enc,
+                  const uint8_t* mask, float* txt_h, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!cfg) return fail(K2_ERR_NULL, "model config is NULL");
+  if (!w) return fail(K2_ERR_NULL, "model weights are NULL");
+  int rc;
+  if (cfg->text.block.dtype != cfg->block.dtype) return fail(K2_ERR_DTYPE, "text and block dtypes differ");
+  if (cfg->block.hidden <= 0 || cfg->block.hidden % 8 || cfg->text.block.hidden % 8)
+    return fail(K2_ERR_CONFIG, "hidden sizes must be positive multiples of 8");
+  if ((rc = check_text(&cfg->text, &w->text, B, T)) != K2_OK) return rc;
+  if (!w->txt_in_w) return fail(K2_ERR_NULL, "txt_in weight is NULL");
+  if (!enc || !txt_h) return fail(K2_ERR_NULL, "encoder_hidden_states / txt_h is NULL");
+  if ((rc = check_align("encoder_hidden_states / txt_h / txt_in", {enc, txt_h, w->txt_in_w, w->txt_in_b})) != K2_OK)
+    return rc;
+  if ((rc = check_ws(workspace, workspace_bytes, text_embed_layout(cfg, B, T).total)) != K2_OK) return rc;
+  g_err.clear();
+  return text_embed_run(cfg, w, B, T, enc, mask, txt_h, T, workspace, (hipStream_t)stream);
+}
+
 int backbone_run(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N, const void* hidden_states,
-                 const void* enc, const float* timestep, const float* pos, const uint8_t* mask, float* out,
-                 void* workspace, hipStream_t s);
+                 const void* enc, const float* txt_cached, const float* timestep, const float* pos,
+                 const uint8_t* mask, float* out, void* workspace, hipStream_t s);
+
+// Validation shared by the backbone entry points; text: the call runs the text path on enc,
+// otherwise txt_h holds its output.
+int check_backbone_call(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N,
+                        const void* hidden_states, const void* enc, const float* txt_h, const float* timestep,
+                        const float* pos, int pos_rows, int pos_cols, const float* out, bool text) {
+  int rc = check_model(cfg, w, B, T, N, text);
+  if (rc != K2_OK) return rc;
+  if (!hidden_states || !timestep || !pos || !out)
+    return fail(K2_ERR_NULL, "hidden_states / timestep / position_ids / out is NULL");
+  if (T > 0 && text && !enc) return fail(K2_ERR_NULL, "encoder_hidden_states is NULL");
+  if (T > 0 && !text && !txt_h) return fail(K2_ERR_NULL, "txt_h is NULL");
+  if ((rc = check_align("hidden_states / encoder_hidden_states / txt_h / out", {hidden_states, enc, txt_h, out})) !=
+      K2_OK)
+    return rc;
+  if (pos_rows != T + N || pos_cols != 3)
+    return fail(K2_ERR_SHAPE, "position_ids must be (T + N, 3) = (%d, 3), got (%d, %d)", T + N, pos_rows, pos_cols);
+  return K2_OK;
+}
 
 int k2_backbone_forward(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N,
                         const void* hidden_states, const void* enc, const float* timestep, const float* pos,
                         int pos_rows, int pos_cols, const uint8_t* mask, float* out, void* workspace,
                         size_t workspace_bytes, void* stream) {
-  int rc = check_model(cfg, w, B, T, N);
+  int rc = check_backbone_call(cfg, w, B, T, N, hidden_states, enc, nullptr, timestep, pos, pos_rows, pos_cols, out,
+                               true);
   if (rc != K2_OK) return rc;
-  if (!hidden_states || !timestep || !pos || !out || (T > 0 && !enc))
-    return fail(K2_ERR_NULL, "hidden_states / encoder_hidden_states / timestep / position_ids / out is NULL");
-  if ((rc = check_align("hidden_states / encoder_hidden_states / out", {hidden_states, enc, out})) != K2_OK) return rc;
-  if (pos_rows != T + N || pos_cols != 3)
-    return fail(K2_ERR_SHAPE, "position_ids must be (T + N, 3) = (%d, 3), got (%d, %d)", T + N, pos_rows, pos_cols);
-  const ModelLayout l = model_layout(cfg, B, T, N);
-  if ((rc = check_ws(workspace, workspace_bytes, l.total)) != K2_OK) return rc;
+  if ((rc = check_ws(workspace, workspace_bytes, model_layout(cfg, B, T, N).total)) != K2_OK) return rc;
   g_err.clear();
-  return backbone_run(cfg, w, B, T, N, hidden_states, enc, timestep, pos, mask, out, workspace, (hipStream_t)stream);
+  return backbone_run(cfg, w, B, T, N, hidden_states, enc, nullptr, timestep, pos, mask, out, workspace,
+                      (hipStream_t)stream);
 }
 
-// The backbone after validation (also the transformer call of k2_denoise_step).
+int k2_backbone_forward_cached(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N,
+                               const void* hidden_states, const float* txt_h, const float* timestep,
+                               const float* pos, int pos_rows, int pos_cols, const uint8_t* mask, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = check_backbone_call(cfg, w, B, T, N, hidden_states, nullptr, txt_h, timestep, pos, pos_rows, pos_cols,
+                               out, false);
+  if (rc != K2_OK) return rc;
+  if ((rc = check_ws(workspace, workspace_bytes, model_layout(cfg, B, T, N, false).total)) != K2_OK) return rc;
+  g_err.clear();
+  return backbone_run(cfg, w, B, T, N, hidden_states, nullptr, txt_h, timestep, pos, mask, out, workspace,
+                      (hipStream_t)stream);
+}
+
+// The backbone after validation (also the transformer call of the sampler steps). The text rows of
+// h come from the text path on enc, or from txt_cached (B, T, hidden) when that is not NULL.
 int backbone_run(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N, const void* hidden_states,
-                 const void* enc, const float* timestep, const float* pos, const uint8_t* mask, float* out,
-                 void* workspace, hipStream_t s) {
+                 const void* enc, const float* txt_cached, const float* timestep, const float* pos,
+                 const uint8_t* mask, float* out, void* workspace, hipStream_t s) {
   int rc;
-  const ModelLayout l = model_layout(cfg, B, T, N);
+  const ModelLayout l = model_layout(cfg, B, T, N, txt_cached == nullptr);
   const int dt = cfg->block.dtype, H = cfg->block.hidden, hd = cfg->block.head_dim, L = T + N;
-  const int Dt = cfg->text.block.hidden, C = cfg->in_channels;
+  const int C = cfg->in_channels;
   float* temb = (float*)at(workspace, l.temb);
   float* e = (float*)at(workspace, l.e);
   float* h = (float*)at(workspace, l.h);
@@ -595,16 +692,16 @@ int backbone_run(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int 
   k2_time_cfg tc = {H, cfg->timestep_embed_dim, dt};
   if ((rc = time_run(&tc, &w->time, B, timestep, temb, e, at(workspace, l.time), s)) != K2_OK) return rc;
 
-  // text path: text fusion -> txt_in into rows [0, T) of every batch row
+  // text path: text fusion -> txt_in into rows [0, T) of every batch row (its workspace regions
+  // txt, txt_t, text are laid out as text_embed_layout's)
   if (T > 0) {
-    float* txt = (float*)at(workspace, l.txt);
-    void* txt_t = at(workspace, l.txt_t);
-    if ((rc = text_run(&cfg->text, &w->text, B, T, enc, mask, txt, at(workspace, l.text), s)) != K2_OK) return rc;
-    K2_RUN("convert", s, from_f32(dt, txt, txt_t, (size_t)B * T * Dt, s));
-    PlainArgs p = {};
-    p.w = w->txt_in_w; p.N = H; p.bias = w->txt_in_b; p.outf = h; p.ldf = H;
-    p.rows_per_b = T; p.out_rows_per_b = L; p.out_row_off = 0;
-    K2_RUN("gemm_plain", s, gemm_plain(dt, GemmA{txt_t, Dt, B * T, Dt}, p, s));
+    if (txt_cached) {
+      const size_t row = (size_t)T * H * sizeof(float);
+      K2_RUN("copy", s, hipMemcpy2DAsync(h, (size_t)L * H * sizeof(float), txt_cached, row, row, B,
+                                         hipMemcpyDeviceToDevice, s));
+    } else if ((rc = text_embed_run(cfg, w, B, T, enc, mask, h, L, at(workspace, l.txt), s)) != K2_OK) {
+      return rc;
+    }
   }
   // image path: img_in into rows [T, L)
   {
@@ -696,7 +793,7 @@ int k2_cfg_euler_update(const float* x, float* x_out, const float* v_cond, const
 struct DenoiseLayout {
   size_t xin, v, t, model, total;
 };
-DenoiseLayout denoise_layout(const k2_model_cfg* c, int T, int N, int guided) {
+DenoiseLayout denoise_layout(const k2_model_cfg* c, int T, int N, int guided, bool text = true) {
   DenoiseLayout l = {};
   const int B = guided ? 2 : 1;
   const size_t nc = (size_t)N * c->in_channels;
@@ -709,7 +806,7 @@ DenoiseLayout denoise_layout(const k2_model_cfg* c, int T, int N, int guided) {
   l.xin = take(B * nc * dt_size(c->block.dtype));
   l.v = take(B * nc * sizeof(float));
   l.t = take(B * sizeof(float));
-  l.model = take(model_layout(c, B, T, N).total);
+  l.model = take(model_layout(c, B, T, N, text).total);
   l.total = off;
   return l;
 }
@@ -719,19 +816,28 @@ size_t k2_denoise_workspace_bytes(const k2_model_cfg* cfg, int T, int N, int gui
   return denoise_layout(cfg, T, N, guided != 0).total;
 }
 
-int k2_denoise_step(const k2_model_cfg* cfg, const k2_model_weights* w, int T, int N, float* latents, const void* enc,
-                    const uint8_t* mask, const float* pos, int pos_rows, int pos_cols, float sigma, float sigma_next,
-                    float guidance, void* workspace, size_t workspace_bytes, void* stream) {
+size_t k2_denoise_cached_workspace_bytes(const k2_model_cfg* cfg, int T, int N, int guided) {
+  if (!cfg || T < 0 || N < 0) return 0;
+  return denoise_layout(cfg, T, N, guided != 0, false).total;
+}
+
+// One sampler step: the transformer on enc (text path run here) or on the cached text rows txt_h.
+int denoise_call(const k2_model_cfg* cfg, const k2_model_weights* w, int T, int N, float* latents, const void* enc,
+                 const float* txt_h, bool text, const uint8_t* mask, const float* pos, int pos_rows, int pos_cols,
+                 float sigma, float sigma_next, float guidance, void* workspace, size_t workspace_bytes,
+                 void* stream) {
   const int guided = guidance > 0.0f, B = guided ? 2 : 1;
-  int rc = check_model(cfg, w, B, T, N);
+  int rc = check_model(cfg, w, B, T, N, text);
   if (rc != K2_OK) return rc;
-  if (!latents || !pos || (T > 0 && !enc)) return fail(K2_ERR_NULL, "latents / encoder_hidden_states / position_ids is NULL");
-  if ((rc = check_align("latents / encoder_hidden_states", {latents, enc})) != K2_OK) return rc;
+  if (!latents || !pos) return fail(K2_ERR_NULL, "latents / position_ids is NULL");
+  if (T > 0 && text && !enc) return fail(K2_ERR_NULL, "encoder_hidden_states is NULL");
+  if (T > 0 && !text && !txt_h) return fail(K2_ERR_NULL, "txt_h is NULL");
+  if ((rc = check_align("latents / encoder_hidden_states / txt_h", {latents, enc, txt_h})) != K2_OK) return rc;
   if (pos_rows != T + N || pos_cols != 3)
     return fail(K2_ERR_SHAPE, "position_ids must be (T + N, 3) = (%d, 3), got (%d, %d)", T + N, pos_rows, pos_cols);
   if (!std::isfinite(guidance) || !std::isfinite(sigma) || !std::isfinite(sigma_next))
     return fail(K2_ERR_SHAPE, "guidance and sigmas must be finite");
-  const DenoiseLayout l = denoise_layout(cfg, T, N, guided);
+  const DenoiseLayout l = denoise_layout(cfg, T, N, guided, text);
   if ((rc = check_ws(workspace, workspace_bytes, l.total)) != K2_OK) return rc;
   g_err.clear();
 
@@ -744,9 +850,26 @@ int k2_denoise_step(const k2_model_cfg* cfg, const k2_model_weights* w, int T, i
   // the transformer input: the latents in the operand dtype, once per guidance branch
   for (int b = 0; b < B; ++b) K2_RUN("convert", s, from_f32(dt, latents, xin + b * nc * es, nc, s));
   K2_RUN("fill", s, fill_f32(t, B, sigma, s));
-  if ((rc = backbone_run(cfg, w, B, T, N, xin, enc, t, pos, mask, v, at(workspace, l.model), s)) != K2_OK) return rc;
+  if ((rc = backbone_run(cfg, w, B, T, N, xin, text ? enc : nullptr, text ? nullptr : txt_h, t, pos, mask, v,
+                         at(workspace, l.model), s)) != K2_OK)
+    return rc;
   K2_RUN("cfg_euler", s, cfg_euler(latents, latents, v, guided ? v + nc : nullptr, nc, guidance, sigma_next - sigma, s));
   return K2_OK;
+}
+
+int k2_denoise_step(const k2_model_cfg* cfg, const k2_model_weights* w, int T, int N, float* latents, const void* enc,
+                    const uint8_t* mask, const float* pos, int pos_rows, int pos_cols, float sigma, float sigma_next,
+                    float guidance, void* workspace, size_t workspace_bytes, void* stream) {
+  return denoise_call(cfg, w, T, N, latents, enc, nullptr, true, mask, pos, pos_rows, pos_cols, sigma, sigma_next,
+                      guidance, workspace, workspace_bytes, stream);
+}
+
+int k2_denoise_step_cached(const k2_model_cfg* cfg, const k2_model_weights* w, int T, int N, float* latents,
+                           const float* txt_h, const uint8_t* mask, const float* pos, int pos_rows, int pos_cols,
+                           float sigma, float sigma_next, float guidance, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return denoise_call(cfg, w, T, N, latents, nullptr, txt_h, false, mask, pos, pos_rows, pos_cols, sigma, sigma_next,
+                      guidance, workspace, workspace_bytes, stream);
 }
 
 const char* k2_last_error(void) { return g_err.c_str(); }

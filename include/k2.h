@@ -215,6 +215,26 @@ int k2_backbone_forward(const k2_model_cfg* cfg, const k2_model_weights* w, int 
                         const uint8_t* encoder_attention_mask, float* out,
                         void* workspace, size_t workspace_bytes, void* stream);
 
+/* Text-path cache ([ARTICLE] §四 data flow, §五: the text stack enters only through text fusion and
+   txt_in, which do not depend on the timestep or the latents, so a sampler computes them once per
+   prompt). k2_text_embed writes txt_in(text_fusion(encoder_hidden_states)) to txt_h, (B, T, hidden)
+   float32: exactly the rows [0, T) that k2_backbone_forward builds before its first block.
+   k2_backbone_forward_cached is k2_backbone_forward with those rows taken from txt_h (B, T, hidden)
+   float32 instead of being computed: given txt_h from k2_text_embed on the same inputs its output is
+   bit-identical. The mask is still required for the blocks' attention; the text-fusion weights
+   (w->text, w->txt_in_*) are not read. Workspaces: k2_text_embed_workspace_bytes and
+   k2_backbone_cached_workspace_bytes (no text-fusion buffers). txt_h must be 16-byte aligned. */
+size_t k2_text_embed_workspace_bytes(const k2_model_cfg* cfg, int B, int T);
+int k2_text_embed(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T,
+                  const void* encoder_hidden_states, const uint8_t* encoder_attention_mask, float* txt_h,
+                  void* workspace, size_t workspace_bytes, void* stream);
+size_t k2_backbone_cached_workspace_bytes(const k2_model_cfg* cfg, int B, int T, int N);
+int k2_backbone_forward_cached(const k2_model_cfg* cfg, const k2_model_weights* w, int B, int T, int N,
+                               const void* hidden_states, const float* txt_h,
+                               const float* timestep, const float* position_ids, int pos_rows, int pos_cols,
+                               const uint8_t* encoder_attention_mask, float* out,
+                               void* workspace, size_t workspace_bytes, void* stream);
+
 /* ------------------------------------------------------------------------------------------------
  * Sampler ([PIPELINE] Krea2Pipeline: FlowMatchEulerDiscreteScheduler with dynamic shifting and
  * Krea 2's shift parameters, is_distilled; __call__: sigmas, guidance_scale, num_inference_steps).
@@ -254,6 +274,15 @@ size_t k2_denoise_workspace_bytes(const k2_model_cfg* cfg, int T, int N, int gui
 int k2_denoise_step(const k2_model_cfg* cfg, const k2_model_weights* w, int T, int N, float* latents, const void* enc,
                     const uint8_t* mask, const float* position_ids, int pos_rows, int pos_cols, float sigma,
                     float sigma_next, float guidance, void* workspace, size_t workspace_bytes, void* stream);
+/* The same step with the text rows from k2_text_embed: txt_h (G, T, hidden) float32 for the G
+   sequences above, computed once per prompt pair and reused at every step. Bit-identical to
+   k2_denoise_step on the encoder states txt_h was computed from.
+   Workspace: k2_denoise_cached_workspace_bytes(cfg, T, N, guidance > 0). */
+size_t k2_denoise_cached_workspace_bytes(const k2_model_cfg* cfg, int T, int N, int guided);
+int k2_denoise_step_cached(const k2_model_cfg* cfg, const k2_model_weights* w, int T, int N, float* latents,
+                           const float* txt_h, const uint8_t* mask, const float* position_ids, int pos_rows,
+                           int pos_cols, float sigma, float sigma_next, float guidance, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
  * Diagnostics

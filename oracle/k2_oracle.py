@@ -297,13 +297,19 @@ def final_layer(h_img, e, table, norm_w, w, b, eps, rnd=None):
     return x @ _f64(w).T + _f64(b)
 
 
+def text_embed(enc, mask, mw, tdims, rnd=None):
+    """The backbone's text rows before the first block ([ARTICLE] data flow of §四): txt_in applied to
+    the text-fusion output. Neither depends on the timestep or the latents. Returns (B, T, hidden)."""
+    r = rnd or _id
+    return r(text_fusion(enc, mask, mw["text"], tdims, rnd=rnd)) @ _f64(mw["txt_in_w"]).T + _f64(mw["txt_in_b"])
+
+
 def backbone_forward(x, enc, t, position_ids, mask, mw, dims, tdims, T, time_dim=256, rnd=None):
     """Krea2Transformer2DModel.forward ([API] forward; [ARTICLE] data flow of §四):
     time path, text fusion + txt_in, img_in, concat [text, image], blocks, image rows only,
     final layer. Returns the velocity (B, N, in_channels)."""
-    r = rnd or _id
     temb, e = time_path(t, mw["time"], time_dim, rnd=rnd)
-    txt = r(text_fusion(enc, mask, mw["text"], tdims, rnd=rnd)) @ _f64(mw["txt_in_w"]).T + _f64(mw["txt_in_b"])
+    txt = text_embed(enc, mask, mw, tdims, rnd=rnd)
     img = _f64(x) @ _f64(mw["img_in_w"]).T + _f64(mw["img_in_b"])
     h = np.concatenate([txt, img], axis=1)
     for bw in mw["blocks"]:

@@ -191,3 +191,35 @@ def test_time_and_text_and_backbone_validation():
     assert args(4607, 0) == ESHAPE
     m.block.axes_dims[2] = 46
     assert args(4608, 0) == ECONFIG
+    m.block.axes_dims[2] = 48
+
+    # text-path cache: the cached backbone needs txt_h, not the text weights, and a smaller workspace
+    cached = lambda txt_h, ws_bytes: lib.k2_backbone_forward_cached(
+        ctypes.byref(m), ctypes.byref(mw), 2, 512, 4096, FAKE, txt_h, FAKE, FAKE, 4608, 3, None, FAKE, FAKE, ws_bytes,
+        None)
+    assert cached(FAKE, 0) == EWS
+    assert cached(None, 0) == ENULL
+    mw.text = _abi.TextWeights(None, None, None)
+    mw.txt_in_w = None
+    assert cached(FAKE, 0) == EWS  # text weights are not needed
+    assert args(4608, 0) == ENULL  # ... but the uncached backbone needs them
+    full = lib.k2_backbone_workspace_bytes(ctypes.byref(m), 2, 512, 4096)
+    small = lib.k2_backbone_cached_workspace_bytes(ctypes.byref(m), 2, 512, 4096)
+    assert 0 < small < full
+    assert lib.k2_backbone_cached_workspace_bytes(ctypes.byref(m), 2, 0, 4096) == \
+        lib.k2_backbone_workspace_bytes(ctypes.byref(m), 2, 0, 4096)
+    mw.text = tw
+    mw.txt_in_w = FAKE
+    embed = lambda enc, out, ws_bytes: lib.k2_text_embed(ctypes.byref(m), ctypes.byref(mw), 2, 512, enc, None, out,
+                                                         FAKE, ws_bytes, None)
+    assert embed(FAKE, FAKE, 0) == EWS
+    assert embed(None, FAKE, 1 << 40) == ENULL
+    assert embed(FAKE, None, 1 << 40) == ENULL
+    assert lib.k2_text_embed_workspace_bytes(ctypes.byref(m), 2, 512) > 0
+    step = lambda txt_h, ws_bytes: lib.k2_denoise_step_cached(ctypes.byref(m), ctypes.byref(mw), 512, 4096, FAKE,
+                                                              txt_h, None, FAKE, 4608, 3, 1.0, 0.9, 4.5, FAKE,
+                                                              ws_bytes, None)
+    assert step(FAKE, 0) == EWS
+    assert step(None, 1 << 40) == ENULL
+    assert lib.k2_denoise_cached_workspace_bytes(ctypes.byref(m), 512, 4096, 1) < \
+        lib.k2_denoise_workspace_bytes(ctypes.byref(m), 512, 4096, 1)

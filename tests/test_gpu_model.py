@@ -87,3 +87,37 @@ def test_backbone_full_width_two_layers():
     # full-size block and text dims, two blocks, short sequences: every kernel at its real width
     got, fn, _ = _backbone_case(S.BlockDims(), S.TextDims(), "bf16", 2, 24, (8, 8), (20, 4), 2, 303)
     parity("backbone full width, 2 layers", "bf16", got, fn)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_text_embed_and_cached_backbone(dt):
+    """k2_text_embed against the oracle's text rows, and k2_backbone_forward_cached on its output
+    bit-identical to k2_backbone_forward (same kernels on the same values), also on a second call
+    with other latents and timesteps (the cache does not depend on them)."""
+    import torch
+    dims = S.BlockDims(hidden=256, num_heads=4, num_kv_heads=1, head_dim=64, intermediate=384, axes_dims=(16, 24, 24))
+    seed = 304
+    wl = S.Workload("bbc", seed, dt, 2, 12, (6, 5), (9, 3), dims=dims, text=TEXT_SMALL, num_layers=2, in_channels=64,
+                    timestep_embed_dim=256)
+    dev = device()
+    mw = S.model_weights(seed, wl)
+    inp = S.backbone_inputs(wl)
+    td = torch.bfloat16 if dt == "bf16" else torch.float32
+    cfg = k2.model_cfg(dims, TEXT_SMALL, 2, 64, 256, dt)
+    wdev = k2.upload(mw, dt, dev)
+    enc = torch.from_numpy(inp["enc"]).to(dev).to(td)
+    mask = torch.from_numpy(inp["mask"]).to(dev)
+    pos = torch.from_numpy(inp["position_ids"]).to(dev)
+    txt_h = k2.text_embed(cfg, wdev, enc, mask)
+    torch.cuda.synchronize()
+    assert txt_h.shape == (2, 12, 256)
+    parity(f"text embed {dt}", dt, txt_h.cpu().numpy(),
+           lambda rnd: O.text_embed(inp["enc"], inp["mask"], mw, S.text_block_dims(TEXT_SMALL), rnd=rnd))
+    for i, t in enumerate(([0.7, 0.7], [0.25, 0.9])):
+        x = torch.from_numpy(S.as_dtype(S.normal(seed + i, "x", (2, 30, 64)), dt)).to(dev).to(td)
+        tt = torch.tensor(t, dtype=torch.float32, device=dev)
+        v_full = k2.backbone_forward(cfg, wdev, x, enc, tt, pos, mask)
+        v_cached = k2.backbone_forward_cached(cfg, wdev, x, txt_h, tt, pos, mask)
+        torch.cuda.synchronize()
+        assert torch.equal(v_full, v_cached), f"call {i}: max diff {(v_full - v_cached).abs().max().item()}"
+    assert k2.backbone_cached_workspace_bytes(cfg, 2, 12, 30) < k2.backbone_workspace_bytes(cfg, 2, 12, 30)

@@ -90,3 +90,25 @@ def test_three_step_loop_f32():
     err, _ = rel_err(lat.cpu().numpy() - x0, x - x0)
     print(f"3-step loop f32: {err:.2e}")
     assert err <= 1e-4
+
+
+@pytest.mark.parametrize("dt,g", [("bf16", 4.5), ("f32", 0.0)])
+def test_cached_denoise_steps_bit_identical(dt, g):
+    """Three sampler steps through k2_denoise_step_cached with the text rows computed once equal three
+    steps of k2_denoise_step bit for bit."""
+    import torch
+    wl, mw, inp, cfg, wdev, td, dev = _case(dt, seed=403)
+    G = 2 if g > 0 else 1
+    enc = torch.from_numpy(S.as_dtype(inp["enc"][:G], dt)).to(dev).to(td)
+    mask = torch.from_numpy(inp["mask"][:G]).to(dev)
+    pos = torch.from_numpy(inp["position_ids"]).to(dev)
+    x0 = torch.from_numpy(inp["x"][:1].astype(np.float32)).to(dev)
+    sig = O.flow_sigmas(3, wl.N)
+    a, b = x0.clone(), x0.clone()
+    txt_h = k2.text_embed(cfg, wdev, enc, mask)
+    for i in range(3):
+        k2.denoise_step(cfg, wdev, a, enc, pos, mask, float(sig[i]), float(sig[i + 1]), g)
+        k2.denoise_step_cached(cfg, wdev, b, txt_h, pos, mask, float(sig[i]), float(sig[i + 1]), g)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b), f"max diff {(a - b).abs().max().item()}"
+    assert bool(torch.isfinite(a).all())
