@@ -16,6 +16,8 @@ Sources (cited by page title and section; the pages hold no code listing we foll
              6 FinalLayer) and the unnumbered "data flow" list that opens §四.
   [PIPELINE] diffusers v0.43.0 pipeline page "Krea 2" (Krea2Pipeline, prepare_position_ids,
              get_text_hidden_states, the guidance convention).
+  [QWEN21]   diffusers model page "QwenImage21Transformer2DModel" (block-causal attention item;
+             build_token_metadata and its image_ids).
 
 Readings where the pages are silent or garbled (each restated where it is used):
   R1  modulation = temb split in 6 chunks + per-block table; x -> (1 + scale) * norm(x) + shift;
@@ -57,6 +59,11 @@ Readings where the pages are silent or garbled (each restated where it is used):
   R16 update ([PIPELINE] __call__, guidance_scale parameter): v = cond + g (cond - uncond), with the
       uncond pass skipped when g <= 0; the Euler step is x <- x + (sigma_{i+1} - sigma_i) v. The
       latent state is kept in float32 between steps.
+  R17 block-causal attention ([QWEN21], block-causal attention item and build_token_metadata):
+      query i may attend key j iff j <= i or i and j lie in the same image block, where image_ids
+      gives -1 for tokens outside every image block and one id >= 0 per block; it combines with
+      the key-padding mask of R5 (both must allow the key). A query left with no key gets a zero
+      attention output (its softmax has no terms).
 """
 from __future__ import annotations
 
@@ -140,21 +147,39 @@ def apply_rope(x, angles):
 # ----------------------------------------------------------------------------------------------
 # Attention
 # ----------------------------------------------------------------------------------------------
-def attention(q, k, v, key_valid):
+def attention(q, k, v, key_valid, visible=None):
     """Softmax attention with GQA and a key mask, [ARTICLE] §四.3.
-    q: (B, nh, Lq, hd); k, v: (B, nkv, Lk, hd); key_valid: (B, Lk) bool or None.
-    K/V heads are repeated with repeat_interleave semantics (R4); scale 1/sqrt(hd) (R3)."""
+    q: (B, nh, Lq, hd); k, v: (B, nkv, Lk, hd); key_valid: (B, Lk) bool or None; visible: (Lq, Lk)
+    bool or None, which keys each query may attend (the same for every batch row and head; R17).
+    K/V heads are repeated with repeat_interleave semantics (R4); scale 1/sqrt(hd) (R3).
+    A query row with no allowed key returns zeros (R17)."""
     nh, nkv, hd = q.shape[1], k.shape[1], q.shape[-1]
     g = nh // nkv
     k = np.repeat(k, g, axis=1)
     v = np.repeat(v, g, axis=1)
     s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(hd)
+    allowed = np.ones(s.shape, dtype=bool)
     if key_valid is not None:
-        s = np.where(key_valid[:, None, None, :], s, -np.inf)
-    s = s - np.max(s, axis=-1, keepdims=True)
+        allowed &= key_valid[:, None, None, :]
+    if visible is not None:
+        allowed &= visible[None, None]
+    s = np.where(allowed, s, -np.inf)
+    some = allowed.any(axis=-1, keepdims=True)
+    s = s - np.where(some, np.max(s, axis=-1, keepdims=True), 0.0)
     p = np.exp(s)
-    p = p / np.sum(p, axis=-1, keepdims=True)
+    p = p / np.where(some, np.sum(p, axis=-1, keepdims=True), 1.0)
     return p @ v
+
+
+def block_causal_visible(image_ids, rows=None):
+    """(Lq, L) bool: query i may attend key j iff j <= i or both carry the same image id >= 0 (R17).
+    image_ids: (L,) ints; rows: the query indices (None = all)."""
+    ids = np.asarray(image_ids)
+    L = ids.size
+    qi = np.arange(L) if rows is None else np.asarray(rows)
+    j = np.arange(L)
+    same = (ids[qi][:, None] >= 0) & (ids[qi][:, None] == ids[None, :])
+    return (j[None, :] <= qi[:, None]) | same
 
 
 def key_valid_mask(B, L, T, mask):
@@ -177,7 +202,8 @@ def modulation(temb, table):
     return _f64(temb).reshape(B, 6, H) + _f64(table)[None]
 
 
-def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermediates=False, rnd=None):
+def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermediates=False, rnd=None,
+                  image_ids=None):
     """One Krea2TransformerBlock forward ([ARTICLE] §四.2 block, §四.3 attention, §四.4 norm).
 
     h: (B, L, H) residual stream; temb: (B, 6H) or None (no modulation: text-fusion blocks);
@@ -185,6 +211,7 @@ def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermedia
     (out, in) layout); dims: BlockDims-like; T: text tokens at the start of the sequence.
     rows: optional sorted sequence indices; only those output rows are computed (keys and
     values still come from every row). rnd: operand rounding of R13 (None = exact).
+    image_ids: (L,) block ids for the block-causal attention of R17 (None = every key visible).
     Returns (B, len(rows) or L, H) float64.
     """
     rnd = rnd or _id
@@ -227,7 +254,8 @@ def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermedia
     q, k = rnd(q), rnd(k)
     out["q"], out["k"], out["v"], out["g"] = q, k, v, graw
 
-    o = attention(q, k, v, key_valid_mask(B, L, T, mask))
+    vis = None if image_ids is None else block_causal_visible(image_ids, rows)
+    o = attention(q, k, v, key_valid_mask(B, L, T, mask), vis)
     o = o.transpose(0, 2, 1, 3).reshape(B, R, nh * hd)
     og = rnd(o * sigmoid(graw))                              # R6
     out["og"] = og

@@ -116,6 +116,93 @@ def test_attention_softmax_rows_and_single_key():
 
 
 # ----------------------------------------------------------------------------------------------
+# Block-causal attention (QwenImage 2.1 page: block-causal attention item; build_token_metadata)
+# ----------------------------------------------------------------------------------------------
+def test_block_causal_visibility_by_hand():
+    # text(3) | image block 0 (3) | image block 1 right after it (2) | text(1) | image block 2 (3):
+    # the rule "j <= i, or same image block" written out row by row
+    ids = np.array([-1, -1, -1, 0, 0, 0, 1, 1, -1, 2, 2, 2])
+    L = ids.size
+    want = np.zeros((L, L), bool)
+    for i in range(L):
+        want[i, :i + 1] = True
+    want[3:6, 3:6] = True      # block 0 sees itself in full, not block 1 although it follows
+    want[6:8, 6:8] = True
+    want[9:12, 9:12] = True
+    np.testing.assert_array_equal(O.block_causal_visible(ids), want)
+    np.testing.assert_array_equal(O.block_causal_visible(ids, rows=[1, 4, 11]), want[[1, 4, 11]])
+
+
+def test_block_causal_special_cases_reduce_to_library():
+    g = np.random.default_rng(21)
+    B, nh, nkv, L, hd = 2, 4, 2, 7, 8
+    q = g.standard_normal((B, nh, L, hd))
+    k = g.standard_normal((B, nkv, L, hd))
+    v = g.standard_normal((B, nkv, L, hd))
+    tq, tk, tv = (torch.from_numpy(a) for a in (q, k, v))
+    # no image block at all: plain causal attention
+    causal = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True, enable_gqa=True).numpy()
+    got = O.attention(q, k, v, None, O.block_causal_visible(np.full(L, -1)))
+    np.testing.assert_allclose(got, causal, rtol=1e-12, atol=1e-13)
+    # one block over the whole sequence: every key visible, the same numbers as no restriction
+    full = O.attention(q, k, v, None)
+    np.testing.assert_array_equal(O.attention(q, k, v, None, O.block_causal_visible(np.zeros(L, int))), full)
+    # text prefix + one target block (the usual layout): the block's rows see every key
+    ids = np.array([-1, -1, -1, 5, 5, 5, 5])
+    got = O.attention(q, k, v, None, O.block_causal_visible(ids))
+    np.testing.assert_array_equal(got[:, :, 3:], full[:, :, 3:])
+    np.testing.assert_allclose(got[:, :, :3], causal[:, :, :3], rtol=1e-12, atol=1e-13)
+
+
+def test_block_causal_bruteforce_with_padding():
+    # explicit loops over allowed keys (padding and block-causal together) against the vectorised form
+    g = np.random.default_rng(22)
+    B, nh, nkv, L, hd = 2, 2, 1, 9, 4
+    q = g.standard_normal((B, nh, L, hd))
+    k = g.standard_normal((B, nkv, L, hd))
+    v = g.standard_normal((B, nkv, L, hd))
+    ids = np.array([-1, -1, -1, -1, 3, 3, 3, -1, -1])
+    valid = np.ones((B, L), bool)
+    valid[0, 2] = False
+    valid[1, 0:4] = False          # row 1: the first text queries have no key left
+    got = O.attention(q, k, v, valid, O.block_causal_visible(ids))
+    for b in range(B):
+        for h in range(nh):
+            for i in range(L):
+                keys = [j for j in range(L) if valid[b, j] and (j <= i or (ids[i] >= 0 and ids[i] == ids[j]))]
+                if not keys:
+                    np.testing.assert_array_equal(got[b, h, i], 0.0)
+                    continue
+                sc = [float(np.dot(q[b, h, i], k[b, h // (nh // nkv), j])) / math.sqrt(hd) for j in keys]
+                mx = max(sc)
+                wts = [math.exp(x - mx) for x in sc]
+                ref = sum(w * v[b, h // (nh // nkv), j] for w, j in zip(wts, keys)) / sum(wts)
+                np.testing.assert_allclose(got[b, h, i], ref, rtol=1e-12, atol=1e-13)
+
+
+def test_block_causal_block_ignores_invisible_tokens():
+    # block level: a row's output cannot depend on tokens it may not attend (their h rows are
+    # randomised); rows that may attend them change
+    wl, inp = micro_inputs(seed=38, B=2, T=4, grid=(2, 3), valid=(3, 4))
+    ids = np.array([-1, -1, -1, -1, 0, 0, 0, 1, 1, 1])   # text, condition block, target block
+    args = (inp["temb"], inp["position_ids"], inp["mask"], inp["weights"], MICRO, wl.T)
+    a = O.block_forward(inp["h"], *args, image_ids=ids)
+    h2 = inp["h"].copy()
+    h2[:, 7:] = 5 * np.random.default_rng(8).standard_normal(h2[:, 7:].shape)   # the target block
+    c = O.block_forward(h2, *args, image_ids=ids)
+    np.testing.assert_array_equal(a[:, :7], c[:, :7])
+    assert np.abs(a[:, 7:] - c[:, 7:]).max() > 1e-3
+    h3 = inp["h"].copy()
+    h3[:, 2] += 3.0                                          # a text token: later rows see it
+    d = O.block_forward(h3, *args, image_ids=ids)
+    np.testing.assert_array_equal(a[:, :2], d[:, :2])
+    assert np.abs(a[:, 3:] - d[:, 3:]).max() > 1e-6
+    # one block over everything equals the unrestricted block
+    np.testing.assert_array_equal(O.block_forward(inp["h"], *args, image_ids=np.zeros(wl.L, int)),
+                                  O.block_forward(inp["h"], *args))
+
+
+# ----------------------------------------------------------------------------------------------
 # RoPE
 # ----------------------------------------------------------------------------------------------
 def test_rope_matches_complex_rotation():
