@@ -163,6 +163,7 @@ class BlockLayout:
     a: int
     rope: int
     mod: int
+    reach: int
     total: int
     ldvt: int
 
@@ -170,13 +171,15 @@ class BlockLayout:
 def block_workspace_layout(cfg, B: int, T: int, N: int) -> BlockLayout:
     lay = _abi.BlockLayout()
     check(load().k2_block_workspace_layout_query(ctypes.byref(cfg), B, T, N, ctypes.byref(lay)))
-    return BlockLayout(lay.x1, lay.q, lay.k, lay.vt, lay.g, lay.og, lay.x2, lay.a, lay.rope, lay.mod, lay.total,
-                       lay.ldvt)
+    return BlockLayout(lay.x1, lay.q, lay.k, lay.vt, lay.g, lay.og, lay.x2, lay.a, lay.rope, lay.mod, lay.reach,
+                       lay.total, lay.ldvt)
 
 
-def block_forward(cfg, weights: dict, h, temb, position_ids, mask, T: int, out=None, workspace=None, stream=None):
-    """k2_block_forward. h: (B, T+N, hidden) float32; temb (B, 6 hidden) float32 or None; position_ids
-    (T+N, 3) float32 or None; mask (B, T) bool/uint8 or None. Returns the output residual stream."""
+def block_forward(cfg, weights: dict, h, temb, position_ids, mask, T: int, out=None, workspace=None, stream=None,
+                  image_ids=None):
+    """k2_block_forward, or k2_block_forward_block_causal when image_ids ((T+N,) int32 device tensor) is
+    given. h: (B, T+N, hidden) float32; temb (B, 6 hidden) float32 or None; position_ids (T+N, 3)
+    float32 or None; mask (B, T) bool/uint8 or None. Returns the output residual stream."""
     torch = _torch()
     lib = load()
     _dev_tensor(h, "h", torch.float32)
@@ -188,9 +191,15 @@ def block_forward(cfg, weights: dict, h, temb, position_ids, mask, T: int, out=N
     ws_bytes = lib.k2_block_workspace_bytes(ctypes.byref(cfg), B, T, N)
     ws = _workspace(ws_bytes, h.device, workspace)
     bw = _block_weights(weights)
-    check(lib.k2_block_forward(ctypes.byref(cfg), ctypes.byref(bw), B, T, N, _ptr(h), _ptr(out), _ptr(temb),
-                               _ptr(position_ids), pos_rows, pos_cols, _ptr(mask), _ptr(ws), ws.numel(),
-                               _stream(stream)))
+    if image_ids is None:
+        check(lib.k2_block_forward(ctypes.byref(cfg), ctypes.byref(bw), B, T, N, _ptr(h), _ptr(out), _ptr(temb),
+                                   _ptr(position_ids), pos_rows, pos_cols, _ptr(mask), _ptr(ws), ws.numel(),
+                                   _stream(stream)))
+    else:
+        _dev_tensor(image_ids, "image_ids", torch.int32, (L,))
+        check(lib.k2_block_forward_block_causal(ctypes.byref(cfg), ctypes.byref(bw), B, T, N, _ptr(h), _ptr(out),
+                                                _ptr(temb), _ptr(position_ids), pos_rows, pos_cols, _ptr(mask),
+                                                _ptr(image_ids), _ptr(ws), ws.numel(), _stream(stream)))
     return out
 
 

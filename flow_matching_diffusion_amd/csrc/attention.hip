@@ -87,6 +87,20 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
   const int ldq = p.nh * HD, ldk = p.nkv * HD;
   const uint4 zero = {0u, 0u, 0u, 0u};
 
+  // Block-causal restriction: query i sees keys j <= reach[i], non-decreasing in i, so the
+  // workgroup's first and last queries bound which tiles need it and where the keys end.
+  const int qlo = blockIdx.x * BQ;
+  int kmin = L - 1, kmax = L - 1;
+  int rq[4];
+#pragma unroll
+  for (int qb = 0; qb < 4; ++qb) rq[qb] = L - 1;
+  if (p.reach) {
+    kmin = p.reach[qlo];
+    kmax = p.reach[min(qlo + BQ, L) - 1];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) rq[qb] = p.reach[min(q0 + qb * 16 + col, L - 1)];
+  }
+
   // Validity bits of the 32-key tiles that hold text keys (bit j: key t*32 + j is a valid key);
   // one wave ballot covers two tiles.
   const int ntt = (T_ + KT - 1) / KT;
@@ -163,7 +177,7 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
   }
 
   __syncthreads();  // sBits ready
-  const int nt = (L + KT - 1) / KT;
+  const int nt = (kmax + KT) / KT;  // tiles holding keys 0 .. kmax
   int t = 0;
   while (t < nt && t < ntt && sBits[t] == 0) ++t;
   if (t < nt) {
@@ -217,6 +231,17 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
           const bool ok = (vbits >> (8 * grp + 4 * kb + r)) & 1u;
 #pragma unroll
           for (int qb = 0; qb < 4; ++qb) s[kb][qb][r] = ok ? s[kb][qb][r] * scale_log2 : -INFINITY;
+        }
+    }
+    if (p.reach && t0 + KT - 1 > kmin) {  // keys past some query's reach
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int key = t0 + 8 * grp + 4 * kb + r;
+#pragma unroll
+          for (int qb = 0; qb < 4; ++qb)
+            if (key > rq[qb]) s[kb][qb][r] = -INFINITY;
         }
     }
 
@@ -371,6 +396,17 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
   const int ldq = p.nh * HD, ldk = p.nkv * HD;
   const int h32 = lane >> 5, c32 = lane & 31;
 
+  // Block-causal restriction: query i sees keys j <= reach[i], non-decreasing in i, so the
+  // workgroup's first and last queries bound which tiles need it and where the keys end; rq is
+  // this lane's query's reach.
+  const int qlo = blockIdx.x * BQ;
+  int kmin = L - 1, kmax = L - 1, rq = L - 1;
+  if (p.reach) {
+    kmin = p.reach[qlo];
+    kmax = p.reach[min(qlo + BQ, L) - 1];
+    rq = p.reach[min(q0 + c32, L - 1)];
+  }
+
   // validity bits of the text tiles (bit j: key 64t + j is a valid key)
   const int ntt = (T_ + KT - 1) / KT;
   for (int u = wave; u < ntt; u += 4) {
@@ -447,7 +483,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
 #define K2_FENCE() __builtin_amdgcn_sched_barrier(0)
 
   __syncthreads();  // sBits
-  const int nt = (L + KT - 1) / KT;
+  const int nt = (kmax + KT) / KT;  // tiles holding keys 0 .. kmax
   auto next_tile = [&](int t) {
     while (t < nt && t < ntt && sBits[t] == 0) ++t;
     return t;
@@ -510,6 +546,11 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
                               ((uint32_t)((vb >> (8 * (4 * kb + 2 + h32))) & 0xFFu) << 8);         \
           _Pragma("unroll") for (int r = 0; r < 16; ++r) if (!((lb >> r) & 1u)) SC[kb][r] = -INFINITY; \
         }                                                                                          \
+      }                                                                                            \
+      if (p.reach && t0 + KT - 1 > kmin) { /* keys past some query's reach */                     \
+        _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                           \
+          _Pragma("unroll") for (int r = 0; r < 16; ++r)                                           \
+            if (t0 + 32 * kb + 16 * (r >> 3) + 8 * h32 + (r & 7) > rq) SC[kb][r] = -INFINITY;       \
       }                                                                                            \
       /* phase A: S of tile tn, interleaved with tile t's max, rescale and exponentials */         \
       _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                             \
@@ -669,13 +710,15 @@ __global__ void __launch_bounds__(256) attn_short_kernel(AttnArgs p, float scale
 #pragma unroll
   for (int st = 0; st < NS; ++st) sacc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[st], qf[st], sacc, 0, 0, 0);
 
-  // softmax over keys (base 2): register r holds key kperm(8(r/4) + 4(l/32) + r%4)
+  // softmax over keys (base 2): register r holds key kperm(8(r/4) + 4(l/32) + r%4); with the
+  // block-causal restriction the lane's query sees keys up to rq only
+  const int rq = p.reach ? p.reach[c32 < L ? c32 : L - 1] : L - 1;
   float sc[16];
   float mx = -INFINITY;
 #pragma unroll
   for (int r = 0; r < 16; ++r) {
     const int key = kperm(8 * (r >> 2) + 4 * h32 + (r & 3));
-    const bool ok = key < L && (key >= T_ || !p.mask || p.mask[(size_t)b * T_ + key] != 0);
+    const bool ok = key <= rq && key < L && (key >= T_ || !p.mask || p.mask[(size_t)b * T_ + key] != 0);
     sc[r] = ok ? sacc[r] * scale_log2 : -INFINITY;
     mx = fmaxf(mx, sc[r]);
   }

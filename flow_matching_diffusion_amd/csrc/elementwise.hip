@@ -10,8 +10,12 @@
 //   time_embed     — cos-first sinusoid of 1000 t ([ARTICLE] §四.5).
 //   layer_compress — Linear(num_layers, 1, bias=False) over the text layer axis ([ARTICLE] §四.1).
 //   to_f32/from_f32 — operand dtype conversions.
+//   block_reach    — per-token reach of the block-causal attention (QwenImage 2.1 model page,
+//                    block-causal attention item): the last position a query may attend.
 #include "k2_device.h"
 #include "k2_kernels.h"
+
+#include <climits>
 
 namespace k2 {
 
@@ -236,6 +240,41 @@ __global__ void fill_f32_kernel(float* out, int n, float v) {
 hipError_t fill_f32(float* out, int n, float v, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(fill_f32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, out, n, v);
+  return hipGetLastError();
+}
+
+// Block-causal reach: the end of each token's image-block run, by a suffix minimum over the run
+// ends taken in chunks of 1024 positions from the back of the sequence (carry: the end of the run
+// holding the first position of the chunk after the current one).
+__global__ void __launch_bounds__(1024) block_reach_kernel(const int* __restrict__ ids, int L, int* __restrict__ reach) {
+  __shared__ int sm[1024];
+  const int tid = threadIdx.x;
+  int carry = INT_MAX;
+  for (int c0 = ((L - 1) / 1024) * 1024; c0 >= 0; c0 -= 1024) {
+    const int i = c0 + tid;
+    int id = -1, v = INT_MAX;
+    if (i < L) {
+      id = ids[i];
+      v = (i == L - 1 || ids[i + 1] != id) ? i : INT_MAX;  // i ends its run
+    }
+    sm[tid] = v;
+    __syncthreads();
+    for (int off = 1; off < 1024; off <<= 1) {  // sm[t] = min(sm[t .. 1023])
+      const int o = tid + off < 1024 ? sm[tid + off] : INT_MAX;
+      __syncthreads();
+      sm[tid] = min(sm[tid], o);
+      __syncthreads();
+    }
+    if (i < L) reach[i] = id >= 0 ? min(sm[tid], carry) : i;
+    const int first = min(sm[0], carry);
+    __syncthreads();
+    carry = first;
+  }
+}
+
+hipError_t block_reach(const int* ids, int L, int* reach, hipStream_t s) {
+  if (L <= 0) return hipSuccess;
+  hipLaunchKernelGGL(block_reach_kernel, dim3(1), dim3(1024), 0, s, ids, L, reach);
   return hipGetLastError();
 }
 

@@ -170,7 +170,7 @@ k2_block_workspace_layout block_layout(const k2_block_cfg* c, int B, int T, int 
   l.a = take(M * (size_t)c->intermediate * es);
   l.rope = take(2 * L * (size_t)(c->head_dim / 2) * sizeof(float));
   l.mod = take((size_t)B * 6 * H * sizeof(float));
-  l.kvalid = take(0);
+  l.reach = take(L * sizeof(int32_t));
   l.total = off;
   return l;
 }
@@ -178,9 +178,10 @@ k2_block_workspace_layout block_layout(const k2_block_cfg* c, int B, int T, int 
 char* at(void* base, size_t off) { return (char*)base + off; }
 
 // One block forward; rope_cos/rope_sin precomputed by the caller when non-NULL.
+// image_ids: (T + N) block ids of the block-causal attention, or NULL for attention over every key.
 int block_run(const k2_block_cfg* c, const k2_block_weights* w, int B, int T, int N, const float* hin, float* hout,
               const float* temb, const float* pos, const uint8_t* mask, void* ws, const float* rope_cos,
-              const float* rope_sin, hipStream_t s) {
+              const float* rope_sin, hipStream_t s, const int32_t* image_ids = nullptr) {
   const int dt = c->dtype;
   const int H = c->hidden, hd = c->head_dim, nq = c->num_heads * hd, nk = c->num_kv_heads * hd, I = c->intermediate;
   const int L = T + N, M = B * L;
@@ -226,6 +227,11 @@ int block_run(const k2_block_cfg* c, const k2_block_weights* w, int B, int T, in
   K2_RUN("gemm_qkvg", s, gemm_qkvg(dt, GemmA{x1, H, M, H}, qa, s));
 
   AttnArgs at_ = {};
+  if (image_ids) {
+    int* reach = (int*)at(ws, lay.reach);
+    K2_RUN("block_reach", s, block_reach(image_ids, L, reach, s));
+    at_.reach = reach;
+  }
   at_.q = q; at_.k = k; at_.vt = vt; at_.g = g; at_.og = og; at_.mask = mask;
   at_.B = B; at_.L = L; at_.T = T; at_.nh = c->num_heads; at_.nkv = c->num_kv_heads; at_.hd = hd; at_.ldvt = lay.ldvt;
   K2_RUN("attention", s, attention(dt, at_, s));
@@ -557,6 +563,20 @@ int k2_block_forward(const k2_block_cfg* cfg, const k2_block_weights* w, int B, 
   g_err.clear();
   return block_run(cfg, w, B, T, N, hidden_in, hidden_out, temb, position_ids, mask, workspace, nullptr, nullptr,
                    (hipStream_t)stream);
+}
+
+int k2_block_forward_block_causal(const k2_block_cfg* cfg, const k2_block_weights* w, int B, int T, int N,
+                                  const float* hidden_in, float* hidden_out, const float* temb,
+                                  const float* position_ids, int pos_rows, int pos_cols, const uint8_t* mask,
+                                  const int32_t* image_ids, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_block_call(cfg, w, B, T, N, hidden_in, hidden_out, temb, position_ids, pos_rows, pos_cols);
+  if (rc != K2_OK) return rc;
+  if (!image_ids) return fail(K2_ERR_NULL, "image_ids is NULL");
+  if ((uintptr_t)image_ids % sizeof(int32_t)) return fail(K2_ERR_ALIGN, "image_ids must be 4-byte aligned");
+  if ((rc = check_ws(workspace, workspace_bytes, k2_block_workspace_bytes(cfg, B, T, N))) != K2_OK) return rc;
+  g_err.clear();
+  return block_run(cfg, w, B, T, N, hidden_in, hidden_out, temb, position_ids, mask, workspace, nullptr, nullptr,
+                   (hipStream_t)stream, image_ids);
 }
 
 size_t k2_timestep_modulation_workspace_bytes(const k2_time_cfg* cfg, int B) {

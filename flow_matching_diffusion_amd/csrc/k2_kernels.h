@@ -79,8 +79,15 @@ struct AttnArgs {
   int B, L, T;
   int nh, nkv, hd;
   int ldvt;
+  // Block-causal restriction (NULL = none): query i attends key j only if j <= reach[i]; reach is
+  // (L,) and non-decreasing with reach[i] >= i (block_reach builds it from image block ids).
+  const int* reach;
 };
 hipError_t attention(int dt, const AttnArgs& p, hipStream_t s);
+
+// reach[i] = i for tokens outside every image block (ids[i] < 0), else the last position of the
+// contiguous run of equal ids that holds i. One workgroup; ids and reach are (L,) device arrays.
+hipError_t block_reach(const int* ids, int L, int* reach, hipStream_t s);
 
 // ---------------------------------------------------------------------------------------------
 // Row kernels

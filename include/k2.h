@@ -11,6 +11,8 @@
  *              §四.5 TimestepEmbedding, §四.6 FinalLayer.
  *   [PIPELINE] diffusers v0.43.0 pipeline page "Krea 2": Krea2Pipeline parameters (scheduler,
  *              is_distilled) and __call__ parameters (num_inference_steps, sigmas, guidance_scale).
+ *   [QWEN21]   diffusers model page "QwenImage21Transformer2DModel": the block-causal attention
+ *              item and build_token_metadata (image_ids), for k2_block_forward_block_causal.
  *
  * Conventions shared by every entry point
  *   - Pointers named *_w, *_b, tables, activations, outputs and workspace are DEVICE pointers owned by
@@ -100,10 +102,11 @@ size_t k2_block_workspace_bytes(const k2_block_cfg* cfg, int B, int T, int N);
    same sizes): x1/x2 (B*L, hidden) modulated norms, q (B*L, nh*hd) and k (B*L, nkv*hd) after q/k norm
    and RoPE, vt (B, nkv, hd, ldvt) values transposed (ldvt = 32 when L <= 32, else L rounded up to
    64), g (B*L, nh*hd) raw gate, og (B*L, nh*hd) gated attention output, a (B*L, intermediate)
-   SwiGLU activation — all of element type dtype — and mod (B, 6, hidden) float32 modulation.
-   Intended for tests and debugging. */
+   SwiGLU activation — all of element type dtype — mod (B, 6, hidden) float32 modulation, and reach
+   (L) int32, the block-causal reach of k2_block_forward_block_causal. Intended for tests and
+   debugging. */
 typedef struct {
-  size_t x1, q, k, vt, g, og, x2, a, rope, mod, kvalid, total;
+  size_t x1, q, k, vt, g, og, x2, a, rope, mod, reach, total;
   int ldvt;
 } k2_block_workspace_layout;
 int k2_block_workspace_layout_query(const k2_block_cfg* cfg, int B, int T, int N,
@@ -129,6 +132,21 @@ int k2_block_forward(const k2_block_cfg* cfg, const k2_block_weights* w, int B, 
                      const float* position_ids, int pos_rows, int pos_cols,
                      const uint8_t* encoder_attention_mask,
                      void* workspace, size_t workspace_bytes, void* stream);
+
+/* The same block with block-causal attention ([QWEN21] model page "QwenImage21Transformer2DModel":
+   block-causal attention item; build_token_metadata): query i attends key j only if j <= i or both
+   tokens lie in the same image block, on top of the key-padding mask. The sequence is causal while
+   every image block stays bidirectional inside.
+   image_ids: (T + N) int32 device array, 4-byte aligned, shared by all batch rows: -1 for tokens
+   outside every image block, one id >= 0 per block. A block is a contiguous run of equal ids;
+   two adjacent blocks must carry different ids (runs are what the kernels see).
+   A query left with no key it may attend (text queries whose earlier text is all padding) gets a
+   zero attention output. Workspace: k2_block_workspace_bytes. */
+int k2_block_forward_block_causal(const k2_block_cfg* cfg, const k2_block_weights* w, int B, int T, int N,
+                                  const float* hidden_in, float* hidden_out, const float* temb,
+                                  const float* position_ids, int pos_rows, int pos_cols,
+                                  const uint8_t* encoder_attention_mask, const int32_t* image_ids,
+                                  void* workspace, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------------------------------
  * Time path ([ARTICLE] §四.5 and §四 data flow): emb = [cos(1000 t f_k)] ++ [sin(1000 t f_k)],

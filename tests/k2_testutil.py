@@ -66,8 +66,9 @@ def temb_for(wl, inp):
     return temb.astype(np.float32)
 
 
-def gpu_block(wl, inp, temb, h=None, mask="default", dev=None, keep_ws=False):
-    """Run k2_block_forward on the workload's inputs; returns the output (and workspace)."""
+def gpu_block(wl, inp, temb, h=None, mask="default", dev=None, keep_ws=False, image_ids=None):
+    """Run k2_block_forward (k2_block_forward_block_causal with image_ids) on the workload's inputs;
+    returns the output (and workspace)."""
     import torch
     import flow_matching_diffusion_amd as k2
     dev = dev or device()
@@ -82,7 +83,8 @@ def gpu_block(wl, inp, temb, h=None, mask="default", dev=None, keep_ws=False):
     B, L, _ = h.shape
     ws = torch.empty(k2.load().k2_block_workspace_bytes(ctypes.byref(cfg), B, wl.T, L - wl.T),
                      dtype=torch.uint8, device=dev)
-    out = k2.block_forward(cfg, w, ht, tt, pt, mt, wl.T, workspace=ws)
+    it = None if image_ids is None else torch.from_numpy(np.ascontiguousarray(image_ids, dtype=np.int32)).to(dev)
+    out = k2.block_forward(cfg, w, ht, tt, pt, mt, wl.T, workspace=ws, image_ids=it)
     torch.cuda.synchronize()
     res = out.cpu().numpy()
     if keep_ws:
