@@ -11,10 +11,12 @@ attention over valid keys only). Also reported: the 28-block backbone with text 
 same resolution as denoise steps/s (one call = one CFG step), the sampler on one image (with guidance
 as the base checkpoint's 28 steps and without as the distilled 8 steps) as time per image, both with
 the text rows computed once per prompt pair (k2_text_embed, then k2_denoise_step_cached) and with
-the text path run at every step (k2_denoise_step), per-kernel times, the roofline of the dominant kernel, and the CPU oracle on a bounded sample.
+the text path run at every step (k2_denoise_step), the block-causal block variant on the same pair
+(a condition block then the target block), per-kernel times, the roofline of the dominant kernel, and
+the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-backbone] [--no-cpu-baseline]
-                       [--cpu-rows R] [--copy-calibration]
+                       [--no-block-causal] [--cpu-rows R] [--copy-calibration]
 --copy-calibration first runs a plain elementwise copy (negation) of 1 GiB float32, a kernel of known
 HBM traffic against which the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled.
 """
@@ -117,6 +119,7 @@ def main():
     ap.add_argument("--sampler-steps", type=int, default=3)
     ap.add_argument("--no-backbone", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-block-causal", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4608)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -223,6 +226,50 @@ def main():
         "kernels": kernels,
         "roofline": roofline,
     }
+
+    # The block-causal variant (k2_block_forward_block_causal) on the same pair: the image tokens as
+    # a 1024-token condition block followed by the target block (condition images first, target
+    # last). Text queries attend causally, condition queries the text and their own block, target
+    # queries everything. Attention FLOPs count the keys each query may attend.
+    if not args.no_block_causal and N > 1024:
+        ids = np.concatenate([np.full(T, -1), np.zeros(1024), np.ones(N - 1024)]).astype(np.int32)
+        reach = np.arange(L)
+        for i in range(L - 2, -1, -1):
+            if ids[i] >= 0 and ids[i + 1] == ids[i]:
+                reach[i] = reach[i + 1]
+        allowed = 0
+        for b in range(B):
+            kv = np.ones(L, bool)
+            if m is not None:
+                kv[:T] = m[b].astype(bool)
+            allowed += int(np.cumsum(kv)[reach].sum())
+        idt = torch.from_numpy(ids).to(dev)
+
+        def bc_step():
+            k2.block_forward(cfg, w, h, temb, pos, mask, T, out=out, workspace=ws, image_ids=idt)
+
+        for _ in range(args.warmup):
+            bc_step()
+        torch.cuda.synchronize()
+        k2.profile_reset()
+        k2.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            bc_step()
+        torch.cuda.synchronize()
+        bc_ms = (time.perf_counter() - t0) * 1e3 / args.steps
+        k2.profile_enable(False)
+        a_tot, a_n = k2.profile_query("attention")
+        bc_attn = 4 * d.head_dim * d.num_heads * allowed
+        bc_flops = block_flops(d, B, L, [0] * B) + bc_attn
+        a_ms = a_tot / a_n
+        result["block_causal"] = {
+            "layout": f"text {T} (causal) + condition block 1024 + target block {N - 1024}",
+            "ms_per_step": round(bc_ms, 4), "tflops": round(bc_flops / (bc_ms * 1e-3) / 1e12, 1),
+            "attention": {"avg_ms": round(a_ms, 4), "tflops": round(bc_attn / (a_ms * 1e-3) / 1e12, 1),
+                          "algorithmic_tflop": round(bc_attn / 1e12, 4),
+                          "bidirectional_algorithmic_tflop": round(attn_flops / 1e12, 4)}}
+        del idt
     del w, h, out, ws
     torch.cuda.empty_cache()
 
