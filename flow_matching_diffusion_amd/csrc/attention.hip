@@ -629,25 +629,41 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
 #undef K2_VFRAG
 #undef K2_SK
 #undef K2_SV
-  // normalise, gate, store: lane holds query q0 + l%32 and head dims 32hb + 8j + 4(l/32) + 0..3
+  // normalise into this wave's LDS area (the K/V stages are free now): 32 query rows of HD floats,
+  // 16-byte chunk c of row r at chunk c ^ (r % 32); then gate and store row-major, HD/8 lanes per
+  // query row with 8 head dims each, so the gate reads and output stores cover whole rows
   const float lsum = l_i + __shfl_xor(l_i, 32);
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
-  const int row = q0 + c32;
-  if (row < L) {
-    const size_t base = (size_t)(b * L + row) * ldq + head * HD;
-    const bf16* gp = (const bf16*)p.g + base;
-    bf16* op = (bf16*)p.og + base;
+  __syncthreads();  // every wave is done with the K/V stages (all DMAs have landed)
+  float4* const st = reinterpret_cast<float4*>(wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1);
+  static_assert(32 * HD * sizeof(float) <= sizeof(sK0), "staging area");
+  constexpr int CPR = HD / 4;  // 16-byte chunks per staged row
 #pragma unroll
-    for (int hb = 0; hb < NHB; ++hb)
+  for (int hb = 0; hb < NHB; ++hb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int d0 = 32 * hb + 8 * j + 4 * h32;
-        const bf16x4 gv = *(const bf16x4*)(gp + d0);
-        bf16x4 out;
+    for (int j = 0; j < 4; ++j) {
+      const int c = 8 * hb + 2 * j + h32;
+      st[c32 * CPR + (c ^ (c32 & (CPR - 1)))] =
+          make_float4(o[hb][4 * j] * inv, o[hb][4 * j + 1] * inv, o[hb][4 * j + 2] * inv, o[hb][4 * j + 3] * inv);
+    }
+  // a wave's LDS accesses complete in order: the reads below see the writes above
+  constexpr int LPR = HD / 8, RPI = 64 / LPR;  // lanes per row, rows per instruction
+  const int rr = lane / LPR, cc = lane % LPR;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = (bf16)(o[hb][4 * j + e] * inv * sigmoidf_((float)gv[e]));
-        *(bf16x4*)(op + d0) = out;
-      }
+  for (int k = 0; k < 32 / RPI; ++k) {
+    const int r = RPI * k + rr;
+    const int row = q0 + r;
+    const float4 a = st[r * CPR + ((2 * cc) ^ (r & (CPR - 1)))];
+    const float4 bq = st[r * CPR + ((2 * cc + 1) ^ (r & (CPR - 1)))];
+    if (row < L) {
+      const size_t base = (size_t)(b * L + row) * ldq + head * HD + 8 * cc;
+      const bf16x8 gv = *(const bf16x8*)((const bf16*)p.g + base);
+      const float v[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+      bf16x8 out;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) out[e] = (bf16)(v[e] * sigmoidf_((float)gv[e]));
+      *(bf16x8*)((bf16*)p.og + base) = out;
+    }
   }
 }
 
