@@ -64,6 +64,13 @@ Readings where the pages are silent or garbled (each restated where it is used):
       gives -1 for tokens outside every image block and one id >= 0 per block; it combines with
       the key-padding mask of R5 (both must allow the key). A query left with no key gets a zero
       attention output (its softmax has no terms).
+  R20 backward pass ([ARTICLE] §四 data flow and §六: the model is trained, and its test matrix
+      includes training and gradient checkpointing): the gradient of the block's output with
+      respect to its input h, its modulation input temb and every weight, by the chain rule through
+      the forward's steps, the forward recomputed from h (checkpointing). In bf16 mode the
+      backward's matrix-product operands are bf16 as well: the gradients that enter a product
+      (dz, dgt, du, dy, the attention output gradient, P and dS inside attention, and the q/k/v/gate
+      projection gradients), with float32 accumulation and float32 weight gradients.
 """
 from __future__ import annotations
 
@@ -269,6 +276,156 @@ def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermedia
     h2 = h1 + qg * (a @ _f64(w["ff_down"]).T)
     out["out"] = h2
     return (h2, out) if intermediates else h2
+
+
+# ----------------------------------------------------------------------------------------------
+# Backward pass of the block (R20)
+# ----------------------------------------------------------------------------------------------
+def rms_norm_backward(x, weight, eps, dy):
+    """Gradients of y = x r (1 + w), r = 1/sqrt(mean(x^2) + eps), over the last axis, for the output
+    gradient dy: returns (dx, dw summed over all leading axes)."""
+    x, dy = _f64(x), _f64(dy)
+    H = x.shape[-1]
+    r = 1.0 / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps)
+    mult = 1.0 + (_f64(weight) if weight is not None else 0.0)
+    dw = (dy * x * r).reshape(-1, H).sum(axis=0)
+    g = dy * mult
+    dx = r * g - x * r ** 3 * np.sum(g * x, axis=-1, keepdims=True) / H
+    return dx, dw
+
+
+def attention_backward(q, k, v, key_valid, do, visible=None, rnd=None):
+    """Gradients of attention() (same arguments) for the output gradient do (B, nh, Lq, hd):
+    returns (dq, dk, dv) with dk, dv summed over the query heads that share each kv head (R4).
+    With P the softmax probabilities and O = P V: dV = P^T dO, dP = dO V^T,
+    dS = P (dP - rowsum(dO * O)), dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd). rnd (R20) rounds P
+    and dS where they become matrix-product operands."""
+    r = rnd or _id
+    nh, nkv, hd = q.shape[1], k.shape[1], q.shape[-1]
+    g = nh // nkv
+    kk = np.repeat(_f64(k), g, axis=1)
+    vv = np.repeat(_f64(v), g, axis=1)
+    s = (_f64(q) @ np.swapaxes(kk, -1, -2)) / math.sqrt(hd)
+    allowed = np.ones(s.shape, dtype=bool)
+    if key_valid is not None:
+        allowed &= key_valid[:, None, None, :]
+    if visible is not None:
+        allowed &= visible[None, None]
+    s = np.where(allowed, s, -np.inf)
+    some = allowed.any(axis=-1, keepdims=True)
+    s = s - np.where(some, np.max(s, axis=-1, keepdims=True), 0.0)
+    p = np.exp(s)
+    p = p / np.where(some, np.sum(p, axis=-1, keepdims=True), 1.0)
+    do = _f64(do)
+    o = p @ vv
+    dvv = np.swapaxes(r(p), -1, -2) @ do
+    dp = do @ np.swapaxes(vv, -1, -2)
+    delta = np.sum(do * o, axis=-1, keepdims=True)
+    ds = r(p * (dp - delta))
+    dq = ds @ kk / math.sqrt(hd)
+    dkk = np.swapaxes(ds, -1, -2) @ _f64(q) / math.sqrt(hd)
+    B, _, Lk, _ = k.shape
+    dk = dkk.reshape(B, nkv, g, Lk, hd).sum(axis=2)
+    dv = dvv.reshape(B, nkv, g, Lk, hd).sum(axis=2)
+    return dq, dk, dv
+
+
+def block_backward(h, temb, position_ids, mask, w, dims, T, dh_out, rnd=None, image_ids=None):
+    """Gradients of block_forward (same arguments) for the output gradient dh_out (B, L, H), by the
+    chain rule through every step of the forward (R20). The forward is recomputed from h.
+    Returns (dh, dtemb or None, grads) where grads holds the gradient of every weight in w (same
+    keys and shapes; None for an absent norm weight). rnd as in block_forward; it also rounds the
+    backward's matrix-product operands (R20)."""
+    r = rnd or _id
+    h = _f64(h)
+    dh2 = _f64(dh_out)
+    B, L, H = h.shape
+    nh, nkv, hd, eps = dims.num_heads, dims.num_kv_heads, dims.head_dim, dims.eps
+    M = B * L
+    # ---- forward, keeping what the backward needs
+    if temb is not None:
+        mod = modulation(temb, w["scale_shift_table"])
+        ps, pt, pg, qs, qt, qg = (mod[:, i, None, :] for i in range(6))
+    else:
+        ps = pt = qs = qt = 0.0
+        pg = qg = 1.0
+    n1 = rms_norm(h, w["norm1_w"], eps)
+    x1 = r((1.0 + ps) * n1 + pt)
+    qraw = (x1 @ _f64(w["to_q"]).T).reshape(B, L, nh, hd).transpose(0, 2, 1, 3)
+    kraw = (x1 @ _f64(w["to_k"]).T).reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
+    v = r(x1 @ _f64(w["to_v"]).T).reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
+    graw = r(x1 @ _f64(w["to_gate"]).T)
+    qn = rms_norm(qraw, w["norm_q_w"], eps)
+    kn = rms_norm(kraw, w["norm_k_w"], eps)
+    ang = None
+    if position_ids is not None:
+        ang = rope_angles(position_ids, dims.axes_dims, dims.rope_theta)
+        qn, kn = apply_rope(qn, ang[None, None]), apply_rope(kn, ang[None, None])
+    q, k = r(qn), r(kn)
+    key_valid = key_valid_mask(B, L, T, mask)
+    vis = None if image_ids is None else block_causal_visible(image_ids)
+    o = attention(q, k, v, key_valid, vis)
+    oc = o.transpose(0, 2, 1, 3).reshape(B, L, nh * hd)
+    sg = sigmoid(graw)
+    og = r(oc * sg)
+    y = og @ _f64(w["to_out"]).T
+    h1 = h + pg * y
+    n2 = rms_norm(h1, w["norm2_w"], eps)
+    x2 = r((1.0 + qs) * n2 + qt)
+    gt = x2 @ _f64(w["ff_gate"]).T
+    u = x2 @ _f64(w["ff_up"]).T
+    sgt = sigmoid(gt)
+    a = r(gt * sgt * u)
+    z = a @ _f64(w["ff_down"]).T
+    # ---- backward, step by step in reverse
+    grads = {}
+    flat = lambda t: t.reshape(M, -1)
+    dqg = np.sum(dh2 * z, axis=1)
+    dz = r(qg * dh2)
+    grads["ff_down"] = flat(dz).T @ flat(a)
+    da = dz @ _f64(w["ff_down"])
+    dgt = r(da * u * sgt * (1.0 + gt * (1.0 - sgt)))      # silu'(x) = s(x) (1 + x (1 - s(x)))
+    du = r(da * gt * sgt)
+    grads["ff_gate"] = flat(dgt).T @ flat(x2)
+    grads["ff_up"] = flat(du).T @ flat(x2)
+    dx2 = dgt @ _f64(w["ff_gate"]) + du @ _f64(w["ff_up"])
+    dqs = np.sum(dx2 * n2, axis=1)
+    dqt = np.sum(dx2, axis=1)
+    dh1_n, grads["norm2_w"] = rms_norm_backward(h1, w["norm2_w"], eps, (1.0 + qs) * dx2)
+    dh1 = dh2 + dh1_n
+    dpg = np.sum(dh1 * y, axis=1)
+    dy = r(pg * dh1)
+    grads["to_out"] = flat(dy).T @ flat(og)
+    dog = dy @ _f64(w["to_out"])
+    do = r(dog * sg).reshape(B, L, nh, hd).transpose(0, 2, 1, 3)
+    dgraw = r(dog * oc * sg * (1.0 - sg))
+    dq, dk, dv = attention_backward(q, k, v, key_valid, do, vis, rnd=rnd)
+    if ang is not None:                                      # the rotation's transpose turns back
+        dq, dk = apply_rope(dq, -ang[None, None]), apply_rope(dk, -ang[None, None])
+    dqraw, grads["norm_q_w"] = rms_norm_backward(qraw, w["norm_q_w"], eps, dq)
+    dkraw, grads["norm_k_w"] = rms_norm_backward(kraw, w["norm_k_w"], eps, dk)
+    dqraw = r(dqraw.transpose(0, 2, 1, 3).reshape(B, L, nh * hd))
+    dkraw = r(dkraw.transpose(0, 2, 1, 3).reshape(B, L, nkv * hd))
+    dv = r(dv.transpose(0, 2, 1, 3).reshape(B, L, nkv * hd))
+    grads["to_q"] = flat(dqraw).T @ flat(x1)
+    grads["to_k"] = flat(dkraw).T @ flat(x1)
+    grads["to_v"] = flat(dv).T @ flat(x1)
+    grads["to_gate"] = flat(dgraw).T @ flat(x1)
+    dx1 = (dqraw @ _f64(w["to_q"]) + dkraw @ _f64(w["to_k"]) + dv @ _f64(w["to_v"])
+           + dgraw @ _f64(w["to_gate"]))
+    dps = np.sum(dx1 * n1, axis=1)
+    dpt = np.sum(dx1, axis=1)
+    dh_n, grads["norm1_w"] = rms_norm_backward(h, w["norm1_w"], eps, (1.0 + ps) * dx1)
+    dh = dh1 + dh_n
+    dtemb = None
+    if temb is not None:
+        dmod = np.stack([dps, dpt, dpg, dqs, dqt, dqg], axis=1)    # (B, 6, H), the chunk order of R1
+        dtemb = dmod.reshape(B, 6 * H)
+        grads["scale_shift_table"] = dmod.sum(axis=0)
+    for key in ("norm1_w", "norm2_w", "norm_q_w", "norm_k_w"):
+        if w.get(key) is None:
+            grads[key] = None
+    return dh, dtemb, grads
 
 
 # ----------------------------------------------------------------------------------------------

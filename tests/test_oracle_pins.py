@@ -259,25 +259,26 @@ def test_rope_relative_position():
 # ----------------------------------------------------------------------------------------------
 # Whole block: library composition and brute force
 # ----------------------------------------------------------------------------------------------
-def torch_block(h, temb, pos, mask, w, d, T):
+def torch_block_t(h, temb, pos, mask, w, d, T, image_ids=None):
     """The block composed from torch library routines in float64 (F.linear, F.rms_norm,
-    F.scaled_dot_product_attention with enable_gqa and a boolean mask, complex RoPE, F.silu)."""
+    F.scaled_dot_product_attention with enable_gqa and a boolean mask, complex RoPE, F.silu) on
+    float64 tensors h, temb (or None) and the weight dict w (tensors; autograd follows them)."""
     t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
-    h = t(h)
     B, L, H = h.shape
     nh, nkv, hd = d.num_heads, d.num_kv_heads, d.head_dim
+    one = lambda key: 1 + w[key] if w.get(key) is not None else None
     if temb is not None:
-        ps, pt, pg, qs, qt, qg = (t(temb).view(B, 6, H) + t(w["scale_shift_table"])).unbind(1)
+        ps, pt, pg, qs, qt, qg = (temb.view(B, 6, H) + w["scale_shift_table"]).unbind(1)
         ps, pt, pg, qs, qt, qg = (u[:, None, :] for u in (ps, pt, pg, qs, qt, qg))
     else:
-        ps = pt = qs = qt = torch.zeros(())
-        pg = qg = torch.ones(())
-    x = (1 + ps) * F.rms_norm(h, (H,), weight=1 + t(w["norm1_w"]), eps=d.eps) + pt
-    q = F.linear(x, t(w["to_q"])).view(B, L, nh, hd).transpose(1, 2)
-    k = F.linear(x, t(w["to_k"])).view(B, L, nkv, hd).transpose(1, 2)
-    v = F.linear(x, t(w["to_v"])).view(B, L, nkv, hd).transpose(1, 2)
-    q = F.rms_norm(q, (hd,), weight=1 + t(w["norm_q_w"]), eps=d.eps)
-    k = F.rms_norm(k, (hd,), weight=1 + t(w["norm_k_w"]), eps=d.eps)
+        ps = pt = qs = qt = torch.zeros((), dtype=torch.float64)
+        pg = qg = torch.ones((), dtype=torch.float64)
+    x = (1 + ps) * F.rms_norm(h, (H,), weight=one("norm1_w"), eps=d.eps) + pt
+    q = F.linear(x, w["to_q"]).view(B, L, nh, hd).transpose(1, 2)
+    k = F.linear(x, w["to_k"]).view(B, L, nkv, hd).transpose(1, 2)
+    v = F.linear(x, w["to_v"]).view(B, L, nkv, hd).transpose(1, 2)
+    q = F.rms_norm(q, (hd,), weight=one("norm_q_w"), eps=d.eps)
+    k = F.rms_norm(k, (hd,), weight=one("norm_k_w"), eps=d.eps)
     if pos is not None:
         freqs = []
         for a, da in enumerate(d.axes_dims):
@@ -289,12 +290,24 @@ def torch_block(h, temb, pos, mask, w, d, T):
     valid = torch.ones(B, L, dtype=torch.bool)
     if mask is not None:
         valid[:, :T] = torch.from_numpy(np.asarray(mask).astype(bool))
-    o = F.scaled_dot_product_attention(q, k, v, attn_mask=valid[:, None, None, :], enable_gqa=True)
-    o = o.transpose(1, 2).reshape(B, L, nh * hd) * torch.sigmoid(F.linear(x, t(w["to_gate"])))
-    h = h + pg * F.linear(o, t(w["to_out"]))
-    x2 = (1 + qs) * F.rms_norm(h, (H,), weight=1 + t(w["norm2_w"]), eps=d.eps) + qt
-    ff = F.linear(F.silu(F.linear(x2, t(w["ff_gate"]))) * F.linear(x2, t(w["ff_up"])), t(w["ff_down"]))
-    return (h + qg * ff).numpy()
+    am = valid[:, None, None, :]
+    if image_ids is not None:
+        ids = torch.from_numpy(np.asarray(image_ids))
+        j = torch.arange(L)
+        vis = (j[None, :] <= j[:, None]) | ((ids[:, None] >= 0) & (ids[:, None] == ids[None, :]))
+        am = am & vis[None, None]
+    o = F.scaled_dot_product_attention(q, k, v, attn_mask=am, enable_gqa=True)
+    o = o.transpose(1, 2).reshape(B, L, nh * hd) * torch.sigmoid(F.linear(x, w["to_gate"]))
+    h = h + pg * F.linear(o, w["to_out"])
+    x2 = (1 + qs) * F.rms_norm(h, (H,), weight=one("norm2_w"), eps=d.eps) + qt
+    ff = F.linear(F.silu(F.linear(x2, w["ff_gate"])) * F.linear(x2, w["ff_up"]), w["ff_down"])
+    return h + qg * ff
+
+
+def torch_block(h, temb, pos, mask, w, d, T):
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    wt = {key: (None if val is None else t(val)) for key, val in w.items()}
+    return torch_block_t(t(h), None if temb is None else t(temb), pos, mask, wt, d, T).numpy()
 
 
 @pytest.mark.parametrize("case", ["gqa2", "gqa4_tiny_axes", "mha_nomask", "unmodulated"])
@@ -491,6 +504,102 @@ def test_rows_with_zero_positions_never_rotate():
     assert np.all(inp["position_ids"][:, 0] == 0)
     ang = O.rope_angles(inp["position_ids"], MICRO.axes_dims, MICRO.rope_theta)
     assert np.all(ang[:, : MICRO.axes_dims[0] // 2] == 0)
+
+
+# ----------------------------------------------------------------------------------------------
+# Backward pass (R20): against torch autograd through the library composition, and against
+# central finite differences of the oracle's own forward
+# ----------------------------------------------------------------------------------------------
+def _bwd_case(case):
+    if case == "gqa2":
+        wl, inp = micro_inputs(seed=60)
+        return MICRO, wl, inp, None
+    if case == "mha_nomask":
+        d = replace(MICRO, num_kv_heads=4)
+        wl, inp = micro_inputs(seed=61, valid=None, dims=d)
+        return d, wl, inp, None
+    if case == "unmodulated":
+        wl, inp = micro_inputs(seed=62, modulated=False)
+        inp["temb"] = None
+        inp["position_ids"] = None
+        return MICRO, wl, inp, None
+    # block-causal: text, a condition block, the target block (no query is left without a key)
+    wl, inp = micro_inputs(seed=63, B=2, T=4, grid=(2, 3), valid=(3, 4))
+    return MICRO, wl, inp, np.array([-1, -1, -1, -1, 0, 0, 0, 1, 1, 1])
+
+
+@pytest.mark.parametrize("case", ["gqa2", "mha_nomask", "unmodulated", "block_causal"])
+def test_block_backward_matches_autograd(case):
+    d, wl, inp, ids = _bwd_case(case)
+    w = inp["weights"]
+    g = np.random.default_rng(70)
+    dh_out = g.standard_normal(inp["h"].shape)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64)).requires_grad_(True)
+    ht = t(inp["h"])
+    tt = None if inp["temb"] is None else t(inp["temb"])
+    wt = {key: (None if val is None else t(val)) for key, val in w.items()}
+    out = torch_block_t(ht, tt, inp["position_ids"], inp["mask"], wt, d, wl.T, image_ids=ids)
+    out.backward(torch.from_numpy(dh_out))
+    dh, dtemb, grads = O.block_backward(inp["h"], inp["temb"], inp["position_ids"], inp["mask"], w, d, wl.T, dh_out,
+                                        image_ids=ids)
+    np.testing.assert_allclose(dh, ht.grad.numpy(), rtol=1e-9, atol=1e-10)
+    if tt is not None:
+        np.testing.assert_allclose(dtemb, tt.grad.numpy(), rtol=1e-9, atol=1e-10)
+    for key, val in wt.items():
+        if val is None:
+            assert grads[key] is None
+            continue
+        np.testing.assert_allclose(grads[key], val.grad.numpy(), rtol=1e-9, atol=1e-10, err_msg=key)
+
+
+def test_block_backward_finite_differences():
+    # <grad, v> against (f(x + e v) - f(x - e v)) / 2e . dh_out for random directions v in h, temb
+    # and three weights: only the oracle's forward enters the reference
+    d, wl, inp, _ = _bwd_case("gqa2")
+    w = inp["weights"]
+    g = np.random.default_rng(71)
+    dh_out = g.standard_normal(inp["h"].shape)
+    args = (inp["position_ids"], inp["mask"])
+    dh, dtemb, grads = O.block_backward(inp["h"], inp["temb"], *args, w, d, wl.T, dh_out)
+    f = lambda h, temb, ww: float(np.sum(O.block_forward(h, temb, *args, ww, d, wl.T) * dh_out))
+    eps = 1e-5
+    checks = [("h", dh), ("temb", dtemb)] + [(k, grads[k]) for k in ("to_k", "norm_q_w", "ff_down", "scale_shift_table")]
+    for name, grad in checks:
+        vdir = g.standard_normal(grad.shape)
+        def at(sign):
+            h, temb, ww = inp["h"].astype(np.float64), inp["temb"].astype(np.float64), dict(w)
+            if name == "h":
+                h = h + sign * eps * vdir
+            elif name == "temb":
+                temb = temb + sign * eps * vdir
+            else:
+                ww[name] = w[name].astype(np.float64) + sign * eps * vdir
+            return f(h, temb, ww)
+        fd = (at(+1) - at(-1)) / (2 * eps)
+        an = float(np.sum(grad * vdir))
+        assert abs(fd - an) <= 1e-6 * max(1.0, abs(an)), f"{name}: finite difference {fd} vs {an}"
+
+
+def test_attention_and_norm_backward_match_autograd():
+    g = np.random.default_rng(72)
+    B, nh, nkv, L, hd = 2, 4, 2, 7, 8
+    q, k, v, do = (g.standard_normal(s) for s in ((B, nh, L, hd), (B, nkv, L, hd), (B, nkv, L, hd), (B, nh, L, hd)))
+    valid = np.ones((B, L), bool)
+    valid[1, :2] = False
+    tq, tk, tv = (torch.from_numpy(a).requires_grad_(True) for a in (q, k, v))
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(valid)[:, None, None, :], enable_gqa=True)
+    o.backward(torch.from_numpy(do))
+    dq, dk, dv = O.attention_backward(q, k, v, valid, do)
+    for got, ref in ((dq, tq.grad), (dk, tk.grad), (dv, tv.grad)):
+        np.testing.assert_allclose(got, ref.numpy(), rtol=1e-10, atol=1e-12)
+    x = g.standard_normal((3, 5, 16))
+    wgt = 0.1 * g.standard_normal(16)
+    dy = g.standard_normal(x.shape)
+    tx, tw = torch.from_numpy(x).requires_grad_(True), torch.from_numpy(wgt).requires_grad_(True)
+    F.rms_norm(tx, (16,), weight=1 + tw, eps=1e-5).backward(torch.from_numpy(dy))
+    dx, dw = O.rms_norm_backward(x, wgt, 1e-5, dy)
+    np.testing.assert_allclose(dx, tx.grad.numpy(), rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(dw, tw.grad.numpy(), rtol=1e-10, atol=1e-12)
 
 
 # ----------------------------------------------------------------------------------------------
