@@ -203,6 +203,42 @@ def block_forward(cfg, weights: dict, h, temb, position_ids, mask, T: int, out=N
     return out
 
 
+def block_backward_workspace_bytes(cfg, B: int, T: int, N: int) -> int:
+    return load().k2_block_backward_workspace_bytes(ctypes.byref(cfg), B, T, N)
+
+
+def block_backward(cfg, weights: dict, h, temb, position_ids, mask, T: int, grad_out, want=None, workspace=None,
+                   stream=None):
+    """k2_block_backward: gradients of the block for grad_out (the gradient of its output), the forward
+    recomputed from h. want: weight names whose gradients to compute (None = every weight present).
+    Returns (grad_in (B, L, hidden), grad_temb (B, 6 hidden) or None, {name: float32 gradient})."""
+    torch = _torch()
+    lib = load()
+    _dev_tensor(h, "h", torch.float32)
+    _dev_tensor(grad_out, "grad_out", torch.float32, h.shape)
+    B, L, H = h.shape
+    N = L - T
+    mask = _mask_u8(mask)
+    pos_rows, pos_cols = (position_ids.shape if position_ids is not None else (0, 0))
+    grad_in = torch.empty_like(h)
+    grad_temb = None if temb is None else torch.empty_like(temb)
+    gs = _abi.BlockGrads()
+    out = {}
+    for n in _abi.BLOCK_WEIGHT_FIELDS:
+        t = weights.get(n)
+        if t is None or (want is not None and n not in want):
+            setattr(gs, n, None)
+            continue
+        out[n] = torch.empty(t.shape, dtype=torch.float32, device=h.device)
+        setattr(gs, n, out[n].data_ptr())
+    ws = _workspace(lib.k2_block_backward_workspace_bytes(ctypes.byref(cfg), B, T, N), h.device, workspace)
+    bw = _block_weights(weights)
+    check(lib.k2_block_backward(ctypes.byref(cfg), ctypes.byref(bw), B, T, N, _ptr(h), _ptr(temb), _ptr(position_ids),
+                                pos_rows, pos_cols, _ptr(mask), _ptr(grad_out), _ptr(grad_in), _ptr(grad_temb),
+                                ctypes.byref(gs), _ptr(ws), ws.numel(), _stream(stream)))
+    return grad_in, grad_temb, out
+
+
 def timestep_modulation_forward(hidden: int, temb_dim: int, dtype: str, weights: dict, timestep, stream=None):
     """k2_timestep_modulation_forward. Returns (temb (B, 6 hidden), e (B, hidden)) float32."""
     torch = _torch()

@@ -27,6 +27,10 @@ class BlockWeights(ctypes.Structure):
     _fields_ = [(n, c_void_p) for n in BLOCK_WEIGHT_FIELDS]
 
 
+class BlockGrads(ctypes.Structure):
+    _fields_ = [(n, c_void_p) for n in BLOCK_WEIGHT_FIELDS]
+
+
 class BlockLayout(ctypes.Structure):
     _fields_ = [(n, c_size_t) for n in ("x1", "q", "k", "vt", "g", "og", "x2", "a", "rope", "mod", "reach", "total")] + \
                [("ldvt", c_int)]
@@ -77,6 +81,10 @@ SIGNATURES = {
     "k2_block_forward_block_causal": (c_int, [POINTER(BlockCfg), POINTER(BlockWeights), c_int, c_int, c_int, c_void_p,
                                               c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p,
                                               c_void_p, c_size_t, c_void_p]),
+    "k2_block_backward_workspace_bytes": (c_size_t, [POINTER(BlockCfg), c_int, c_int, c_int]),
+    "k2_block_backward": (c_int, [POINTER(BlockCfg), POINTER(BlockWeights), c_int, c_int, c_int, c_void_p, c_void_p,
+                                  c_void_p, c_int, c_int, c_void_p, c_void_p, c_void_p, c_void_p,
+                                  POINTER(BlockGrads), c_void_p, c_size_t, c_void_p]),
     "k2_timestep_modulation_workspace_bytes": (c_size_t, [POINTER(TimeCfg), c_int]),
     "k2_timestep_modulation_forward": (c_int, [POINTER(TimeCfg), POINTER(TimeWeights), c_int, c_void_p, c_void_p,
                                                c_void_p, c_void_p, c_size_t, c_void_p]),

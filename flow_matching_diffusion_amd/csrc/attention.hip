@@ -317,6 +317,8 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
     const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
     const int row = q0 + qb * 16 + col;
     if (row >= L) continue;
+    if (p.lse && grp == 0)  // log-sum-exp in base 2 of the scaled scores, for the backward
+      p.lse[((size_t)b * p.nh + head) * L + row] = lsum > 0.0f ? m_i[qb] + __log2f(lsum) : INFINITY;
     const size_t base = (size_t)(b * L + row) * ldq + head * HD;
 #pragma unroll
     for (int hb = 0; hb < NHB; ++hb) {
@@ -324,7 +326,9 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float gv = to_f(gp[base + d0 + r]);
-        op[base + d0 + r] = to_t<T>(o[hb][qb][r] * inv * sigmoidf_(gv));
+        const float ov = o[hb][qb][r] * inv;
+        if (p.o_pre) ((T*)p.o_pre)[base + d0 + r] = to_t<T>(ov);
+        op[base + d0 + r] = to_t<T>(ov * sigmoidf_(gv));
       }
     }
   }
@@ -634,6 +638,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
   // query row with 8 head dims each, so the gate reads and output stores cover whole rows
   const float lsum = l_i + __shfl_xor(l_i, 32);
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  if (p.lse && h32 == 0 && q0 + c32 < L)  // log-sum-exp in base 2 of the scaled scores, for the backward
+    p.lse[((size_t)b * p.nh + head) * L + q0 + c32] = lsum > 0.0f ? m_i + __log2f(lsum) : INFINITY;
   __syncthreads();  // every wave is done with the K/V stages (all DMAs have landed)
   float4* const st = reinterpret_cast<float4*>(wave == 0 ? sK0 : wave == 1 ? sK1 : wave == 2 ? sV0 : sV1);
   static_assert(32 * HD * sizeof(float) <= sizeof(sK0), "staging area");
@@ -659,6 +665,12 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
       const size_t base = (size_t)(b * L + row) * ldq + head * HD + 8 * cc;
       const bf16x8 gv = *(const bf16x8*)((const bf16*)p.g + base);
       const float v[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+      if (p.o_pre) {
+        bf16x8 ov;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) ov[e] = (bf16)v[e];
+        *(bf16x8*)((bf16*)p.o_pre + base) = ov;
+      }
       bf16x8 out;
 #pragma unroll
       for (int e = 0; e < 8; ++e) out[e] = (bf16)(v[e] * sigmoidf_((float)gv[e]));
@@ -764,6 +776,8 @@ __global__ void __launch_bounds__(256) attn_short_kernel(AttnArgs p, float scale
   // normalise, gate, store: lane holds query l%32 and head dims 32hb + 8j + 4(l/32) + 0..3
   const float lsum = ls + __shfl_xor(ls, 32);
   const float inv = lsum > 0.0f ? 1.0f / lsum : 0.0f;
+  if (p.lse && h32 == 0 && c32 < L)  // log-sum-exp in base 2 of the scaled scores, for the backward
+    p.lse[((size_t)b * p.nh + head) * L + c32] = lsum > 0.0f ? mx + __log2f(lsum) : INFINITY;
   if (c32 < L) {
     const size_t base = (size_t)(b * L + c32) * ldq + head * HD;
     const bf16* gp = (const bf16*)p.g + base;
@@ -778,6 +792,12 @@ __global__ void __launch_bounds__(256) attn_short_kernel(AttnArgs p, float scale
 #pragma unroll
         for (int e = 0; e < 4; ++e) out[e] = (bf16)(o[hb][4 * j + e] * inv * sigmoidf_((float)gv[e]));
         *(bf16x4*)(op + d0) = out;
+        if (p.o_pre) {
+          bf16x4 ov;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ov[e] = (bf16)(o[hb][4 * j + e] * inv);
+          *(bf16x4*)((bf16*)p.o_pre + base + d0) = ov;
+        }
       }
   }
 }

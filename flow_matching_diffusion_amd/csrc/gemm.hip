@@ -208,11 +208,29 @@ struct EpiSwiglu : EpiNoStage {
   static constexpr int kLdsOutFloats = sizeof(T) == 2 ? 128 * kPitch / 4 : 0;  // 128 rows per wave
   T* a;
   int I;
+  float* gsave;  // optional float32 copies of the gate and up projections (the backward's recompute)
+  float* usave;
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
                                         int M, float* stg = nullptr) const {
     static_assert(NJ * (LY::NQ == 1 ? 16 : 32) == WN, "wave width");
     const int cbase = (col0 / WN) * (WN / 2);
+    if (gsave) {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int m = row0 + LY::row(i, lane);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < NJ / 2; ++j)
+#pragma unroll
+          for (int q = 0; q < LY::NQ; ++q) {
+            const int c = cbase + LY::col(j, q, lane);
+            if (c >= I) continue;
+            st4(gsave + (size_t)m * I + c, quad(acc[i][j], q));
+            st4(usave + (size_t)m * I + c, quad(acc[i][j + NJ / 2], q));
+          }
+      }
+    }
     if constexpr (kLdsOut) {
       static_assert(LY::NQ == 4 && WN == 128 && MI * 32 <= 128, "staged layout: 32x32 blocks, 64 bf16 per row");
       char* const sm = reinterpret_cast<char*>(stg);
@@ -281,6 +299,12 @@ struct EpiQkvg {
   const float* rs;
   int nq, nk, L, ldvt;
   float eps;
+  // extra outputs of the backward's recompute (NULL = none): raw q / k before their norms
+  // (float32), v row-major, k after norm and RoPE transposed like vt
+  float* qraw;
+  float* kraw;
+  T* vrow;
+  T* kt;
 
   // The bf16 kernel stages in LDS, after its main loop and for tiles holding q or k heads: the
   // multipliers 1 + w of the q and k norms (HD floats each), then for each of the tile's 256 rows
@@ -331,9 +355,17 @@ struct EpiQkvg {
         const int ld = seg == 0 ? nq : nk;
         const int cb = seg == 0 ? nh0 : nh0 - nq;
         const float* wn = seg == 0 ? wnq : wnk;
+        float* const raw = seg == 0 ? qraw : kraw;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const int m = row0 + LY::row(i, lane);  // every lane sharing this row takes the same branches
+          if (raw && m < M) {
+#pragma unroll
+            for (int jj = 0; jj < HB; ++jj)
+#pragma unroll
+              for (int qq = 0; qq < LY::NQ; ++qq)
+                st4(raw + (size_t)m * ld + cb + LY::col(jj, qq, lane), quad(acc[i][h0 + jj], qq));
+          }
           float ss = 0.0f;
 #pragma unroll
           for (int jj = 0; jj < HB; ++jj)
@@ -367,7 +399,18 @@ struct EpiQkvg {
                                   y.z * c2.y - y.w * s2.y, y.w * c2.y + y.z * s2.y);
                 }
               }
-              if (m < M) st4(dst + (size_t)m * ld + cb + d, y);
+              if (m < M) {
+                st4(dst + (size_t)m * ld + cb + d, y);
+                if (seg == 1 && kt) {  // k transposed per (batch, kv head), like vt
+                  const int b = m / L;
+                  T* kp = kt + (size_t)(b * (nk / HD) + cb / HD) * HD * ldvt + (m - b * L);
+                  const int dd = cb % HD + d;
+                  kp[(size_t)dd * ldvt] = to_t<T>(y.x);
+                  kp[(size_t)(dd + 1) * ldvt] = to_t<T>(y.y);
+                  kp[(size_t)(dd + 2) * ldvt] = to_t<T>(y.z);
+                  kp[(size_t)(dd + 3) * ldvt] = to_t<T>(y.w);
+                }
+              }
             }
         }
       } else if (seg == 2) {
@@ -379,6 +422,13 @@ struct EpiQkvg {
           if (m >= M) continue;
           const int b = m / L, l = m - b * L;
           T* base = vt + (size_t)(b * nkvh + kvh) * HD * ldvt + l;
+          if (vrow) {
+#pragma unroll
+            for (int jj = 0; jj < HB; ++jj)
+#pragma unroll
+              for (int qq = 0; qq < LY::NQ; ++qq)
+                st4(vrow + (size_t)m * nk + (nh0 - nq - nk) + LY::col(jj, qq, lane), quad(acc[i][h0 + jj], qq));
+          }
 #pragma unroll
           for (int jj = 0; jj < HB; ++jj)
 #pragma unroll
@@ -941,6 +991,7 @@ static hipError_t qkvg_t(const GemmA& a, const QkvgArgs& p, hipStream_t s) {
   e.q = (T*)p.q; e.k = (T*)p.k; e.vt = (T*)p.vt; e.g = (T*)p.g;
   e.wnq = p.wnq; e.wnk = p.wnk; e.rc = p.rope_cos; e.rs = p.rope_sin;
   e.nq = p.nq; e.nk = p.nk; e.L = p.L; e.ldvt = p.ldvt; e.eps = p.eps;
+  e.qraw = p.qraw; e.kraw = p.kraw; e.vrow = (T*)p.vrow; e.kt = (T*)p.kt;
   return launch<T>(a, 2 * p.nq + 2 * p.nk, bm, e, s);
 }
 
@@ -952,7 +1003,7 @@ static hipError_t swiglu_t(const GemmA& a, const SwigluArgs& p, hipStream_t s) {
   BSwiglu<T, WN> bm;
   bm.gate = (const T*)p.wgate; bm.up = (const T*)p.wup; bm.I = p.I; bm.ldb = a.K;
   EpiSwiglu<T, WN> e;
-  e.a = (T*)p.a; e.I = p.I;
+  e.a = (T*)p.a; e.I = p.I; e.gsave = p.gsave; e.usave = p.usave;
   const int ntot = ((p.I + WN / 2 - 1) / (WN / 2)) * WN;
   return launch<T, BSwiglu<T, WN>, EpiSwiglu<T, WN>, false, 2>(a, ntot, bm, e, s);
 }

@@ -2,6 +2,7 @@
 // Declarations and the contract of every entry point are in include/k2.h.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -497,6 +498,305 @@ int text_embed_run(const k2_model_cfg* cfg, const k2_model_weights* w, int B, in
   return K2_OK;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Block backward: recompute the forward from the block input keeping what the chain rule needs,
+// then the gradients step by step in reverse. Every matrix product is the forward's GEMM with a
+// plain epilogue, fed K-contiguous operands by transposes.
+// ---------------------------------------------------------------------------------------------
+constexpr int kBwdRows = 16;  // rows per partial-sum chunk of the column reductions
+
+struct BwdLayout {
+  // recompute
+  size_t mod, rope, x1, qraw, kraw, q, k, vt, vrow, kt, g, o, og, lse, y, h1, x2, gt, u, a, z;
+  // backward
+  size_t dh1, dz, dzT, aT, da, dgu, dguT, x2T, dx2, dy, dyT, ogT, dog, dO, dOT, qT, delta, dq, dk, dqkvg, dqkvgT,
+      x1T, dx1, wT, dmod;
+  size_t p_qg, p_pg, p_w2, p_qs, p_qt, p_w1, p_ps, p_pt, p_wq, p_wk;
+  int ldvt, Mp, ncb, qk_blocks;
+  size_t total;
+};
+
+BwdLayout bwd_layout(const k2_block_cfg* c, int B, int T, int N) {
+  BwdLayout l = {};
+  const size_t es = dt_size(c->dtype), f4 = sizeof(float);
+  const size_t L = (size_t)T + N, M = (size_t)B * L;
+  const size_t H = c->hidden, I = c->intermediate, hd = c->head_dim;
+  const size_t nq = (size_t)c->num_heads * hd, nk = (size_t)c->num_kv_heads * hd, nall = 2 * nq + 2 * nk;
+  l.ldvt = L <= 32 ? 32 : (int)((L + 63) / 64 * 64);
+  l.Mp = (int)((M + 63) / 64 * 64);
+  l.ncb = (int)((L + kBwdRows - 1) / kBwdRows);
+  l.qk_blocks = 1024;
+  const size_t Mp = l.Mp, chunks = (size_t)B * l.ncb;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off = align_up(off + bytes);
+    return o;
+  };
+  l.mod = take((size_t)B * 6 * H * f4);
+  l.rope = take(2 * L * (hd / 2) * f4);
+  l.x1 = take(M * H * es);
+  l.qraw = take(M * nq * f4);
+  l.kraw = take(M * nk * f4);
+  l.q = take(M * nq * es);
+  l.k = take(M * nk * es);
+  l.vt = take((size_t)B * nk * l.ldvt * es);
+  l.vrow = take(M * nk * es);
+  l.kt = take((size_t)B * nk * l.ldvt * es);
+  l.g = take(M * nq * es);
+  l.o = take(M * nq * es);
+  l.og = take(M * nq * es);
+  l.lse = take((size_t)B * c->num_heads * L * f4);
+  l.y = take(M * H * f4);
+  l.h1 = take(M * H * f4);
+  l.x2 = take(M * H * es);
+  l.gt = take(M * I * f4);
+  l.u = take(M * I * f4);
+  l.a = take(M * I * es);
+  l.z = take(M * H * f4);
+  l.dh1 = take(M * H * f4);
+  l.dz = take(M * H * es);
+  l.dzT = take(H * Mp * es);
+  l.aT = take(I * Mp * es);
+  l.da = take(M * I * f4);
+  l.dgu = take(M * 2 * I * es);
+  l.dguT = take(2 * I * Mp * es);
+  l.x2T = take(H * Mp * es);
+  l.dx2 = take(M * H * f4);
+  l.dy = take(M * H * es);
+  l.dyT = take(H * Mp * es);
+  l.ogT = take(nq * Mp * es);
+  l.dog = take(M * nq * f4);
+  l.dO = take(M * nq * es);
+  l.dOT = take((size_t)B * nq * l.ldvt * es);
+  l.qT = take((size_t)B * nq * l.ldvt * es);
+  l.delta = take((size_t)B * c->num_heads * L * f4);
+  l.dq = take(M * nq * f4);
+  l.dk = take(M * nk * f4);
+  l.dqkvg = take(M * nall * es);
+  l.dqkvgT = take(nall * Mp * es);
+  l.x1T = take(H * Mp * es);
+  l.dx1 = take(M * H * f4);
+  l.wT = take(std::max({I * H, H * 2 * I, nq * H, H * nall}) * es);
+  l.dmod = take((size_t)B * 6 * H * f4);
+  l.p_qg = take(chunks * H * f4);
+  l.p_pg = take(chunks * H * f4);
+  l.p_w2 = take(chunks * H * f4);
+  l.p_qs = take(chunks * H * f4);
+  l.p_qt = take(chunks * H * f4);
+  l.p_w1 = take(chunks * H * f4);
+  l.p_ps = take(chunks * H * f4);
+  l.p_pt = take(chunks * H * f4);
+  l.p_wq = take((size_t)l.qk_blocks * hd * f4);
+  l.p_wk = take((size_t)l.qk_blocks * hd * f4);
+  l.total = off;
+  return l;
+}
+
+// dst (C x Rpad, row stride ldd) = transpose of src (R x C, row stride lds), zeros in rows past R
+hipError_t transpose2d(int dt, const void* src, int R, int C, int lds, void* dst, int Rpad, int ldd, hipStream_t s) {
+  TransposeArgs t = {};
+  t.src = src; t.dst = dst; t.R = R; t.C = C; t.Rpad = Rpad; t.lds = lds; t.ldd = ldd; t.Z = 1; t.zdiv = 1;
+  return transpose(dt, t, s);
+}
+
+// per (batch, head): (B, L, heads, hd) row-major -> (B, heads, hd, ldt)
+hipError_t transpose_heads(int dt, const void* src, int B, int L, int heads, int hd, void* dst, int ldt, hipStream_t s) {
+  TransposeArgs t = {};
+  t.src = src; t.dst = dst; t.R = L; t.C = hd; t.Rpad = ldt; t.lds = heads * hd; t.ldd = ldt;
+  t.Z = B * heads; t.zdiv = heads;
+  t.sz0 = (size_t)L * heads * hd; t.sz1 = hd;
+  t.dz0 = (size_t)heads * hd * ldt; t.dz1 = (size_t)hd * ldt;
+  return transpose(dt, t, s);
+}
+
+// C (rows x N) float32 = A (rows x K) * Bw (N x K)^T, both K-contiguous with row strides lda and K
+hipError_t gemm_f32out(int dt, const void* A, int lda, int rows, int K, const void* Bw, int N, float* C, int ldc,
+                       hipStream_t s) {
+  PlainArgs p = {};
+  p.w = Bw; p.N = N; p.outf = C; p.ldf = ldc;
+  p.rows_per_b = rows; p.out_rows_per_b = rows; p.out_row_off = 0;
+  return gemm_plain(dt, GemmA{A, lda, rows, K}, p, s);
+}
+
+int block_backward_run(const k2_block_cfg* c, const k2_block_weights* w, int B, int T, int N, const float* hin,
+                       const float* temb, const float* pos, const uint8_t* mask, const float* dh2, float* dh_in,
+                       float* dtemb, const k2_block_grads* gr, void* ws, hipStream_t s) {
+  const int dt = c->dtype;
+  const int H = c->hidden, hd = c->head_dim, nh = c->num_heads, nkv = c->num_kv_heads, I = c->intermediate;
+  const int nq = nh * hd, nk = nkv * hd, nall = 2 * nq + 2 * nk;
+  const int L = T + N, M = B * L;
+  const BwdLayout l = bwd_layout(c, B, T, N);
+  const int Mp = l.Mp, ldt = l.ldvt;
+  const bool modulated = w->scale_shift_table != nullptr;
+  auto P = [&](size_t off) { return at(ws, off); };
+  float* mod = (float*)P(l.mod);
+  const float* ps = modulated ? mod : nullptr;
+  const float* pt = modulated ? mod + H : nullptr;
+  const float* pg = modulated ? mod + 2 * H : nullptr;
+  const float* qs = modulated ? mod + 3 * H : nullptr;
+  const float* qt = modulated ? mod + 4 * H : nullptr;
+  const float* qg = modulated ? mod + 5 * H : nullptr;
+  const int ms = 6 * H;
+
+  // ---- recompute the forward from hin
+  if (modulated) K2_RUN("modulation", s, modulation(temb, 6 * H, H, w->scale_shift_table, mod, B, 6, H, s));
+  float* rc = nullptr;
+  float* rsn = nullptr;
+  if (pos) {
+    rc = (float*)P(l.rope);
+    rsn = rc + (size_t)L * (hd / 2);
+    K2_RUN("rope", s, rope_table(pos, L, c->axes_dims[0], c->axes_dims[1], c->axes_dims[2], c->rope_theta, rc, rsn, s));
+  }
+  ModnormArgs mn = {};
+  mn.in = hin; mn.out = P(l.x1); mn.rows = M; mn.H = H;
+  mn.rows_per_b = L; mn.in_rows_per_b = L; mn.in_row_off = 0;
+  mn.w = w->norm1_w; mn.scale = ps; mn.shift = pt; mn.mod_stride = ms; mn.eps = c->eps;
+  K2_RUN("modnorm", s, modnorm(dt, mn, s));
+  QkvgArgs qa = {};
+  qa.wq = w->to_q; qa.wk = w->to_k; qa.wv = w->to_v; qa.wg = w->to_gate;
+  qa.nq = nq; qa.nk = nk; qa.hd = hd; qa.L = L;
+  qa.q = P(l.q); qa.k = P(l.k); qa.vt = P(l.vt); qa.g = P(l.g); qa.ldvt = ldt;
+  qa.wnq = w->norm_q_w; qa.wnk = w->norm_k_w; qa.rope_cos = rc; qa.rope_sin = rsn; qa.eps = c->eps;
+  qa.qraw = (float*)P(l.qraw); qa.kraw = (float*)P(l.kraw); qa.vrow = P(l.vrow); qa.kt = P(l.kt);
+  K2_RUN("gemm_qkvg", s, gemm_qkvg(dt, GemmA{P(l.x1), H, M, H}, qa, s));
+  AttnArgs aa = {};
+  aa.q = P(l.q); aa.k = P(l.k); aa.vt = P(l.vt); aa.g = P(l.g); aa.og = P(l.og); aa.mask = mask;
+  aa.B = B; aa.L = L; aa.T = T; aa.nh = nh; aa.nkv = nkv; aa.hd = hd; aa.ldvt = ldt;
+  aa.o_pre = P(l.o); aa.lse = (float*)P(l.lse);
+  K2_RUN("attention", s, attention(dt, aa, s));
+  float* y = (float*)P(l.y);
+  float* h1 = (float*)P(l.h1);
+  K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.og), nq, M, nq, w->to_out, H, y, H, s));
+  K2_RUN("gated_add", s, gated_add(hin, y, pg, ms, L, M, H, h1, s));
+  mn.in = h1; mn.out = P(l.x2); mn.w = w->norm2_w; mn.scale = qs; mn.shift = qt;
+  K2_RUN("modnorm", s, modnorm(dt, mn, s));
+  SwigluArgs sa = {};
+  sa.wgate = w->ff_gate; sa.wup = w->ff_up; sa.I = I; sa.a = P(l.a);
+  sa.gsave = (float*)P(l.gt); sa.usave = (float*)P(l.u);
+  K2_RUN("gemm_swiglu", s, gemm_swiglu(dt, GemmA{P(l.x2), H, M, H}, sa, s));
+  float* z = (float*)P(l.z);
+  K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.a), I, M, I, w->ff_down, H, z, H, s));
+
+  // ---- backward, in reverse
+  GatedGradArgs gg = {};
+  gg.dh = dh2; gg.br = modulated ? z : nullptr; gg.gate = qg; gg.gate_stride = ms; gg.out = P(l.dz);
+  gg.part = modulated ? (float*)P(l.p_qg) : nullptr;
+  gg.B = B; gg.L = L; gg.H = H; gg.RC = kBwdRows; gg.ncb = l.ncb;
+  K2_RUN("gated_grad", s, gated_grad(dt, gg, s));  // dz = qg dh2; dqg partials
+  if (gr->ff_down) {  // dWd = dz^T a
+    K2_RUN("transpose", s, transpose2d(dt, P(l.dz), M, H, H, P(l.dzT), Mp, Mp, s));
+    K2_RUN("transpose", s, transpose2d(dt, P(l.a), M, I, I, P(l.aT), Mp, Mp, s));
+    K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dzT), Mp, H, Mp, P(l.aT), I, gr->ff_down, I, s));
+  }
+  // da = dz Wd
+  K2_RUN("transpose", s, transpose2d(dt, w->ff_down, H, I, I, P(l.wT), H, H, s));
+  K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dz), H, M, H, P(l.wT), I, (float*)P(l.da), I, s));
+  K2_RUN("swiglu_bwd", s, swiglu_bwd(dt, (float*)P(l.da), (float*)P(l.gt), (float*)P(l.u), M, I, P(l.dgu), s));
+  if (gr->ff_gate || gr->ff_up) {  // [dWgate; dWup] = [dgt du]^T x2
+    K2_RUN("transpose", s, transpose2d(dt, P(l.dgu), M, 2 * I, 2 * I, P(l.dguT), Mp, Mp, s));
+    K2_RUN("transpose", s, transpose2d(dt, P(l.x2), M, H, H, P(l.x2T), Mp, Mp, s));
+    if (gr->ff_gate)
+      K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dguT), Mp, I, Mp, P(l.x2T), H, gr->ff_gate, H, s));
+    if (gr->ff_up)
+      K2_RUN("gemm_plain", s, gemm_f32out(dt, at(P(l.dguT), (size_t)I * Mp * dt_size(dt)), Mp, I, Mp, P(l.x2T), H,
+                                          gr->ff_up, H, s));
+  }
+  // dx2 = dgt Wgate + du Wup = [dgt du] [Wgate; Wup]
+  K2_RUN("transpose", s, transpose2d(dt, w->ff_gate, I, H, H, P(l.wT), I, 2 * I, s));
+  K2_RUN("transpose", s, transpose2d(dt, w->ff_up, I, H, H, at(P(l.wT), (size_t)I * dt_size(dt)), I, 2 * I, s));
+  K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dgu), 2 * I, M, 2 * I, P(l.wT), H, (float*)P(l.dx2), H, s));
+  // norm 2: dh1 = dh2 + its input gradient; partials for norm2_w, dqs, dqt
+  NormBwdArgs nb = {};
+  nb.x = h1; nb.dout = (float*)P(l.dx2); nb.dres = dh2; nb.dx = (float*)P(l.dh1);
+  nb.w = w->norm2_w; nb.scale = qs; nb.mod_stride = ms;
+  nb.pw = (float*)P(l.p_w2); nb.psc = (float*)P(l.p_qs); nb.psh = (float*)P(l.p_qt);
+  nb.B = B; nb.L = L; nb.H = H; nb.RC = kBwdRows; nb.ncb = l.ncb; nb.eps = c->eps;
+  K2_RUN("norm_bwd", s, norm_bwd(nb, s));
+  float* dh1 = (float*)P(l.dh1);
+  gg = GatedGradArgs{};
+  gg.dh = dh1; gg.br = modulated ? y : nullptr; gg.gate = pg; gg.gate_stride = ms; gg.out = P(l.dy);
+  gg.part = modulated ? (float*)P(l.p_pg) : nullptr;
+  gg.B = B; gg.L = L; gg.H = H; gg.RC = kBwdRows; gg.ncb = l.ncb;
+  K2_RUN("gated_grad", s, gated_grad(dt, gg, s));  // dy = pg dh1; dpg partials
+  if (gr->to_out) {  // dWo = dy^T og
+    K2_RUN("transpose", s, transpose2d(dt, P(l.dy), M, H, H, P(l.dyT), Mp, Mp, s));
+    K2_RUN("transpose", s, transpose2d(dt, P(l.og), M, nq, nq, P(l.ogT), Mp, Mp, s));
+    K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dyT), Mp, H, Mp, P(l.ogT), nq, gr->to_out, nq, s));
+  }
+  // dog = dy Wo
+  K2_RUN("transpose", s, transpose2d(dt, w->to_out, H, nq, nq, P(l.wT), H, H, s));
+  K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dy), H, M, H, P(l.wT), nq, (float*)P(l.dog), nq, s));
+  // output gate: dO, dgraw (into the gate columns of dqkvg), Delta
+  GateBwdArgs gb = {};
+  gb.dog = (float*)P(l.dog); gb.g = P(l.g); gb.o = P(l.o); gb.dout = P(l.dO);
+  gb.dg = at(P(l.dqkvg), (size_t)(nq + 2 * nk) * dt_size(dt)); gb.ldg = nall;
+  gb.delta = (float*)P(l.delta); gb.M = M; gb.L = L; gb.nh = nh; gb.nq = nq; gb.hd = hd;
+  K2_RUN("gate_bwd", s, gate_bwd(dt, gb, s));
+  // attention
+  K2_RUN("transpose", s, transpose_heads(dt, P(l.q), B, L, nh, hd, P(l.qT), ldt, s));
+  K2_RUN("transpose", s, transpose_heads(dt, P(l.dO), B, L, nh, hd, P(l.dOT), ldt, s));
+  AttnBwdArgs ab = {};
+  ab.q = P(l.q); ab.k = P(l.k); ab.v = P(l.vrow); ab.qt = P(l.qT); ab.kt = P(l.kt); ab.dot = P(l.dOT);
+  ab.dout = P(l.dO); ab.lse = (float*)P(l.lse); ab.delta = (float*)P(l.delta); ab.mask = mask;
+  ab.dq = (float*)P(l.dq); ab.lddq = nq; ab.dk = (float*)P(l.dk); ab.lddk = nk;
+  ab.dv = at(P(l.dqkvg), (size_t)(nq + nk) * dt_size(dt)); ab.lddv = nall;
+  ab.B = B; ab.L = L; ab.T = T; ab.nh = nh; ab.nkv = nkv; ab.hd = hd; ab.ldt = ldt;
+  K2_RUN("attention_bwd", s, attention_backward(dt, ab, s));
+  // q / k: RoPE transpose + head norm backward into the q and k columns of dqkvg
+  QkNormBwdArgs qn = {};
+  qn.dr = (float*)P(l.dq); qn.lddr = nq; qn.x = (float*)P(l.qraw); qn.ldx = nq; qn.rc = rc; qn.rs = rsn;
+  qn.w = w->norm_q_w; qn.dx = P(l.dqkvg); qn.lddx = nall; qn.part = (float*)P(l.p_wq);
+  qn.M = M; qn.L = L; qn.heads = nh; qn.hd = hd; qn.eps = c->eps;
+  K2_RUN("qknorm_bwd", s, qknorm_bwd(dt, qn, l.qk_blocks, s));
+  qn.dr = (float*)P(l.dk); qn.lddr = nk; qn.x = (float*)P(l.kraw); qn.ldx = nk; qn.w = w->norm_k_w;
+  qn.dx = at(P(l.dqkvg), (size_t)nq * dt_size(dt)); qn.part = (float*)P(l.p_wk); qn.heads = nkv;
+  K2_RUN("qknorm_bwd", s, qknorm_bwd(dt, qn, l.qk_blocks, s));
+  // projection weights: [dWq; dWk; dWv; dWg] = dqkvg^T x1
+  if (gr->to_q || gr->to_k || gr->to_v || gr->to_gate) {
+    K2_RUN("transpose", s, transpose2d(dt, P(l.dqkvg), M, nall, nall, P(l.dqkvgT), Mp, Mp, s));
+    K2_RUN("transpose", s, transpose2d(dt, P(l.x1), M, H, H, P(l.x1T), Mp, Mp, s));
+    float* outs[4] = {gr->to_q, gr->to_k, gr->to_v, gr->to_gate};
+    const int start[4] = {0, nq, nq + nk, nq + 2 * nk}, rows[4] = {nq, nk, nk, nq};
+    for (int i = 0; i < 4; ++i)
+      if (outs[i])
+        K2_RUN("gemm_plain", s, gemm_f32out(dt, at(P(l.dqkvgT), (size_t)start[i] * Mp * dt_size(dt)), Mp, rows[i], Mp,
+                                            P(l.x1T), H, outs[i], H, s));
+  }
+  // dx1 = dqkvg [Wq; Wk; Wv; Wg]
+  {
+    const void* ws4[4] = {w->to_q, w->to_k, w->to_v, w->to_gate};
+    const int start[4] = {0, nq, nq + nk, nq + 2 * nk}, rows[4] = {nq, nk, nk, nq};
+    for (int i = 0; i < 4; ++i)
+      K2_RUN("transpose", s, transpose2d(dt, ws4[i], rows[i], H, H, at(P(l.wT), (size_t)start[i] * dt_size(dt)),
+                                         rows[i], nall, s));
+  }
+  K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dqkvg), nall, M, nall, P(l.wT), H, (float*)P(l.dx1), H, s));
+  // norm 1: dh = dh1 + its input gradient; partials for norm1_w, dps, dpt
+  nb = NormBwdArgs{};
+  nb.x = hin; nb.dout = (float*)P(l.dx1); nb.dres = dh1; nb.dx = dh_in;
+  nb.w = w->norm1_w; nb.scale = ps; nb.mod_stride = ms;
+  nb.pw = (float*)P(l.p_w1); nb.psc = (float*)P(l.p_ps); nb.psh = (float*)P(l.p_pt);
+  nb.B = B; nb.L = L; nb.H = H; nb.RC = kBwdRows; nb.ncb = l.ncb; nb.eps = c->eps;
+  K2_RUN("norm_bwd", s, norm_bwd(nb, s));
+
+  // ---- reductions of the partial sums
+  const int chunks = B * l.ncb;
+  if (gr->norm1_w) K2_RUN("reduce_rows", s, reduce_rows((float*)P(l.p_w1), 1, chunks, H, H, gr->norm1_w, H, s));
+  if (gr->norm2_w) K2_RUN("reduce_rows", s, reduce_rows((float*)P(l.p_w2), 1, chunks, H, H, gr->norm2_w, H, s));
+  if (gr->norm_q_w) K2_RUN("reduce_rows", s, reduce_rows((float*)P(l.p_wq), 1, l.qk_blocks, hd, hd, gr->norm_q_w, hd, s));
+  if (gr->norm_k_w) K2_RUN("reduce_rows", s, reduce_rows((float*)P(l.p_wk), 1, l.qk_blocks, hd, hd, gr->norm_k_w, hd, s));
+  if (modulated && (dtemb || gr->scale_shift_table)) {
+    float* dm = dtemb ? dtemb : (float*)P(l.dmod);
+    const size_t parts[6] = {l.p_ps, l.p_pt, l.p_pg, l.p_qs, l.p_qt, l.p_qg};  // the chunk order of the modulation
+    for (int cc = 0; cc < 6; ++cc)
+      K2_RUN("reduce_rows", s, reduce_rows((float*)P(parts[cc]), B, l.ncb, H, H, dm + (size_t)cc * H, 6 * H, s));
+    if (gr->scale_shift_table)
+      K2_RUN("reduce_rows", s, reduce_rows(dm, 1, B, 6 * H, 6 * H, gr->scale_shift_table, 6 * H, s));
+  }
+  return K2_OK;
+}
+
 }  // namespace
 
 // =================================================================================================
@@ -577,6 +877,35 @@ int k2_block_forward_block_causal(const k2_block_cfg* cfg, const k2_block_weight
   g_err.clear();
   return block_run(cfg, w, B, T, N, hidden_in, hidden_out, temb, position_ids, mask, workspace, nullptr, nullptr,
                    (hipStream_t)stream, image_ids);
+}
+
+size_t k2_block_backward_workspace_bytes(const k2_block_cfg* cfg, int B, int T, int N) {
+  if (!cfg || B < 0 || T < 0 || N < 0) return 0;
+  return bwd_layout(cfg, B, T, N).total;
+}
+
+int k2_block_backward(const k2_block_cfg* cfg, const k2_block_weights* w, int B, int T, int N,
+                      const float* hidden_in, const float* temb, const float* position_ids, int pos_rows,
+                      int pos_cols, const uint8_t* mask, const float* grad_out, float* grad_in, float* grad_temb,
+                      const k2_block_grads* grads, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc = validate_block_call(cfg, w, B, T, N, hidden_in, grad_in, temb, position_ids, pos_rows, pos_cols);
+  if (rc != K2_OK) return rc;
+  if (!grad_out || !grad_in) return fail(K2_ERR_NULL, "grad_out / grad_in is NULL");
+  if (!grads) return fail(K2_ERR_NULL, "grads is NULL (pass a struct of NULLs for no weight gradients)");
+  if (grad_in == hidden_in || grad_in == grad_out) return fail(K2_ERR_CONFIG, "grad_in may not alias hidden_in or grad_out");
+  if (cfg->hidden % 4 || cfg->hidden > 8192) return fail(K2_ERR_CONFIG, "the backward needs hidden <= 8192");
+  if (grad_temb && !w->scale_shift_table) return fail(K2_ERR_CONFIG, "grad_temb given for an unmodulated block");
+  if (grads->scale_shift_table && !w->scale_shift_table)
+    return fail(K2_ERR_CONFIG, "a scale_shift_table gradient asked of an unmodulated block");
+  if ((rc = check_align("grad_out / grad_in / grad_temb / weight gradients",
+                        {grad_out, grad_in, grad_temb, grads->scale_shift_table, grads->norm1_w, grads->norm2_w,
+                         grads->norm_q_w, grads->norm_k_w, grads->to_q, grads->to_k, grads->to_v, grads->to_gate,
+                         grads->to_out, grads->ff_gate, grads->ff_up, grads->ff_down})) != K2_OK)
+    return rc;
+  if ((rc = check_ws(workspace, workspace_bytes, bwd_layout(cfg, B, T, N).total)) != K2_OK) return rc;
+  g_err.clear();
+  return block_backward_run(cfg, w, B, T, N, hidden_in, temb, position_ids, mask, grad_out, grad_in, grad_temb, grads,
+                            workspace, (hipStream_t)stream);
 }
 
 size_t k2_timestep_modulation_workspace_bytes(const k2_time_cfg* cfg, int B) {

@@ -34,6 +34,11 @@ struct QkvgArgs {
   const float* wnq; const float* wnk;  // (hd) zero-centred, may be NULL
   const float* rope_cos; const float* rope_sin;  // (L, hd/2) or NULL (no RoPE)
   float eps;
+  // optional extra outputs for the backward's recompute (NULL = not written): the raw q and k
+  // projections before their norms (float32, (M, nq) and (M, nk)), v row-major (M, nk) in the
+  // operand dtype, and k after norm and RoPE transposed like vt (B, nkv, hd, ldvt)
+  float* qraw; float* kraw;
+  void* vrow; void* kt;
 };
 
 // SwiGLU up projection: a = silu(x Wgate^T) * (x Wup^T), a: (M, I).
@@ -41,6 +46,7 @@ struct SwigluArgs {
   const void* wgate; const void* wup;
   int I;
   void* a;
+  float* gsave; float* usave;  // optional float32 (M, I) copies of x Wgate^T and x Wup^T (NULL = none)
 };
 
 // Residual projection: hout[m, n] = hin[m, n] + gate[m / L, n] * (A Bw^T)[m, n]; gate NULL = 1.
@@ -82,8 +88,84 @@ struct AttnArgs {
   // Block-causal restriction (NULL = none): query i attends key j only if j <= reach[i]; reach is
   // (L,) and non-decreasing with reach[i] >= i (block_reach builds it from image block ids).
   const int* reach;
+  // optional extra outputs for the backward (NULL = not written): the attention output before the
+  // gate (M, nh*hd) in the operand dtype, and per (batch, head, query) the log-sum-exp of the
+  // scores in base 2 with the scale folded in, log2 sum_j 2^(s_j log2(e) / sqrt(hd)) (+inf for a
+  // query with no key)
+  void* o_pre;
+  float* lse;
 };
 hipError_t attention(int dt, const AttnArgs& p, hipStream_t s);
+
+// ---------------------------------------------------------------------------------------------
+// Backward pass (backward.hip)
+// ---------------------------------------------------------------------------------------------
+struct TransposeArgs {
+  const void* src; void* dst;
+  int R, C, Rpad;         // source rows and columns; destination row length covered (zeros past R)
+  int lds, ldd;           // row strides of source and destination (elements)
+  int Z, zdiv;            // batch count; batch z offsets: (z / zdiv) * s0 + (z % zdiv) * s1
+  size_t sz0, sz1, dz0, dz1;
+};
+hipError_t transpose(int dt, const TransposeArgs& p, hipStream_t s);
+hipError_t gated_add(const float* h, const float* y, const float* gate, int gate_stride, int L, int M, int H,
+                     float* out, hipStream_t s);
+struct GatedGradArgs {
+  const float* dh; const float* br;   // (B*L, H) float32; br NULL = no partial sums
+  const float* gate; int gate_stride; // gate row b, NULL = 1
+  void* out;                          // (B*L, H) operand dtype: gate * dh
+  float* part;                        // (B * ncb, H) column sums of dh * br per chunk, or NULL
+  int B, L, H, RC, ncb;               // chunks of RC rows, ncb = ceil(L / RC) per batch row
+};
+hipError_t gated_grad(int dt, const GatedGradArgs& p, hipStream_t s);
+hipError_t swiglu_bwd(int dt, const float* da, const float* gt, const float* up, int M, int I, void* dgu,
+                      hipStream_t s);
+struct NormBwdArgs {
+  const float* x;      // (B*L, H) the norm's input
+  const float* dout;   // (B*L, H) gradient of the modulated output
+  const float* dres;   // (B*L, H) added to the input gradient, or NULL
+  float* dx;           // (B*L, H) input gradient (may alias dres)
+  const float* w;      // (H) zero-centred norm weight or NULL
+  const float* scale; int mod_stride;  // modulation scale row b at scale + b * mod_stride, or NULL
+  float* pw; float* psc; float* psh;   // (B * ncb, H) partials, each may be NULL
+  int B, L, H, RC, ncb;
+  float eps;
+};
+hipError_t norm_bwd(const NormBwdArgs& p, hipStream_t s);
+struct GateBwdArgs {
+  const float* dog;       // (M, nq) float32 gradient of the gated attention output
+  const void* g;          // (M, nq) raw gate projection
+  const void* o;          // (M, nq) attention output before the gate
+  void* dout;             // (M, nq) gradient of the attention output, operand dtype
+  void* dg; int ldg;      // gradient of the raw gate, operand dtype, row stride ldg
+  float* delta;           // (B, nh, L)
+  int M, L, nh, nq, hd;
+};
+hipError_t gate_bwd(int dt, const GateBwdArgs& p, hipStream_t s);
+struct AttnBwdArgs {
+  const void* q; const void* k; const void* v;  // (M, nh*hd), (M, nkv*hd), (M, nkv*hd) row-major
+  const void* qt; const void* kt; const void* dot;  // (B, nh, hd, ldt), (B, nkv, hd, ldt), (B, nh, hd, ldt)
+  const void* dout;                              // (M, nh*hd) gradient of the attention output
+  const float* lse; const float* delta;          // (B, nh, L)
+  const uint8_t* mask;                           // (B, T) or NULL
+  float* dq; int lddq;                           // (M, .) float32, head h at column h*hd
+  float* dk; int lddk;                           // (M, .) float32, kv head at column kvh*hd
+  void* dv; int lddv;                            // (M, .) operand dtype
+  int B, L, T, nh, nkv, hd, ldt;
+};
+hipError_t attention_backward(int dt, const AttnBwdArgs& p, hipStream_t s);
+struct QkNormBwdArgs {
+  const float* dr; int lddr;   // gradient of the rotated, normed heads (float32)
+  const float* x; int ldx;     // raw projection (float32)
+  const float* rc; const float* rs;  // (L, hd/2) rotation table or NULL
+  const float* w;              // (hd) zero-centred norm weight or NULL
+  void* dx; int lddx;          // raw projection gradient, operand dtype
+  float* part;                 // (blocks, hd) partial sums for the norm weight, or NULL
+  int M, L, heads, hd;
+  float eps;
+};
+hipError_t qknorm_bwd(int dt, const QkNormBwdArgs& p, int blocks, hipStream_t s);
+hipError_t reduce_rows(const float* part, int G, int nc, int ncols, int ldp, float* out, int ldo, hipStream_t s);
 
 // reach[i] = i for tokens outside every image block (ids[i] < 0), else the last position of the
 // contiguous run of equal ids that holds i. One workgroup; ids and reach are (L,) device arrays.

@@ -133,6 +133,43 @@ int k2_block_forward(const k2_block_cfg* cfg, const k2_block_weights* w, int B, 
                      const uint8_t* encoder_attention_mask,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* Backward pass of one block ([ARTICLE] §四 data flow; §六: the model's test matrix trains it, with
+   gradient checkpointing): the gradients of a loss with respect to the block's input, its
+   modulation input and its weights, given the gradient grad_out of the block's output
+   hidden_out. The forward is recomputed from hidden_in (checkpointing), then the chain rule runs
+   through its steps in reverse. Matrix products use the block's dtype for their operands with
+   float32 accumulation; gradients come out in float32.
+   hidden_in, temb, position_ids, mask: exactly as given to k2_block_forward (attention over every
+   allowed key; the block-causal variant has no backward here).
+   grad_out: (B, L, hidden) float32 gradient of hidden_out.  grad_in: (B, L, hidden) float32,
+   written (not accumulated); must not alias hidden_in or grad_out.
+   grad_temb: (B, 6*hidden) float32 or NULL; NULL is required when the block has no
+   scale_shift_table.  grads: one float32 device pointer per weight, same shapes as
+   k2_block_weights' tensors, each written (not accumulated), or NULL to skip that gradient (the
+   product it needs is then not run). Requires hidden <= 8192.
+   Workspace: k2_block_backward_workspace_bytes(cfg, B, T, N). */
+typedef struct {
+  float* scale_shift_table; /* (6, hidden) */
+  float* norm1_w;           /* (hidden) */
+  float* norm2_w;           /* (hidden) */
+  float* norm_q_w;          /* (head_dim) */
+  float* norm_k_w;          /* (head_dim) */
+  float* to_q;              /* (num_heads*head_dim, hidden) */
+  float* to_k;              /* (num_kv_heads*head_dim, hidden) */
+  float* to_v;              /* (num_kv_heads*head_dim, hidden) */
+  float* to_gate;           /* (num_heads*head_dim, hidden) */
+  float* to_out;            /* (hidden, num_heads*head_dim) */
+  float* ff_gate;           /* (intermediate, hidden) */
+  float* ff_up;             /* (intermediate, hidden) */
+  float* ff_down;           /* (hidden, intermediate) */
+} k2_block_grads;
+size_t k2_block_backward_workspace_bytes(const k2_block_cfg* cfg, int B, int T, int N);
+int k2_block_backward(const k2_block_cfg* cfg, const k2_block_weights* w, int B, int T, int N,
+                      const float* hidden_in, const float* temb, const float* position_ids, int pos_rows,
+                      int pos_cols, const uint8_t* encoder_attention_mask, const float* grad_out, float* grad_in,
+                      float* grad_temb, const k2_block_grads* grads, void* workspace, size_t workspace_bytes,
+                      void* stream);
+
 /* The same block with block-causal attention ([QWEN21] model page "QwenImage21Transformer2DModel":
    block-causal attention item; build_token_metadata): query i attends key j only if j <= i or both
    tokens lie in the same image block, on top of the key-padding mask. The sequence is causal while

@@ -70,7 +70,9 @@ Readings where the pages are silent or garbled (each restated where it is used):
       the forward's steps, the forward recomputed from h (checkpointing). In bf16 mode the
       backward's matrix-product operands are bf16 as well: the gradients that enter a product
       (dz, dgt, du, dy, the attention output gradient, P and dS inside attention, and the q/k/v/gate
-      projection gradients), with float32 accumulation and float32 weight gradients.
+      projection gradients), with float32 accumulation and float32 weight gradients; the attention
+      output before the gate, which the bf16 model's attention returns as a bf16 tensor, enters the
+      gate's and the softmax's gradients rounded to bf16.
 """
 from __future__ import annotations
 
@@ -294,12 +296,13 @@ def rms_norm_backward(x, weight, eps, dy):
     return dx, dw
 
 
-def attention_backward(q, k, v, key_valid, do, visible=None, rnd=None):
+def attention_backward(q, k, v, key_valid, do, visible=None, rnd=None, o=None):
     """Gradients of attention() (same arguments) for the output gradient do (B, nh, Lq, hd):
     returns (dq, dk, dv) with dk, dv summed over the query heads that share each kv head (R4).
     With P the softmax probabilities and O = P V: dV = P^T dO, dP = dO V^T,
     dS = P (dP - rowsum(dO * O)), dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd). rnd (R20) rounds P
-    and dS where they become matrix-product operands."""
+    and dS where they become matrix-product operands; o, if given, is the forward output O as the
+    model holds it (R20), used in rowsum(dO * O)."""
     r = rnd or _id
     nh, nkv, hd = q.shape[1], k.shape[1], q.shape[-1]
     g = nh // nkv
@@ -317,7 +320,7 @@ def attention_backward(q, k, v, key_valid, do, visible=None, rnd=None):
     p = np.exp(s)
     p = p / np.where(some, np.sum(p, axis=-1, keepdims=True), 1.0)
     do = _f64(do)
-    o = p @ vv
+    o = p @ vv if o is None else _f64(o)
     dvv = np.swapaxes(r(p), -1, -2) @ do
     dp = do @ np.swapaxes(vv, -1, -2)
     delta = np.sum(do * o, axis=-1, keepdims=True)
@@ -370,6 +373,7 @@ def block_backward(h, temb, position_ids, mask, w, dims, T, dh_out, rnd=None, im
     og = r(oc * sg)
     y = og @ _f64(w["to_out"]).T
     h1 = h + pg * y
+    o_m, oc_m = r(o), r(oc)          # the attention output as the model holds it (R20)
     n2 = rms_norm(h1, w["norm2_w"], eps)
     x2 = r((1.0 + qs) * n2 + qt)
     gt = x2 @ _f64(w["ff_gate"]).T
@@ -398,8 +402,8 @@ def block_backward(h, temb, position_ids, mask, w, dims, T, dh_out, rnd=None, im
     grads["to_out"] = flat(dy).T @ flat(og)
     dog = dy @ _f64(w["to_out"])
     do = r(dog * sg).reshape(B, L, nh, hd).transpose(0, 2, 1, 3)
-    dgraw = r(dog * oc * sg * (1.0 - sg))
-    dq, dk, dv = attention_backward(q, k, v, key_valid, do, vis, rnd=rnd)
+    dgraw = r(dog * oc_m * sg * (1.0 - sg))
+    dq, dk, dv = attention_backward(q, k, v, key_valid, do, vis, rnd=rnd, o=o_m)
     if ang is not None:                                      # the rotation's transpose turns back
         dq, dk = apply_rope(dq, -ang[None, None]), apply_rope(dk, -ang[None, None])
     dqraw, grads["norm_q_w"] = rms_norm_backward(qraw, w["norm_q_w"], eps, dq)

@@ -1,0 +1,78 @@
+"""GPU parity of k2_block_backward (the block's backward pass, forward recomputed from its input)
+against the CPU oracle's chain-rule gradients, which are pinned to torch autograd and to finite
+differences on the CPU. Every output is compared: the input gradient, the temb gradient and each
+weight gradient, as max |gpu - oracle| / rms(oracle). float32: <= 1e-4. bf16: the block tests' bar
+against the oracle's own bf16-operand deviation (tests/k2_testutil.parity), with the oracle rounding
+the backward's matrix-product operands as the bf16 path does (reading R20)."""
+import numpy as np
+import pytest
+
+from flow_matching_diffusion_amd import synth as S
+from oracle import k2_oracle as O
+from tests.k2_testutil import device, parity, temb_for
+
+pytestmark = pytest.mark.gpu
+
+G4 = S.BlockDims(hidden=512, num_heads=4, num_kv_heads=1, head_dim=128, intermediate=256, axes_dims=(32, 48, 48))
+G2 = S.BlockDims(hidden=256, num_heads=4, num_kv_heads=2, head_dim=64, intermediate=200, axes_dims=(16, 24, 24))
+G1 = S.BlockDims(hidden=256, num_heads=2, num_kv_heads=2, head_dim=128, intermediate=320, axes_dims=(32, 48, 48))
+
+CASES = {
+    # several 32-key tiles, ragged tails, a text mask with a nearly empty row
+    "g4_hd128_f32": (G4, "f32", 2, 12, (6, 5), (12, 3), True),
+    "g4_hd128_bf16": (G4, "bf16", 2, 12, (6, 5), (12, 3), True),
+    # G = 2, head_dim 64, intermediate not a multiple of 64
+    "g2_hd64_f32": (G2, "f32", 1, 7, (5, 3), (5,), True),
+    "g2_hd64_bf16": (G2, "bf16", 2, 7, (9, 8), (5, 0), True),
+    # MHA over 70 tokens, no mask
+    "g1_hd128_bf16": (G1, "bf16", 1, 6, (8, 8), None, True),
+    # text-fusion style: no modulation, no RoPE
+    "unmodulated_f32": (G2, "f32", 2, 0, (4, 5), None, False),
+}
+
+
+def _case(name):
+    dims, dt, B, T, grid, valid, modulated = CASES[name]
+    wl = S.Workload(name, 500 + sorted(CASES).index(name), dt, B, T, grid, valid, dims=dims)
+    inp = S.block_inputs(wl)
+    temb = temb_for(wl, inp)
+    if not modulated:
+        inp["weights"].pop("scale_shift_table")
+        inp["position_ids"] = None
+        temb = None
+    g = np.random.default_rng(wl.seed)
+    dh_out = g.standard_normal(inp["h"].shape).astype(np.float32)
+    return wl, inp, temb, dh_out
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_block_backward(name):
+    import torch
+    import flow_matching_diffusion_amd as k2
+    wl, inp, temb, dh_out = _case(name)
+    dev = device()
+    cfg = k2.block_cfg(wl.dims, wl.dtype)
+    wdev = k2.upload(inp["weights"], wl.dtype, dev)
+    ht = torch.from_numpy(np.ascontiguousarray(inp["h"])).to(dev)
+    tt = None if temb is None else torch.from_numpy(np.ascontiguousarray(temb, dtype=np.float32)).to(dev)
+    pt = None if inp["position_ids"] is None else torch.from_numpy(inp["position_ids"]).to(dev)
+    mt = None if inp["mask"] is None else torch.from_numpy(inp["mask"]).to(dev)
+    gi, gtemb, grads = k2.block_backward(cfg, wdev, ht, tt, pt, mt, wl.T, torch.from_numpy(dh_out).to(dev))
+    torch.cuda.synchronize()
+    got = {"h": gi.cpu().numpy()}
+    if gtemb is not None:
+        got["temb"] = gtemb.cpu().numpy()
+    got.update({k: v.cpu().numpy() for k, v in grads.items()})
+    cache = {}
+
+    def oracle(rnd):
+        key = rnd is not None
+        if key not in cache:
+            dh, dtemb, gr = O.block_backward(inp["h"], temb, inp["position_ids"], inp["mask"], inp["weights"], wl.dims,
+                                             wl.T, dh_out, rnd=rnd)
+            cache[key] = dict(gr, h=dh, temb=dtemb)
+        return cache[key]
+
+    assert set(got) == {k for k, v in oracle(None).items() if v is not None}
+    for k in sorted(got):
+        parity(f"{name} d{k}", wl.dtype, got[k], lambda rnd, k=k: oracle(rnd)[k])
