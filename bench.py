@@ -12,11 +12,11 @@ same resolution as denoise steps/s (one call = one CFG step), the sampler on one
 as the base checkpoint's 28 steps and without as the distilled 8 steps) as time per image, both with
 the text rows computed once per prompt pair (k2_text_embed, then k2_denoise_step_cached) and with
 the text path run at every step (k2_denoise_step), the block-causal block variant on the same pair
-(a condition block then the target block), per-kernel times, the roofline of the dominant kernel, and
+(a condition block then the target block), the block's backward pass (k2_block_backward), per-kernel times, the roofline of the dominant kernel, and
 the CPU oracle on a bounded sample.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-backbone] [--no-cpu-baseline]
-                       [--no-block-causal] [--cpu-rows R] [--copy-calibration]
+                       [--no-block-causal] [--no-backward] [--cpu-rows R] [--copy-calibration]
 --copy-calibration first runs a plain elementwise copy (negation) of 1 GiB float32, a kernel of known
 HBM traffic against which the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled.
 """
@@ -120,6 +120,7 @@ def main():
     ap.add_argument("--no-backbone", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-block-causal", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4608)
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
@@ -270,6 +271,46 @@ def main():
                           "algorithmic_tflop": round(bc_attn / 1e12, 4),
                           "bidirectional_algorithmic_tflop": round(attn_flops / 1e12, 4)}}
         del idt
+
+    # The block's backward pass (k2_block_backward: the forward recomputed from the block input, then
+    # every gradient: input, temb and all weights) on the same pair. Algorithmic FLOPs: the recompute
+    # (the forward's) plus, for each projection, the input-gradient and weight-gradient products
+    # (2x the forward's GEMM FLOPs), plus attention's four backward products (2x its forward).
+    if not args.no_backward:
+        del ws
+        torch.cuda.empty_cache()
+        gout = S.device_normal(wl.seed, "grad_out", (B, L, d.hidden), 1.0, f32, dev)
+        bws = torch.empty(k2.block_backward_workspace_bytes(cfg, B, T, N), dtype=torch.uint8, device=dev)
+
+        def bwd_step():
+            return k2.block_backward(cfg, w, h, temb, pos, mask, T, gout, workspace=bws)
+
+        for _ in range(max(1, args.warmup // 2)):
+            res = bwd_step()
+        del res
+        torch.cuda.synchronize()
+        nb = max(1, args.steps // 4)
+        k2.profile_reset()
+        k2.profile_enable(True)
+        t0 = time.perf_counter()
+        for _ in range(nb):
+            res = bwd_step()
+        torch.cuda.synchronize()
+        b_ms = (time.perf_counter() - t0) * 1e3 / nb
+        k2.profile_enable(False)
+        gemm_f = block_flops(d, B, L, [0] * B)
+        b_flops = 3 * gemm_f + 3 * attn_flops
+        bk = {}
+        for name in ("gemm_qkvg", "attention", "gemm_swiglu", "gemm_plain", "transpose", "attention_bwd", "norm_bwd",
+                     "gated_grad", "swiglu_bwd", "gate_bwd", "qknorm_bwd", "modnorm", "gated_add", "reduce_rows"):
+            tot, n = k2.profile_query(name)
+            if n:
+                bk[name] = {"ms_per_call": round(tot / nb, 3), "launches": n // nb}
+        result["backward"] = {"ms_per_step": round(b_ms, 3), "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 1),
+                              "algorithmic_tflop": round(b_flops / 1e12, 3), "kernels": bk,
+                              "note": "forward recompute + all gradients; TFLOP = 3x forward GEMMs + 3x attention"}
+        del res, bws, gout
+        ws = None
     del w, h, out, ws
     torch.cuda.empty_cache()
 

@@ -652,20 +652,34 @@ hipError_t qknorm_bwd(int dt, const QkNormBwdArgs& p, int blocks, hipStream_t s)
 // ---------------------------------------------------------------------------------------------
 // out[gr * ldo + j] = sum_{c < nc} part[(gr * nc + c) * ldp + j] for gr < G, j < ncols
 // ---------------------------------------------------------------------------------------------
-__global__ void reduce_rows_kernel(const float* __restrict__ part, int G, int nc, int ncols, int ldp,
-                                   float* __restrict__ out, int ldo) {
-  const int j = blockIdx.x * blockDim.x + threadIdx.x;
+// 256 threads = 64 columns x 4 chunk lanes; each thread keeps 4 independent sums so that many loads
+// are in flight, then the 4 chunk lanes meet in LDS
+__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ part, int G, int nc, int ncols,
+                                                          int ldp, float* __restrict__ out, int ldo) {
+  __shared__ float red[4][64];
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + tx;
   const int gr = blockIdx.y;
-  if (j >= ncols) return;
-  const float* pp = part + (size_t)gr * nc * ldp + j;
-  float acc = 0.0f;
-  for (int cc = 0; cc < nc; ++cc) acc += pp[(size_t)cc * ldp];
-  out[(size_t)gr * ldo + j] = acc;
+  float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
+  if (j < ncols) {
+    const float* pp = part + (size_t)gr * nc * ldp + j;
+    int cc = ty;
+    for (; cc + 12 < nc; cc += 16) {
+      a0 += pp[(size_t)cc * ldp];
+      a1 += pp[(size_t)(cc + 4) * ldp];
+      a2 += pp[(size_t)(cc + 8) * ldp];
+      a3 += pp[(size_t)(cc + 12) * ldp];
+    }
+    for (; cc < nc; cc += 4) a0 += pp[(size_t)cc * ldp];
+  }
+  red[ty][tx] = (a0 + a1) + (a2 + a3);
+  __syncthreads();
+  if (ty == 0 && j < ncols) out[(size_t)gr * ldo + j] = (red[0][tx] + red[1][tx]) + (red[2][tx] + red[3][tx]);
 }
 
 hipError_t reduce_rows(const float* part, int G, int nc, int ncols, int ldp, float* out, int ldo, hipStream_t s) {
   if (G <= 0 || ncols <= 0) return hipSuccess;
-  hipLaunchKernelGGL(reduce_rows_kernel, dim3((ncols + 255) / 256, G), dim3(256), 0, s, part, G, nc, ncols, ldp, out,
+  hipLaunchKernelGGL(reduce_rows_kernel, dim3((ncols + 63) / 64, G), dim3(256), 0, s, part, G, nc, ncols, ldp, out,
                      ldo);
   return hipGetLastError();
 }

@@ -76,3 +76,40 @@ def test_block_backward(name):
     assert set(got) == {k for k, v in oracle(None).items() if v is not None}
     for k in sorted(got):
         parity(f"{name} d{k}", wl.dtype, got[k], lambda rnd, k=k: oracle(rnd)[k])
+
+
+def test_block512_backward_full_width():
+    """The full-size block (hidden 6144, 48/12 heads, intermediate 16384) on the 512^2 shape
+    (1280 tokens, 192 of 256 text tokens valid), every gradient compared in full."""
+    import torch
+    import flow_matching_diffusion_amd as k2
+    from tests.k2_testutil import workload
+    wl = workload("block512")
+    inp = S.block_inputs(wl)
+    temb = temb_for(wl, inp)
+    dh_out = np.random.default_rng(wl.seed + 1).standard_normal(inp["h"].shape).astype(np.float32)
+    dev = device()
+    cfg = k2.block_cfg(wl.dims, wl.dtype)
+    wdev = k2.upload(inp["weights"], wl.dtype, dev)
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+    gi, gtemb, grads = k2.block_backward(cfg, wdev, t(inp["h"]), t(temb.astype(np.float32)), t(inp["position_ids"]),
+                                         t(inp["mask"]), wl.T, t(dh_out))
+    torch.cuda.synchronize()
+    got = dict({k: v.cpu().numpy() for k, v in grads.items()}, h=gi.cpu().numpy(), temb=gtemb.cpu().numpy())
+    del grads, gi, gtemb, wdev
+    cache = {}
+
+    def oracle(rnd):
+        key = rnd is not None
+        if key not in cache:
+            cache.clear()
+            dh, dtemb, gr = O.block_backward(inp["h"], temb, inp["position_ids"], inp["mask"], inp["weights"], wl.dims,
+                                             wl.T, dh_out, rnd=rnd)
+            cache[key] = dict(gr, h=dh, temb=dtemb)
+        return cache[key]
+
+    # exact first for every tensor, then the bf16 emulation (one oracle pass of each at a time)
+    exact = {k: oracle(None)[k] for k in got}
+    for k in sorted(got):
+        ex = exact[k]
+        parity(f"block512 d{k}", wl.dtype, got[k], lambda rnd, k=k, ex=ex: ex if rnd is None else oracle(rnd)[k])
