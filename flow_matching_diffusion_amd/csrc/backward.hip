@@ -14,18 +14,16 @@
 //   norm_bwd       — RMSNorm + modulation backward over whole rows, plus per-chunk column sums
 //                    for the norm weight and the scale / shift gradients
 //   gate_bwd       — sigmoid output gate backward and Delta = rowsum(dO * O) per (row, head)
-//   attn_bwd_dq    — dQ = dS K / sqrt(hd), one wave per 16 queries of one head
+//   attn_bwd_dq    — dQ = dS K / sqrt(hd), one wave per 32 queries of one head
 //   attn_bwd_dkv   — dK = dS^T Q / sqrt(hd) and dV = P^T dO over the query heads of a kv head,
-//                    one wave per 16 keys
+//                    one wave per 32 keys
 //   qknorm_bwd     — the RoPE rotation's transpose, then the per-head RMSNorm backward
 //   reduce_rows    — sums of the per-chunk partials
 //
 // Attention backward, with P = softmax(S), S = Q K^T / sqrt(hd) under the key mask, O = P V:
 // dV = P^T dO, dP = dO V^T, dS = P (dP - Delta), Delta = rowsum(dO * O); P is recomputed from the
 // forward's per-row log-sum-exp. Both kernels use the 16x16 matrix-core block of k2_device.h for
-// bf16 and float32 operands; fragments load straight from memory (no LDS), and the permuted row
-// order of the forward's float32 kernel (accumulator row 4g + r of 16-row block kb is index
-// 8g + 4kb + r) makes the probabilities a lane holds the operand of the next product.
+// bf16 and float32 operands, with the tiles a workgroup's waves share staged in LDS.
 #include "k2_device.h"
 #include "k2_kernels.h"
 
@@ -353,217 +351,431 @@ hipError_t gate_bwd(int dt, const GateBwdArgs& p, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Attention backward, dQ: one wave per (batch row, query head, 16 queries), 4 waves per
-// workgroup on consecutive query blocks. Per 32-key tile (two 16-key blocks kb):
-//   S^T = K Q^T     A: K rows (keys permuted by perm32), B: Q^T (query column, 8 head dims)
-//   P^T = exp2(S^T scale_log2 - lse2[q]) on allowed keys
-//   dP^T = V dO^T   A: V rows (same permutation), B: dO^T
-//   dS^T = P^T (dP^T - Delta[q])
-//   dQ^T += K^T dS^T A: K^T rows (head dim, 8 consecutive keys), B: dS^T from registers
-// Lane l holds query column l % 16; lane group g = l / 16 holds keys 8g .. 8g + 7 of the tile.
+// Attention backward. Two kernels, both on 16x16 matrix-core blocks (bf16 or float32 operands),
+// with the tiles all four waves of a workgroup use staged once in LDS (two stages, one barrier per
+// tile; rows padded by one 16-byte chunk so that 16 rows read at one chunk hit different banks).
+// The permuted row order perm32 (accumulator row 4g + r of 16-row block kb is index 8g + 4kb + r
+// of the 32-wide tile) hands every lane group 8 consecutive keys or queries, which are the k slots
+// of the next product's register operand.
+//
+// dQ: a workgroup is (batch row, kv head, 32 * 4/G queries); wave w takes query head
+// kvh G + w % G and 32 queries (two 16-query column blocks). Per 32-key tile:
+//   S^T = K Q^T      A: K rows from LDS,   B: Q^T (registers, loaded once)
+//   dP^T = V dO^T    A: V rows from LDS,   B: dO^T (registers)
+//   P^T = exp2(S^T scale_log2 - lse2[q]) on allowed keys, dS^T = P^T (dP^T - Delta[q])
+//   dQ^T += K^T dS^T A: K^T rows from LDS, B: dS^T from registers
+// dK, dV: a workgroup is (batch row, kv head, 128 keys); wave w takes 32 keys (two 16-key column
+// blocks) and runs over the G query heads of the kv head and every 32-query tile:
+//   S = Q K^T        A: Q rows from LDS,   B: K^T (registers)
+//   dP = dO V^T      A: dO rows from LDS,  B: V^T (registers)
+//   P, dS as above (lse and Delta of the tile's queries staged in LDS)
+//   dV^T += dO^T P   A: dO^T rows from LDS, B: P from registers
+//   dK^T += Q^T dS   A: Q^T rows from LDS,  B: dS from registers
 // ---------------------------------------------------------------------------------------------
-template <typename T, int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs p, float scale_log2, float scale) {
-  typedef typename FragOf<T>::type Frag;
-  constexpr int NC = HD / 32;  // 32-wide head-dim chunks
-  constexpr int NDB = HD / 16; // 16-row head-dim blocks of dQ^T
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int g = lane >> 4, c = lane & 15;
-  const int b = blockIdx.z, head = blockIdx.y;
-  const int kvh = head / (p.nh / p.nkv);
-  const int L = p.L, T_ = p.T;
-  const int q0 = (blockIdx.x * 4 + wave) * 16;
-  if (q0 >= L) return;  // no barriers in this kernel
-  const int ldq = p.nh * HD, ldk = p.nkv * HD;
-  const int qi = q0 + c;
-  const bool qok = qi < L;
-  const T* qrow = (const T*)p.q + (size_t)(b * L + (qok ? qi : 0)) * ldq + head * HD;
-  const T* drow = (const T*)p.dout + (size_t)(b * L + (qok ? qi : 0)) * ldq + head * HD;
-  Frag qf[NC], df[NC];
+namespace {
+
+// zero the elements at positions >= n of a 16-byte chunk of T (0 <= n)
+template <typename T>
+__device__ __forceinline__ uint4 chunk_keep(uint4 v, int n) {
+  constexpr int E = 16 / sizeof(T);
+  T* e = reinterpret_cast<T*>(&v);
 #pragma unroll
-  for (int kc = 0; kc < NC; ++kc) {
-    qf[kc] = qok ? ld_frag<T>(qrow + 32 * kc + 8 * g) : zero_frag<T>();
-    df[kc] = qok ? ld_frag<T>(drow + 32 * kc + 8 * g) : zero_frag<T>();
-  }
-  const size_t rowstat = ((size_t)b * p.nh + head) * L + (qok ? qi : 0);
-  const float lse = qok ? p.lse[rowstat] : INFINITY;
-  const float delta = qok ? p.delta[rowstat] : 0.0f;
-  f32x4 acc[NDB];
-#pragma unroll
-  for (int db = 0; db < NDB; ++db) acc[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const T* kbase = (const T*)p.k + (size_t)b * L * ldk + kvh * HD;
-  const T* vbase = (const T*)p.v + (size_t)b * L * ldk + kvh * HD;
-  const T* ktbase = (const T*)p.kt + (size_t)(b * p.nkv + kvh) * HD * p.ldt;
-  for (int t0 = 0; t0 < L; t0 += 32) {
-    f32x4 s[2], dp[2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = dp[kb] = f32x4{0.f, 0.f, 0.f, 0.f};
-      const int key = t0 + perm32(kb, c);  // this lane's A row
-      const bool kok = key < L;
-      const T* kr = kbase + (size_t)(kok ? key : 0) * ldk + 8 * g;
-      const T* vr = vbase + (size_t)(kok ? key : 0) * ldk + 8 * g;
-#pragma unroll
-      for (int kc = 0; kc < NC; ++kc) {
-        const Frag ka = kok ? ld_frag<T>(kr + 32 * kc) : zero_frag<T>();
-        const Frag va = kok ? ld_frag<T>(vr + 32 * kc) : zero_frag<T>();
-        s[kb] = mma16(s[kb], ka, qf[kc]);
-        dp[kb] = mma16(dp[kb], va, df[kc]);
-      }
-    }
-    // accumulator row 4g + r of block kb is key t0 + 8g + 4kb + r, column c is query qi
-    float ds[8];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int key = t0 + 8 * g + 4 * kb + r;
-        const bool ok = key < L && (key >= T_ || !p.mask || p.mask[(size_t)b * T_ + key] != 0);
-        const float pr = ok ? exp2f(s[kb][r] * scale_log2 - lse) : 0.0f;
-        ds[4 * kb + r] = pr * (dp[kb][r] - delta);
-      }
-    Frag dsf;
-    pack8(dsf, ds);
-    const int kn = min(8, L - (t0 + 8 * g));  // valid keys among this lane group's 8
-#pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      const T* ktr = ktbase + (size_t)(16 * db + c) * p.ldt + t0 + 8 * g;
-      const Frag ka = kn > 0 ? ld_frag_n<T>(ktr, kn) : zero_frag<T>();
-      acc[db] = mma16(acc[db], ka, dsf);
-    }
-  }
-  // dQ^T block db: lane holds query column c, head dims 16 db + 4 g + r
-  if (qok) {
-    float* out = p.dq + (size_t)(b * L + qi) * p.lddq + head * HD;
-#pragma unroll
-    for (int db = 0; db < NDB; ++db)
-      *(float4*)(out + 16 * db + 4 * g) =
-          make_float4(acc[db][0] * scale, acc[db][1] * scale, acc[db][2] * scale, acc[db][3] * scale);
+  for (int i = 0; i < E; ++i)
+    if (i >= n) e[i] = (T)0.0f;
+  return v;
+}
+
+// 16 bytes at p, or zeros when !ok (p is then not read)
+__device__ __forceinline__ uint4 ld16_or_zero(const void* p, bool ok) {
+  uint4 v = make_uint4(0u, 0u, 0u, 0u);
+  if (ok) v = *(const uint4*)p;
+  return v;
+}
+
+// the 8-element fragment starting at chunk `chunk` of an LDS row
+template <typename T>
+__device__ __forceinline__ typename FragOf<T>::type lds_frag(const uint4* row, int chunk) {
+  if constexpr (sizeof(T) == 2) {
+    return __builtin_bit_cast(bf16x8, row[chunk]);
+  } else {
+    const uint4 a = row[chunk], b = row[chunk + 1];
+    f32x8 f;
+    f[0] = __uint_as_float(a.x); f[1] = __uint_as_float(a.y); f[2] = __uint_as_float(a.z); f[3] = __uint_as_float(a.w);
+    f[4] = __uint_as_float(b.x); f[5] = __uint_as_float(b.y); f[6] = __uint_as_float(b.z); f[7] = __uint_as_float(b.w);
+    return f;
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// Attention backward, dK and dV: one wave per (batch row, kv head, 16 keys), 4 waves per workgroup
-// on consecutive key blocks; each wave runs over the G query heads of its kv head and all query
-// tiles. Per 32-query tile (two 16-query blocks qb):
-//   S = Q K^T       A: Q rows (queries permuted by perm32), B: K^T (key column, 8 head dims)
-//   P = exp2(S scale_log2 - lse2[q]) on allowed keys
-//   dP = dO V^T     A: dO rows (same permutation), B: V^T (key column)
-//   dS = P (dP - Delta[q])
-//   dV^T += dO^T P  A: dO^T rows (head dim, 8 consecutive queries), B: P from registers
-//   dK^T += Q^T dS  A: Q^T rows, B: dS from registers
-// ---------------------------------------------------------------------------------------------
+}  // namespace
+
+template <typename T, int HD, int G>
+__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs p, float scale_log2, float scale) {
+  typedef typename FragOf<T>::type Frag;
+  constexpr int E = 16 / sizeof(T);     // elements per 16-byte chunk
+  constexpr int NC = HD / 32;            // k steps over head_dim
+  constexpr int NDB = HD / 16;           // 16-row head-dim blocks of dQ^T
+  constexpr int RCH = HD / E, RP = RCH + 1;  // chunks per K / V row, row pitch
+  constexpr int TCH = 32 / E, TP = TCH + 1;  // chunks per K^T row (32 keys), row pitch
+  constexpr int NKV = 32 * RCH / 256, NT = HD * TCH / 256;  // chunks per thread per tile
+  constexpr int QW = 32 * (4 / G);       // queries per workgroup
+  static_assert(NKV >= 1 && NT >= 1, "tile / thread mismatch");
+  __shared__ uint4 sK[2][32 * RP], sV[2][32 * RP], sT[2][HD * TP];
+  __shared__ float4 sB[2][8];  // per key of the tile: 0 if it may be attended, -inf if not
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 4, c = lane & 15;
+  const int b = blockIdx.z, kvh = blockIdx.y;
+  const int head = kvh * G + wave % G;
+  const int q0 = blockIdx.x * QW + (wave / G) * 32;
+  const int L = p.L, T_ = p.T;
+  const int ldq = p.nh * HD, ldk = p.nkv * HD;
+  const bool active = q0 < L;  // wave-uniform; an idle wave still loads its share and meets the barriers
+
+  Frag qf[2][NC], df[2][NC];
+  float lse[2], dl[2];
+#pragma unroll
+  for (int qc = 0; qc < 2; ++qc) {
+    const int qi = q0 + 16 * qc + c;
+    const bool ok = qi < L;
+    const size_t row = (size_t)(b * L + (ok ? qi : 0)) * ldq + head * HD + 8 * g;
+#pragma unroll
+    for (int kc = 0; kc < NC; ++kc) {
+      qf[qc][kc] = ok ? ld_frag<T>((const T*)p.q + row + 32 * kc) : zero_frag<T>();
+      df[qc][kc] = ok ? ld_frag<T>((const T*)p.dout + row + 32 * kc) : zero_frag<T>();
+    }
+    const size_t rs = ((size_t)b * p.nh + head) * L + (ok ? qi : 0);
+    lse[qc] = ok ? p.lse[rs] : INFINITY;
+    dl[qc] = ok ? p.delta[rs] : 0.0f;
+  }
+  f32x4 acc[NDB][2];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const T* kg = (const T*)p.k + (size_t)b * L * ldk + kvh * HD;
+  const T* vg = (const T*)p.v + (size_t)b * L * ldk + kvh * HD;
+  const T* tg = (const T*)p.kt + (size_t)(b * p.nkv + kvh) * HD * p.ldt;
+  // two register sets (tile loads run two tiles ahead of the products); macros rather than
+  // lambdas keep both sets in registers
+  uint4 rk[2][NKV], rv[2][NKV], rt[2][NT];
+  float rb[2] = {0.0f, 0.0f};
+#define K2_DQ_GLOAD(RS, t)                                                                         \
+  do {                                                                                             \
+    const int t0_ = 32 * (t);                                                                      \
+    if (tid < 32) {                                                                                \
+      const int key_ = t0_ + tid;                                                                  \
+      rb[RS] = key_ < L && (key_ >= T_ || !p.mask || p.mask[(size_t)b * T_ + key_] != 0) ? 0.0f : -INFINITY; \
+    }                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < NKV; ++i) {                                              \
+      const int ch_ = tid + 256 * i, row_ = ch_ / RCH, cc_ = ch_ % RCH, key_ = t0_ + row_;          \
+      rk[RS][i] = ld16_or_zero(kg + (size_t)(key_ < L ? key_ : 0) * ldk + cc_ * E, key_ < L);      \
+      rv[RS][i] = ld16_or_zero(vg + (size_t)(key_ < L ? key_ : 0) * ldk + cc_ * E, key_ < L);      \
+    }                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                               \
+      const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH, k0_ = t0_ + cc_ * E;          \
+      rt[RS][i] = ld16_or_zero(tg + (size_t)d_ * p.ldt + (k0_ < L ? k0_ : 0), k0_ < L);           \
+      /* the workspace past L holds anything */                                                    \
+      if (k0_ < L && k0_ + E > L) rt[RS][i] = chunk_keep<T>(rt[RS][i], L - k0_);                   \
+    }                                                                                              \
+  } while (0)
+#define K2_DQ_LSTORE(RS, ST)                                                                       \
+  do {                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < NKV; ++i) {                                              \
+      const int ch_ = tid + 256 * i, row_ = ch_ / RCH, cc_ = ch_ % RCH;                             \
+      sK[ST][row_ * RP + cc_] = rk[RS][i];                                                         \
+      sV[ST][row_ * RP + cc_] = rv[RS][i];                                                         \
+    }                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                               \
+      const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH;                               \
+      sT[ST][d_ * TP + cc_] = rt[RS][i];                                                           \
+    }                                                                                              \
+    if (tid < 32) reinterpret_cast<float*>(sB[ST])[tid] = rb[RS];                                  \
+  } while (0)
+
+  const int nt = (L + 31) / 32;
+  K2_DQ_GLOAD(0, 0);
+  if (nt > 1) K2_DQ_GLOAD(1, 1);
+  K2_DQ_LSTORE(0, 0);
+  __syncthreads();
+  // tile t: products from LDS stage t & 1, whose register set is free and takes tile t + 2; the
+  // other register set (tile t + 1) goes to LDS stage (t + 1) & 1 after the products. The loop runs
+  // two tiles per turn so that both register sets are fixed at compile time.
+  auto tile = [&](int t, int st) {
+    if (active) {
+      f32x4 s[2][2], dp[2][2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb][0] = s[kb][1] = dp[kb][0] = dp[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint4* kr = sK[st] + perm32(kb, c) * RP;
+        const uint4* vr = sV[st] + perm32(kb, c) * RP;
+#pragma unroll
+        for (int kc = 0; kc < NC; ++kc) {
+          const Frag ka = lds_frag<T>(kr, (32 * kc + 8 * g) / E);
+          const Frag va = lds_frag<T>(vr, (32 * kc + 8 * g) / E);
+#pragma unroll
+          for (int qc = 0; qc < 2; ++qc) {
+            s[kb][qc] = mma16(s[kb][qc], ka, qf[qc][kc]);
+            dp[kb][qc] = mma16(dp[kb][qc], va, df[qc][kc]);
+          }
+        }
+      }
+      // keys 8g + 4kb + r of the tile: their biases are float4 2g + kb
+      const float4 kbias[2] = {sB[st][2 * g], sB[st][2 * g + 1]};
+      Frag dsf[2];
+#pragma unroll
+      for (int qc = 0; qc < 2; ++qc) {
+        float ds[8];
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const float bias[4] = {kbias[kb].x, kbias[kb].y, kbias[kb].z, kbias[kb].w};
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][qc][r], scale_log2, -lse[qc]) + bias[r]);
+            ds[4 * kb + r] = pr * (dp[kb][qc][r] - dl[qc]);
+          }
+        }
+        pack8(dsf[qc], ds);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const Frag ta = lds_frag<T>(sT[st] + (16 * db + c) * TP, (8 * g) / E);
+        acc[db][0] = mma16(acc[db][0], ta, dsf[0]);
+        acc[db][1] = mma16(acc[db][1], ta, dsf[1]);
+      }
+    }
+  };
+  for (int t = 0; t < nt; t += 2) {
+    if (t + 2 < nt) K2_DQ_GLOAD(0, t + 2);
+    tile(t, 0);
+    if (t + 1 < nt) K2_DQ_LSTORE(1, 1);
+    __syncthreads();
+    if (t + 1 >= nt) break;
+    if (t + 3 < nt) K2_DQ_GLOAD(1, t + 3);
+    tile(t + 1, 1);
+    if (t + 2 < nt) K2_DQ_LSTORE(0, 0);
+    __syncthreads();
+  }
+#undef K2_DQ_GLOAD
+#undef K2_DQ_LSTORE
+  // dQ^T block (db, qc): lane holds query q0 + 16 qc + c, head dims 16 db + 4 g + r
+  if (active) {
+#pragma unroll
+    for (int qc = 0; qc < 2; ++qc) {
+      const int qi = q0 + 16 * qc + c;
+      if (qi >= L) continue;
+      float* out = p.dq + (size_t)(b * L + qi) * p.lddq + head * HD;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db)
+        *(float4*)(out + 16 * db + 4 * g) = make_float4(acc[db][qc][0] * scale, acc[db][qc][1] * scale,
+                                                        acc[db][qc][2] * scale, acc[db][qc][3] * scale);
+    }
+  }
+}
+
 template <typename T, int HD>
 __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float scale_log2, float scale) {
   typedef typename FragOf<T>::type Frag;
+  constexpr int E = 16 / sizeof(T);
   constexpr int NC = HD / 32;
   constexpr int NDB = HD / 16;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int RCH = HD / E, RP = RCH + 1;  // chunks per Q / dO row, row pitch
+  constexpr int TCH = 32 / E, TP = TCH + 1;  // chunks per Q^T / dO^T row (32 queries), row pitch
+  constexpr int NQ = 32 * RCH / 256, NT = HD * TCH / 256;
+  static_assert(NQ >= 1 && NT >= 1, "tile / thread mismatch");
+  __shared__ uint4 sQ[2][32 * RP], sD[2][32 * RP], sQT[2][HD * TP], sDT[2][HD * TP];
+  __shared__ float4 sL[2][8], sDl[2][8];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.z, kvh = blockIdx.y;
   const int G = p.nh / p.nkv;
   const int L = p.L, T_ = p.T;
-  const int k0 = (blockIdx.x * 4 + wave) * 16;
-  if (k0 >= L) return;  // no barriers in this kernel
   const int ldq = p.nh * HD, ldk = p.nkv * HD;
-  const int ki = k0 + c;
-  const bool kok = ki < L && (ki >= T_ || !p.mask || p.mask[(size_t)b * T_ + ki] != 0);
-  const T* krow = (const T*)p.k + (size_t)(b * L + (ki < L ? ki : 0)) * ldk + kvh * HD;
-  const T* vrow = (const T*)p.v + (size_t)(b * L + (ki < L ? ki : 0)) * ldk + kvh * HD;
-  Frag kf[NC], vf[NC];
+  const int k0 = blockIdx.x * 128 + 32 * wave;
+  const bool active = k0 < L;  // wave-uniform
+
+  Frag kf[2][NC], vf[2][NC];
+  bool kok[2];
 #pragma unroll
-  for (int kc = 0; kc < NC; ++kc) {
-    kf[kc] = ki < L ? ld_frag<T>(krow + 32 * kc + 8 * g) : zero_frag<T>();
-    vf[kc] = ki < L ? ld_frag<T>(vrow + 32 * kc + 8 * g) : zero_frag<T>();
-  }
-  f32x4 dk[NDB], dv[NDB];
+  for (int j = 0; j < 2; ++j) {
+    const int ki = k0 + 16 * j + c;
+    kok[j] = ki < L && (ki >= T_ || !p.mask || p.mask[(size_t)b * T_ + ki] != 0);
+    const size_t row = (size_t)(b * L + (ki < L ? ki : 0)) * ldk + kvh * HD + 8 * g;
 #pragma unroll
-  for (int db = 0; db < NDB; ++db) dk[db] = dv[db] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int hh = 0; hh < G; ++hh) {
-    const int head = kvh * G + hh;
-    const T* qbase = (const T*)p.q + (size_t)b * L * ldq + head * HD;
-    const T* dbase = (const T*)p.dout + (size_t)b * L * ldq + head * HD;
-    const T* qtbase = (const T*)p.qt + (size_t)(b * p.nh + head) * HD * p.ldt;
-    const T* dtbase = (const T*)p.dot + (size_t)(b * p.nh + head) * HD * p.ldt;
-    const float* lse = p.lse + ((size_t)b * p.nh + head) * L;
-    const float* dl = p.delta + ((size_t)b * p.nh + head) * L;
-    for (int t0 = 0; t0 < L; t0 += 32) {
-      f32x4 s[2], dp[2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb] = dp[qb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int q = t0 + perm32(qb, c);  // this lane's A row
-        const bool qok = q < L;
-        const T* qr = qbase + (size_t)(qok ? q : 0) * ldq + 8 * g;
-        const T* dr = dbase + (size_t)(qok ? q : 0) * ldq + 8 * g;
-#pragma unroll
-        for (int kc = 0; kc < NC; ++kc) {
-          const Frag qa = qok ? ld_frag<T>(qr + 32 * kc) : zero_frag<T>();
-          const Frag da = qok ? ld_frag<T>(dr + 32 * kc) : zero_frag<T>();
-          s[qb] = mma16(s[qb], qa, kf[kc]);
-          dp[qb] = mma16(dp[qb], da, vf[kc]);
-        }
-      }
-      // accumulator row 4g + r of block qb is query t0 + 8g + 4qb + r, column c is key ki
-      float pv[8], ds[8];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const int q = t0 + 8 * g + 4 * qb + r;
-          float pr = 0.0f, dd = 0.0f;
-          if (kok && q < L) {
-            pr = exp2f(s[qb][r] * scale_log2 - lse[q]);
-            dd = pr * (dp[qb][r] - dl[q]);
-          }
-          pv[4 * qb + r] = pr;
-          ds[4 * qb + r] = dd;
-        }
-      Frag pf, dsf;
-      pack8(pf, pv);
-      pack8(dsf, ds);
-      const int qn = min(8, L - (t0 + 8 * g));  // valid queries among this lane group's 8
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const size_t off = (size_t)(16 * db + c) * p.ldt + t0 + 8 * g;
-        const Frag da = qn > 0 ? ld_frag_n<T>(dtbase + off, qn) : zero_frag<T>();
-        const Frag qa = qn > 0 ? ld_frag_n<T>(qtbase + off, qn) : zero_frag<T>();
-        dv[db] = mma16(dv[db], da, pf);
-        dk[db] = mma16(dk[db], qa, dsf);
-      }
+    for (int kc = 0; kc < NC; ++kc) {
+      kf[j][kc] = ki < L ? ld_frag<T>((const T*)p.k + row + 32 * kc) : zero_frag<T>();
+      vf[j][kc] = ki < L ? ld_frag<T>((const T*)p.v + row + 32 * kc) : zero_frag<T>();
     }
   }
-  // dK^T / dV^T block db: lane holds key column c, head dims 16 db + 4 g + r
-  if (ki < L) {
-    float* ko = p.dk + (size_t)(b * L + ki) * p.lddk + kvh * HD;
-    T* vo = (T*)p.dv + (size_t)(b * L + ki) * p.lddv + kvh * HD;
+  f32x4 dk[NDB][2], dv[NDB][2];
 #pragma unroll
-    for (int db = 0; db < NDB; ++db) {
-      *(float4*)(ko + 16 * db + 4 * g) =
-          make_float4(dk[db][0] * scale, dk[db][1] * scale, dk[db][2] * scale, dk[db][3] * scale);
+  for (int db = 0; db < NDB; ++db) dk[db][0] = dk[db][1] = dv[db][0] = dv[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nt = (L + 31) / 32;
+  // two register sets (tile loads run two tiles ahead of the products); macros rather than
+  // lambdas keep both sets in registers. Tile u: query head kvh G + u / nt, queries 32 (u % nt) ..
+  uint4 rq[2][NQ], rd[2][NQ], rqt[2][NT], rdt[2][NT];
+  float rl[2] = {INFINITY, INFINITY}, rdl[2] = {0.0f, 0.0f};
+#define K2_DKV_GLOAD(RS, u)                                                                        \
+  do {                                                                                             \
+    const int head_ = kvh * G + (u) / nt, t0_ = 32 * ((u) % nt);                                   \
+    const T* qg_ = (const T*)p.q + (size_t)b * L * ldq + head_ * HD;                               \
+    const T* dg_ = (const T*)p.dout + (size_t)b * L * ldq + head_ * HD;                            \
+    const size_t tb_ = (size_t)(b * p.nh + head_) * HD * p.ldt + t0_;                              \
+    _Pragma("unroll") for (int i = 0; i < NQ; ++i) {                                               \
+      const int ch_ = tid + 256 * i, row_ = ch_ / RCH, cc_ = ch_ % RCH, q_ = t0_ + row_;            \
+      rq[RS][i] = ld16_or_zero(qg_ + (size_t)(q_ < L ? q_ : 0) * ldq + cc_ * E, q_ < L);           \
+      rd[RS][i] = ld16_or_zero(dg_ + (size_t)(q_ < L ? q_ : 0) * ldq + cc_ * E, q_ < L);           \
+    }                                                                                              \
+    /* Q^T, dO^T: zero past L (written so by the transposes) */                                    \
+    _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                               \
+      const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH;                               \
+      rqt[RS][i] = ld16_or_zero((const T*)p.qt + tb_ + (size_t)d_ * p.ldt + cc_ * E, true);           \
+      rdt[RS][i] = ld16_or_zero((const T*)p.dot + tb_ + (size_t)d_ * p.ldt + cc_ * E, true);          \
+    }                                                                                              \
+    if (tid < 32) {                                                                                \
+      const int q_ = t0_ + tid;                                                                    \
+      const size_t ri_ = ((size_t)b * p.nh + head_) * L + (q_ < L ? q_ : 0);                       \
+      rl[RS] = q_ < L ? p.lse[ri_] : INFINITY;                                                     \
+      rdl[RS] = q_ < L ? p.delta[ri_] : 0.0f;                                                      \
+    }                                                                                              \
+  } while (0)
+#define K2_DKV_LSTORE(RS, ST)                                                                      \
+  do {                                                                                             \
+    _Pragma("unroll") for (int i = 0; i < NQ; ++i) {                                               \
+      const int ch_ = tid + 256 * i, row_ = ch_ / RCH, cc_ = ch_ % RCH;                             \
+      sQ[ST][row_ * RP + cc_] = rq[RS][i];                                                         \
+      sD[ST][row_ * RP + cc_] = rd[RS][i];                                                         \
+    }                                                                                              \
+    _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                               \
+      const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH;                               \
+      sQT[ST][d_ * TP + cc_] = rqt[RS][i];                                                         \
+      sDT[ST][d_ * TP + cc_] = rdt[RS][i];                                                         \
+    }                                                                                              \
+    if (tid < 32) {                                                                                \
+      reinterpret_cast<float*>(sL[ST])[tid] = rl[RS];                                              \
+      reinterpret_cast<float*>(sDl[ST])[tid] = rdl[RS];                                            \
+    }                                                                                              \
+  } while (0)
+
+  const int nu = G * nt;
+  K2_DKV_GLOAD(0, 0);
+  if (nu > 1) K2_DKV_GLOAD(1, 1);
+  K2_DKV_LSTORE(0, 0);
+  __syncthreads();
+  auto tile = [&](int u, int st) {
+    if (active) {
+      f32x4 s[2][2], dp[2][2];
 #pragma unroll
-      for (int r = 0; r < 4; ++r) vo[16 * db + 4 * g + r] = (T)dv[db][r];
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb][0] = s[qb][1] = dp[qb][0] = dp[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint4* qr = sQ[st] + perm32(qb, c) * RP;
+        const uint4* dr = sD[st] + perm32(qb, c) * RP;
+#pragma unroll
+        for (int kc = 0; kc < NC; ++kc) {
+          const Frag qa = lds_frag<T>(qr, (32 * kc + 8 * g) / E);
+          const Frag da = lds_frag<T>(dr, (32 * kc + 8 * g) / E);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) {
+            s[qb][j] = mma16(s[qb][j], qa, kf[j][kc]);
+            dp[qb][j] = mma16(dp[qb][j], da, vf[j][kc]);
+          }
+        }
+      }
+      // queries 8g + 4qb + r of the tile (lse +inf past L, so their P is 0): float4 2g + qb
+      float ql[8], qd[8];
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        const float4 a = sL[st][2 * g + qb], d4 = sDl[st][2 * g + qb];
+        ql[4 * qb] = a.x; ql[4 * qb + 1] = a.y; ql[4 * qb + 2] = a.z; ql[4 * qb + 3] = a.w;
+        qd[4 * qb] = d4.x; qd[4 * qb + 1] = d4.y; qd[4 * qb + 2] = d4.z; qd[4 * qb + 3] = d4.w;
+      }
+      Frag pf[2], dsf[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        float pv[8], ds[8];
+#pragma unroll
+        for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) {
+            const int e = 4 * qb + r;
+            const float pr = kok[j] ? __builtin_amdgcn_exp2f(fmaf(s[qb][j][r], scale_log2, -ql[e])) : 0.0f;
+            pv[e] = pr;
+            ds[e] = pr * (dp[qb][j][r] - qd[e]);
+          }
+        pack8(pf[j], pv);
+        pack8(dsf[j], ds);
+      }
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        const Frag ta = lds_frag<T>(sDT[st] + (16 * db + c) * TP, (8 * g) / E);
+        const Frag qa = lds_frag<T>(sQT[st] + (16 * db + c) * TP, (8 * g) / E);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+          dv[db][j] = mma16(dv[db][j], ta, pf[j]);
+          dk[db][j] = mma16(dk[db][j], qa, dsf[j]);
+        }
+      }
+    }
+  };
+  for (int u = 0; u < nu; u += 2) {
+    if (u + 2 < nu) K2_DKV_GLOAD(0, u + 2);
+    tile(u, 0);
+    if (u + 1 < nu) K2_DKV_LSTORE(1, 1);
+    __syncthreads();
+    if (u + 1 >= nu) break;
+    if (u + 3 < nu) K2_DKV_GLOAD(1, u + 3);
+    tile(u + 1, 1);
+    if (u + 2 < nu) K2_DKV_LSTORE(0, 0);
+    __syncthreads();
+  }
+#undef K2_DKV_GLOAD
+#undef K2_DKV_LSTORE
+  // dK^T / dV^T block (db, j): lane holds key k0 + 16 j + c, head dims 16 db + 4 g + r
+  if (active) {
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ki = k0 + 16 * j + c;
+      if (ki >= L) continue;
+      float* ko = p.dk + (size_t)(b * L + ki) * p.lddk + kvh * HD;
+      T* vo = (T*)p.dv + (size_t)(b * L + ki) * p.lddv + kvh * HD;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        *(float4*)(ko + 16 * db + 4 * g) = make_float4(dk[db][j][0] * scale, dk[db][j][1] * scale,
+                                                       dk[db][j][2] * scale, dk[db][j][3] * scale);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vo[16 * db + 4 * g + r] = (T)dv[db][j][r];
+      }
     }
   }
 }
 
-template <typename T, int HD>
+template <typename T, int HD, int G>
 static hipError_t attn_bwd_t(const AttnBwdArgs& p, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)HD);
   const float scale_log2 = 1.4426950408889634f * scale;
-  const int nb = (p.L + 63) / 64;
-  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD>), dim3(nb, p.nh, p.B), dim3(256), 0, s, p, scale_log2, scale);
+  constexpr int QW = 32 * (4 / G);
+  hipLaunchKernelGGL((attn_bwd_dq_kernel<T, HD, G>), dim3((p.L + QW - 1) / QW, p.nkv, p.B), dim3(256), 0, s, p,
+                     scale_log2, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, HD>), dim3(nb, p.nkv, p.B), dim3(256), 0, s, p, scale_log2, scale);
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, HD>), dim3((p.L + 127) / 128, p.nkv, p.B), dim3(256), 0, s, p, scale_log2,
+                     scale);
   return hipGetLastError();
+}
+
+template <typename T, int HD>
+static hipError_t attn_bwd_g(const AttnBwdArgs& p, hipStream_t s) {
+  const int G = p.nh / p.nkv;
+  if (G == 4) return attn_bwd_t<T, HD, 4>(p, s);
+  if (G == 2) return attn_bwd_t<T, HD, 2>(p, s);
+  if (G == 1) return attn_bwd_t<T, HD, 1>(p, s);
+  return hipErrorInvalidValue;
 }
 
 hipError_t attention_backward(int dt, const AttnBwdArgs& p, hipStream_t s) {
   if (p.B <= 0 || p.L <= 0) return hipSuccess;
-  if (p.nh % p.nkv || p.ldt < p.L || p.ldt % 8) return hipErrorInvalidValue;
-  if (p.hd == 128) return dt == DT_BF16 ? attn_bwd_t<bf16, 128>(p, s) : attn_bwd_t<float, 128>(p, s);
-  if (p.hd == 64) return dt == DT_BF16 ? attn_bwd_t<bf16, 64>(p, s) : attn_bwd_t<float, 64>(p, s);
+  // the K^T, Q^T and dO^T rows hold 32-key / 32-query tiles up to the last one
+  if (p.nh % p.nkv || p.ldt < (p.L + 31) / 32 * 32 || p.ldt % 8) return hipErrorInvalidValue;
+  if (p.hd == 128) return dt == DT_BF16 ? attn_bwd_g<bf16, 128>(p, s) : attn_bwd_g<float, 128>(p, s);
+  if (p.hd == 64) return dt == DT_BF16 ? attn_bwd_g<bf16, 64>(p, s) : attn_bwd_g<float, 64>(p, s);
   return hipErrorInvalidValue;
 }
 
