@@ -450,6 +450,11 @@ def profile_enable(on: bool = True):
     load().k2_profile_enable(1 if on else 0)
 
 
+def profile_filter(kernel=None):
+    """Record only `kernel` while profiling is enabled (None = every kernel)."""
+    load().k2_profile_filter(None if kernel is None else kernel.encode())
+
+
 def profile_reset():
     load().k2_profile_reset()
 

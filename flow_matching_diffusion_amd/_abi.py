@@ -115,6 +115,7 @@ SIGNATURES = {
                                        c_void_p]),
     "k2_last_error": (c_char_p, []),
     "k2_profile_enable": (None, [c_int]),
+    "k2_profile_filter": (None, [c_char_p]),
     "k2_profile_reset": (None, []),
     "k2_profile_query": (c_int, [c_char_p, POINTER(c_double), POINTER(c_int)]),
 }

@@ -196,7 +196,9 @@ struct EpiPlain : EpiNoStage {
 };
 
 // a = silu(gate) * up; the wave's first WN/2 columns are gate, the last WN/2 the matching up columns.
-template <typename T, int WN>
+// kSave: also store float32 copies of the gate and up projections (the backward's recompute); a
+// compile-time switch, so that the forward's instantiation carries none of that code.
+template <typename T, int WN, bool kSave = false>
 struct EpiSwiglu : EpiNoStage {
   // bf16: each 32-row block of the wave's output (32 rows x WN/2 columns) is written to the wave's
   // LDS area in the accumulator layout, then read back row-major, 8 lanes per 128-byte row, so
@@ -208,14 +210,14 @@ struct EpiSwiglu : EpiNoStage {
   static constexpr int kLdsOutFloats = sizeof(T) == 2 ? 128 * kPitch / 4 : 0;  // 128 rows per wave
   T* a;
   int I;
-  float* gsave;  // optional float32 copies of the gate and up projections (the backward's recompute)
+  float* gsave;  // kSave only
   float* usave;
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
                                         int M, float* stg = nullptr) const {
     static_assert(NJ * (LY::NQ == 1 ? 16 : 32) == WN, "wave width");
     const int cbase = (col0 / WN) * (WN / 2);
-    if (gsave) {
+    if constexpr (kSave) {
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int m = row0 + LY::row(i, lane);
@@ -287,7 +289,9 @@ struct EpiSwiglu : EpiNoStage {
 // Fused QKV + output-gate projection: per head of q and k, RMSNorm over the head's HD columns
 // (weight 1 + w) then rotary embedding on interleaved pairs (2c, 2c+1); v goes out transposed
 // (vt[b][kv head][d][token], leading dimension ldvt); the gate projection goes out as is.
-template <typename T, int HD>
+// kSave: the backward's recompute also stores raw q / k before their norms (float32), v row-major
+// and k after norm and RoPE transposed like vt; compile-time, so the forward carries none of it.
+template <typename T, int HD, bool kSave = false>
 struct EpiQkvg {
   T* q;
   T* k;
@@ -299,9 +303,7 @@ struct EpiQkvg {
   const float* rs;
   int nq, nk, L, ldvt;
   float eps;
-  // extra outputs of the backward's recompute (NULL = none): raw q / k before their norms
-  // (float32), v row-major, k after norm and RoPE transposed like vt
-  float* qraw;
+  float* qraw;  // kSave only
   float* kraw;
   T* vrow;
   T* kt;
@@ -359,7 +361,7 @@ struct EpiQkvg {
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const int m = row0 + LY::row(i, lane);  // every lane sharing this row takes the same branches
-          if (raw && m < M) {
+          if (kSave && m < M) {
 #pragma unroll
             for (int jj = 0; jj < HB; ++jj)
 #pragma unroll
@@ -401,7 +403,7 @@ struct EpiQkvg {
               }
               if (m < M) {
                 st4(dst + (size_t)m * ld + cb + d, y);
-                if (seg == 1 && kt) {  // k transposed per (batch, kv head), like vt
+                if (kSave && seg == 1) {  // k transposed per (batch, kv head), like vt
                   const int b = m / L;
                   T* kp = kt + (size_t)(b * (nk / HD) + cb / HD) * HD * ldvt + (m - b * L);
                   const int dd = cb % HD + d;
@@ -422,7 +424,7 @@ struct EpiQkvg {
           if (m >= M) continue;
           const int b = m / L, l = m - b * L;
           T* base = vt + (size_t)(b * nkvh + kvh) * HD * ldvt + l;
-          if (vrow) {
+          if constexpr (kSave) {
 #pragma unroll
             for (int jj = 0; jj < HB; ++jj)
 #pragma unroll
@@ -979,7 +981,7 @@ static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& 
   }
 }
 
-template <typename T, int HD>
+template <typename T, int HD, bool kSave>
 static hipError_t qkvg_t(const GemmA& a, const QkvgArgs& p, hipStream_t s) {
   BSegs<T> bm;
   bm.p[0] = (const T*)p.wq; bm.p[1] = (const T*)p.wk; bm.p[2] = (const T*)p.wv; bm.p[3] = (const T*)p.wg;
@@ -987,25 +989,25 @@ static hipError_t qkvg_t(const GemmA& a, const QkvgArgs& p, hipStream_t s) {
   bm.start[4] = 2 * p.nq + 2 * p.nk;
   bm.nseg = 4;
   bm.ldb = a.K;
-  EpiQkvg<T, HD> e;
+  EpiQkvg<T, HD, kSave> e;
   e.q = (T*)p.q; e.k = (T*)p.k; e.vt = (T*)p.vt; e.g = (T*)p.g;
   e.wnq = p.wnq; e.wnk = p.wnk; e.rc = p.rope_cos; e.rs = p.rope_sin;
   e.nq = p.nq; e.nk = p.nk; e.L = p.L; e.ldvt = p.ldvt; e.eps = p.eps;
   e.qraw = p.qraw; e.kraw = p.kraw; e.vrow = (T*)p.vrow; e.kt = (T*)p.kt;
-  return launch<T>(a, 2 * p.nq + 2 * p.nk, bm, e, s);
+  return launch<T, BSegs<T>, EpiQkvg<T, HD, kSave>>(a, 2 * p.nq + 2 * p.nk, bm, e, s);
 }
 
-template <typename T>
+template <typename T, bool kSave>
 static hipError_t swiglu_t(const GemmA& a, const SwigluArgs& p, hipStream_t s) {
   constexpr int WN = Cfg<T>::WN;
   constexpr int RSTEP = (Cfg<T>::BM / Cfg<T>::WM) * (Cfg<T>::BN / Cfg<T>::WN) * 64 / 8;
   static_assert((WN / 2) % RSTEP == 0, "a load group must not straddle gate and up rows");
   BSwiglu<T, WN> bm;
   bm.gate = (const T*)p.wgate; bm.up = (const T*)p.wup; bm.I = p.I; bm.ldb = a.K;
-  EpiSwiglu<T, WN> e;
+  EpiSwiglu<T, WN, kSave> e;
   e.a = (T*)p.a; e.I = p.I; e.gsave = p.gsave; e.usave = p.usave;
   const int ntot = ((p.I + WN / 2 - 1) / (WN / 2)) * WN;
-  return launch<T, BSwiglu<T, WN>, EpiSwiglu<T, WN>, false, 2>(a, ntot, bm, e, s);
+  return launch<T, BSwiglu<T, WN>, EpiSwiglu<T, WN, kSave>, false, 2>(a, ntot, bm, e, s);
 }
 
 template <typename T>
@@ -1027,13 +1029,23 @@ static hipError_t plain_t(const GemmA& a, const PlainArgs& p, hipStream_t s) {
   return launch<T, BSegs<T>, EpiPlain<T>, true>(a, p.N, bm, e, s);
 }
 
+template <bool kSave>
+static hipError_t qkvg_d(int dt, const GemmA& a, const QkvgArgs& p, hipStream_t s) {
+  if (p.hd == 128) return dt == DT_BF16 ? qkvg_t<bf16, 128, kSave>(a, p, s) : qkvg_t<float, 128, kSave>(a, p, s);
+  if (p.hd == 64) return dt == DT_BF16 ? qkvg_t<bf16, 64, kSave>(a, p, s) : qkvg_t<float, 64, kSave>(a, p, s);
+  return hipErrorInvalidValue;
+}
+// The saving variants run when all their outputs are given, the plain ones when none is.
 hipError_t gemm_qkvg(int dt, const GemmA& a, const QkvgArgs& p, hipStream_t s) {
-  if (p.hd == 128) return dt == DT_BF16 ? qkvg_t<bf16, 128>(a, p, s) : qkvg_t<float, 128>(a, p, s);
-  if (p.hd == 64) return dt == DT_BF16 ? qkvg_t<bf16, 64>(a, p, s) : qkvg_t<float, 64>(a, p, s);
+  const int n = !!p.qraw + !!p.kraw + !!p.vrow + !!p.kt;
+  if (n == 0) return qkvg_d<false>(dt, a, p, s);
+  if (n == 4) return qkvg_d<true>(dt, a, p, s);
   return hipErrorInvalidValue;
 }
 hipError_t gemm_swiglu(int dt, const GemmA& a, const SwigluArgs& p, hipStream_t s) {
-  return dt == DT_BF16 ? swiglu_t<bf16>(a, p, s) : swiglu_t<float>(a, p, s);
+  if (!p.gsave != !p.usave) return hipErrorInvalidValue;
+  if (p.gsave) return dt == DT_BF16 ? swiglu_t<bf16, true>(a, p, s) : swiglu_t<float, true>(a, p, s);
+  return dt == DT_BF16 ? swiglu_t<bf16, false>(a, p, s) : swiglu_t<float, false>(a, p, s);
 }
 hipError_t gemm_resid(int dt, const GemmA& a, const ResidArgs& p, hipStream_t s) {
   return dt == DT_BF16 ? resid_t<bf16>(a, p, s) : resid_t<float>(a, p, s);

@@ -43,6 +43,7 @@ struct ProfEvent {
 };
 std::mutex g_pm;
 bool g_prof = false;
+std::string g_pfilter;  // record only kernels of this name ("" = all)
 std::vector<ProfEvent> g_pev;
 std::vector<hipEvent_t> g_pool;
 
@@ -62,9 +63,11 @@ int run(const char* name, hipStream_t s, F f) {
   hipEvent_t a = nullptr, b = nullptr;
   if (g_prof) {
     std::lock_guard<std::mutex> lk(g_pm);
-    a = take_event();
-    b = take_event();
-    if (a) (void)hipEventRecord(a, s);
+    if (g_pfilter.empty() || g_pfilter == name) {
+      a = take_event();
+      b = take_event();
+      if (a) (void)hipEventRecord(a, s);
+    }
   }
   hipError_t e = f();
   if (a && b) {
@@ -1226,6 +1229,11 @@ const char* k2_last_error(void) { return g_err.c_str(); }
 void k2_profile_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_pm);
   g_prof = enable != 0;
+}
+
+void k2_profile_filter(const char* kernel) {
+  std::lock_guard<std::mutex> lk(g_pm);
+  g_pfilter = kernel ? kernel : "";
 }
 
 void k2_profile_reset(void) {

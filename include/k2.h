@@ -352,6 +352,9 @@ const char* k2_last_error(void);
    "gemm_plain", "time_embed", "layer_compress", "convert", "fill", "cfg_euler", ...). Returns K2_OK or
    K2_ERR_HIP. */
 void k2_profile_enable(int enable);
+/* Record only kernels named `kernel` while enabled (NULL or "" = every kernel): two events per
+   launch of that kernel alone, so that timing one kernel disturbs the rest as little as possible. */
+void k2_profile_filter(const char* kernel);
 void k2_profile_reset(void);
 int k2_profile_query(const char* kernel, double* total_ms, int* launches);
 
