@@ -265,6 +265,7 @@ def main():
             bc_step()
         torch.cuda.synchronize()
         k2.profile_reset()
+        k2.profile_filter("attention")  # events around the attention launches only
         k2.profile_enable(True)
         t0 = time.perf_counter()
         for _ in range(args.steps):
@@ -272,6 +273,7 @@ def main():
         torch.cuda.synchronize()
         bc_ms = (time.perf_counter() - t0) * 1e3 / args.steps
         k2.profile_enable(False)
+        k2.profile_filter(None)
         a_tot, a_n = k2.profile_query("attention")
         bc_attn = 4 * d.head_dim * d.num_heads * allowed
         bc_flops = block_flops(d, B, L, [0] * B) + bc_attn
@@ -302,13 +304,16 @@ def main():
         del res
         torch.cuda.synchronize()
         nb = max(1, args.steps // 4)
-        k2.profile_reset()
-        k2.profile_enable(True)
         t0 = time.perf_counter()
         for _ in range(nb):
             res = bwd_step()
         torch.cuda.synchronize()
         b_ms = (time.perf_counter() - t0) * 1e3 / nb
+        # per-kernel split: one more step with events around every launch (not timed above)
+        k2.profile_reset()
+        k2.profile_enable(True)
+        res = bwd_step()
+        torch.cuda.synchronize()
         k2.profile_enable(False)
         gemm_f = block_flops(d, B, L, [0] * B)
         b_flops = 3 * gemm_f + 3 * attn_flops
@@ -316,8 +321,8 @@ def main():
         for name in ("gemm_qkvg", "attention", "gemm_swiglu", "gemm_plain", "transpose", "attention_bwd", "norm_bwd",
                      "gated_grad", "swiglu_bwd", "gate_bwd", "qknorm_bwd", "modnorm", "gated_add", "reduce_rows"):
             tot, n = k2.profile_query(name)
-            if n:
-                bk[name] = {"ms_per_call": round(tot / nb, 3), "launches": n // nb}
+            if n:  # all launches of that kernel in the step
+                bk[name] = {"ms_per_step": round(tot, 3), "launches": n}
         result["backward"] = {"ms_per_step": round(b_ms, 3), "tflops": round(b_flops / (b_ms * 1e-3) / 1e12, 1),
                               "algorithmic_tflop": round(b_flops / 1e12, 3), "kernels": bk,
                               "note": "forward recompute + all gradients; TFLOP = 3x forward GEMMs + 3x attention"}

@@ -345,112 +345,141 @@ struct EpiQkvg {
                                         int M, float* stg = nullptr) const {
     constexpr int BS = LY::NQ == 1 ? 16 : 32;
     constexpr int HB = HD / BS;  // column blocks per head
-    static_assert(NJ % HB == 0, "a wave covers whole heads");
     const int ntot = 2 * nq + 2 * nk;
+    if constexpr (NJ % HB != 0) {
+      // A wave narrower than a head (the 256x128 halves of a last partial round): the host runs
+      // such tiles only over v and gate columns (tail_allowed), which need no per-head reduction.
 #pragma unroll
-    for (int h0 = 0; h0 < NJ; h0 += HB) {
-      const int nh0 = col0 + h0 * BS;  // first column of this head (wave-uniform)
-      if (nh0 >= ntot) break;
-      const int seg = nh0 < nq ? 0 : nh0 < nq + nk ? 1 : nh0 < nq + 2 * nk ? 2 : 3;
-      if (seg <= 1) {
-        T* dst = seg == 0 ? q : k;
-        const int ld = seg == 0 ? nq : nk;
-        const int cb = seg == 0 ? nh0 : nh0 - nq;
-        const float* wn = seg == 0 ? wnq : wnk;
-        float* const raw = seg == 0 ? qraw : kraw;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const int m = row0 + LY::row(i, lane);  // every lane sharing this row takes the same branches
-          if (kSave && m < M) {
-#pragma unroll
-            for (int jj = 0; jj < HB; ++jj)
-#pragma unroll
-              for (int qq = 0; qq < LY::NQ; ++qq)
-                st4(raw + (size_t)m * ld + cb + LY::col(jj, qq, lane), quad(acc[i][h0 + jj], qq));
-          }
-          float ss = 0.0f;
-#pragma unroll
-          for (int jj = 0; jj < HB; ++jj)
-#pragma unroll
-            for (int r = 0; r < 4 * LY::NQ; ++r) ss += acc[i][h0 + jj][r] * acc[i][h0 + jj][r];
-          ss = LY::rowsum(ss);
-          const float inv = rsqrtf(ss * (1.0f / HD) + eps);
-          const int l = (m < M ? m : 0) % L;
-#pragma unroll
-          for (int jj = 0; jj < HB; ++jj)
-#pragma unroll
-            for (int qq = 0; qq < LY::NQ; ++qq) {
-              const int d = LY::col(jj, qq, lane);
-              float4 y = quad(acc[i][h0 + jj], qq);
-              if (stg) {  // staged multipliers and (cos, sin) pairs
-                const float4 w4 = ld4(stg + (seg == 0 ? 0 : HD) + d);
-                y.x *= inv * w4.x; y.y *= inv * w4.y; y.z *= inv * w4.z; y.w *= inv * w4.w;
-                if (rc) {
-                  const float4 cs = ld4(stg + 2 * HD + ((row0 & 255) + LY::row(i, lane)) * kStgRow + d);
-                  y = make_float4(y.x * cs.x - y.y * cs.y, y.y * cs.x + y.x * cs.y,
-                                  y.z * cs.z - y.w * cs.w, y.w * cs.z + y.z * cs.w);
-                }
-              } else {
-                const float4 w4 = wn ? ld4(wn + d) : make_float4(0.f, 0.f, 0.f, 0.f);
-                y.x *= inv * (1.0f + w4.x); y.y *= inv * (1.0f + w4.y);
-                y.z *= inv * (1.0f + w4.z); y.w *= inv * (1.0f + w4.w);
-                if (rc) {
-                  const float2 c2 = *reinterpret_cast<const float2*>(rc + (size_t)l * (HD / 2) + (d >> 1));
-                  const float2 s2 = *reinterpret_cast<const float2*>(rs + (size_t)l * (HD / 2) + (d >> 1));
-                  y = make_float4(y.x * c2.x - y.y * s2.x, y.y * c2.x + y.x * s2.x,
-                                  y.z * c2.y - y.w * s2.y, y.w * c2.y + y.z * s2.y);
-                }
-              }
-              if (m < M) {
-                st4(dst + (size_t)m * ld + cb + d, y);
-                if (kSave && seg == 1) {  // k transposed per (batch, kv head), like vt
-                  const int b = m / L;
-                  T* kp = kt + (size_t)(b * (nk / HD) + cb / HD) * HD * ldvt + (m - b * L);
-                  const int dd = cb % HD + d;
-                  kp[(size_t)dd * ldvt] = to_t<T>(y.x);
-                  kp[(size_t)(dd + 1) * ldvt] = to_t<T>(y.y);
-                  kp[(size_t)(dd + 2) * ldvt] = to_t<T>(y.z);
-                  kp[(size_t)(dd + 3) * ldvt] = to_t<T>(y.w);
-                }
-              }
-            }
-        }
-      } else if (seg == 2) {
-        const int kvh = (nh0 - nq - nk) / HD;
-        const int nkvh = nk / HD;
+      for (int j = 0; j < NJ; ++j) {
+        const int nb = col0 + j * BS;  // first column of this block (wave-uniform)
+        if (nb >= ntot) break;
 #pragma unroll
         for (int i = 0; i < MI; ++i) {
           const int m = row0 + LY::row(i, lane);
           if (m >= M) continue;
-          const int b = m / L, l = m - b * L;
-          T* base = vt + (size_t)(b * nkvh + kvh) * HD * ldvt + l;
-          if constexpr (kSave) {
-#pragma unroll
-            for (int jj = 0; jj < HB; ++jj)
-#pragma unroll
-              for (int qq = 0; qq < LY::NQ; ++qq)
-                st4(vrow + (size_t)m * nk + (nh0 - nq - nk) + LY::col(jj, qq, lane), quad(acc[i][h0 + jj], qq));
-          }
-#pragma unroll
-          for (int jj = 0; jj < HB; ++jj)
+          if (nb < nq + 2 * nk) {
+            const int b = m / L, l = m - b * L;
 #pragma unroll
             for (int qq = 0; qq < LY::NQ; ++qq) {
-              const int d = LY::col(jj, qq, lane);
+              const int vc = col0 - nq - nk + LY::col(j, qq, lane);  // column within v
+              if constexpr (kSave) st4(vrow + (size_t)m * nk + vc, quad(acc[i][j], qq));
+              T* base = vt + (size_t)(b * (nk / HD) + vc / HD) * HD * ldvt + l;
 #pragma unroll
-              for (int e = 0; e < 4; ++e) base[(size_t)(d + e) * ldvt] = to_t<T>(acc[i][h0 + jj][4 * qq + e]);
+              for (int e = 0; e < 4; ++e) base[(size_t)(vc % HD + e) * ldvt] = to_t<T>(acc[i][j][4 * qq + e]);
             }
-        }
-      } else {
-        const int cb = nh0 - nq - 2 * nk;
-#pragma unroll
-        for (int i = 0; i < MI; ++i) {
-          const int m = row0 + LY::row(i, lane);
-          if (m >= M) continue;
-#pragma unroll
-          for (int jj = 0; jj < HB; ++jj)
+          } else {
 #pragma unroll
             for (int qq = 0; qq < LY::NQ; ++qq)
-              st4(g + (size_t)m * nq + cb + LY::col(jj, qq, lane), quad(acc[i][h0 + jj], qq));
+              st4(g + (size_t)m * nq + (col0 - nq - 2 * nk) + LY::col(j, qq, lane), quad(acc[i][j], qq));
+          }
+        }
+      }
+    } else {
+#pragma unroll
+      for (int h0 = 0; h0 < NJ; h0 += HB) {
+        const int nh0 = col0 + h0 * BS;  // first column of this head (wave-uniform)
+        if (nh0 >= ntot) break;
+        const int seg = nh0 < nq ? 0 : nh0 < nq + nk ? 1 : nh0 < nq + 2 * nk ? 2 : 3;
+        if (seg <= 1) {
+          T* dst = seg == 0 ? q : k;
+          const int ld = seg == 0 ? nq : nk;
+          const int cb = seg == 0 ? nh0 : nh0 - nq;
+          const float* wn = seg == 0 ? wnq : wnk;
+          float* const raw = seg == 0 ? qraw : kraw;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            const int m = row0 + LY::row(i, lane);  // every lane sharing this row takes the same branches
+            if (kSave && m < M) {
+#pragma unroll
+              for (int jj = 0; jj < HB; ++jj)
+#pragma unroll
+                for (int qq = 0; qq < LY::NQ; ++qq)
+                  st4(raw + (size_t)m * ld + cb + LY::col(jj, qq, lane), quad(acc[i][h0 + jj], qq));
+            }
+            float ss = 0.0f;
+#pragma unroll
+            for (int jj = 0; jj < HB; ++jj)
+#pragma unroll
+              for (int r = 0; r < 4 * LY::NQ; ++r) ss += acc[i][h0 + jj][r] * acc[i][h0 + jj][r];
+            ss = LY::rowsum(ss);
+            const float inv = rsqrtf(ss * (1.0f / HD) + eps);
+            const int l = (m < M ? m : 0) % L;
+#pragma unroll
+            for (int jj = 0; jj < HB; ++jj)
+#pragma unroll
+              for (int qq = 0; qq < LY::NQ; ++qq) {
+                const int d = LY::col(jj, qq, lane);
+                float4 y = quad(acc[i][h0 + jj], qq);
+                if (stg) {  // staged multipliers and (cos, sin) pairs
+                  const float4 w4 = ld4(stg + (seg == 0 ? 0 : HD) + d);
+                  y.x *= inv * w4.x; y.y *= inv * w4.y; y.z *= inv * w4.z; y.w *= inv * w4.w;
+                  if (rc) {
+                    const float4 cs = ld4(stg + 2 * HD + ((row0 & 255) + LY::row(i, lane)) * kStgRow + d);
+                    y = make_float4(y.x * cs.x - y.y * cs.y, y.y * cs.x + y.x * cs.y,
+                                    y.z * cs.z - y.w * cs.w, y.w * cs.z + y.z * cs.w);
+                  }
+                } else {
+                  const float4 w4 = wn ? ld4(wn + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+                  y.x *= inv * (1.0f + w4.x); y.y *= inv * (1.0f + w4.y);
+                  y.z *= inv * (1.0f + w4.z); y.w *= inv * (1.0f + w4.w);
+                  if (rc) {
+                    const float2 c2 = *reinterpret_cast<const float2*>(rc + (size_t)l * (HD / 2) + (d >> 1));
+                    const float2 s2 = *reinterpret_cast<const float2*>(rs + (size_t)l * (HD / 2) + (d >> 1));
+                    y = make_float4(y.x * c2.x - y.y * s2.x, y.y * c2.x + y.x * s2.x,
+                                    y.z * c2.y - y.w * s2.y, y.w * c2.y + y.z * s2.y);
+                  }
+                }
+                if (m < M) {
+                  st4(dst + (size_t)m * ld + cb + d, y);
+                  if (kSave && seg == 1) {  // k transposed per (batch, kv head), like vt
+                    const int b = m / L;
+                    T* kp = kt + (size_t)(b * (nk / HD) + cb / HD) * HD * ldvt + (m - b * L);
+                    const int dd = cb % HD + d;
+                    kp[(size_t)dd * ldvt] = to_t<T>(y.x);
+                    kp[(size_t)(dd + 1) * ldvt] = to_t<T>(y.y);
+                    kp[(size_t)(dd + 2) * ldvt] = to_t<T>(y.z);
+                    kp[(size_t)(dd + 3) * ldvt] = to_t<T>(y.w);
+                  }
+                }
+              }
+          }
+        } else if (seg == 2) {
+          const int kvh = (nh0 - nq - nk) / HD;
+          const int nkvh = nk / HD;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            const int m = row0 + LY::row(i, lane);
+            if (m >= M) continue;
+            const int b = m / L, l = m - b * L;
+            T* base = vt + (size_t)(b * nkvh + kvh) * HD * ldvt + l;
+            if constexpr (kSave) {
+#pragma unroll
+              for (int jj = 0; jj < HB; ++jj)
+#pragma unroll
+                for (int qq = 0; qq < LY::NQ; ++qq)
+                  st4(vrow + (size_t)m * nk + (nh0 - nq - nk) + LY::col(jj, qq, lane), quad(acc[i][h0 + jj], qq));
+            }
+#pragma unroll
+            for (int jj = 0; jj < HB; ++jj)
+#pragma unroll
+              for (int qq = 0; qq < LY::NQ; ++qq) {
+                const int d = LY::col(jj, qq, lane);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) base[(size_t)(d + e) * ldvt] = to_t<T>(acc[i][h0 + jj][4 * qq + e]);
+              }
+          }
+        } else {
+          const int cb = nh0 - nq - 2 * nk;
+#pragma unroll
+          for (int i = 0; i < MI; ++i) {
+            const int m = row0 + LY::row(i, lane);
+            if (m >= M) continue;
+#pragma unroll
+            for (int jj = 0; jj < HB; ++jj)
+#pragma unroll
+              for (int qq = 0; qq < LY::NQ; ++qq)
+                st4(g + (size_t)m * nq + cb + LY::col(jj, qq, lane), quad(acc[i][h0 + jj], qq));
+          }
         }
       }
     }
@@ -931,6 +960,13 @@ static int compute_units() {
 // projection unchanged; 3 + 2 loses on SwiGLU. The weights' slabs are the ones that arrive late:
 // each super-column starts on weight rows that are still in HBM.
 constexpr int kRingA = 2, kRingB = 3;
+
+// Whether the 256x128 halves of a last partial round may start at column n0 (every epilogue but
+// the QKV+gate one takes any column; that one takes only v and gate columns in narrow waves).
+template <class Epi>
+static bool tail_allowed(const Epi&, int) { return true; }
+template <typename T, int HD, bool kSave>
+static bool tail_allowed(const EpiQkvg<T, HD, kSave>& e, int n0) { return n0 >= e.nq + e.nk; }
 template <typename T, class C, class BMap, class Epi, int SPREAD, bool KFULL, bool TAIL>
 static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap, const Epi& epi, hipStream_t s) {
   constexpr int NT = (C::BM / C::WM) * (C::BN / C::WN) * 64;
@@ -940,7 +976,14 @@ static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap
     if constexpr (TAIL) {
       const int ncu = compute_units();
       const int tail = tiles % ncu;
-      if (tiles > ncu && tail > 0 && 2 * tail <= ncu) {
+      bool ok = tiles > ncu && tail > 0 && 2 * tail <= ncu;
+      const int tiles_m = (a.M + 255) / 256, tiles_n = (Ntot + 255) / 256;
+      for (int u = tiles - tail; ok && u < tiles; ++u) {
+        int tm, tn;
+        tile_coords(u, tiles_m, tiles_n, scn, tm, tn);
+        ok = tail_allowed(epi, tn * 256);
+      }
+      if (ok) {
         nmain = tiles - tail;
         grid = nmain + 2 * tail;
       }
@@ -994,7 +1037,7 @@ static hipError_t qkvg_t(const GemmA& a, const QkvgArgs& p, hipStream_t s) {
   e.wnq = p.wnq; e.wnk = p.wnk; e.rc = p.rope_cos; e.rs = p.rope_sin;
   e.nq = p.nq; e.nk = p.nk; e.L = p.L; e.ldvt = p.ldvt; e.eps = p.eps;
   e.qraw = p.qraw; e.kraw = p.kraw; e.vrow = (T*)p.vrow; e.kt = (T*)p.kt;
-  return launch<T, BSegs<T>, EpiQkvg<T, HD, kSave>>(a, 2 * p.nq + 2 * p.nk, bm, e, s);
+  return launch<T, BSegs<T>, EpiQkvg<T, HD, kSave>, true>(a, 2 * p.nq + 2 * p.nk, bm, e, s);
 }
 
 template <typename T, bool kSave>
