@@ -100,14 +100,73 @@ __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs p) {
   }
 }
 
+// The same transpose in 16-byte chunks of EPC elements, for operands whose row strides, batch
+// offsets, C and Rpad are multiples of EPC and whose base pointers are 16-byte aligned. A lane
+// loads one chunk of a source row (8 lanes cover a 128-byte row segment) and stores one chunk of a
+// destination row, gathered from EPC consecutive source rows of the LDS tile. Chunk cc of tile row
+// r sits at cc ^ ((r / EPC) % CPR): the chunk writes fill whole rows, and the gathers of a lane
+// group (EPC rows apart, one column) fall in distinct banks. The element-wise kernel above moved 2
+// or 4 bytes per lane per memory instruction and ran at about 2.5 TB/s.
+template <typename T>
+__global__ void __launch_bounds__(256) transpose_vec_kernel(TransposeArgs p) {
+  constexpr int EPC = 16 / sizeof(T);  // elements per chunk
+  constexpr int CPR = 64 / EPC;        // chunks per 64-element tile row
+  __shared__ uint4 tile[64 * CPR];
+  const int z = blockIdx.z;
+  const T* src = (const T*)p.src + (size_t)(z / p.zdiv) * p.sz0 + (size_t)(z % p.zdiv) * p.sz1;
+  T* dst = (T*)p.dst + (size_t)(z / p.zdiv) * p.dz0 + (size_t)(z % p.zdiv) * p.dz1;
+  const int r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
+#pragma unroll
+  for (int k = 0; k < 64 * CPR / 256; ++k) {
+    const int u = threadIdx.x + 256 * k;
+    const int row = u / CPR, cc = u % CPR;
+    const int r = r0 + row, c = c0 + cc * EPC;
+    uint4 v = make_uint4(0u, 0u, 0u, 0u);
+    if (r < p.R && c < p.C) v = *(const uint4*)(src + (size_t)r * p.lds + c);
+    tile[row * CPR + (cc ^ ((row / EPC) % CPR))] = v;
+  }
+  __syncthreads();
+  const T* t = reinterpret_cast<const T*>(tile);
+#pragma unroll
+  for (int k = 0; k < 64 * CPR / 256; ++k) {
+    const int u = threadIdx.x + 256 * k;
+    const int col = u / CPR, rc = u % CPR;  // destination row c0 + col, source rows r0 + EPC rc ..
+    const int c = c0 + col, r = r0 + rc * EPC;
+    if (c < p.C && r < p.Rpad) {
+      union { uint4 v; T e[EPC]; } out;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const int row = rc * EPC + e;  // (row / EPC) % CPR == rc
+        out.e[e] = t[(row * CPR + ((col / EPC) ^ rc)) * EPC + col % EPC];
+      }
+      *(uint4*)(dst + (size_t)c * p.ldd + r) = out.v;
+    }
+  }
+}
+
+template <typename T>
+static bool transpose_vec_ok(const TransposeArgs& p) {
+  constexpr size_t EPC = 16 / sizeof(T);
+  const bool aligned = ((uintptr_t)p.src % 16 == 0) && ((uintptr_t)p.dst % 16 == 0);
+  return aligned && p.C % EPC == 0 && p.Rpad % EPC == 0 && p.lds % EPC == 0 && p.ldd % EPC == 0 &&
+         p.sz0 % EPC == 0 && p.sz1 % EPC == 0 && p.dz0 % EPC == 0 && p.dz1 % EPC == 0;
+}
+
 hipError_t transpose(int dt, const TransposeArgs& p, hipStream_t s) {
   if (p.R <= 0 || p.C <= 0 || p.Z <= 0) return hipSuccess;
   if (p.Rpad < p.R || p.ldd < p.Rpad || p.zdiv <= 0) return hipErrorInvalidValue;
   dim3 grid((p.C + 63) / 64, (p.Rpad + 63) / 64, p.Z);
-  if (dt == DT_BF16)
-    hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s, p);
-  else
-    hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, p);
+  if (dt == DT_BF16) {
+    if (transpose_vec_ok<bf16>(p))
+      hipLaunchKernelGGL(transpose_vec_kernel<bf16>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(transpose_kernel<bf16>, grid, dim3(256), 0, s, p);
+  } else {
+    if (transpose_vec_ok<float>(p))
+      hipLaunchKernelGGL(transpose_vec_kernel<float>, grid, dim3(256), 0, s, p);
+    else
+      hipLaunchKernelGGL(transpose_kernel<float>, grid, dim3(256), 0, s, p);
+  }
   return hipGetLastError();
 }
 
@@ -210,9 +269,14 @@ hipError_t swiglu_bwd(int dt, const float* da, const float* gt, const float* up,
 // batch row each): pw = sum dn x r, psc = sum dout n, psh = sum dout. One workgroup per chunk,
 // each row held in registers (H <= 8192).
 // ---------------------------------------------------------------------------------------------
-__global__ void __launch_bounds__(256) norm_bwd_kernel(NormBwdArgs p) {
-  constexpr int CACHE = 8;
-  __shared__ float red[2][4];
+// NT threads per workgroup and CACHE float4s of each row per thread (H <= 4 NT CACHE): 1024 x 2
+// for the 6144-wide rows of the block, 108 registers, 16 waves per compute unit. The residual
+// gradient is loaded with x and dout, so a row's three reads are in flight together; the two row
+// sums go through LDS slots that alternate between rows, one barrier per row.
+template <int NT, int CACHE>
+__global__ void __launch_bounds__(NT) norm_bwd_kernel(NormBwdArgs p) {
+  constexpr int NW = NT / 64;  // waves
+  __shared__ float red[2][2][NW];
   const int chunk = blockIdx.x;
   const int b = chunk / p.ncb, c = chunk - b * p.ncb;
   const int l0 = c * p.RC, l1 = min(p.L, l0 + p.RC);
@@ -223,7 +287,7 @@ __global__ void __launch_bounds__(256) norm_bwd_kernel(NormBwdArgs p) {
 #pragma unroll
   for (int u = 0; u < CACHE; ++u) {
     pw[u] = psc[u] = psh[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-    const int cc = tid + u * 256;
+    const int cc = tid + u * NT;
     mw[u] = ms[u] = make_float4(1.f, 1.f, 1.f, 1.f);
     if (cc < H4) {
       if (w4) { const float4 t = w4[cc]; mw[u] = make_float4(1.f + t.x, 1.f + t.y, 1.f + t.z, 1.f + t.w); }
@@ -234,41 +298,50 @@ __global__ void __launch_bounds__(256) norm_bwd_kernel(NormBwdArgs p) {
     const size_t row = (size_t)b * p.L + l;
     const float4* x4 = (const float4*)(p.x + row * p.H);
     const float4* d4 = (const float4*)(p.dout + row * p.H);
-    float4 xv[CACHE], dv[CACHE];
-    float ss = 0.0f, dot = 0.0f;
+    const float4* res4 = p.dres ? (const float4*)(p.dres + row * p.H) : nullptr;
+    float4 xv[CACHE], dv[CACHE], rv[CACHE];
 #pragma unroll
     for (int u = 0; u < CACHE; ++u) {
-      const int cc = tid + u * 256;
-      xv[u] = dv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+      const int cc = tid + u * NT;
+      xv[u] = dv[u] = rv[u] = make_float4(0.f, 0.f, 0.f, 0.f);
       if (cc < H4) {
         xv[u] = x4[cc];
         dv[u] = d4[cc];
-        ss += xv[u].x * xv[u].x + xv[u].y * xv[u].y + xv[u].z * xv[u].z + xv[u].w * xv[u].w;
-        // g = dout (1 + sc) (1 + w)
-        dot += dv[u].x * ms[u].x * mw[u].x * xv[u].x + dv[u].y * ms[u].y * mw[u].y * xv[u].y +
-               dv[u].z * ms[u].z * mw[u].z * xv[u].z + dv[u].w * ms[u].w * mw[u].w * xv[u].w;
+        if (res4) rv[u] = res4[cc];
       }
+    }
+    float ss = 0.0f, dot = 0.0f;
+#pragma unroll
+    for (int u = 0; u < CACHE; ++u) {
+      ss += xv[u].x * xv[u].x + xv[u].y * xv[u].y + xv[u].z * xv[u].z + xv[u].w * xv[u].w;
+      // g = dout (1 + sc) (1 + w)
+      dot += dv[u].x * ms[u].x * mw[u].x * xv[u].x + dv[u].y * ms[u].y * mw[u].y * xv[u].y +
+             dv[u].z * ms[u].z * mw[u].z * xv[u].z + dv[u].w * ms[u].w * mw[u].w * xv[u].w;
     }
     ss = wave_sum(ss);
     dot = wave_sum(dot);
+    const int slot = (l - l0) & 1;  // a row's slots are rewritten two rows later, after a barrier
     if ((tid & 63) == 0) {
-      red[0][wv] = ss;
-      red[1][wv] = dot;
+      red[slot][0][wv] = ss;
+      red[slot][1][wv] = dot;
     }
     __syncthreads();
-    ss = red[0][0] + red[0][1] + red[0][2] + red[0][3];
-    dot = red[1][0] + red[1][1] + red[1][2] + red[1][3];
-    __syncthreads();
+    ss = 0.0f;
+    dot = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NW; ++k) {
+      ss += red[slot][0][k];
+      dot += red[slot][1][k];
+    }
     const float r = rsqrtf(ss / (float)p.H + p.eps);
     const float k3 = r * r * r * dot / (float)p.H;
-    const float4* res4 = p.dres ? (const float4*)(p.dres + row * p.H) : nullptr;
     float4* o4 = (float4*)(p.dx + row * p.H);
 #pragma unroll
     for (int u = 0; u < CACHE; ++u) {
-      const int cc = tid + u * 256;
+      const int cc = tid + u * NT;
       if (cc >= H4) continue;
       const float4 x = xv[u], d = dv[u], m1 = ms[u], m2 = mw[u];
-      float4 res = res4 ? res4[cc] : make_float4(0.f, 0.f, 0.f, 0.f);
+      float4 res = rv[u];
       res.x += r * d.x * m1.x * m2.x - x.x * k3;
       res.y += r * d.y * m1.y * m2.y - x.y * k3;
       res.z += r * d.z * m1.z * m2.z - x.z * k3;
@@ -283,7 +356,7 @@ __global__ void __launch_bounds__(256) norm_bwd_kernel(NormBwdArgs p) {
   }
 #pragma unroll
   for (int u = 0; u < CACHE; ++u) {
-    const int cc = tid + u * 256;
+    const int cc = tid + u * NT;
     if (cc >= H4) continue;
     if (p.pw) ((float4*)(p.pw + (size_t)chunk * p.H))[cc] = pw[u];
     if (p.psc) ((float4*)(p.psc + (size_t)chunk * p.H))[cc] = psc[u];
@@ -293,8 +366,15 @@ __global__ void __launch_bounds__(256) norm_bwd_kernel(NormBwdArgs p) {
 
 hipError_t norm_bwd(const NormBwdArgs& p, hipStream_t s) {
   if (p.B <= 0 || p.L <= 0) return hipSuccess;
-  if (p.H % 4 || p.H > 8 * 256 * 4 || p.RC <= 0 || p.ncb != (p.L + p.RC - 1) / p.RC) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(norm_bwd_kernel, dim3(p.B * p.ncb), dim3(256), 0, s, p);
+  if (p.H % 4 || p.H > 4 * 1024 * 2 || p.RC <= 0 || p.ncb != (p.L + p.RC - 1) / p.RC) return hipErrorInvalidValue;
+  const int H4 = p.H / 4;
+  const dim3 grid(p.B * p.ncb);
+  if (H4 <= 512)
+    hipLaunchKernelGGL((norm_bwd_kernel<512, 1>), grid, dim3(512), 0, s, p);
+  else if (H4 <= 1024)
+    hipLaunchKernelGGL((norm_bwd_kernel<512, 2>), grid, dim3(512), 0, s, p);
+  else
+    hipLaunchKernelGGL((norm_bwd_kernel<1024, 2>), grid, dim3(1024), 0, s, p);
   return hipGetLastError();
 }
 
