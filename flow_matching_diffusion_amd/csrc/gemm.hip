@@ -217,7 +217,44 @@ struct EpiSwiglu : EpiNoStage {
                                         int M, float* stg = nullptr) const {
     static_assert(NJ * (LY::NQ == 1 ? 16 : 32) == WN, "wave width");
     const int cbase = (col0 / WN) * (WN / 2);
-    if constexpr (kSave) {
+    if constexpr (kSave && kLdsOut) {
+      // float32 saves through the same LDS area: per 32-row block, gate then up (32 rows x WN/2
+      // floats each, rows padded to kSavePitch bytes), read back 16 lanes per 256-byte row so that
+      // every store writes whole lines. Stored from the accumulator layout, each 16-byte store hit a
+      // different row. The bf16 staging below reuses the area: a wave's LDS accesses complete in
+      // order, so its writes come after these reads.
+      constexpr int kSavePitch = 272;
+      static_assert(2 * 32 * kSavePitch <= 4 * kLdsOutFloats, "save staging");
+      char* const sm = reinterpret_cast<char*>(stg);
+      const int hi = lane >> 5, r = lane & 31;   // writer: row r, columns 8 q + 4 hi of each block
+      const int rr = lane >> 4, ch = lane & 15;  // reader: row 4 k + rr, columns 4 ch .. 4 ch + 3
+      const int c = cbase + 4 * ch;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {  // gate, up
+          char* const blk = sm + h * 32 * kSavePitch;
+#pragma unroll
+          for (int j = 0; j < NJ / 2; ++j)
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              *reinterpret_cast<float4*>(blk + r * kSavePitch + 128 * j + 32 * q + 16 * hi) =
+                  quad(acc[i][j + h * (NJ / 2)], q);
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const char* const blk = sm + h * 32 * kSavePitch;
+          float* const dst = h ? usave : gsave;
+#pragma unroll
+          for (int k = 0; k < 8; ++k) {
+            const int row = 4 * k + rr;
+            const float4 v = *reinterpret_cast<const float4*>(blk + row * kSavePitch + 16 * ch);
+            const int m = row0 + 32 * i + row;
+            if (m < M && c < I) st4(dst + (size_t)m * I + c, v);  // I is a multiple of 4
+          }
+        }
+      }
+    } else if constexpr (kSave) {
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
         const int m = row0 + LY::row(i, lane);
