@@ -651,7 +651,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs p, float s
 }
 
 template <typename T, int HD>
-__global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float scale_log2, float scale) {
+__global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float scale_log2, float scale, int nsplit) {
   typedef typename FragOf<T>::type Frag;
   constexpr int E = 16 / sizeof(T);
   constexpr int NC = HD / 32;
@@ -668,7 +668,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
   const int G = p.nh / p.nkv;
   const int L = p.L, T_ = p.T;
   const int ldq = p.nh * HD, ldk = p.nkv * HD;
-  const int k0 = blockIdx.x * 128 + 32 * wave;
+  // nsplit workgroups share a key block, each taking a contiguous share of its query tiles
+  const int split = blockIdx.x % nsplit;
+  const int k0 = (blockIdx.x / nsplit) * 128 + 32 * wave;
   const bool active = k0 < L;  // wave-uniform
 
   Frag kf[2][NC], vf[2][NC];
@@ -736,8 +738,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
   } while (0)
 
   const int nu = G * nt;
-  K2_DKV_GLOAD(0, 0);
-  if (nu > 1) K2_DKV_GLOAD(1, 1);
+  const int u0 = split * nu / nsplit, u1 = (split + 1) * nu / nsplit;  // u0 < u1: nu >= nsplit
+  K2_DKV_GLOAD(0, u0);
+  if (u0 + 1 < u1) K2_DKV_GLOAD(1, u0 + 1);
   K2_DKV_LSTORE(0, 0);
   __syncthreads();
   auto tile = [&](int u, int st) {
@@ -795,21 +798,36 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
       }
     }
   };
-  for (int u = 0; u < nu; u += 2) {
-    if (u + 2 < nu) K2_DKV_GLOAD(0, u + 2);
+  for (int u = u0; u < u1; u += 2) {
+    if (u + 2 < u1) K2_DKV_GLOAD(0, u + 2);
     tile(u, 0);
-    if (u + 1 < nu) K2_DKV_LSTORE(1, 1);
+    if (u + 1 < u1) K2_DKV_LSTORE(1, 1);
     __syncthreads();
-    if (u + 1 >= nu) break;
-    if (u + 3 < nu) K2_DKV_GLOAD(1, u + 3);
+    if (u + 1 >= u1) break;
+    if (u + 3 < u1) K2_DKV_GLOAD(1, u + 3);
     tile(u + 1, 1);
-    if (u + 2 < nu) K2_DKV_LSTORE(0, 0);
+    if (u + 2 < u1) K2_DKV_LSTORE(0, 0);
     __syncthreads();
   }
 #undef K2_DKV_GLOAD
 #undef K2_DKV_LSTORE
   // dK^T / dV^T block (db, j): lane holds key k0 + 16 j + c, head dims 16 db + 4 g + r
-  if (active) {
+  if (active && nsplit > 1) {  // partial sums: dK into plane 2 split, dV into plane 2 split + 1
+    const size_t plane = (size_t)p.B * L * ldk;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int ki = k0 + 16 * j + c;
+      if (ki >= L) continue;
+      float* ko = p.dkv_part + 2 * split * plane + (size_t)(b * L + ki) * ldk + kvh * HD;
+      float* vo = ko + plane;
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
+        *(float4*)(ko + 16 * db + 4 * g) = make_float4(dk[db][j][0] * scale, dk[db][j][1] * scale,
+                                                       dk[db][j][2] * scale, dk[db][j][3] * scale);
+        *(float4*)(vo + 16 * db + 4 * g) = make_float4(dv[db][j][0], dv[db][j][1], dv[db][j][2], dv[db][j][3]);
+      }
+    }
+  } else if (active) {
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int ki = k0 + 16 * j + c;
@@ -827,6 +845,33 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
   }
 }
 
+// dK = dK part 0 + dK part 1 (float32), dV = T(dV part 0 + dV part 1); planes of `plane` floats in
+// the order dK0, dV0, dK1, dV1; rows of nk columns.
+template <typename T>
+__global__ void __launch_bounds__(256) dkv_combine_kernel(const float* __restrict__ part, size_t n4, int nk, size_t plane,
+                                                          float* __restrict__ dk, int lddk, T* __restrict__ dv, int lddv) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (size_t)gridDim.x * 256) {
+    const size_t e = 4 * i, m = e / nk, c = e - m * nk;
+    const float4 k0 = *(const float4*)(part + e), v0 = *(const float4*)(part + plane + e);
+    const float4 k1 = *(const float4*)(part + 2 * plane + e), v1 = *(const float4*)(part + 3 * plane + e);
+    *(float4*)(dk + m * lddk + c) = make_float4(k0.x + k1.x, k0.y + k1.y, k0.z + k1.z, k0.w + k1.w);
+    T* o = dv + m * lddv + c;
+    o[0] = (T)(v0.x + v1.x);
+    o[1] = (T)(v0.y + v1.y);
+    o[2] = (T)(v0.z + v1.z);
+    o[3] = (T)(v0.w + v1.w);
+  }
+}
+
+// compute units of the current device
+static int cu_count() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    return 256;
+  return n;
+}
+
 template <typename T, int HD, int G>
 static hipError_t attn_bwd_t(const AttnBwdArgs& p, hipStream_t s) {
   const float scale = 1.0f / sqrtf((float)HD);
@@ -836,8 +881,22 @@ static hipError_t attn_bwd_t(const AttnBwdArgs& p, hipStream_t s) {
                      scale_log2, scale);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, HD>), dim3((p.L + 127) / 128, p.nkv, p.B), dim3(256), 0, s, p, scale_log2,
-                     scale);
+  // dK/dV: one workgroup per compute unit (registers). Its grid of key blocks often leaves the last
+  // round part-empty (block1024: 864 workgroups = 3.4 rounds of 256); splitting each key block's
+  // query tiles over two workgroups fills the rounds better (6.75 of 7) at the price of one pass
+  // summing the float32 partials.
+  const int W = (p.L + 127) / 128 * p.nkv * p.B, ncu = cu_count();
+  const double e1 = (double)W / ((double)((W + ncu - 1) / ncu) * ncu);
+  const double e2 = (double)(2 * W) / ((double)((2 * W + ncu - 1) / ncu) * ncu);
+  const int nsplit = p.dkv_part && G * ((p.L + 31) / 32) >= 2 && e2 > e1 ? 2 : 1;
+  hipLaunchKernelGGL((attn_bwd_dkv_kernel<T, HD>), dim3((p.L + 127) / 128 * nsplit, p.nkv, p.B), dim3(256), 0, s, p,
+                     scale_log2, scale, nsplit);
+  e = hipGetLastError();
+  if (e != hipSuccess || nsplit == 1) return e;
+  const size_t n4 = (size_t)p.B * p.L * p.nkv * HD / 4;
+  const int blocks = (int)((n4 + 255) / 256 < 8192 ? (n4 + 255) / 256 : 8192);
+  hipLaunchKernelGGL(dkv_combine_kernel<T>, dim3(blocks), dim3(256), 0, s, (const float*)p.dkv_part, n4,
+                     p.nkv * HD, (size_t)p.B * p.L * p.nkv * HD, p.dk, p.lddk, (T*)p.dv, p.lddv);
   return hipGetLastError();
 }
 

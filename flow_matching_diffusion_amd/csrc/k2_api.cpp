@@ -512,8 +512,8 @@ struct BwdLayout {
   // recompute
   size_t mod, rope, x1, qraw, kraw, q, k, vt, vrow, kt, g, o, og, lse, y, h1, x2, gt, u, a, z;
   // backward
-  size_t dh1, dz, dzT, aT, da, dgu, dguT, x2T, dx2, dy, dyT, ogT, dog, dO, dOT, qT, delta, dq, dk, dqkvg, dqkvgT,
-      x1T, dx1, wT, dmod;
+  size_t dh1, dz, dzT, aT, da, dgu, dguT, x2T, dx2, dy, dyT, ogT, dog, dO, dOT, qT, delta, dq, dk, dkv_part, dqkvg,
+      dqkvgT, x1T, dx1, wT, dmod;
   size_t p_qg, p_pg, p_w2, p_qs, p_qt, p_w1, p_ps, p_pt, p_wq, p_wk;
   int ldvt, Mp, ncb, qk_blocks;
   size_t total;
@@ -576,6 +576,7 @@ BwdLayout bwd_layout(const k2_block_cfg* c, int B, int T, int N) {
   l.delta = take((size_t)B * c->num_heads * L * f4);
   l.dq = take(M * nq * f4);
   l.dk = take(M * nk * f4);
+  l.dkv_part = take(4 * M * nk * f4);  // dK / dV partial sums of a split dK/dV pass
   l.dqkvg = take(M * nall * es);
   l.dqkvgT = take(nall * Mp * es);
   l.x1T = take(H * Mp * es);
@@ -744,6 +745,7 @@ int block_backward_run(const k2_block_cfg* c, const k2_block_weights* w, int B, 
   ab.dout = P(l.dO); ab.lse = (float*)P(l.lse); ab.delta = (float*)P(l.delta); ab.mask = mask;
   ab.dq = (float*)P(l.dq); ab.lddq = nq; ab.dk = (float*)P(l.dk); ab.lddk = nk;
   ab.dv = at(P(l.dqkvg), (size_t)(nq + nk) * dt_size(dt)); ab.lddv = nall;
+  ab.dkv_part = (float*)P(l.dkv_part);
   ab.B = B; ab.L = L; ab.T = T; ab.nh = nh; ab.nkv = nkv; ab.hd = hd; ab.ldt = ldt;
   K2_RUN("attention_bwd", s, attention_backward(dt, ab, s));
   // q / k: RoPE transpose + head norm backward into the q and k columns of dqkvg

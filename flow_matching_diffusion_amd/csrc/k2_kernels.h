@@ -151,6 +151,9 @@ struct AttnBwdArgs {
   float* dq; int lddq;                           // (M, .) float32, head h at column h*hd
   float* dk; int lddk;                           // (M, .) float32, kv head at column kvh*hd
   void* dv; int lddv;                            // (M, .) operand dtype
+  // (4, M, nkv*hd) float32 scratch: the dK / dV partial sums when the dK/dV pass splits each key
+  // block's query tiles over two workgroups (NULL: never split)
+  float* dkv_part;
   int B, L, T, nh, nkv, hd, ldt;
 };
 hipError_t attention_backward(int dt, const AttnBwdArgs& p, hipStream_t s);
