@@ -578,40 +578,50 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs p, float s
   // tile t: products from LDS stage t & 1, whose register set is free and takes tile t + 2; the
   // other register set (tile t + 1) goes to LDS stage (t + 1) & 1 after the products. The loop runs
   // two tiles per turn so that both register sets are fixed at compile time.
+  // One tile: S = Q K^T; dP = dO V^T with P = exp2(S log2(e)/sqrt(hd) - lse + key bias) computed
+  // alongside (the matrix cores have independent work during the exponentials); dS = P (dP - Delta);
+  // dQ += dS K.
   auto tile = [&](int t, int st) {
     if (active) {
+      // keys 8g + 4kb + r of the tile: their biases are float4 2g + kb
+      const float4 kbias[2] = {sB[st][2 * g], sB[st][2 * g + 1]};
       f32x4 s[2][2], dp[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        s[kb][0] = s[kb][1] = dp[kb][0] = dp[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
         const uint4* kr = sK[st] + perm32(kb, c) * RP;
-        const uint4* vr = sV[st] + perm32(kb, c) * RP;
 #pragma unroll
         for (int kc = 0; kc < NC; ++kc) {
           const Frag ka = lds_frag<T>(kr, (32 * kc + 8 * g) / E);
+#pragma unroll
+          for (int qc = 0; qc < 2; ++qc) s[kb][qc] = mma16(s[kb][qc], ka, qf[qc][kc]);
+        }
+      }
+      float pv[2][8];  // P for query block qc: entry 4 kb + r
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        dp[kb][0] = dp[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint4* vr = sV[st] + perm32(kb, c) * RP;
+        const float bias[4] = {kbias[kb].x, kbias[kb].y, kbias[kb].z, kbias[kb].w};
+#pragma unroll
+        for (int kc = 0; kc < NC; ++kc) {
           const Frag va = lds_frag<T>(vr, (32 * kc + 8 * g) / E);
 #pragma unroll
-          for (int qc = 0; qc < 2; ++qc) {
-            s[kb][qc] = mma16(s[kb][qc], ka, qf[qc][kc]);
-            dp[kb][qc] = mma16(dp[kb][qc], va, df[qc][kc]);
+          for (int qc = 0; qc < 2; ++qc) dp[kb][qc] = mma16(dp[kb][qc], va, df[qc][kc]);
+          // 8 / NC exponentials of key block kb per step
+#pragma unroll
+          for (int x = kc * 8 / NC; x < (kc + 1) * 8 / NC; ++x) {
+            const int qc = x >> 2, r = x & 3;
+            pv[qc][4 * kb + r] = __builtin_amdgcn_exp2f(fmaf(s[kb][qc][r], scale_log2, -lse[qc]) + bias[r]);
           }
         }
       }
-      // keys 8g + 4kb + r of the tile: their biases are float4 2g + kb
-      const float4 kbias[2] = {sB[st][2 * g], sB[st][2 * g + 1]};
       Frag dsf[2];
 #pragma unroll
       for (int qc = 0; qc < 2; ++qc) {
         float ds[8];
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const float bias[4] = {kbias[kb].x, kbias[kb].y, kbias[kb].z, kbias[kb].w};
-#pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const float pr = __builtin_amdgcn_exp2f(fmaf(s[kb][qc][r], scale_log2, -lse[qc]) + bias[r]);
-            ds[4 * kb + r] = pr * (dp[kb][qc][r] - dl[qc]);
-          }
-        }
+        for (int e = 0; e < 8; ++e) ds[e] = pv[qc][e] * (dp[e >> 2][qc][e & 3] - dl[qc]);
         pack8(dsf[qc], ds);
       }
 #pragma unroll
@@ -743,25 +753,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
   if (u0 + 1 < u1) K2_DKV_GLOAD(1, u0 + 1);
   K2_DKV_LSTORE(0, 0);
   __syncthreads();
+  // One tile, ordered so that the matrix cores have independent work during the vector steps:
+  // S = K Q^T; dP = V dO^T with P = exp2(S log2(e)/sqrt(hd) - lse) computed alongside; dV += P^T dO
+  // with dS = P (dP - Delta) computed alongside; dK += dS^T Q.
   auto tile = [&](int u, int st) {
     if (active) {
-      f32x4 s[2][2], dp[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb][0] = s[qb][1] = dp[qb][0] = dp[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint4* qr = sQ[st] + perm32(qb, c) * RP;
-        const uint4* dr = sD[st] + perm32(qb, c) * RP;
-#pragma unroll
-        for (int kc = 0; kc < NC; ++kc) {
-          const Frag qa = lds_frag<T>(qr, (32 * kc + 8 * g) / E);
-          const Frag da = lds_frag<T>(dr, (32 * kc + 8 * g) / E);
-#pragma unroll
-          for (int j = 0; j < 2; ++j) {
-            s[qb][j] = mma16(s[qb][j], qa, kf[j][kc]);
-            dp[qb][j] = mma16(dp[qb][j], da, vf[j][kc]);
-          }
-        }
-      }
       // queries 8g + 4qb + r of the tile (lse +inf past L, so their P is 0): float4 2g + qb
       float ql[8], qd[8];
 #pragma unroll
@@ -770,31 +766,59 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
         ql[4 * qb] = a.x; ql[4 * qb + 1] = a.y; ql[4 * qb + 2] = a.z; ql[4 * qb + 3] = a.w;
         qd[4 * qb] = d4.x; qd[4 * qb + 1] = d4.y; qd[4 * qb + 2] = d4.z; qd[4 * qb + 3] = d4.w;
       }
-      Frag pf[2], dsf[2];
+      f32x4 s[2][2], dp[2][2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        float pv[8], ds[8];
+      for (int qb = 0; qb < 2; ++qb) {
+        s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint4* qr = sQ[st] + perm32(qb, c) * RP;
 #pragma unroll
-        for (int qb = 0; qb < 2; ++qb)
+        for (int kc = 0; kc < NC; ++kc) {
+          const Frag qa = lds_frag<T>(qr, (32 * kc + 8 * g) / E);
 #pragma unroll
-          for (int r = 0; r < 4; ++r) {
-            const int e = 4 * qb + r;
-            const float pr = kok[j] ? __builtin_amdgcn_exp2f(fmaf(s[qb][j][r], scale_log2, -ql[e])) : 0.0f;
-            pv[e] = pr;
-            ds[e] = pr * (dp[qb][j][r] - qd[e]);
-          }
-        pack8(pf[j], pv);
-        pack8(dsf[j], ds);
+          for (int j = 0; j < 2; ++j) s[qb][j] = mma16(s[qb][j], qa, kf[j][kc]);
+        }
       }
+      float pv[2][8];  // P of key block j: entry 4 qb + r
+#pragma unroll
+      for (int qb = 0; qb < 2; ++qb) {
+        dp[qb][0] = dp[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const uint4* dr = sD[st] + perm32(qb, c) * RP;
+#pragma unroll
+        for (int kc = 0; kc < NC; ++kc) {
+          const Frag da = lds_frag<T>(dr, (32 * kc + 8 * g) / E);
+#pragma unroll
+          for (int j = 0; j < 2; ++j) dp[qb][j] = mma16(dp[qb][j], da, vf[j][kc]);
+          // 8 / NC exponentials of query block qb per step
+#pragma unroll
+          for (int x = kc * 8 / NC; x < (kc + 1) * 8 / NC; ++x) {
+            const int j = x >> 2, r = x & 3;
+            pv[j][4 * qb + r] = kok[j] ? __builtin_amdgcn_exp2f(fmaf(s[qb][j][r], scale_log2, -ql[4 * qb + r])) : 0.0f;
+          }
+        }
+      }
+      Frag pf[2], dsf[2];
+      pack8(pf[0], pv[0]);
+      pack8(pf[1], pv[1]);
+      float dsv[2][8];
 #pragma unroll
       for (int db = 0; db < NDB; ++db) {
         const Frag ta = lds_frag<T>(sDT[st] + (16 * db + c) * TP, (8 * g) / E);
+#pragma unroll
+        for (int j = 0; j < 2; ++j) dv[db][j] = mma16(dv[db][j], ta, pf[j]);
+        // 16 / NDB entries of dS per step
+#pragma unroll
+        for (int x = db * 16 / NDB; x < (db + 1) * 16 / NDB; ++x) {
+          const int j = x >> 3, e = x & 7;
+          dsv[j][e] = pv[j][e] * (dp[e >> 2][j][e & 3] - qd[e]);
+        }
+      }
+      pack8(dsf[0], dsv[0]);
+      pack8(dsf[1], dsv[1]);
+#pragma unroll
+      for (int db = 0; db < NDB; ++db) {
         const Frag qa = lds_frag<T>(sQT[st] + (16 * db + c) * TP, (8 * g) / E);
 #pragma unroll
-        for (int j = 0; j < 2; ++j) {
-          dv[db][j] = mma16(dv[db][j], ta, pf[j]);
-          dk[db][j] = mma16(dk[db][j], qa, dsf[j]);
-        }
+        for (int j = 0; j < 2; ++j) dk[db][j] = mma16(dk[db][j], qa, dsf[j]);
       }
     }
   };
