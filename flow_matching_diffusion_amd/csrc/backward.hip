@@ -489,7 +489,7 @@ __device__ __forceinline__ typename FragOf<T>::type lds_frag(const uint4* row, i
 }  // namespace
 
 template <typename T, int HD, int G>
-__global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs p, float scale_log2, float scale) {
+__global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, float scale_log2, float scale) {
   typedef typename FragOf<T>::type Frag;
   constexpr int E = 16 / sizeof(T);     // elements per 16-byte chunk
   constexpr int NC = HD / 32;            // k steps over head_dim
@@ -533,10 +533,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs p, float s
   const T* kg = (const T*)p.k + (size_t)b * L * ldk + kvh * HD;
   const T* vg = (const T*)p.v + (size_t)b * L * ldk + kvh * HD;
   const T* tg = (const T*)p.kt + (size_t)(b * p.nkv + kvh) * HD * p.ldt;
-  // two register sets (tile loads run two tiles ahead of the products); macros rather than
-  // lambdas keep both sets in registers
-  uint4 rk[2][NKV], rv[2][NKV], rt[2][NT];
-  float rb[2] = {0.0f, 0.0f};
+  // one register set: tile loads run one tile ahead of the products, which keeps the kernel within
+  // 256 registers, so two waves share a SIMD and one's exponentials overlap the other's matrix-core
+  // work (two sets, two tiles ahead, took 324 registers and one wave per SIMD: 2.9 ms at block1024)
+  uint4 rk[1][NKV], rv[1][NKV], rt[1][NT];
+  float rb[1] = {0.0f};
 #define K2_DQ_GLOAD(RS, t)                                                                         \
   do {                                                                                             \
     const int t0_ = 32 * (t);                                                                      \
@@ -572,12 +573,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs p, float s
 
   const int nt = (L + 31) / 32;
   K2_DQ_GLOAD(0, 0);
-  if (nt > 1) K2_DQ_GLOAD(1, 1);
   K2_DQ_LSTORE(0, 0);
   __syncthreads();
-  // tile t: products from LDS stage t & 1, whose register set is free and takes tile t + 2; the
-  // other register set (tile t + 1) goes to LDS stage (t + 1) & 1 after the products. The loop runs
-  // two tiles per turn so that both register sets are fixed at compile time.
+  // Tile t: its loads for tile t + 1 are issued first, then the products from LDS stage t & 1, then
+  // tile t + 1 goes to stage (t + 1) & 1 (read by tile t - 1 before the last barrier). The loop runs
+  // two tiles per turn so that the stages are fixed at compile time.
   // One tile: S = Q K^T; dP = dO V^T with P = exp2(S log2(e)/sqrt(hd) - lse + key bias) computed
   // alongside (the matrix cores have independent work during the exponentials); dS = P (dP - Delta);
   // dQ += dS K.
@@ -633,12 +633,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dq_kernel(AttnBwdArgs p, float s
     }
   };
   for (int t = 0; t < nt; t += 2) {
-    if (t + 2 < nt) K2_DQ_GLOAD(0, t + 2);
+    if (t + 1 < nt) K2_DQ_GLOAD(0, t + 1);
     tile(t, 0);
-    if (t + 1 < nt) K2_DQ_LSTORE(1, 1);
+    if (t + 1 < nt) K2_DQ_LSTORE(0, 1);
     __syncthreads();
     if (t + 1 >= nt) break;
-    if (t + 3 < nt) K2_DQ_GLOAD(1, t + 3);
+    if (t + 2 < nt) K2_DQ_GLOAD(0, t + 2);
     tile(t + 1, 1);
     if (t + 2 < nt) K2_DQ_LSTORE(0, 0);
     __syncthreads();
