@@ -513,7 +513,7 @@ struct BwdLayout {
   size_t mod, rope, x1, qraw, kraw, q, k, vt, vrow, kt, g, o, og, lse, y, h1, x2, gt, u, a, z;
   // backward
   size_t dh1, dz, dzT, aT, da, dgu, dguT, x2T, dx2, dy, dyT, ogT, dog, dO, dOT, qT, delta, dq, dk, dkv_part, dqkvg,
-      dqkvgT, x1T, dx1, wT, dmod;
+      dqkvgT, x1T, dx1, wT, dmod, dwqkvg;
   size_t p_qg, p_pg, p_w2, p_qs, p_qt, p_w1, p_ps, p_pt, p_wq, p_wk;
   int ldvt, Mp, ncb, qk_blocks;
   size_t total;
@@ -583,6 +583,7 @@ BwdLayout bwd_layout(const k2_block_cfg* c, int B, int T, int N) {
   l.dx1 = take(M * H * f4);
   l.wT = take(std::max({I * H, H * 2 * I, nq * H, H * nall}) * es);
   l.dmod = take((size_t)B * 6 * H * f4);
+  l.dwqkvg = take(nall * H * f4);  // [dWq; dWk; dWv; dWg] before they are copied out
   l.p_qg = take(chunks * H * f4);
   l.p_pg = take(chunks * H * f4);
   l.p_w2 = take(chunks * H * f4);
@@ -706,10 +707,19 @@ int block_backward_run(const k2_block_cfg* c, const k2_block_weights* w, int B, 
       K2_RUN("gemm_plain", s, gemm_f32out(dt, at(P(l.dguT), (size_t)I * Mp * dt_size(dt)), Mp, I, Mp, P(l.x2T), H,
                                           gr->ff_up, H, s));
   }
-  // dx2 = dgt Wgate + du Wup = [dgt du] [Wgate; Wup]
-  K2_RUN("transpose", s, transpose2d(dt, w->ff_gate, I, H, H, P(l.wT), I, 2 * I, s));
-  K2_RUN("transpose", s, transpose2d(dt, w->ff_up, I, H, H, at(P(l.wT), (size_t)I * dt_size(dt)), I, 2 * I, s));
-  K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dgu), 2 * I, M, 2 * I, P(l.wT), H, (float*)P(l.dx2), H, s));
+  // dx2 = dgt Wgate + du Wup, as two products over K = I: the second adds onto the first through
+  // the residual epilogue (no gate). One product over K = 2I read 403 MB of weights, more than the
+  // last-level cache holds (3.55 ms); each half's 201 MB stays there.
+  void* const wTu = at(P(l.wT), (size_t)H * I * dt_size(dt));
+  K2_RUN("transpose", s, transpose2d(dt, w->ff_gate, I, H, H, P(l.wT), I, I, s));
+  K2_RUN("transpose", s, transpose2d(dt, w->ff_up, I, H, H, wTu, I, I, s));
+  K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dgu), 2 * I, M, I, P(l.wT), H, (float*)P(l.dx2), H, s));
+  {
+    ResidArgs ra = {};
+    ra.w = wTu; ra.N = H; ra.hin = (float*)P(l.dx2); ra.hout = (float*)P(l.dx2); ra.gate = nullptr;
+    ra.gate_stride = 0; ra.L = M;
+    K2_RUN("gemm_plain", s, gemm_resid(dt, GemmA{at(P(l.dgu), (size_t)I * dt_size(dt)), 2 * I, M, I}, ra, s));
+  }
   // norm 2: dh1 = dh2 + its input gradient; partials for norm2_w, dqs, dqt
   NormBwdArgs nb = {};
   nb.x = h1; nb.dout = (float*)P(l.dx2); nb.dres = dh2; nb.dx = (float*)P(l.dh1);
@@ -761,12 +771,18 @@ int block_backward_run(const k2_block_cfg* c, const k2_block_weights* w, int B, 
   if (gr->to_q || gr->to_k || gr->to_v || gr->to_gate) {
     K2_RUN("transpose", s, transpose2d(dt, P(l.dqkvg), M, nall, nall, P(l.dqkvgT), Mp, Mp, s));
     K2_RUN("transpose", s, transpose2d(dt, P(l.x1), M, H, H, P(l.x1T), Mp, Mp, s));
+    // one product for the four weights (their 1536-row k and v parts alone filled 144 of the 256
+    // compute units), then each requested part copied out
     float* outs[4] = {gr->to_q, gr->to_k, gr->to_v, gr->to_gate};
     const int start[4] = {0, nq, nq + nk, nq + 2 * nk}, rows[4] = {nq, nk, nk, nq};
+    float* const dwall = (float*)P(l.dwqkvg);
+    K2_RUN("gemm_plain", s, gemm_f32out(dt, P(l.dqkvgT), Mp, nall, Mp, P(l.x1T), H, dwall, H, s));
     for (int i = 0; i < 4; ++i)
-      if (outs[i])
-        K2_RUN("gemm_plain", s, gemm_f32out(dt, at(P(l.dqkvgT), (size_t)start[i] * Mp * dt_size(dt)), Mp, rows[i], Mp,
-                                            P(l.x1T), H, outs[i], H, s));
+      if (outs[i]) {
+        const hipError_t e = hipMemcpyAsync(outs[i], dwall + (size_t)start[i] * H, (size_t)rows[i] * H * sizeof(float),
+                                            hipMemcpyDeviceToDevice, s);
+        if (e != hipSuccess) return fail(K2_ERR_HIP, "weight gradient copy: %s", hipGetErrorString(e));
+      }
   }
   // dx1 = dqkvg [Wq; Wk; Wv; Wg]
   {
