@@ -195,6 +195,59 @@ struct EpiPlain : EpiNoStage {
   }
 };
 
+// acc into a float32 output only (row m to row m, no bias): the backward's products. bf16: each
+// 32-row block of the wave's output (32 rows x WN floats, rows padded to kPitchF) goes through the
+// wave's LDS area in the accumulator layout and is read back row-major, 32 lanes per 512-byte row
+// segment, so that every store writes whole lines. Stored from the accumulator layout, each
+// 16-byte store hit a different row, and the weight-gradient products wrote up to twice their bytes.
+template <typename T>
+struct EpiPlainF32 : EpiNoStage {
+  static constexpr bool kLdsOut = sizeof(T) == 2;
+  static constexpr int kPitchF = 132;  // floats per staged row: 128 + 4 of padding
+  static constexpr int kLdsOutFloats = sizeof(T) == 2 ? 32 * kPitchF : 0;
+  float* outf;
+  int ldf, N;
+  template <class LY, int MI, int NJ>
+  __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
+                                        int M, float* stg = nullptr) const {
+    if constexpr (kLdsOut) {
+      static_assert(LY::NQ == 4 && NJ * 32 <= 128, "staged layout: 32x32 blocks, up to 128 columns per wave");
+      const int hi = lane >> 5, r = lane & 31;  // writer: row r, columns 32 j + 8 q + 4 hi
+      const int rr = lane >> 5, ch = lane & 31;  // reader: row 2 k + rr, columns 4 ch .. 4 ch + 3
+      const int n = col0 + 4 * ch;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(stg + r * kPitchF + 32 * j + 8 * q + 4 * hi) = quad(acc[i][j], q);
+        // a wave's LDS accesses complete in order: the reads below see the writes above, and the
+        // next block's writes come after these reads
+#pragma unroll
+        for (int k = 0; k < 16; ++k) {
+          const int row = 2 * k + rr;
+          const float4 v = *reinterpret_cast<const float4*>(stg + row * kPitchF + 4 * ch);
+          const int m = row0 + 32 * i + row;
+          if (ch < 8 * NJ && m < M && n < N) st4(outf + (size_t)m * ldf + n, v);  // N is a multiple of 4
+        }
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int m = row0 + LY::row(i, lane);
+        if (m >= M) continue;
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < LY::NQ; ++q) {
+            const int n = col0 + LY::col(j, q, lane);
+            if (n < N) st4(outf + (size_t)m * ldf + n, quad(acc[i][j], q));
+          }
+      }
+    }
+  }
+};
+
 // a = silu(gate) * up; the wave's first WN/2 columns are gate, the last WN/2 the matching up columns.
 // kSave: also store float32 copies of the gate and up projections (the backward's recompute); a
 // compile-time switch, so that the forward's instantiation carries none of that code.
@@ -1103,6 +1156,12 @@ template <typename T>
 static hipError_t plain_t(const GemmA& a, const PlainArgs& p, hipStream_t s) {
   BSegs<T> bm = {};
   bm.p[0] = (const T*)p.w; bm.start[0] = 0; bm.start[1] = p.N; bm.nseg = 1; bm.ldb = a.K;
+  if (p.outf && !p.outt && !p.bias && p.out_rows_per_b == p.rows_per_b && p.out_row_off == 0 && p.N % 4 == 0 &&
+      p.ldf % 4 == 0) {  // float32 output only, row m to row m
+    EpiPlainF32<T> e;
+    e.outf = p.outf; e.ldf = p.ldf; e.N = p.N;
+    return launch<T, BSegs<T>, EpiPlainF32<T>, true>(a, p.N, bm, e, s);
+  }
   EpiPlain<T> e;
   e.bias = p.bias; e.outf = p.outf; e.ldf = p.ldf; e.outt = (T*)p.outt; e.ldt = p.ldt; e.act = p.act;
   e.N = p.N; e.rpb = p.rows_per_b; e.orpb = p.out_rows_per_b; e.ooff = p.out_row_off;
