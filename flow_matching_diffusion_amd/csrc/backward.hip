@@ -233,6 +233,27 @@ hipError_t gated_grad(int dt, const GatedGradArgs& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// 8 consecutive elements (16-byte aligned for bf16, 32-byte for float) to / from float
+__device__ __forceinline__ void load8f(const bf16* p, float (&v)[8]) {
+  const bf16x8 x = *reinterpret_cast<const bf16x8*>(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (float)x[e];
+}
+__device__ __forceinline__ void load8f(const float* p, float (&v)[8]) {
+  const float4 a = reinterpret_cast<const float4*>(p)[0], b = reinterpret_cast<const float4*>(p)[1];
+  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w; v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+}
+__device__ __forceinline__ void store8(bf16* p, const float (&v)[8]) {
+  bf16x8 x;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) x[e] = (bf16)v[e];
+  *reinterpret_cast<bf16x8*>(p) = x;
+}
+__device__ __forceinline__ void store8(float* p, const float (&v)[8]) {
+  reinterpret_cast<float4*>(p)[0] = make_float4(v[0], v[1], v[2], v[3]);
+  reinterpret_cast<float4*>(p)[1] = make_float4(v[4], v[5], v[6], v[7]);
+}
+
 // ---------------------------------------------------------------------------------------------
 // SwiGLU backward: dgu[m][i] = T(da * up * silu'(g)), dgu[m][I + i] = T(da * silu(g)),
 // silu'(x) = s(x) (1 + x (1 - s(x))). da, g, up: (M, I) float32; dgu: (M, 2I).
@@ -250,10 +271,40 @@ __global__ void swiglu_bwd_kernel(const float* __restrict__ da, const float* __r
   }
 }
 
+// The same, 8 consecutive elements per thread with 16- and 32-byte accesses (I a multiple of 8).
+template <typename T>
+__global__ void swiglu_bwd8_kernel(const float* __restrict__ da, const float* __restrict__ gt,
+                                   const float* __restrict__ up, int M, int I, T* __restrict__ dgu) {
+  const size_t n8 = (size_t)M * I / 8;
+  for (size_t c = (size_t)blockIdx.x * blockDim.x + threadIdx.x; c < n8; c += (size_t)gridDim.x * blockDim.x) {
+    const size_t e = 8 * c, m = e / I, i = e - m * I;
+    float x[8], u[8], d[8], dg[8], du[8];
+    load8f(gt + e, x);
+    load8f(up + e, u);
+    load8f(da + e, d);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const float sg = sigm(x[k]);
+      dg[k] = d[k] * u[k] * sg * (1.0f + x[k] * (1.0f - sg));
+      du[k] = d[k] * x[k] * sg;
+    }
+    store8(dgu + m * 2 * I + i, dg);
+    store8(dgu + m * 2 * I + I + i, du);
+  }
+}
+
 hipError_t swiglu_bwd(int dt, const float* da, const float* gt, const float* up, int M, int I, void* dgu,
                       hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const size_t n = (size_t)M * I;
+  if (I % 8 == 0) {
+    const int blocks = (int)((n / 8 + 255) / 256 < 8192 ? (n / 8 + 255) / 256 : 8192);
+    if (dt == DT_BF16)
+      hipLaunchKernelGGL(swiglu_bwd8_kernel<bf16>, dim3(blocks), dim3(256), 0, s, da, gt, up, M, I, (bf16*)dgu);
+    else
+      hipLaunchKernelGGL(swiglu_bwd8_kernel<float>, dim3(blocks), dim3(256), 0, s, da, gt, up, M, I, (float*)dgu);
+    return hipGetLastError();
+  }
   const int blocks = (int)((n + 255) / 256 < 8192 ? (n + 255) / 256 : 8192);
   if (dt == DT_BF16)
     hipLaunchKernelGGL(swiglu_bwd_kernel<bf16>, dim3(blocks), dim3(256), 0, s, da, gt, up, M, I, (bf16*)dgu);
@@ -397,15 +448,21 @@ __global__ void __launch_bounds__(256) gate_bwd_kernel(GateBwdArgs p) {
   const T* o = (const T*)p.o + (size_t)m * p.nq + col;
   T* dout = (T*)p.dout + (size_t)m * p.nq + col;
   T* dg = (T*)p.dg + (size_t)m * p.ldg + col;
+  // 16-byte loads and stores (written as element loops between stores, they stayed 2-byte accesses)
+  float gv[8], ov[8], dv[8], dov[8], dgv[8];
+  load8f(g, gv);
+  load8f(o, ov);
+  load8f(dog, dv);
   float dsum = 0.0f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    const float s = sigm((float)g[e]), ov = (float)o[e], d = dog[e];
-    const T dt = (T)(d * s);
-    dout[e] = dt;
-    dg[e] = (T)(d * ov * s * (1.0f - s));
-    dsum += (float)dt * ov;
+    const float s = sigm(gv[e]);
+    dov[e] = (float)(T)(dv[e] * s);  // dO as the operand dtype holds it
+    dgv[e] = dv[e] * ov[e] * s * (1.0f - s);
+    dsum += dov[e] * ov[e];
   }
+  store8(dout, dov);
+  store8(dg, dgv);
   dsum = group_sum<TPI>(dsum);
   if (ch == 0) {
     const int b = m / p.L, l = m - b * p.L;
