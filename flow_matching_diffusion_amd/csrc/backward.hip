@@ -24,6 +24,8 @@
 // dV = P^T dO, dP = dO V^T, dS = P (dP - Delta), Delta = rowsum(dO * O); P is recomputed from the
 // forward's per-row log-sum-exp. Both kernels use the 16x16 matrix-core block of k2_device.h for
 // bf16 and float32 operands, with the tiles a workgroup's waves share staged in LDS.
+#include <algorithm>
+
 #include "k2_device.h"
 #include "k2_kernels.h"
 
@@ -1086,12 +1088,11 @@ hipError_t qknorm_bwd(int dt, const QkNormBwdArgs& p, int blocks, hipStream_t s)
 // ---------------------------------------------------------------------------------------------
 // 256 threads = 64 columns x 4 chunk lanes; each thread keeps 4 independent sums so that many loads
 // are in flight, then the 4 chunk lanes meet in LDS
-__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ part, int G, int nc, int ncols,
-                                                          int ldp, float* __restrict__ out, int ldo) {
+__device__ __forceinline__ void reduce_rows_block(const float* __restrict__ part, int nc, int ncols, int ldp,
+                                                  float* __restrict__ out, int ldo, int gr, int cb) {
   __shared__ float red[4][64];
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
-  const int j = blockIdx.x * 64 + tx;
-  const int gr = blockIdx.y;
+  const int j = cb * 64 + tx;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;
   if (j < ncols) {
     const float* pp = part + (size_t)gr * nc * ldp + j;
@@ -1109,10 +1110,35 @@ __global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restric
   if (ty == 0 && j < ncols) out[(size_t)gr * ldo + j] = (red[0][tx] + red[1][tx]) + (red[2][tx] + red[3][tx]);
 }
 
+__global__ void __launch_bounds__(256) reduce_rows_kernel(const float* __restrict__ part, int G, int nc, int ncols,
+                                                          int ldp, float* __restrict__ out, int ldo) {
+  reduce_rows_block(part, nc, ncols, ldp, out, ldo, blockIdx.y, blockIdx.x);
+}
+
+// several independent reductions in one launch: blockIdx.z picks the job; blocks past a job's
+// columns or groups leave at once (the whole block, before its barrier)
+__global__ void __launch_bounds__(256) reduce_rows_multi_kernel(ReduceJobs jobs) {
+  const ReduceJob& jb = jobs.job[blockIdx.z];
+  if ((int)blockIdx.x * 64 >= jb.ncols || (int)blockIdx.y >= jb.G) return;
+  reduce_rows_block(jb.part, jb.nc, jb.ncols, jb.ldp, jb.out, jb.ldo, blockIdx.y, blockIdx.x);
+}
+
 hipError_t reduce_rows(const float* part, int G, int nc, int ncols, int ldp, float* out, int ldo, hipStream_t s) {
   if (G <= 0 || ncols <= 0) return hipSuccess;
   hipLaunchKernelGGL(reduce_rows_kernel, dim3((ncols + 63) / 64, G), dim3(256), 0, s, part, G, nc, ncols, ldp, out,
                      ldo);
+  return hipGetLastError();
+}
+
+hipError_t reduce_rows_multi(const ReduceJobs& jobs, hipStream_t s) {
+  if (jobs.n <= 0) return hipSuccess;
+  if (jobs.n > kMaxReduceJobs) return hipErrorInvalidValue;
+  int gx = 1, gy = 1;
+  for (int i = 0; i < jobs.n; ++i) {
+    gx = std::max(gx, (jobs.job[i].ncols + 63) / 64);
+    gy = std::max(gy, jobs.job[i].G);
+  }
+  hipLaunchKernelGGL(reduce_rows_multi_kernel, dim3(gx, gy, jobs.n), dim3(256), 0, s, jobs);
   return hipGetLastError();
 }
 

@@ -802,19 +802,25 @@ int block_backward_run(const k2_block_cfg* c, const k2_block_weights* w, int B, 
   K2_RUN("norm_bwd", s, norm_bwd(nb, s));
 
   // ---- reductions of the partial sums
+  // (independent column sums in one launch; the table's gradient sums the temb gradient after it)
   const int chunks = B * l.ncb;
-  if (gr->norm1_w) K2_RUN("reduce_rows", s, reduce_rows((float*)P(l.p_w1), 1, chunks, H, H, gr->norm1_w, H, s));
-  if (gr->norm2_w) K2_RUN("reduce_rows", s, reduce_rows((float*)P(l.p_w2), 1, chunks, H, H, gr->norm2_w, H, s));
-  if (gr->norm_q_w) K2_RUN("reduce_rows", s, reduce_rows((float*)P(l.p_wq), 1, l.qk_blocks, hd, hd, gr->norm_q_w, hd, s));
-  if (gr->norm_k_w) K2_RUN("reduce_rows", s, reduce_rows((float*)P(l.p_wk), 1, l.qk_blocks, hd, hd, gr->norm_k_w, hd, s));
+  ReduceJobs rj = {};
+  auto add_job = [&](const float* part, int G, int nc, int ncols, int ldp, float* out, int ldo) {
+    rj.job[rj.n++] = ReduceJob{part, out, G, nc, ncols, ldp, ldo};
+  };
+  if (gr->norm1_w) add_job((float*)P(l.p_w1), 1, chunks, H, H, gr->norm1_w, H);
+  if (gr->norm2_w) add_job((float*)P(l.p_w2), 1, chunks, H, H, gr->norm2_w, H);
+  if (gr->norm_q_w) add_job((float*)P(l.p_wq), 1, l.qk_blocks, hd, hd, gr->norm_q_w, hd);
+  if (gr->norm_k_w) add_job((float*)P(l.p_wk), 1, l.qk_blocks, hd, hd, gr->norm_k_w, hd);
+  float* dm = nullptr;
   if (modulated && (dtemb || gr->scale_shift_table)) {
-    float* dm = dtemb ? dtemb : (float*)P(l.dmod);
+    dm = dtemb ? dtemb : (float*)P(l.dmod);
     const size_t parts[6] = {l.p_ps, l.p_pt, l.p_pg, l.p_qs, l.p_qt, l.p_qg};  // the chunk order of the modulation
-    for (int cc = 0; cc < 6; ++cc)
-      K2_RUN("reduce_rows", s, reduce_rows((float*)P(parts[cc]), B, l.ncb, H, H, dm + (size_t)cc * H, 6 * H, s));
-    if (gr->scale_shift_table)
-      K2_RUN("reduce_rows", s, reduce_rows(dm, 1, B, 6 * H, 6 * H, gr->scale_shift_table, 6 * H, s));
+    for (int cc = 0; cc < 6; ++cc) add_job((float*)P(parts[cc]), B, l.ncb, H, H, dm + (size_t)cc * H, 6 * H);
   }
+  K2_RUN("reduce_rows", s, reduce_rows_multi(rj, s));
+  if (dm && gr->scale_shift_table)
+    K2_RUN("reduce_rows", s, reduce_rows(dm, 1, B, 6 * H, 6 * H, gr->scale_shift_table, 6 * H, s));
   return K2_OK;
 }
 

@@ -169,6 +169,17 @@ struct QkNormBwdArgs {
 };
 hipError_t qknorm_bwd(int dt, const QkNormBwdArgs& p, int blocks, hipStream_t s);
 hipError_t reduce_rows(const float* part, int G, int nc, int ncols, int ldp, float* out, int ldo, hipStream_t s);
+// up to kMaxReduceJobs independent reduce_rows in one launch
+struct ReduceJob {
+  const float* part; float* out;
+  int G, nc, ncols, ldp, ldo;
+};
+constexpr int kMaxReduceJobs = 12;
+struct ReduceJobs {
+  ReduceJob job[kMaxReduceJobs];
+  int n;
+};
+hipError_t reduce_rows_multi(const ReduceJobs& jobs, hipStream_t s);
 
 // reach[i] = i for tokens outside every image block (ids[i] < 0), else the last position of the
 // contiguous run of equal ids that holds i. One workgroup; ids and reach are (L,) device arrays.
