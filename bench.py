@@ -125,7 +125,7 @@ def main():
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
-        print("bench.py: this build runs on one GPU only; --gpus must be 1 (no multi-GPU path is built)",
+        print("bench.py: the library runs on one GPU only; --gpus must be 1 (no multi-GPU path exists)",
               file=sys.stderr)
         sys.exit(2)
 
