@@ -125,10 +125,94 @@ __global__ void __launch_bounds__(256) modnorm_kernel(ModnormArgs p) {
   }
 }
 
+// bf16 output, H a multiple of 8 up to 8 NT: each thread owns 8 consecutive columns of R rows (two
+// 16-byte loads and one 16-byte store per row); NT threads cover the row. At 9216 x 6144: 65 us
+// against 75-77 us for modnorm_kernel (4-column chunks, 256 threads), 5.2 TB/s.
+template <int R, int NT>
+__global__ void __launch_bounds__(NT) modnorm8_kernel(ModnormArgs p) {
+  __shared__ float red[R][NT / 64];
+  const int r0 = R * blockIdx.x;
+  const int nr = min(R, p.rows - r0);
+  const int c = threadIdx.x;  // 8-column chunk
+  const bool on = c < (p.H >> 3);
+  const float4* x[R];
+  bf16* y[R];
+  int bb[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int r = k < nr ? r0 + k : r0;
+    const int b = r / p.rows_per_b, i = r - b * p.rows_per_b;
+    bb[k] = b;
+    x[k] = (const float4*)(p.in + ((size_t)b * p.in_rows_per_b + p.in_row_off + i) * p.H);
+    y[k] = (bf16*)p.out + (size_t)r * p.H;
+  }
+  float4 v[R][2];
+  float ss[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    v[k][0] = v[k][1] = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (on) {
+      v[k][0] = x[k][2 * c];
+      v[k][1] = x[k][2 * c + 1];
+    }
+    ss[k] = v[k][0].x * v[k][0].x + v[k][0].y * v[k][0].y + v[k][0].z * v[k][0].z + v[k][0].w * v[k][0].w +
+            v[k][1].x * v[k][1].x + v[k][1].y * v[k][1].y + v[k][1].z * v[k][1].z + v[k][1].w * v[k][1].w;
+    ss[k] = wave_sum(ss[k]);
+  }
+  const int wv = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+#pragma unroll
+    for (int k = 0; k < R; ++k) red[k][wv] = ss[k];
+  }
+  __syncthreads();
+  if (!on) return;
+  // (16-byte aligned vectors: checked by the host)
+  auto ld8 = [](const float* q, float (&d)[8]) {
+    const float4 a = reinterpret_cast<const float4*>(q)[0], b = reinterpret_cast<const float4*>(q)[1];
+    d[0] = a.x; d[1] = a.y; d[2] = a.z; d[3] = a.w; d[4] = b.x; d[5] = b.y; d[6] = b.z; d[7] = b.w;
+  };
+  float w8[8] = {}, sc8[8] = {}, sh8[8] = {};
+  if (p.w) ld8(p.w + 8 * c, w8);
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (k >= nr) break;
+    float t = 0.0f;
+#pragma unroll
+    for (int q = 0; q < NT / 64; ++q) t += red[k][q];
+    const float inv = rsqrtf(t / (float)p.H + p.eps);
+    if (k == 0 || bb[k] != bb[k - 1]) {  // a new batch row: its modulation vectors
+      if (p.scale) ld8(p.scale + (size_t)bb[k] * p.mod_stride + 8 * c, sc8);
+      if (p.shift) ld8(p.shift + (size_t)bb[k] * p.mod_stride + 8 * c, sh8);
+    }
+    const float t8[8] = {v[k][0].x, v[k][0].y, v[k][0].z, v[k][0].w, v[k][1].x, v[k][1].y, v[k][1].z, v[k][1].w};
+    bf16x8 o;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[e] = (bf16)((1.0f + sc8[e]) * (t8[e] * inv * (1.0f + w8[e])) + sh8[e]);
+    *(bf16x8*)(y[k] + 8 * c) = o;
+  }
+}
+
 constexpr int kModnormRows = 2;
+
+template <int NT>
+static hipError_t modnorm8(const ModnormArgs& p, hipStream_t s) {
+  hipLaunchKernelGGL((modnorm8_kernel<kModnormRows, NT>), dim3((p.rows + kModnormRows - 1) / kModnormRows), dim3(NT),
+                     0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t modnorm(int dt, const ModnormArgs& p, hipStream_t s) {
   if (p.rows <= 0) return hipSuccess;
+  const bool aligned = (((uintptr_t)p.w | (uintptr_t)p.scale | (uintptr_t)p.shift) & 15) == 0;
+  if (dt == DT_BF16 && p.H % 8 == 0 && p.H <= 8 * 1024 && p.mod_stride % 4 == 0 && aligned) {
+    const int h8 = p.H / 8;
+    if (h8 <= 64) return modnorm8<64>(p, s);
+    if (h8 <= 128) return modnorm8<128>(p, s);
+    if (h8 <= 256) return modnorm8<256>(p, s);
+    if (h8 <= 512) return modnorm8<512>(p, s);
+    if (h8 <= 768) return modnorm8<768>(p, s);
+    return modnorm8<1024>(p, s);
+  }
   const int grid = (p.rows + kModnormRows - 1) / kModnormRows;
   if (dt == DT_BF16)
     hipLaunchKernelGGL((modnorm_kernel<bf16, kModnormRows>), dim3(grid), dim3(256), 0, s, p);
