@@ -43,11 +43,27 @@ Readings where the pages are silent or garbled (each restated where it is used):
   R13 bf16 operands: the model runs in bfloat16 ([PIPELINE] examples load it with
       torch_dtype=bfloat16) and RMSNorm computes in float32 and casts back to the model dtype
       ([ARTICLE] §四.4). With `rnd=bf16_round` the oracle rounds to bf16 exactly where the bf16
-      model hands a matrix product a bf16 operand: the modulated norm outputs, the q/k (after norm
-      and RoPE), v and gate projections, the gated attention output, the SwiGLU activation, the
-      time-MLP inputs, the fused text before txt_in and the final-layer norm output. Everything
-      else (residual stream, statistics, softmax, accumulation) stays float64. rnd=None is the
-      exact function.
+      model holds a bf16 tensor that a later step consumes. Each such place is a named rounding
+      point, and rnd(x, point) is called with its name, so a caller can switch single points off:
+        block: "x1", "x2" (modulated norm outputs), "q", "k" (after norm and RoPE), "v", "g" (the
+               projections), "p" (the attention probabilities entering the P V product), "o" (the
+               attention output, a bf16 tensor in the bf16 model), "og" (the gated attention output
+               entering the out projection), "a" (the SwiGLU activation entering the down product);
+        time path: "temb_in", "temb_act", "temb_e" (the three time-MLP inputs);
+        text: "text_fused" (the fused text before txt_in); final layer: "final_x";
+        sampler: "latents" (the transformer input drawn from the float state).
+      Elementwise steps between two points (the gate product, SiLU, modulation) run in full
+      precision. Everything else (residual stream, statistics, softmax, accumulation) stays
+      float64. rnd=None is the exact function.
+      Softmax rounding form: the plain definition rounds the normalised probabilities (softmax,
+      then the bf16 P V product), which is the default. flash=True takes the other legitimate form
+      of the same bf16 model, that of fused (flash) attention: the unnormalised exp(s - rowmax) is
+      rounded for the product and the row sum is taken before rounding and divided at the end. The
+      two forms differ only in where the probabilities are rounded. f32_products=True is a third
+      legitimate form: every matrix product accumulates in float32, as matrix cores do, instead of
+      float64. The spread between these forms measures how much any bf16 implementation may
+      legitimately differ from the plain one (a small change anywhere re-draws the rounding of
+      every later point).
   R14 sampler shift ([PIPELINE] Krea2Pipeline, scheduler and is_distilled parameters): mu is the
       straight line through (base_image_seq_len, base_shift) = (256, 0.5) and
       (max_image_seq_len, max_shift) = (6400, 1.15) evaluated at the image token count; the
@@ -67,12 +83,12 @@ Readings where the pages are silent or garbled (each restated where it is used):
   R20 backward pass ([ARTICLE] §四 data flow and §六: the model is trained, and its test matrix
       includes training and gradient checkpointing): the gradient of the block's output with
       respect to its input h, its modulation input temb and every weight, by the chain rule through
-      the forward's steps, the forward recomputed from h (checkpointing). In bf16 mode the
-      backward's matrix-product operands are bf16 as well: the gradients that enter a product
-      (dz, dgt, du, dy, the attention output gradient, P and dS inside attention, and the q/k/v/gate
-      projection gradients), with float32 accumulation and float32 weight gradients; the attention
-      output before the gate, which the bf16 model's attention returns as a bf16 tensor, enters the
-      gate's and the softmax's gradients rounded to bf16.
+      the forward's steps, the forward recomputed from h (checkpointing). In bf16 mode the forward
+      part rounds at the same named points as block_forward (R13: "p" normalised, "o" the bf16
+      attention output), and the backward's matrix-product operands are bf16 as well: the
+      gradients that enter a product ("dz", "dgt", "du", "dy", "do", "dgraw", "dq", "dk", "dv")
+      and dS inside attention ("ds"), with float32 accumulation and float32 weight gradients. The
+      rounded attention output enters the gate's and the softmax's gradients.
 """
 from __future__ import annotations
 
@@ -87,14 +103,32 @@ def _f64(a):
     return None if a is None else np.asarray(a, dtype=F64)
 
 
-def _id(x):
+def _id(x, point=None):
     return x
 
 
-def bf16_round(x):
+def bf16_form(flash=False, f32_products=False):
+    """bf16 rounding at R13's named points in one of R13's legitimate forms: the returned rounding
+    function carries the softmax rounding form and the product accumulation type, which
+    block_forward reads when its own flash / f32_products arguments are left at None, so the form
+    also reaches the blocks inside text fusion and the backbone."""
+    def rnd(x, point=None):
+        return bf16_round(x)
+    rnd.flash, rnd.f32_products = bool(flash), bool(f32_products)
+    return rnd
+
+
+def _mm32(a, b):
+    """Matrix product with float32 operands and float32 accumulation, widened back to float64: how
+    matrix cores accumulate (the emulation R13 calls f32_products)."""
+    return (np.asarray(a, np.float32) @ np.asarray(b, np.float32)).astype(F64)
+
+
+def bf16_round(x, point=None):
     """Round to the nearest bfloat16 (ties to even) via float32; returns float64 (R13).
     A bfloat16 is the upper 16 bits of a float32, so rounding adds half of the dropped range
-    (0x7FFF, plus 1 when the kept lsb is odd) and clears the low 16 bits."""
+    (0x7FFF, plus 1 when the kept lsb is odd) and clears the low 16 bits. point names the rounding
+    point (R13); every point rounds the same way here."""
     f = np.ascontiguousarray(np.asarray(x, dtype=np.float32))
     u = f.view(np.uint32).astype(np.uint64)
     u = (u + 0x7FFF + ((u >> 16) & 1)) & 0xFFFF0000
@@ -156,28 +190,39 @@ def apply_rope(x, angles):
 # ----------------------------------------------------------------------------------------------
 # Attention
 # ----------------------------------------------------------------------------------------------
-def attention(q, k, v, key_valid, visible=None):
+def attention(q, k, v, key_valid, visible=None, rnd=None, flash=False, f32_products=False):
     """Softmax attention with GQA and a key mask, [ARTICLE] §四.3.
     q: (B, nh, Lq, hd); k, v: (B, nkv, Lk, hd); key_valid: (B, Lk) bool or None; visible: (Lq, Lk)
     bool or None, which keys each query may attend (the same for every batch row and head; R17).
-    K/V heads are repeated with repeat_interleave semantics (R4); scale 1/sqrt(hd) (R3).
-    A query row with no allowed key returns zeros (R17)."""
-    nh, nkv, hd = q.shape[1], k.shape[1], q.shape[-1]
+    Query head hq reads kv head hq // (nh / nkv) (repeat_interleave, R4); scale 1/sqrt(hd) (R3).
+    A query row with no allowed key returns zeros (R17). rnd rounds the probabilities at "p" where
+    they enter the P V product (R13); flash selects where (R13's softmax rounding form);
+    f32_products accumulates the two products in float32 (R13). Heads are taken one at a time,
+    which bounds memory and changes no arithmetic."""
+    r = rnd or _id
+    mm = _mm32 if f32_products else np.matmul
+    B, nh, Lq, hd = q.shape
+    nkv, Lk = k.shape[1], k.shape[2]
     g = nh // nkv
-    k = np.repeat(k, g, axis=1)
-    v = np.repeat(v, g, axis=1)
-    s = (q @ np.swapaxes(k, -1, -2)) / math.sqrt(hd)
-    allowed = np.ones(s.shape, dtype=bool)
+    allowed = np.ones((B, Lq, Lk), dtype=bool)
     if key_valid is not None:
-        allowed &= key_valid[:, None, None, :]
+        allowed &= np.asarray(key_valid, dtype=bool)[:, None, :]
     if visible is not None:
-        allowed &= visible[None, None]
-    s = np.where(allowed, s, -np.inf)
+        allowed &= visible[None]
     some = allowed.any(axis=-1, keepdims=True)
-    s = s - np.where(some, np.max(s, axis=-1, keepdims=True), 0.0)
-    p = np.exp(s)
-    p = p / np.where(some, np.sum(p, axis=-1, keepdims=True), 1.0)
-    return p @ v
+    out = np.empty((B, nh, Lq, v.shape[-1]), dtype=F64)
+    for hq in range(nh):
+        kh, vh = _f64(k[:, hq // g]), _f64(v[:, hq // g])
+        s = mm(_f64(q[:, hq]), np.swapaxes(kh, -1, -2)) / math.sqrt(hd)
+        s = np.where(allowed, s, -np.inf)
+        s = s - np.where(some, np.max(s, axis=-1, keepdims=True), 0.0)
+        e = np.exp(s)
+        denom = np.where(some, np.sum(e, axis=-1, keepdims=True), 1.0)
+        if flash:
+            out[:, hq] = mm(r(e, "p"), vh) / denom
+        else:
+            out[:, hq] = mm(r(e / denom, "p"), vh)
+    return out
 
 
 def block_causal_visible(image_ids, rows=None):
@@ -212,18 +257,23 @@ def modulation(temb, table):
 
 
 def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermediates=False, rnd=None,
-                  image_ids=None):
+                  image_ids=None, flash=None, f32_products=None):
     """One Krea2TransformerBlock forward ([ARTICLE] §四.2 block, §四.3 attention, §四.4 norm).
 
     h: (B, L, H) residual stream; temb: (B, 6H) or None (no modulation: text-fusion blocks);
     position_ids: (L, 3) or None (no RoPE); mask: (B, T) or None; w: weight dict (nn.Linear
     (out, in) layout); dims: BlockDims-like; T: text tokens at the start of the sequence.
     rows: optional sorted sequence indices; only those output rows are computed (keys and
-    values still come from every row). rnd: operand rounding of R13 (None = exact).
-    image_ids: (L,) block ids for the block-causal attention of R17 (None = every key visible).
+    values still come from every row). rnd: rounding of R13 at its named points (None = exact);
+    flash: R13's softmax rounding form; f32_products: every matrix product accumulates in float32
+    (R13); both default to the form rnd carries (bf16_form), else False. image_ids: (L,) block ids for the block-causal attention of R17 (None = every key
+    visible).
     Returns (B, len(rows) or L, H) float64.
     """
+    flash = getattr(rnd, "flash", False) if flash is None else flash
+    f32_products = getattr(rnd, "f32_products", False) if f32_products is None else f32_products
     rnd = rnd or _id
+    mm = _mm32 if f32_products else np.matmul
     h = _f64(h)
     B, L, H = h.shape
     nh, nkv, hd, eps = dims.num_heads, dims.num_kv_heads, dims.head_dim, dims.eps
@@ -239,15 +289,15 @@ def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermedia
         pg = qg = 1.0
 
     # (1 + prescale) * norm1(h) + preshift
-    x1 = rnd((1.0 + ps) * rms_norm(h, w["norm1_w"], eps) + pt)
+    x1 = rnd((1.0 + ps) * rms_norm(h, w["norm1_w"], eps) + pt, "x1")
     out["x1"] = x1
 
     # projections (R7: no bias); k and v for every row, q and gate for the requested rows
-    k = x1 @ _f64(w["to_k"]).T
-    v = rnd(x1 @ _f64(w["to_v"]).T)
+    k = mm(x1, _f64(w["to_k"]).T)
+    v = rnd(mm(x1, _f64(w["to_v"]).T), "v")
     xr = x1[:, rows]
-    q = xr @ _f64(w["to_q"]).T
-    graw = rnd(xr @ _f64(w["to_gate"]).T)
+    q = mm(xr, _f64(w["to_q"]).T)
+    graw = rnd(mm(xr, _f64(w["to_gate"]).T), "g")
 
     q = q.reshape(B, R, nh, hd).transpose(0, 2, 1, 3)
     k = k.reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
@@ -260,22 +310,22 @@ def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermedia
         ang = rope_angles(position_ids, dims.axes_dims, dims.rope_theta)
         q = apply_rope(q, ang[rows][None, None])
         k = apply_rope(k, ang[None, None])
-    q, k = rnd(q), rnd(k)
+    q, k = rnd(q, "q"), rnd(k, "k")
     out["q"], out["k"], out["v"], out["g"] = q, k, v, graw
 
     vis = None if image_ids is None else block_causal_visible(image_ids, rows)
-    o = attention(q, k, v, key_valid_mask(B, L, T, mask), vis)
-    o = o.transpose(0, 2, 1, 3).reshape(B, R, nh * hd)
-    og = rnd(o * sigmoid(graw))                              # R6
-    out["og"] = og
+    o = attention(q, k, v, key_valid_mask(B, L, T, mask), vis, rnd=rnd, flash=flash, f32_products=f32_products)
+    o = rnd(o.transpose(0, 2, 1, 3).reshape(B, R, nh * hd), "o")
+    og = rnd(o * sigmoid(graw), "og")                        # R6
+    out["o"], out["og"] = o, og
 
-    h1 = h[:, rows] + pg * (og @ _f64(w["to_out"]).T)
+    h1 = h[:, rows] + pg * mm(og, _f64(w["to_out"]).T)
     out["h1"] = h1
-    x2 = rnd((1.0 + qs) * rms_norm(h1, w["norm2_w"], eps) + qt)
+    x2 = rnd((1.0 + qs) * rms_norm(h1, w["norm2_w"], eps) + qt, "x2")
     out["x2"] = x2
-    a = rnd(silu(x2 @ _f64(w["ff_gate"]).T) * (x2 @ _f64(w["ff_up"]).T))   # R9
+    a = rnd(silu(mm(x2, _f64(w["ff_gate"]).T)) * mm(x2, _f64(w["ff_up"]).T), "a")   # R9
     out["a"] = a
-    h2 = h1 + qg * (a @ _f64(w["ff_down"]).T)
+    h2 = h1 + qg * mm(a, _f64(w["ff_down"]).T)
     out["out"] = h2
     return (h2, out) if intermediates else h2
 
@@ -296,19 +346,21 @@ def rms_norm_backward(x, weight, eps, dy):
     return dx, dw
 
 
-def attention_backward(q, k, v, key_valid, do, visible=None, rnd=None, o=None):
+def attention_backward(q, k, v, key_valid, do, visible=None, rnd=None, o=None, f32_products=False):
     """Gradients of attention() (same arguments) for the output gradient do (B, nh, Lq, hd):
     returns (dq, dk, dv) with dk, dv summed over the query heads that share each kv head (R4).
     With P the softmax probabilities and O = P V: dV = P^T dO, dP = dO V^T,
     dS = P (dP - rowsum(dO * O)), dQ = dS K / sqrt(hd), dK = dS^T Q / sqrt(hd). rnd (R20) rounds P
-    and dS where they become matrix-product operands; o, if given, is the forward output O as the
-    model holds it (R20), used in rowsum(dO * O)."""
+    (at "p", normalised, as in attention()) and dS (at "ds") where they become matrix-product
+    operands; o, if given, is the forward output O as the model holds it (R20), used in
+    rowsum(dO * O). f32_products: the products accumulate in float32 (R13)."""
     r = rnd or _id
+    mm = _mm32 if f32_products else np.matmul
     nh, nkv, hd = q.shape[1], k.shape[1], q.shape[-1]
     g = nh // nkv
     kk = np.repeat(_f64(k), g, axis=1)
     vv = np.repeat(_f64(v), g, axis=1)
-    s = (_f64(q) @ np.swapaxes(kk, -1, -2)) / math.sqrt(hd)
+    s = mm(_f64(q), np.swapaxes(kk, -1, -2)) / math.sqrt(hd)
     allowed = np.ones(s.shape, dtype=bool)
     if key_valid is not None:
         allowed &= key_valid[:, None, None, :]
@@ -320,25 +372,30 @@ def attention_backward(q, k, v, key_valid, do, visible=None, rnd=None, o=None):
     p = np.exp(s)
     p = p / np.where(some, np.sum(p, axis=-1, keepdims=True), 1.0)
     do = _f64(do)
-    o = p @ vv if o is None else _f64(o)
-    dvv = np.swapaxes(r(p), -1, -2) @ do
-    dp = do @ np.swapaxes(vv, -1, -2)
+    o = mm(p, vv) if o is None else _f64(o)
+    dvv = mm(np.swapaxes(r(p, "p"), -1, -2), do)
+    dp = mm(do, np.swapaxes(vv, -1, -2))
     delta = np.sum(do * o, axis=-1, keepdims=True)
-    ds = r(p * (dp - delta))
-    dq = ds @ kk / math.sqrt(hd)
-    dkk = np.swapaxes(ds, -1, -2) @ _f64(q) / math.sqrt(hd)
+    ds = r(p * (dp - delta), "ds")
+    dq = mm(ds, kk) / math.sqrt(hd)
+    dkk = mm(np.swapaxes(ds, -1, -2), _f64(q)) / math.sqrt(hd)
     B, _, Lk, _ = k.shape
     dk = dkk.reshape(B, nkv, g, Lk, hd).sum(axis=2)
     dv = dvv.reshape(B, nkv, g, Lk, hd).sum(axis=2)
     return dq, dk, dv
 
 
-def block_backward(h, temb, position_ids, mask, w, dims, T, dh_out, rnd=None, image_ids=None):
+def block_backward(h, temb, position_ids, mask, w, dims, T, dh_out, rnd=None, image_ids=None, flash=None,
+                   f32_products=None):
     """Gradients of block_forward (same arguments) for the output gradient dh_out (B, L, H), by the
     chain rule through every step of the forward (R20). The forward is recomputed from h.
     Returns (dh, dtemb or None, grads) where grads holds the gradient of every weight in w (same
     keys and shapes; None for an absent norm weight). rnd as in block_forward; it also rounds the
-    backward's matrix-product operands (R20)."""
+    backward's matrix-product operands (R20). flash and f32_products as in block_forward (flash
+    applies to the recomputed forward's attention)."""
+    flash = getattr(rnd, "flash", False) if flash is None else flash
+    f32_products = getattr(rnd, "f32_products", False) if f32_products is None else f32_products
+    mm = _mm32 if f32_products else np.matmul
     r = rnd or _id
     h = _f64(h)
     dh2 = _f64(dh_out)
@@ -353,70 +410,70 @@ def block_backward(h, temb, position_ids, mask, w, dims, T, dh_out, rnd=None, im
         ps = pt = qs = qt = 0.0
         pg = qg = 1.0
     n1 = rms_norm(h, w["norm1_w"], eps)
-    x1 = r((1.0 + ps) * n1 + pt)
-    qraw = (x1 @ _f64(w["to_q"]).T).reshape(B, L, nh, hd).transpose(0, 2, 1, 3)
-    kraw = (x1 @ _f64(w["to_k"]).T).reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
-    v = r(x1 @ _f64(w["to_v"]).T).reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
-    graw = r(x1 @ _f64(w["to_gate"]).T)
+    x1 = r((1.0 + ps) * n1 + pt, "x1")
+    qraw = mm(x1, _f64(w["to_q"]).T).reshape(B, L, nh, hd).transpose(0, 2, 1, 3)
+    kraw = mm(x1, _f64(w["to_k"]).T).reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
+    v = r(mm(x1, _f64(w["to_v"]).T), "v").reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
+    graw = r(mm(x1, _f64(w["to_gate"]).T), "g")
     qn = rms_norm(qraw, w["norm_q_w"], eps)
     kn = rms_norm(kraw, w["norm_k_w"], eps)
     ang = None
     if position_ids is not None:
         ang = rope_angles(position_ids, dims.axes_dims, dims.rope_theta)
         qn, kn = apply_rope(qn, ang[None, None]), apply_rope(kn, ang[None, None])
-    q, k = r(qn), r(kn)
+    q, k = r(qn, "q"), r(kn, "k")
     key_valid = key_valid_mask(B, L, T, mask)
     vis = None if image_ids is None else block_causal_visible(image_ids)
-    o = attention(q, k, v, key_valid, vis)
+    o = r(attention(q, k, v, key_valid, vis, rnd=rnd, flash=flash, f32_products=f32_products),
+          "o")   # the attention output as the model holds it
     oc = o.transpose(0, 2, 1, 3).reshape(B, L, nh * hd)
     sg = sigmoid(graw)
-    og = r(oc * sg)
-    y = og @ _f64(w["to_out"]).T
+    og = r(oc * sg, "og")
+    y = mm(og, _f64(w["to_out"]).T)
     h1 = h + pg * y
-    o_m, oc_m = r(o), r(oc)          # the attention output as the model holds it (R20)
     n2 = rms_norm(h1, w["norm2_w"], eps)
-    x2 = r((1.0 + qs) * n2 + qt)
-    gt = x2 @ _f64(w["ff_gate"]).T
-    u = x2 @ _f64(w["ff_up"]).T
+    x2 = r((1.0 + qs) * n2 + qt, "x2")
+    gt = mm(x2, _f64(w["ff_gate"]).T)
+    u = mm(x2, _f64(w["ff_up"]).T)
     sgt = sigmoid(gt)
-    a = r(gt * sgt * u)
-    z = a @ _f64(w["ff_down"]).T
+    a = r(gt * sgt * u, "a")
+    z = mm(a, _f64(w["ff_down"]).T)
     # ---- backward, step by step in reverse
     grads = {}
     flat = lambda t: t.reshape(M, -1)
     dqg = np.sum(dh2 * z, axis=1)
-    dz = r(qg * dh2)
-    grads["ff_down"] = flat(dz).T @ flat(a)
-    da = dz @ _f64(w["ff_down"])
-    dgt = r(da * u * sgt * (1.0 + gt * (1.0 - sgt)))      # silu'(x) = s(x) (1 + x (1 - s(x)))
-    du = r(da * gt * sgt)
-    grads["ff_gate"] = flat(dgt).T @ flat(x2)
-    grads["ff_up"] = flat(du).T @ flat(x2)
-    dx2 = dgt @ _f64(w["ff_gate"]) + du @ _f64(w["ff_up"])
+    dz = r(qg * dh2, "dz")
+    grads["ff_down"] = mm(flat(dz).T, flat(a))
+    da = mm(dz, _f64(w["ff_down"]))
+    dgt = r(da * u * sgt * (1.0 + gt * (1.0 - sgt)), "dgt")      # silu'(x) = s(x) (1 + x (1 - s(x)))
+    du = r(da * gt * sgt, "du")
+    grads["ff_gate"] = mm(flat(dgt).T, flat(x2))
+    grads["ff_up"] = mm(flat(du).T, flat(x2))
+    dx2 = mm(dgt, _f64(w["ff_gate"])) + mm(du, _f64(w["ff_up"]))
     dqs = np.sum(dx2 * n2, axis=1)
     dqt = np.sum(dx2, axis=1)
     dh1_n, grads["norm2_w"] = rms_norm_backward(h1, w["norm2_w"], eps, (1.0 + qs) * dx2)
     dh1 = dh2 + dh1_n
     dpg = np.sum(dh1 * y, axis=1)
-    dy = r(pg * dh1)
-    grads["to_out"] = flat(dy).T @ flat(og)
-    dog = dy @ _f64(w["to_out"])
-    do = r(dog * sg).reshape(B, L, nh, hd).transpose(0, 2, 1, 3)
-    dgraw = r(dog * oc_m * sg * (1.0 - sg))
-    dq, dk, dv = attention_backward(q, k, v, key_valid, do, vis, rnd=rnd, o=o_m)
+    dy = r(pg * dh1, "dy")
+    grads["to_out"] = mm(flat(dy).T, flat(og))
+    dog = mm(dy, _f64(w["to_out"]))
+    do = r(dog * sg, "do").reshape(B, L, nh, hd).transpose(0, 2, 1, 3)
+    dgraw = r(dog * oc * sg * (1.0 - sg), "dgraw")
+    dq, dk, dv = attention_backward(q, k, v, key_valid, do, vis, rnd=rnd, o=o, f32_products=f32_products)
     if ang is not None:                                      # the rotation's transpose turns back
         dq, dk = apply_rope(dq, -ang[None, None]), apply_rope(dk, -ang[None, None])
     dqraw, grads["norm_q_w"] = rms_norm_backward(qraw, w["norm_q_w"], eps, dq)
     dkraw, grads["norm_k_w"] = rms_norm_backward(kraw, w["norm_k_w"], eps, dk)
-    dqraw = r(dqraw.transpose(0, 2, 1, 3).reshape(B, L, nh * hd))
-    dkraw = r(dkraw.transpose(0, 2, 1, 3).reshape(B, L, nkv * hd))
-    dv = r(dv.transpose(0, 2, 1, 3).reshape(B, L, nkv * hd))
-    grads["to_q"] = flat(dqraw).T @ flat(x1)
-    grads["to_k"] = flat(dkraw).T @ flat(x1)
-    grads["to_v"] = flat(dv).T @ flat(x1)
-    grads["to_gate"] = flat(dgraw).T @ flat(x1)
-    dx1 = (dqraw @ _f64(w["to_q"]) + dkraw @ _f64(w["to_k"]) + dv @ _f64(w["to_v"])
-           + dgraw @ _f64(w["to_gate"]))
+    dqraw = r(dqraw.transpose(0, 2, 1, 3).reshape(B, L, nh * hd), "dq")
+    dkraw = r(dkraw.transpose(0, 2, 1, 3).reshape(B, L, nkv * hd), "dk")
+    dv = r(dv.transpose(0, 2, 1, 3).reshape(B, L, nkv * hd), "dv")
+    grads["to_q"] = mm(flat(dqraw).T, flat(x1))
+    grads["to_k"] = mm(flat(dkraw).T, flat(x1))
+    grads["to_v"] = mm(flat(dv).T, flat(x1))
+    grads["to_gate"] = mm(flat(dgraw).T, flat(x1))
+    dx1 = (mm(dqraw, _f64(w["to_q"])) + mm(dkraw, _f64(w["to_k"])) + mm(dv, _f64(w["to_v"]))
+           + mm(dgraw, _f64(w["to_gate"])))
     dps = np.sum(dx1 * n1, axis=1)
     dpt = np.sum(dx1, axis=1)
     dh_n, grads["norm1_w"] = rms_norm_backward(h, w["norm1_w"], eps, (1.0 + ps) * dx1)
@@ -449,10 +506,10 @@ def time_path(t, tw, dim=256, rnd=None):
     """time_embed -> GELU -> time_mod_proj ([ARTICLE] data flow of §四; R10; rnd: R13).
     Returns (temb (B, 6H), e (B, H)) where e is time_embed's output (before the GELU)."""
     rnd = rnd or _id
-    emb = rnd(timestep_embedding(t, dim))
-    h1 = rnd(gelu_tanh(emb @ _f64(tw["lin1_w"]).T + _f64(tw["lin1_b"])))
+    emb = rnd(timestep_embedding(t, dim), "temb_in")
+    h1 = rnd(gelu_tanh(emb @ _f64(tw["lin1_w"]).T + _f64(tw["lin1_b"])), "temb_act")
     e = h1 @ _f64(tw["lin2_w"]).T + _f64(tw["lin2_b"])
-    temb = rnd(gelu_tanh(e)) @ _f64(tw["mod_w"]).T + _f64(tw["mod_b"])
+    temb = rnd(gelu_tanh(e), "temb_e") @ _f64(tw["mod_w"]).T + _f64(tw["mod_b"])
     return temb, e
 
 
@@ -482,7 +539,7 @@ def final_layer(h_img, e, table, norm_w, w, b, eps, rnd=None):
     rnd = rnd or _id
     scale = _f64(table)[0][None, None] + _f64(e)[:, None, :]
     shift = _f64(table)[1][None, None] + _f64(e)[:, None, :]
-    x = rnd((1.0 + scale) * rms_norm(h_img, norm_w, eps) + shift)
+    x = rnd((1.0 + scale) * rms_norm(h_img, norm_w, eps) + shift, "final_x")
     return x @ _f64(w).T + _f64(b)
 
 
@@ -490,21 +547,35 @@ def text_embed(enc, mask, mw, tdims, rnd=None):
     """The backbone's text rows before the first block ([ARTICLE] data flow of §四): txt_in applied to
     the text-fusion output. Neither depends on the timestep or the latents. Returns (B, T, hidden)."""
     r = rnd or _id
-    return r(text_fusion(enc, mask, mw["text"], tdims, rnd=rnd)) @ _f64(mw["txt_in_w"]).T + _f64(mw["txt_in_b"])
+    fused = r(text_fusion(enc, mask, mw["text"], tdims, rnd=rnd), "text_fused")
+    return fused @ _f64(mw["txt_in_w"]).T + _f64(mw["txt_in_b"])
+
+
+def backbone_stem(x, enc, t, mask, mw, tdims, time_dim=256, rnd=None):
+    """What the backbone computes before its first block ([ARTICLE] data flow of §四): the time path,
+    the text rows txt_in(text_fusion(enc)) and the image rows img_in(x), concatenated [text, image].
+    Returns (h (B, T + N, hidden), temb (B, 6 hidden), e (B, hidden))."""
+    temb, e = time_path(t, mw["time"], time_dim, rnd=rnd)
+    txt = text_embed(enc, mask, mw, tdims, rnd=rnd)
+    img = _f64(x) @ _f64(mw["img_in_w"]).T + _f64(mw["img_in_b"])
+    return np.concatenate([txt, img], axis=1), temb, e
+
+
+def backbone_head(h, e, mw, dims, T, rnd=None):
+    """What follows the last block: the image rows only, through the final layer (R11)."""
+    return final_layer(h[:, T:], e, mw["final_table"], mw.get("final_norm_w"), mw["final_w"], mw["final_b"],
+                       dims.eps, rnd=rnd)
 
 
 def backbone_forward(x, enc, t, position_ids, mask, mw, dims, tdims, T, time_dim=256, rnd=None):
     """Krea2Transformer2DModel.forward ([API] forward; [ARTICLE] data flow of §四):
     time path, text fusion + txt_in, img_in, concat [text, image], blocks, image rows only,
-    final layer. Returns the velocity (B, N, in_channels)."""
-    temb, e = time_path(t, mw["time"], time_dim, rnd=rnd)
-    txt = text_embed(enc, mask, mw, tdims, rnd=rnd)
-    img = _f64(x) @ _f64(mw["img_in_w"]).T + _f64(mw["img_in_b"])
-    h = np.concatenate([txt, img], axis=1)
+    final layer. mw["blocks"] may be any iterable of block weights (it is walked once).
+    Returns the velocity (B, N, in_channels)."""
+    h, temb, e = backbone_stem(x, enc, t, mask, mw, tdims, time_dim, rnd=rnd)
     for bw in mw["blocks"]:
         h = block_forward(h, temb, position_ids, mask, bw, dims, T=T, rnd=rnd)
-    return final_layer(h[:, T:], e, mw["final_table"], mw.get("final_norm_w"), mw["final_w"],
-                       mw["final_b"], dims.eps, rnd=rnd)
+    return backbone_head(h, e, mw, dims, T, rnd=rnd)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -556,7 +627,7 @@ def denoise_step(x, enc, enc_neg, mask, mask_neg, position_ids, mw, dims, tdims,
     enc / enc_neg: (1, T, layers, D) prompt and negative-prompt stacks; masks (1, T) or None.
     The transformer input is x in the operand precision (rnd), the state stays float64."""
     r = rnd or _id
-    xin = r(_f64(x))
+    xin = r(_f64(x), "latents")
     if guidance > 0:
         xb = np.concatenate([xin, xin], axis=0)
         eb = np.concatenate([_f64(enc), _f64(enc_neg)], axis=0)

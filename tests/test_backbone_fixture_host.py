@@ -1,0 +1,47 @@
+"""The streamed backbone that writes the 28-block fixture computes exactly oracle.backbone_forward
+(checked on a small model on the CPU), and the fixture's key tracks the code it was made with."""
+import importlib.util
+import os
+
+import numpy as np
+
+from flow_matching_diffusion_amd import synth as S
+from oracle import k2_oracle as O
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def _script():
+    spec = importlib.util.spec_from_file_location("bb_fixture", os.path.join(HERE, "golden", "backbone1024_oracle.py"))
+    mod = importlib.util.module_from_spec(spec)
+    spec.loader.exec_module(mod)
+    return mod
+
+
+def test_streamed_backbone_equals_oracle_backbone():
+    m = _script()
+    td = S.TextDims(hidden=32, num_heads=4, num_kv_heads=4, head_dim=8, intermediate=24, num_layers=3)
+    d = S.BlockDims(hidden=32, num_heads=4, num_kv_heads=2, head_dim=8, intermediate=16, axes_dims=(2, 2, 4))
+    wl = S.Workload("mb", 57, "bf16", 2, 4, (2, 3), (3, 1), t=(0.7, 0.7), dims=d, text=td, num_layers=3,
+                    in_channels=8, timestep_embed_dim=16)
+    got = m.streamed_backbone(wl, m.FORMS, log=lambda s: None)
+    mw = S.model_weights(wl.seed, wl)
+    inp = S.backbone_inputs(wl)
+    for name, rnd in m.FORMS.items():
+        ref = O.backbone_forward(S.as_dtype(inp["x"], wl.dtype), inp["enc"], inp["timestep"], inp["position_ids"],
+                                 inp["mask"], mw, d, S.text_block_dims(td), wl.T, time_dim=16, rnd=rnd)
+        np.testing.assert_array_equal(got[name], ref, err_msg=name)
+
+
+def test_fixture_key_ignores_docstrings_only():
+    m = _script()
+    src = "def f(x):\n    'doc'\n    return x + 1\n"
+    import tempfile
+    with tempfile.TemporaryDirectory() as d:
+        p = os.path.join(d, "a.py")
+        open(p, "w").write(src)
+        h0 = m.code_hash(p)
+        open(p, "w").write(src.replace("'doc'", "'other doc'  # comment"))
+        assert m.code_hash(p) == h0
+        open(p, "w").write(src.replace("x + 1", "x + 2"))
+        assert m.code_hash(p) != h0

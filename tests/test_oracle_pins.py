@@ -259,11 +259,52 @@ def test_rope_relative_position():
 # ----------------------------------------------------------------------------------------------
 # Whole block: library composition and brute force
 # ----------------------------------------------------------------------------------------------
-def torch_block_t(h, temb, pos, mask, w, d, T, image_ids=None):
+class _Round(torch.autograd.Function):
+    """Rounds in the forward pass; passes the gradient through unchanged (the oracle's backward
+    treats a rounding point's derivative as 1)."""
+    @staticmethod
+    def forward(ctx, x, fn):
+        return fn(x)
+
+    @staticmethod
+    def backward(ctx, g):
+        return g, None
+
+
+class _GradRound(torch.autograd.Function):
+    """Identity in the forward pass; rounds the gradient that flows back through it."""
+    @staticmethod
+    def forward(ctx, x, fn):
+        ctx.fn = fn
+        return x.view_as(x)
+
+    @staticmethod
+    def backward(ctx, g):
+        return ctx.fn(g), None
+
+
+def torch_bf16(x, point=None):
+    """bf16 rounding by torch's own conversions: float64 -> float32 -> bfloat16 -> float64."""
+    return x.to(torch.float32).to(torch.bfloat16).to(torch.float64)
+
+
+def skip_point(off, base=torch_bf16):
+    """A rounding hook that rounds at every named point except `off`."""
+    return lambda x, point=None: x if point == off else base(x, point)
+
+
+def torch_block_t(h, temb, pos, mask, w, d, T, image_ids=None, rnd=None, flash=False):
     """The block composed from torch library routines in float64 (F.linear, F.rms_norm,
     F.scaled_dot_product_attention with enable_gqa and a boolean mask, complex RoPE, F.silu) on
-    float64 tensors h, temb (or None) and the weight dict w (tensors; autograd follows them)."""
+    float64 tensors h, temb (or None) and the weight dict w (tensors; autograd follows them).
+    rnd(x, point): a rounding hook applied at the named points of the bf16 model (x1, q, k, v, g,
+    p, o, og, x2, a) in the forward pass, and to the gradients that enter the backward's matrix
+    products (dz, dgt, du, dy, do, dgraw, dq, dk, dv, ds). With a hook, attention is written out
+    (repeat_interleave, masked torch.softmax, then the rounded probabilities times V; flash=True
+    rounds exp(s - rowmax) and divides by the unrounded row sum afterwards)."""
     t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    R = (lambda x, n: x) if rnd is None else (lambda x, n: _Round.apply(x, lambda y: rnd(y, n)))
+    GR = (lambda x, n: x) if rnd is None else (lambda x, n: _GradRound.apply(x, lambda y: rnd(y, n)))
     B, L, H = h.shape
     nh, nkv, hd = d.num_heads, d.num_kv_heads, d.head_dim
     one = lambda key: 1 + w[key] if w.get(key) is not None else None
@@ -273,10 +314,10 @@ def torch_block_t(h, temb, pos, mask, w, d, T, image_ids=None):
     else:
         ps = pt = qs = qt = torch.zeros((), dtype=torch.float64)
         pg = qg = torch.ones((), dtype=torch.float64)
-    x = (1 + ps) * F.rms_norm(h, (H,), weight=one("norm1_w"), eps=d.eps) + pt
-    q = F.linear(x, w["to_q"]).view(B, L, nh, hd).transpose(1, 2)
-    k = F.linear(x, w["to_k"]).view(B, L, nkv, hd).transpose(1, 2)
-    v = F.linear(x, w["to_v"]).view(B, L, nkv, hd).transpose(1, 2)
+    x = R((1 + ps) * F.rms_norm(h, (H,), weight=one("norm1_w"), eps=d.eps) + pt, "x1")
+    q = GR(F.linear(x, w["to_q"]), "dq").view(B, L, nh, hd).transpose(1, 2)
+    k = GR(F.linear(x, w["to_k"]), "dk").view(B, L, nkv, hd).transpose(1, 2)
+    v = GR(R(F.linear(x, w["to_v"]), "v"), "dv").view(B, L, nkv, hd).transpose(1, 2)
     q = F.rms_norm(q, (hd,), weight=one("norm_q_w"), eps=d.eps)
     k = F.rms_norm(k, (hd,), weight=one("norm_k_w"), eps=d.eps)
     if pos is not None:
@@ -287,6 +328,7 @@ def torch_block_t(h, temb, pos, mask, w, d, T, image_ids=None):
         rot = torch.polar(torch.ones(L, hd // 2, dtype=torch.float64), torch.cat(freqs, dim=1))
         q = torch.view_as_real(torch.view_as_complex(q.reshape(B, nh, L, hd // 2, 2).contiguous()) * rot).flatten(-2)
         k = torch.view_as_real(torch.view_as_complex(k.reshape(B, nkv, L, hd // 2, 2).contiguous()) * rot).flatten(-2)
+    q, k = R(q, "q"), R(k, "k")
     valid = torch.ones(B, L, dtype=torch.bool)
     if mask is not None:
         valid[:, :T] = torch.from_numpy(np.asarray(mask).astype(bool))
@@ -296,18 +338,30 @@ def torch_block_t(h, temb, pos, mask, w, d, T, image_ids=None):
         j = torch.arange(L)
         vis = (j[None, :] <= j[:, None]) | ((ids[:, None] >= 0) & (ids[:, None] == ids[None, :]))
         am = am & vis[None, None]
-    o = F.scaled_dot_product_attention(q, k, v, attn_mask=am, enable_gqa=True)
-    o = o.transpose(1, 2).reshape(B, L, nh * hd) * torch.sigmoid(F.linear(x, w["to_gate"]))
-    h = h + pg * F.linear(o, w["to_out"])
-    x2 = (1 + qs) * F.rms_norm(h, (H,), weight=one("norm2_w"), eps=d.eps) + qt
-    ff = F.linear(F.silu(F.linear(x2, w["ff_gate"])) * F.linear(x2, w["ff_up"]), w["ff_down"])
-    return h + qg * ff
+    if rnd is None:
+        o = F.scaled_dot_product_attention(q, k, v, attn_mask=am, enable_gqa=True)
+    else:
+        kk, vv = k.repeat_interleave(nh // nkv, dim=1), v.repeat_interleave(nh // nkv, dim=1)
+        s = GR((q @ kk.transpose(-1, -2)) / math.sqrt(hd), "ds").masked_fill(~am, float("-inf"))
+        if flash:
+            e = torch.exp(s - s.amax(dim=-1, keepdim=True))
+            o = (R(e, "p") @ vv) / e.sum(dim=-1, keepdim=True)
+        else:
+            o = R(torch.softmax(s, dim=-1), "p") @ vv
+    o = GR(R(o.transpose(1, 2).reshape(B, L, nh * hd), "o"), "do")
+    gate = GR(R(F.linear(x, w["to_gate"]), "g"), "dgraw")
+    og = R(o * torch.sigmoid(gate), "og")
+    h = h + pg * GR(F.linear(og, w["to_out"]), "dy")
+    x2 = R((1 + qs) * F.rms_norm(h, (H,), weight=one("norm2_w"), eps=d.eps) + qt, "x2")
+    a = R(F.silu(GR(F.linear(x2, w["ff_gate"]), "dgt")) * GR(F.linear(x2, w["ff_up"]), "du"), "a")
+    return h + qg * GR(F.linear(a, w["ff_down"]), "dz")
 
 
-def torch_block(h, temb, pos, mask, w, d, T):
+def torch_block(h, temb, pos, mask, w, d, T, image_ids=None, rnd=None, flash=False):
     t = lambda a: torch.from_numpy(np.asarray(a, np.float64))
     wt = {key: (None if val is None else t(val)) for key, val in w.items()}
-    return torch_block_t(t(h), None if temb is None else t(temb), pos, mask, wt, d, T).numpy()
+    return torch_block_t(t(h), None if temb is None else t(temb), pos, mask, wt, d, T, image_ids=image_ids,
+                         rnd=rnd, flash=flash).numpy()
 
 
 @pytest.mark.parametrize("case", ["gqa2", "gqa4_tiny_axes", "mha_nomask", "unmodulated"])
@@ -681,16 +735,16 @@ def test_text_fusion_padded_tokens_cannot_change_valid_tokens():
     np.testing.assert_array_equal(a[1, :2], b[1, :2])
 
 
-def torch_text_fusion(enc, mask, tw, td):
+def torch_text_fusion(enc, mask, tw, td, rnd=None):
     B, T, NL, D = enc.shape
     x = enc.reshape(B * T, NL, D)
     for bw in tw["layerwise"]:
-        x = torch_block(x, None, None, None, bw, td, 0)
+        x = torch_block(x, None, None, None, bw, td, 0, rnd=rnd)
     y = F.linear(torch.from_numpy(np.ascontiguousarray(np.swapaxes(x, 1, 2))),
                  torch.from_numpy(tw["compress_w"].astype(np.float64))[None]).squeeze(-1).numpy()
     y = y.reshape(B, T, D)
     for bw in tw["refiner"]:
-        y = torch_block(y, None, None, mask, bw, td, T)
+        y = torch_block(y, None, None, mask, bw, td, T, rnd=rnd)
     return y
 
 
@@ -719,26 +773,33 @@ def test_backbone_quickstart_output_shape():
     assert list(out.shape) == g["printed_shape"]
 
 
+def torch_backbone(wl, d, mw, inp, td, rnd=None):
+    """The backbone composed from torch routines in float64, with the rounding hook of R13."""
+    R = (lambda x, n: x) if rnd is None else rnd
+    tt = lambda a: torch.from_numpy(np.asarray(a, np.float64))
+    tw = mw["time"]
+    emb = R(tt(O.timestep_embedding(inp["timestep"], 16)), "temb_in")
+    e = F.linear(R(F.gelu(F.linear(emb, tt(tw["lin1_w"]), tt(tw["lin1_b"])), approximate="tanh"), "temb_act"),
+                 tt(tw["lin2_w"]), tt(tw["lin2_b"]))
+    temb = F.linear(R(F.gelu(e, approximate="tanh"), "temb_e"), tt(tw["mod_w"]), tt(tw["mod_b"]))
+    fused = R(tt(torch_text_fusion(inp["enc"], inp["mask"], mw["text"], td, rnd=rnd)), "text_fused")
+    txt = F.linear(fused, tt(mw["txt_in_w"]), tt(mw["txt_in_b"]))
+    img = F.linear(tt(inp["x"]), tt(mw["img_in_w"]), tt(mw["img_in_b"]))
+    h = torch.cat([txt, img], dim=1).numpy()
+    for bw in mw["blocks"]:
+        h = torch_block(h, temb.numpy(), inp["position_ids"], inp["mask"], bw, d, wl.T, rnd=rnd)
+    hi = tt(h[:, wl.T:])
+    scale, shift = (tt(mw["final_table"])[None] + e[:, None]).unbind(1)
+    x = R((1 + scale[:, None]) * F.rms_norm(hi, (d.hidden,), eps=d.eps) + shift[:, None], "final_x")
+    return F.linear(x, tt(mw["final_w"]), tt(mw["final_b"])).numpy(), temb.numpy(), txt.numpy()
+
+
 def test_backbone_matches_library_composition():
     wl, d, mw, inp = micro_backbone(seed=52, B=2, T=4, grid=(2, 3), valid=(3, 1), in_ch=8)
     td = S.text_block_dims(TEXT_MICRO)
     got = O.backbone_forward(inp["x"], inp["enc"], inp["timestep"], inp["position_ids"], inp["mask"], mw, d,
                              td, wl.T, time_dim=16)
-    tt = lambda a: torch.from_numpy(np.asarray(a, np.float64))
-    tw = mw["time"]
-    emb = tt(O.timestep_embedding(inp["timestep"], 16))
-    e = F.linear(F.gelu(F.linear(emb, tt(tw["lin1_w"]), tt(tw["lin1_b"])), approximate="tanh"),
-                 tt(tw["lin2_w"]), tt(tw["lin2_b"]))
-    temb = F.linear(F.gelu(e, approximate="tanh"), tt(tw["mod_w"]), tt(tw["mod_b"]))
-    txt = F.linear(tt(torch_text_fusion(inp["enc"], inp["mask"], mw["text"], td)), tt(mw["txt_in_w"]), tt(mw["txt_in_b"]))
-    img = F.linear(tt(inp["x"]), tt(mw["img_in_w"]), tt(mw["img_in_b"]))
-    h = torch.cat([txt, img], dim=1).numpy()
-    for bw in mw["blocks"]:
-        h = torch_block(h, temb.numpy(), inp["position_ids"], inp["mask"], bw, d, wl.T)
-    hi = tt(h[:, wl.T:])
-    scale, shift = (tt(mw["final_table"])[None] + e[:, None]).unbind(1)
-    x = (1 + scale[:, None]) * F.rms_norm(hi, (d.hidden,), eps=d.eps) + shift[:, None]
-    ref = F.linear(x, tt(mw["final_w"]), tt(mw["final_b"])).numpy()
+    ref = torch_backbone(wl, d, mw, inp, td)[0]
     assert got.shape == (2, wl.N, 8)
     np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
 
@@ -801,22 +862,174 @@ def test_bf16_round_matches_library_conversion():
     np.testing.assert_array_equal(O.bf16_round(x), ref)
 
 
-def test_block_bf16_operand_mode():
-    wl, inp = micro_inputs(seed=61)
-    args = (inp["h"], inp["temb"], inp["position_ids"], inp["mask"], inp["weights"], MICRO, wl.T)
+BLOCK_POINTS = ("x1", "q", "k", "v", "g", "p", "o", "og", "x2", "a")
+BWD_POINTS = ("dz", "dgt", "du", "dy", "do", "dgraw", "dq", "dk", "dv", "ds")
+
+
+def _np_hook(off):
+    """The oracle's rounding at every named point except `off`."""
+    return lambda x, point=None: x if point == off else O.bf16_round(x)
+
+
+def _rnd_cases():
+    d4 = S.BlockDims(hidden=64, num_heads=4, num_kv_heads=1, head_dim=16, intermediate=40,
+                     axes_dims=(4, 6, 6), rope_theta=1000.0, eps=1e-5)
+    yield "gqa2", MICRO, *micro_inputs(seed=61), None
+    yield "gqa4", d4, *micro_inputs(seed=62, B=1, T=5, grid=(3, 2), valid=(4,), dims=d4), None
+    wl, inp = micro_inputs(seed=63, modulated=False)
+    inp["temb"], inp["position_ids"] = None, None
+    yield "unmodulated", MICRO, wl, inp, None
+    wl, inp = micro_inputs(seed=64, B=2, T=4, grid=(2, 3), valid=(3, 4))
+    yield "block_causal", MICRO, wl, inp, np.array([-1, -1, -1, -1, 0, 0, 0, 1, 1, 1])
+
+
+@pytest.mark.parametrize("flash", [False, True])
+def test_block_bf16_mode_matches_library_composition(flash):
+    # R13: the oracle's bf16 mode against the torch composition with torch's own bf16 conversion at
+    # the same named points, in both softmax rounding forms; and it is not the exact function.
+    for name, d, wl, inp, ids in _rnd_cases():
+        args = (inp["h"], inp["temb"], inp["position_ids"], inp["mask"], inp["weights"], d, wl.T)
+        got = O.block_forward(*args, rnd=O.bf16_round, image_ids=ids, flash=flash)
+        ref = torch_block(*args, image_ids=ids, rnd=torch_bf16, flash=flash)
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11, err_msg=name)
+        exact = O.block_forward(*args, image_ids=ids)
+        assert np.abs(got - exact).max() > 1e-6 * np.sqrt(np.mean(exact ** 2)), name
+
+
+def test_block_bf16_each_point_is_applied_where_the_composition_applies_it():
+    # Switching one named point off on both sides keeps them equal (the point sits at the same place
+    # in both) and changes the result (the point is applied), for every point of the block.
+    _, d, wl, inp, _ = next(_rnd_cases())
+    args = (inp["h"], inp["temb"], inp["position_ids"], inp["mask"], inp["weights"], d, wl.T)
+    full = O.block_forward(*args, rnd=O.bf16_round)
+    rms = np.sqrt(np.mean(full ** 2))
+    for point in BLOCK_POINTS:
+        got = O.block_forward(*args, rnd=_np_hook(point))
+        ref = torch_block(*args, rnd=skip_point(point))
+        np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11, err_msg=point)
+        assert np.abs(got - full).max() > 1e-6 * rms, f"point {point} has no effect"
+
+
+def test_block_bf16_mode_forms_and_identity_hook():
+    # An identity hook gives the exact function bit for bit; the two softmax rounding forms agree
+    # without rounding and differ with it.
+    _, d, wl, inp, _ = next(_rnd_cases())
+    args = (inp["h"], inp["temb"], inp["position_ids"], inp["mask"], inp["weights"], d, wl.T)
     exact = O.block_forward(*args)
-    np.testing.assert_array_equal(O.block_forward(*args, rnd=lambda x: x), exact)
-    b = O.block_forward(*args, rnd=O.bf16_round)
-    rel = np.abs(b - exact).max() / np.sqrt(np.mean(exact ** 2))
-    assert 1e-5 < rel < 5e-2
-    # rounding every operand point to bf16 equals rounding the same inputs of the exact steps:
-    # with weights, h and temb already bf16-representable, zero gates still give the identity
+    np.testing.assert_array_equal(O.block_forward(*args, rnd=lambda x, point=None: x), exact)
+    np.testing.assert_allclose(O.block_forward(*args, flash=True), exact, rtol=1e-12, atol=1e-13)
+    a = O.block_forward(*args, rnd=O.bf16_round)
+    b = O.block_forward(*args, rnd=O.bf16_round, flash=True)
+    assert np.abs(a - b).max() > 1e-7 * np.sqrt(np.mean(exact ** 2))
+    # rounding every point leaves zero gates the identity (weights, h and temb are bf16 values)
     w = dict(inp["weights"])
-    H = MICRO.hidden
+    H = d.hidden
     tab = w["scale_shift_table"].astype(np.float64).copy()
     tab[2] = -inp["temb"][0, 2 * H:3 * H]
     tab[5] = -inp["temb"][0, 5 * H:6 * H]
     w["scale_shift_table"] = tab
-    got = O.block_forward(inp["h"][:1], inp["temb"][:1], inp["position_ids"], inp["mask"][:1], w, MICRO, wl.T,
+    got = O.block_forward(inp["h"][:1], inp["temb"][:1], inp["position_ids"], inp["mask"][:1], w, d, wl.T,
                           rnd=O.bf16_round)
     np.testing.assert_array_equal(got, inp["h"][:1].astype(np.float64))
+
+
+DELTA_FREE = ("ff_down", "ff_gate", "ff_up", "norm2_w", "to_out", "to_v", "to_gate")
+
+
+def _bwd_rnd(case, hook_np, hook_t):
+    d, wl, inp, ids = _bwd_case(case)
+    w = inp["weights"]
+    dh_out = np.random.default_rng(72).standard_normal(inp["h"].shape)
+    t = lambda a: torch.from_numpy(np.asarray(a, np.float64)).requires_grad_(True)
+    ht = t(inp["h"])
+    tt = None if inp["temb"] is None else t(inp["temb"])
+    wt = {key: (None if val is None else t(val)) for key, val in w.items()}
+    out = torch_block_t(ht, tt, inp["position_ids"], inp["mask"], wt, d, wl.T, image_ids=ids, rnd=hook_t)
+    out.backward(torch.from_numpy(dh_out))
+    dh, dtemb, grads = O.block_backward(inp["h"], inp["temb"], inp["position_ids"], inp["mask"], w, d, wl.T, dh_out,
+                                        rnd=hook_np, image_ids=ids)
+    ref = {key: val.grad.numpy() for key, val in wt.items() if val is not None}
+    ref["h"] = ht.grad.numpy()
+    got = {key: val for key, val in grads.items() if val is not None}
+    got["h"] = dh
+    if tt is not None:
+        ref["temb"], got["temb"] = tt.grad.numpy(), dtemb
+    return got, ref
+
+
+@pytest.mark.parametrize("case", ["gqa2", "block_causal"])
+def test_block_backward_bf16_mode_matches_autograd_with_hooks(case):
+    # R20 in bf16 mode against autograd through the composition, with forward rounding (straight
+    # through) and gradient rounding at the same named points. The oracle's softmax gradient uses
+    # rowsum(dO * O) with O the attention output the model holds (rounded P and o), autograd uses
+    # rowsum(dP * P) with P unrounded; with "p" and "o" off the two are the same quantity, so every
+    # gradient must agree. With every point on, the gradients that do not pass through the softmax
+    # gradient must still agree exactly.
+    hook_np = lambda x, point=None: x if point in ("p", "o") else O.bf16_round(x)
+    hook_t = lambda x, point=None: x if point in ("p", "o") else torch_bf16(x)
+    got, ref = _bwd_rnd(case, hook_np, hook_t)
+    for key in ref:
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-9, atol=1e-10, err_msg=key)
+    got, ref = _bwd_rnd(case, O.bf16_round, torch_bf16)
+    for key in DELTA_FREE:
+        np.testing.assert_allclose(got[key], ref[key], rtol=1e-9, atol=1e-10, err_msg=key)
+
+
+def test_block_backward_bf16_each_point_is_applied():
+    d, wl, inp, _ = _bwd_case("gqa2")
+    w = inp["weights"]
+    dh_out = np.random.default_rng(73).standard_normal(inp["h"].shape)
+    run = lambda r: O.block_backward(inp["h"], inp["temb"], inp["position_ids"], inp["mask"], w, d, wl.T, dh_out,
+                                     rnd=r)
+    full = run(O.bf16_round)
+    flat = lambda res: np.concatenate([res[0].ravel(), res[1].ravel()] +
+                                      [v.ravel() for v in res[2].values() if v is not None])
+    f = flat(full)
+    for point in BLOCK_POINTS + BWD_POINTS:
+        diff = np.abs(flat(run(_np_hook(point))) - f).max()
+        assert diff > 1e-6 * np.sqrt(np.mean(f ** 2)), f"point {point} has no effect on the backward"
+
+
+def test_time_text_backbone_bf16_mode_match_library_composition():
+    # R13's time-path, text and final-layer points, against the torch compositions with the hook.
+    # Each point is checked where it acts first (time path -> temb, text -> the text rows, final
+    # layer -> the velocity): downstream, later rounding points can absorb a small change.
+    wl, d, mw, inp = micro_backbone(seed=54, B=2, T=4, grid=(2, 3), valid=(3, 1), in_ch=8)
+    td = S.text_block_dims(TEXT_MICRO)
+    run = lambda r: O.backbone_forward(inp["x"], inp["enc"], inp["timestep"], inp["position_ids"], inp["mask"], mw,
+                                       d, td, wl.T, time_dim=16, rnd=r)
+    got = run(O.bf16_round)
+    ref, _, _ = torch_backbone(wl, d, mw, inp, td, rnd=torch_bf16)
+    np.testing.assert_allclose(got, ref, rtol=1e-10, atol=1e-11)
+    parts = lambda r: (O.time_path(inp["timestep"], mw["time"], 16, rnd=r)[0],
+                       O.text_embed(inp["enc"], inp["mask"], mw, td, rnd=r), run(r))
+    full = parts(O.bf16_round)
+    where = {"temb_in": 0, "temb_act": 0, "temb_e": 0, "text_fused": 1, "final_x": 2}
+    for point, i in where.items():
+        a = parts(_np_hook(point))
+        b = torch_backbone(wl, d, mw, inp, td, rnd=skip_point(point))
+        for x, y in zip(a, (b[1], b[2], b[0])):
+            np.testing.assert_allclose(x, y, rtol=1e-10, atol=1e-11, err_msg=point)
+        assert np.abs(a[i] - full[i]).max() > 1e-7 * np.sqrt(np.mean(full[i] ** 2)), f"point {point} has no effect"
+
+
+def test_float32_product_form():
+    # R13's f32_products form: the products are float32 matrix products (torch's float32 matmul on the
+    # same operands), and without rounding points the block stays within float32 accuracy of the
+    # exact function; with them it is a different realisation of the bf16 model than the float64 form.
+    g = np.random.default_rng(80)
+    a, b = g.standard_normal((3, 7, 33)), g.standard_normal((33, 5))
+    ref = (torch.from_numpy(a).float() @ torch.from_numpy(b).float()).double().numpy()
+    np.testing.assert_allclose(O._mm32(a, b), ref, rtol=1e-5, atol=1e-5)
+    _, d, wl, inp, _ = next(_rnd_cases())
+    args = (inp["h"], inp["temb"], inp["position_ids"], inp["mask"], inp["weights"], d, wl.T)
+    exact = O.block_forward(*args)
+    rms = np.sqrt(np.mean(exact ** 2))
+    assert np.abs(O.block_forward(*args, f32_products=True) - exact).max() < 1e-5 * rms
+    c = O.block_forward(*args, rnd=O.bf16_form(flash=True, f32_products=True))
+    np.testing.assert_array_equal(c, O.block_forward(*args, rnd=O.bf16_round, flash=True, f32_products=True))
+    assert np.abs(c - O.block_forward(*args, rnd=O.bf16_round, flash=True)).max() > 0.0
+    dh_out = g.standard_normal(inp["h"].shape)
+    bx = O.block_backward(*args, dh_out)
+    bf = O.block_backward(*args, dh_out, flash=True, f32_products=True)
+    np.testing.assert_allclose(bf[0], bx[0], rtol=1e-4, atol=1e-5 * np.abs(bx[0]).max())
