@@ -104,7 +104,8 @@ def cpu_baseline(wl, rows):
         4 * d.head_dim * d.num_heads * len(sel) * valid
     threads = [i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
     return {"value": round(flops / dt / 1e12, 4), "unit": "TFLOP/s", "cores": max(threads) if threads else 1,
-            "kind": "oracle", "seconds": round(dt, 2),
+            "cores_note": "BLAS threads the oracle's products ran on", "host_cpu_count": os.cpu_count(),
+            "host_cpus_usable": len(os.sched_getaffinity(0)), "kind": "oracle", "seconds": round(dt, 2),
             "sample": f"{wl.name} batch row 0: keys/values for all {L} rows + the whole block for {len(sel)} "
                       f"seeded query rows ({flops / 1e12:.3f} TFLOP), float64 NumPy"}
 

@@ -78,6 +78,7 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
   __shared__ uint4 sK[2][K_CH];
   __shared__ uint4 sV[2][V_CH];
   __shared__ uint32_t sBits[kMaxTextTiles];
+  K2_LDS_CHECK(sizeof(sK) + sizeof(sV) + sizeof(sBits), 1);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, grp = lane >> 4, col = lane & 15;
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -326,7 +327,8 @@ __global__ void __launch_bounds__(256) attn_kernel(AttnArgs p, float scale_log2)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float gv = to_f(gp[base + d0 + r]);
-        const float ov = o[hb][qb][r] * inv;
+        // the attention output is a T tensor (bf16 in the bf16 model); the gate multiplies that
+        const float ov = to_f(to_t<T>(o[hb][qb][r] * inv));
         if (p.o_pre) ((T*)p.o_pre)[base + d0 + r] = to_t<T>(ov);
         op[base + d0 + r] = to_t<T>(ov * sigmoidf_(gv));
       }
@@ -388,6 +390,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
   __shared__ uint4 sK0[KT * KCH], sK1[KT * KCH];
   __shared__ uint4 sV0[HD * VCH], sV1[HD * VCH];
   __shared__ uint64_t sBits[kMaxTextTiles64];
+  K2_LDS_CHECK(sizeof(sK0) + sizeof(sK1) + sizeof(sV0) + sizeof(sV1) + sizeof(sBits), 2);  // 2 per CU
 #define K2_SK(st) ((st) ? sK1 : sK0)
 #define K2_SV(st) ((st) ? sV1 : sV0)
 
@@ -671,9 +674,10 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
         for (int e = 0; e < 8; ++e) ov[e] = (bf16)v[e];
         *(bf16x8*)((bf16*)p.o_pre + base) = ov;
       }
+      // the attention output is a bf16 tensor in the bf16 model: the gate multiplies the rounded value
       bf16x8 out;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = (bf16)(v[e] * sigmoidf_((float)gv[e]));
+      for (int e = 0; e < 8; ++e) out[e] = (bf16)((float)(bf16)v[e] * sigmoidf_((float)gv[e]));
       *(bf16x8*)((bf16*)p.og + base) = out;
     }
   }
@@ -790,7 +794,8 @@ __global__ void __launch_bounds__(256) attn_short_kernel(AttnArgs p, float scale
         const bf16x4 gv = *(const bf16x4*)(gp + d0);
         bf16x4 out;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) out[e] = (bf16)(o[hb][4 * j + e] * inv * sigmoidf_((float)gv[e]));
+        for (int e = 0; e < 4; ++e)  // the gate multiplies the bf16 attention output
+          out[e] = (bf16)((float)(bf16)(o[hb][4 * j + e] * inv) * sigmoidf_((float)gv[e]));
         *(bf16x4*)(op + d0) = out;
         if (p.o_pre) {
           bf16x4 ov;

@@ -84,6 +84,7 @@ __device__ __forceinline__ float group_sum(float v) {  // over N consecutive lan
 template <typename T>
 __global__ void __launch_bounds__(256) transpose_kernel(TransposeArgs p) {
   __shared__ T tile[64][65];
+  K2_LDS_CHECK(sizeof(tile), 1);
   const int z = blockIdx.z;
   const T* src = (const T*)p.src + (size_t)(z / p.zdiv) * p.sz0 + (size_t)(z % p.zdiv) * p.sz1;
   T* dst = (T*)p.dst + (size_t)(z / p.zdiv) * p.dz0 + (size_t)(z % p.zdiv) * p.dz1;
@@ -114,6 +115,7 @@ __global__ void __launch_bounds__(256) transpose_vec_kernel(TransposeArgs p) {
   constexpr int EPC = 16 / sizeof(T);  // elements per chunk
   constexpr int CPR = 64 / EPC;        // chunks per 64-element tile row
   __shared__ uint4 tile[64 * CPR];
+  K2_LDS_CHECK(sizeof(tile), 1);
   const int z = blockIdx.z;
   const T* src = (const T*)p.src + (size_t)(z / p.zdiv) * p.sz0 + (size_t)(z % p.zdiv) * p.sz1;
   T* dst = (T*)p.dst + (size_t)(z / p.zdiv) * p.dz0 + (size_t)(z % p.zdiv) * p.dz1;
@@ -330,6 +332,7 @@ template <int NT, int CACHE>
 __global__ void __launch_bounds__(NT) norm_bwd_kernel(NormBwdArgs p) {
   constexpr int NW = NT / 64;  // waves
   __shared__ float red[2][2][NW];
+  K2_LDS_CHECK(sizeof(red), 1);
   const int chunk = blockIdx.x;
   const int b = chunk / p.ncb, c = chunk - b * p.ncb;
   const int l0 = c * p.RC, l1 = min(p.L, l0 + p.RC);
@@ -560,6 +563,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
   static_assert(NKV >= 1 && NT >= 1, "tile / thread mismatch");
   __shared__ uint4 sK[2][32 * RP], sV[2][32 * RP], sT[2][HD * TP];
   __shared__ float4 sB[2][8];  // per key of the tile: 0 if it may be attended, -inf if not
+  // at most one workgroup's LDS per compute unit; two per compute unit (the launch bounds' aim) in bf16
+  K2_LDS_CHECK(sizeof(sK) + sizeof(sV) + sizeof(sT) + sizeof(sB), sizeof(T) == 2 ? 2 : 1);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -731,6 +736,7 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
   static_assert(NQ >= 1 && NT >= 1, "tile / thread mismatch");
   __shared__ uint4 sQ[2][32 * RP], sD[2][32 * RP], sQT[2][HD * TP], sDT[2][HD * TP];
   __shared__ float4 sL[2][8], sDl[2][8];
+  K2_LDS_CHECK(sizeof(sQ) + sizeof(sD) + sizeof(sQT) + sizeof(sDT) + sizeof(sL) + sizeof(sDl), 1);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -1012,6 +1018,7 @@ template <typename T, int HD>
 __global__ void __launch_bounds__(256) qknorm_bwd_kernel(QkNormBwdArgs p) {
   constexpr int TPI = HD / 8, IPB = 256 / TPI;  // threads per item, items per pass of a block
   __shared__ float red[IPB][HD];
+  K2_LDS_CHECK(sizeof(red), 1);
   const int ch = threadIdx.x % TPI, slot = threadIdx.x / TPI;
   float wd[8];
 #pragma unroll
@@ -1091,6 +1098,7 @@ hipError_t qknorm_bwd(int dt, const QkNormBwdArgs& p, int blocks, hipStream_t s)
 __device__ __forceinline__ void reduce_rows_block(const float* __restrict__ part, int nc, int ncols, int ldp,
                                                   float* __restrict__ out, int ldo, int gr, int cb) {
   __shared__ float red[4][64];
+  K2_LDS_CHECK(sizeof(red), 1);
   const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
   const int j = cb * 64 + tx;
   float a0 = 0.0f, a1 = 0.0f, a2 = 0.0f, a3 = 0.0f;

@@ -36,6 +36,7 @@ template <typename TO, int R>
 __global__ void __launch_bounds__(256) modnorm_kernel(ModnormArgs p) {
   constexpr int CACHE = 8;  // float4 per thread and row kept in registers (rows up to 8192 wide)
   __shared__ float red[R][4];
+  K2_LDS_CHECK(sizeof(red), 1);
   const int r0 = R * blockIdx.x;
   const int nr = min(R, p.rows - r0);
   const int H4 = p.H >> 2;
@@ -131,6 +132,7 @@ __global__ void __launch_bounds__(256) modnorm_kernel(ModnormArgs p) {
 template <int R, int NT>
 __global__ void __launch_bounds__(NT) modnorm8_kernel(ModnormArgs p) {
   __shared__ float red[R][NT / 64];
+  K2_LDS_CHECK(sizeof(red), 1);
   const int r0 = R * blockIdx.x;
   const int nr = min(R, p.rows - r0);
   const int c = threadIdx.x;  // 8-column chunk
@@ -376,6 +378,7 @@ hipError_t fill_f32(float* out, int n, float v, hipStream_t s) {
 // holding the first position of the chunk after the current one).
 __global__ void __launch_bounds__(1024) block_reach_kernel(const int* __restrict__ ids, int L, int* __restrict__ reach) {
   __shared__ int sm[1024];
+  K2_LDS_CHECK(sizeof(sm), 1);
   const int tid = threadIdx.x;
   int carry = INT_MAX;
   for (int c0 = ((L - 1) / 1024) * 1024; c0 >= 0; c0 -= 1024) {

@@ -611,6 +611,7 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, int scn, B
   auto swz = [](int row) { return W32 ? swz128(row) : swz8(row); };
 
   __shared__ uint4 smem[2][(BM + BN) * CPR];
+  K2_LDS_CHECK(sizeof(smem), 1);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
@@ -1008,6 +1009,7 @@ __global__ void __launch_bounds__(256)
 gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int scn, int nmain, BMap bmap,
                  Epi epi) {
   __shared__ uint4 lds[Rings<RA, RB>::units(4)];
+  K2_LDS_CHECK(sizeof(lds), 1);
   const int tiles_m = (M + 255) / 256, tiles_n = (Ntot + 255) / 256;
   const int bid = blockIdx.x;
   int tm, tn;

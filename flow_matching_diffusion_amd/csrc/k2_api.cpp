@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <climits>
 #include <mutex>
 #include <initializer_list>
 #include <string>
@@ -140,6 +141,20 @@ int check_sizes(int B, int T, int N) {
   return K2_OK;
 }
 
+// The attention kernels reach one batch row's keys through one buffer descriptor (byte offsets below
+// 0x7FFFFFF0: keys past it would read as zeros and take softmax mass) and index rows and V^T with
+// 32-bit integers, so the sequence and the row count are bounded for the block's dims.
+int check_extent(const k2_block_cfg* c, long long B, long long L) {
+  const long long es = (long long)dt_size(c->dtype), nk = (long long)c->num_kv_heads * c->head_dim;
+  const long long ldvt = L <= 32 ? 32 : (L + 63) / 64 * 64;
+  if (B * L > INT_MAX) return fail(K2_ERR_SHAPE, "B * (T + N) = %lld rows exceeds 2^31 - 1", B * L);
+  if (L * nk * es > 0x7FFFFFF0LL)
+    return fail(K2_ERR_SHAPE, "sequence of %lld tokens too long: its keys (%lld bytes per batch row) exceed 2^31 - 16 bytes",
+                L, L * nk * es);
+  if (B * nk * ldvt > INT_MAX) return fail(K2_ERR_SHAPE, "B * kv columns * padded sequence exceeds 2^31 - 1");
+  return K2_OK;
+}
+
 int check_ws(const void* ws, size_t have, size_t need) {
   if (need == 0) return K2_OK;
   if (!ws) return fail(K2_ERR_NULL, "workspace is NULL");
@@ -267,6 +282,7 @@ int validate_block_call(const k2_block_cfg* cfg, const k2_block_weights* w, int 
   if ((rc = check_block_cfg(cfg, pos != nullptr)) != K2_OK) return rc;
   if ((rc = check_block_weights(w)) != K2_OK) return rc;
   if ((rc = check_sizes(B, T, N)) != K2_OK) return rc;
+  if ((rc = check_extent(cfg, B, (long long)T + N)) != K2_OK) return rc;
   if (!hin || !hout) return fail(K2_ERR_NULL, "hidden_in / hidden_out is NULL");
   if (w->scale_shift_table && !temb) return fail(K2_ERR_NULL, "temb is NULL but the block has a scale_shift_table");
   if (!w->scale_shift_table && temb) return fail(K2_ERR_CONFIG, "temb given for a block without scale_shift_table");
@@ -377,6 +393,8 @@ int check_text(const k2_text_cfg* c, const k2_text_weights* w, int B, int T) {
   if (B <= 0 || T <= 0) return fail(K2_ERR_SHAPE, "text fusion needs B >= 1 and T >= 1");
   if ((long long)B * T > 65535) return fail(K2_ERR_SHAPE, "B * T must be <= 65535");
   if (T > 16384) return fail(K2_ERR_SHAPE, "at most 16384 text tokens (got %d)", T);
+  if ((rc = check_extent(&c->block, (long long)B * T, c->num_layers)) != K2_OK) return rc;
+  if ((rc = check_extent(&c->block, B, T)) != K2_OK) return rc;
   return K2_OK;
 }
 
@@ -458,6 +476,7 @@ int check_model(const k2_model_cfg* c, const k2_model_weights* w, int B, int T, 
   k2_time_cfg tc = {c->block.hidden, c->timestep_embed_dim, c->block.dtype};
   if ((rc = check_time(&tc, &w->time, B)) != K2_OK) return rc;
   if ((rc = check_sizes(B, T, N)) != K2_OK) return rc;
+  if ((rc = check_extent(&c->block, B, (long long)T + N)) != K2_OK) return rc;
   if (N <= 0) return fail(K2_ERR_SHAPE, "the backbone needs N >= 1 image tokens");
   if (text && T > 0 && (rc = check_text(&c->text, &w->text, B, T)) != K2_OK) return rc;
   return K2_OK;

@@ -92,6 +92,13 @@ __device__ __forceinline__ float wave_sum(float v) {
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 constexpr uint32_t kOOB = 0x80000000u;
 
+// LDS a workgroup may hold on gfx950 (static plus dynamic); a dispatch asking for more is rejected
+// and aborts the queue, so every kernel checks its static LDS at compile time. wgs: workgroups the
+// kernel's launch bounds expect to share one compute unit.
+constexpr size_t kLdsBytes = 163840;
+#define K2_LDS_CHECK(bytes, wgs) \
+  static_assert((size_t)(bytes) * (wgs) <= kLdsBytes, "static LDS exceeds what the launch bounds allow")
+
 __device__ __forceinline__ rsrc_t make_rsrc(const void* p, size_t bytes) {
   const uint32_t n = bytes > 0x7FFFFFF0ull ? 0x7FFFFFF0u : (uint32_t)bytes;
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)n, 0x00020000);

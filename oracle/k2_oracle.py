@@ -61,7 +61,9 @@ Readings where the pages are silent or garbled (each restated where it is used):
       rounded for the product and the row sum is taken before rounding and divided at the end. The
       two forms differ only in where the probabilities are rounded. f32_products=True is a third
       legitimate form: every matrix product accumulates in float32, as matrix cores do, instead of
-      float64. The spread between these forms measures how much any bf16 implementation may
+      float64. In the fused form the running maximum may lag the row maximum (a fused kernel that
+      rescales only on large growth): lag_seed draws that lag, which re-draws the probabilities'
+      rounding. The spread between these forms measures how much any bf16 implementation may
       legitimately differ from the plain one (a small change anywhere re-draws the rounding of
       every later point).
   R14 sampler shift ([PIPELINE] Krea2Pipeline, scheduler and is_distilled parameters): mu is the
@@ -107,14 +109,14 @@ def _id(x, point=None):
     return x
 
 
-def bf16_form(flash=False, f32_products=False):
+def bf16_form(flash=False, f32_products=False, lag_seed=None):
     """bf16 rounding at R13's named points in one of R13's legitimate forms: the returned rounding
-    function carries the softmax rounding form and the product accumulation type, which
-    block_forward reads when its own flash / f32_products arguments are left at None, so the form
-    also reaches the blocks inside text fusion and the backbone."""
+    function carries the softmax rounding form, the product accumulation type and (fused form
+    only) the seed of the running-maximum lag, which block_forward reads when its own arguments
+    are left at None, so the form also reaches the blocks inside text fusion and the backbone."""
     def rnd(x, point=None):
         return bf16_round(x)
-    rnd.flash, rnd.f32_products = bool(flash), bool(f32_products)
+    rnd.flash, rnd.f32_products, rnd.lag_seed = bool(flash), bool(f32_products), lag_seed
     return rnd
 
 
@@ -190,15 +192,18 @@ def apply_rope(x, angles):
 # ----------------------------------------------------------------------------------------------
 # Attention
 # ----------------------------------------------------------------------------------------------
-def attention(q, k, v, key_valid, visible=None, rnd=None, flash=False, f32_products=False):
+def attention(q, k, v, key_valid, visible=None, rnd=None, flash=False, f32_products=False, lag_seed=None):
     """Softmax attention with GQA and a key mask, [ARTICLE] §四.3.
     q: (B, nh, Lq, hd); k, v: (B, nkv, Lk, hd); key_valid: (B, Lk) bool or None; visible: (Lq, Lk)
     bool or None, which keys each query may attend (the same for every batch row and head; R17).
     Query head hq reads kv head hq // (nh / nkv) (repeat_interleave, R4); scale 1/sqrt(hd) (R3).
     A query row with no allowed key returns zeros (R17). rnd rounds the probabilities at "p" where
     they enter the P V product (R13); flash selects where (R13's softmax rounding form);
-    f32_products accumulates the two products in float32 (R13). Heads are taken one at a time,
-    which bounds memory and changes no arithmetic."""
+    f32_products accumulates the two products in float32 (R13); lag_seed (fused form): the
+    probabilities are formed against a running maximum that lags the row maximum by a seeded
+    amount in [0, 8) (log2 units), as a fused kernel that rescales only on large growth holds them,
+    which scales exp(s - max) by 2^lag before rounding and cancels in the division. Heads are taken
+    one at a time, which bounds memory and changes no arithmetic."""
     r = rnd or _id
     mm = _mm32 if f32_products else np.matmul
     B, nh, Lq, hd = q.shape
@@ -211,12 +216,15 @@ def attention(q, k, v, key_valid, visible=None, rnd=None, flash=False, f32_produ
         allowed &= visible[None]
     some = allowed.any(axis=-1, keepdims=True)
     out = np.empty((B, nh, Lq, v.shape[-1]), dtype=F64)
+    lag = None
+    if flash and lag_seed is not None:
+        lag = np.random.default_rng(lag_seed).random((B, nh, Lq, 1)) * 8.0 * math.log(2.0)
     for hq in range(nh):
         kh, vh = _f64(k[:, hq // g]), _f64(v[:, hq // g])
         s = mm(_f64(q[:, hq]), np.swapaxes(kh, -1, -2)) / math.sqrt(hd)
         s = np.where(allowed, s, -np.inf)
         s = s - np.where(some, np.max(s, axis=-1, keepdims=True), 0.0)
-        e = np.exp(s)
+        e = np.exp(s if lag is None else s + lag[:, hq])
         denom = np.where(some, np.sum(e, axis=-1, keepdims=True), 1.0)
         if flash:
             out[:, hq] = mm(r(e, "p"), vh) / denom
@@ -272,6 +280,7 @@ def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermedia
     """
     flash = getattr(rnd, "flash", False) if flash is None else flash
     f32_products = getattr(rnd, "f32_products", False) if f32_products is None else f32_products
+    lag_seed = getattr(rnd, "lag_seed", None)
     rnd = rnd or _id
     mm = _mm32 if f32_products else np.matmul
     h = _f64(h)
@@ -314,7 +323,8 @@ def block_forward(h, temb, position_ids, mask, w, dims, T, rows=None, intermedia
     out["q"], out["k"], out["v"], out["g"] = q, k, v, graw
 
     vis = None if image_ids is None else block_causal_visible(image_ids, rows)
-    o = attention(q, k, v, key_valid_mask(B, L, T, mask), vis, rnd=rnd, flash=flash, f32_products=f32_products)
+    o = attention(q, k, v, key_valid_mask(B, L, T, mask), vis, rnd=rnd, flash=flash, f32_products=f32_products,
+                  lag_seed=lag_seed)
     o = rnd(o.transpose(0, 2, 1, 3).reshape(B, R, nh * hd), "o")
     og = rnd(o * sigmoid(graw), "og")                        # R6
     out["o"], out["og"] = o, og
@@ -424,8 +434,8 @@ def block_backward(h, temb, position_ids, mask, w, dims, T, dh_out, rnd=None, im
     q, k = r(qn, "q"), r(kn, "k")
     key_valid = key_valid_mask(B, L, T, mask)
     vis = None if image_ids is None else block_causal_visible(image_ids)
-    o = r(attention(q, k, v, key_valid, vis, rnd=rnd, flash=flash, f32_products=f32_products),
-          "o")   # the attention output as the model holds it
+    o = r(attention(q, k, v, key_valid, vis, rnd=rnd, flash=flash, f32_products=f32_products,
+                    lag_seed=getattr(rnd, "lag_seed", None)), "o")   # the attention output as the model holds it
     oc = o.transpose(0, 2, 1, 3).reshape(B, L, nh * hd)
     sg = sigmoid(graw)
     og = r(oc * sg, "og")

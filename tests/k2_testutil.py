@@ -2,6 +2,8 @@
 from __future__ import annotations
 
 import ctypes
+import json
+import os
 
 import numpy as np
 import pytest
@@ -26,34 +28,67 @@ def rel_err(got, ref):
 
 
 TOL = {"f32": 1e-4, "bf16": 2e-2}
+# How far one more bf16 realisation's error statistic can land above the largest of the three forms
+# the tests compute, per kind of output; measured on the oracle alone by tests/golden/bf16_spread_study.py.
+SPREAD = json.load(open(os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden", "bf16_spread.json")))
 
 
-def parity(tag, dtype, got, oracle_fn):
-    """fp32: max rel err <= 1e-4 against the exact oracle.
+def err_stats(got, ref, rms):
+    """max, 99.9th percentile and rms of |got - ref| relative to rms (the exact output's), and the
+    fraction of elements above the 2e-2 figure."""
+    d = np.abs(np.asarray(got, np.float64) - np.asarray(ref, np.float64))
+    return {"max": d.max() / rms, "p999": float(np.quantile(d, 0.999)) / rms,
+            "rms": float(np.sqrt(np.mean(d * d))) / rms, "frac": float(np.mean(d > TOL["bf16"] * rms))}
 
-    bf16: the bf16 model hands its matrix products bf16 operands, which costs a deviation from the
-    exact function that no bf16-operand implementation avoids. The oracle measures that deviation
-    itself (its bf16-operand mode against its exact mode, on the same inputs); the GPU must stay
-    within it: rms <= 1.25 x the oracle's rms deviation (+1e-4) and max <= 1.5 x its max deviation
-    (+2e-3), both relative to the exact output's RMS. The GPU's rounding noise is independent of the
-    oracle's (flash attention rounds unnormalised probabilities, accumulation orders differ), so it
-    is compared with the deviation's size, not with the emulated values. The 2e-2 figure is printed.
-    """
+
+def _fmt(st):
+    return f"max {st['max']:.3e} p99.9 {st['p999']:.3e} rms {st['rms']:.3e} >2e-2: {st['frac']:.2e}"
+
+
+def parity(tag, dtype, got, oracle_fn, kind="forward"):
+    """fp32: max|gpu - exact| / rms(exact) <= 1e-4.
+
+    bf16: the bf16 model hands its matrix products bf16 operands; its deviation from the exact
+    function is set by that rounding, not by the kernels, and a small change anywhere re-draws the
+    rounding of every later point. The oracle computes three legitimate realisations of the bf16
+    model on the same inputs (R13): A, the plain one (normalised probabilities rounded, float64
+    products); B, the fused-attention softmax form; C, form B with float32 products, as matrix
+    cores accumulate. The GPU is one more realisation. Asserted:
+      * against the exact oracle: max, p99.9 and rms of the GPU's error are each at most the largest
+        of A's, B's and C's times SPREAD's factor for that statistic and kind of output (how far one
+        more realisation was seen to land above the largest of those three, on the oracle alone);
+      * against A, the bf16-operand oracle: p99.9 and rms of |gpu - A| are at most sqrt(2) times the
+        largest of the GPU's and the emulations' deviation from exact (times the rms factor): two
+        realisations with independent rounding noise differ by that much, and only a GPU error that
+        is larger than the model's or anti-correlated with it exceeds it.
+    Printed for every case: the statistics of the GPU and of A, B and C against exact, of the GPU
+    and of B and C against A, and whether the 2e-2 figure holds. Returns the GPU's statistics."""
     from oracle import k2_oracle as O
     assert np.all(np.isfinite(got)), f"{tag}: non-finite output"
     exact = oracle_fn(None)
-    err, rms = rel_err(got, exact)
+    rms = float(np.sqrt(np.mean(np.asarray(exact, np.float64) ** 2)))
+    g = err_stats(got, exact, rms)
     if dtype == "f32":
-        print(f"{tag}: max rel err {err:.3e}, rms {rms:.3e}", flush=True)
-        assert err <= TOL["f32"], f"{tag}: {err:.3e} > {TOL['f32']}"
-        return
-    ref16 = oracle_fn(O.bf16_round)
-    err16, rms16 = rel_err(got, ref16)
-    imax, irms = rel_err(ref16, exact)
-    print(f"{tag}: vs exact max {err:.3e} rms {rms:.3e} (<= 2e-2: {err <= TOL['bf16']}); oracle bf16-vs-exact "
-          f"max {imax:.3e} rms {irms:.3e}; vs bf16-operand oracle max {err16:.3e} rms {rms16:.3e}", flush=True)
-    assert rms <= 1.25 * irms + 1e-4, f"{tag}: rms {rms:.3e} > 1.25 x {irms:.3e} + 1e-4"
-    assert err <= 1.5 * imax + 2e-3, f"{tag}: max {err:.3e} > 1.5 x {imax:.3e} + 2e-3"
+        print(f"{tag}: max rel err {g['max']:.3e}, rms {g['rms']:.3e}", flush=True)
+        assert g["max"] <= TOL["f32"], f"{tag}: {g['max']:.3e} > {TOL['f32']}"
+        return g
+    em = {"A": oracle_fn(O.bf16_form()), "B": oracle_fn(O.bf16_form(flash=True)),
+          "C": oracle_fn(O.bf16_form(flash=True, f32_products=True))}
+    e = {k: err_stats(v, exact, rms) for k, v in em.items()}
+    gA = err_stats(got, em["A"], rms)
+    eA = {k: err_stats(em[k], em["A"], rms) for k in ("B", "C")}
+    fac = SPREAD["factor"][kind]
+    print(f"{tag}: GPU vs exact {_fmt(g)} | 2e-2 {'met' if g['max'] <= TOL['bf16'] else 'NOT met'}", flush=True)
+    for k in "ABC":
+        print(f"{tag}:   {k} vs exact {_fmt(e[k])}", flush=True)
+    print(f"{tag}: GPU vs A {_fmt(gA)}; B vs A {_fmt(eA['B'])}; C vs A {_fmt(eA['C'])}", flush=True)
+    for s in ("max", "p999", "rms"):
+        bound = fac[s] * max(e[k][s] for k in "ABC")
+        assert g[s] <= bound, f"{tag}: GPU {s} vs exact {g[s]:.3e} > {fac[s]:.3f} x largest of A/B/C = {bound:.3e}"
+    for s in ("p999", "rms"):
+        lim = fac["rms"] * np.sqrt(2.0) * max([g[s]] + [e[k][s] for k in "ABC"])
+        assert gA[s] <= lim, f"{tag}: GPU {s} vs A {gA[s]:.3e} > independent-noise limit {lim:.3e}"
+    return g
 
 
 def temb_for(wl, inp):

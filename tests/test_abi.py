@@ -113,6 +113,12 @@ def test_block_validation_codes():
     assert call_block(cols=2) == ESHAPE
     assert call_block(B=0) == ESHAPE
     assert call_block(T=-1) == ESHAPE
+    # one batch row's keys must fit one 2 GiB buffer range (bf16: 1536 columns x 2 bytes per token),
+    # and B * (T + N) rows a 32-bit index
+    L_max = 0x7FFFFFF0 // (12 * 128 * 2)
+    assert call_block(T=512, N=L_max - 512, rows=L_max) == EWS   # passes validation, fails on ws
+    assert call_block(T=512, N=L_max - 511, rows=L_max + 1) == ESHAPE and b"too long" in lib.k2_last_error()
+    assert call_block(B=65535, T=512, N=40000, rows=40512) == ESHAPE and b"2^31" in lib.k2_last_error()
     w = good_weights(); w.to_k = None
     assert call_block(w=w) == ENULL
     assert call_block(temb=None) == ENULL

@@ -1,11 +1,13 @@
 """GPU parity of k2_block_forward against the CPU oracle (needs an MI355X and libk2.so).
 
-Sizes: the tiny fp32 block and micro shapes with ragged tails are compared element by element;
-the full-size 512^2 block in full; the 1024^2 pair and the 2048^2 long block on seeded row samples
-(keys and values of every row enter each sampled row's attention, so the sample still checks the
-whole key range). Tolerances on max|gpu - oracle| / rms(oracle): fp32 <= 1e-4 against the exact
-oracle; bf16 <= 2e-2 against the oracle with bf16 operands, and against the exact oracle no worse
-than that oracle's own bf16-vs-exact deviation (tests/k2_testutil.parity).
+Sizes: the tiny fp32 block and micro shapes with ragged tails; the full-size 512^2 block and the
+1024^2 pair over every output; the 2048^2 long block on a seeded row sample (keys and values of every
+row enter each sampled row's attention, so the sample still checks the whole key range). Bars on
+|gpu - oracle| / rms(oracle): fp32 max <= 1e-4 against the exact oracle; bf16 the bounds of
+tests/k2_testutil.parity, derived from three legitimate realisations of the bf16 model (the 2e-2
+figure is printed for every case, and where it is not met it is the bf16 model's own deviation).
+The bf16 stage chain compares every kernel's bf16 output element by element with the oracle's
+step applied to the GPU's own input to that step, within per-element bounds stated there.
 """
 import numpy as np
 import pytest
@@ -143,9 +145,9 @@ def test_block512_full():
     _check(wl, S.block_inputs(wl))
 
 
-def test_block1024_sampled_rows():
+def test_block1024_full():
     wl = workload("block1024")
-    _check(wl, S.block_inputs(wl), rows=S.sample_rows(wl, 96))
+    _check(wl, S.block_inputs(wl))
 
 
 def test_block2048_sampled_rows():
@@ -154,3 +156,111 @@ def test_block2048_sampled_rows():
     rows = S.sample_rows(wl, 256)
     assert {0, 511, 512, 16895} <= set(rows.tolist())
     _check(wl, inp, rows=rows)
+
+
+def _excess_elem(got, ref, K):
+    """Per element, |got - ref| minus what two roundings of nearly equal values allow: 1 bf16 ulp of
+    the larger magnitude, plus the float32 arithmetic before the rounding, 4 sqrt(K) 2^-24 rms(ref)
+    for a K-term sum (a random walk of K float32 roundings, 4 standard deviations, at the scale of
+    the stage's values). Near-zero results of cancelling sums need the second term. <= 0 passes."""
+    got, ref = np.asarray(got, np.float64), np.asarray(ref, np.float64)
+    m = np.maximum(np.abs(got), np.abs(ref))
+    ulp = np.exp2(np.floor(np.log2(np.maximum(m, 2.0 ** -126))) - 7)
+    acc = 4.0 * np.sqrt(K) * 2.0 ** -24 * np.sqrt(np.mean(ref * ref))
+    return np.abs(got - ref) - (ulp + acc)
+
+
+def _bf16_stage_chain(wl, inp, temb):
+    """Each bf16 kernel's output against the oracle's step applied to the GPU's own input to it.
+    Bounds, per element:
+      x1 (modnorm from h), q, k, v^T, g (projection, q/k norm, RoPE from the GPU's x1), x2 (modnorm of
+      h + pregate * (og Wo^T) from the GPU's og), a (SwiGLU from the GPU's x2): both sides round to
+      bf16 values that differ only by float32 arithmetic, so <= 1 ulp plus that arithmetic's error
+      (_excess, with K the length of the stage's sums: hidden for the norms and projections);
+      og (attention from the GPU's q, k, v, gated by its g): the kernel rounds exp(s - m) at its own
+      running maximum m, the oracle's fused form at the final one, each within 2^-9 relative, so
+      |o_gpu - o_ref| <= 2^-8 sum_j p_j |v_j| (plus 1e-5 of it for float32 arithmetic); both then
+      round o and o * sigmoid(g): |og_gpu - og_ref| <= sigmoid(g) (that bound + 1 ulp of o) + 1 ulp
+      of og;
+      out (down projection + residual from the GPU's a): max error <= 1e-4 of rms(out), the float32 bar.
+    """
+    import torch
+    import flow_matching_diffusion_amd as k2
+    d, T = wl.dims, wl.T
+    w = inp["weights"]
+    got, ws, cfg = gpu_block(wl, inp, temb, keep_ws=True)
+    lay = k2.block_workspace_layout(cfg, wl.B, T, wl.N)
+    B, L, H, M = wl.B, wl.L, d.hidden, wl.M
+    nh, nkv, hd, I, eps = d.num_heads, d.num_kv_heads, d.head_dim, d.intermediate, d.eps
+    nq, nk = nh * hd, nkv * hd
+
+    def view(off, n, shape):
+        return ws[off:off + 2 * n].view(torch.bfloat16).float().reshape(shape).cpu().numpy().astype(np.float64)
+
+    g_x1 = view(lay.x1, M * H, (B, L, H))
+    g_q = view(lay.q, M * nq, (B, L, nh, hd)).transpose(0, 2, 1, 3)
+    g_k = view(lay.k, M * nk, (B, L, nkv, hd)).transpose(0, 2, 1, 3)
+    g_vt = view(lay.vt, B * nk * lay.ldvt, (B, nkv, hd, lay.ldvt))[..., :L]
+    g_g = view(lay.g, M * nq, (B, L, nq))
+    g_og = view(lay.og, M * nq, (B, L, nq))
+    g_x2 = view(lay.x2, M * H, (B, L, H))
+    g_a = view(lay.a, M * I, (B, L, I))
+    del ws
+    h = inp["h"].astype(np.float64)
+    mod = O.modulation(temb, w["scale_shift_table"])
+    ps, pt, pg, qs, qt, qg = (mod[:, i, None, :] for i in range(6))
+    W = {k_: np.asarray(v_, np.float64) for k_, v_ in w.items()}
+    r = O.bf16_round
+    res = {}
+    rel = {}
+
+    def _excess(got_, ref_, K):
+        rel[len(rel)] = np.abs(np.asarray(got_, np.float64) - ref_).max() / np.sqrt(np.mean(np.asarray(ref_) ** 2))
+        return _excess_elem(got_, ref_, K)
+
+    res["x1"] = _excess(g_x1, r((1 + ps) * O.rms_norm(h, W["norm1_w"], eps) + pt), H).max()
+    ang = O.rope_angles(inp["position_ids"], d.axes_dims, d.rope_theta)[None, None]
+    q = O.apply_rope(O.rms_norm((g_x1 @ W["to_q"].T).reshape(B, L, nh, hd).transpose(0, 2, 1, 3), W["norm_q_w"], eps), ang)
+    k = O.apply_rope(O.rms_norm((g_x1 @ W["to_k"].T).reshape(B, L, nkv, hd).transpose(0, 2, 1, 3), W["norm_k_w"], eps), ang)
+    v = (g_x1 @ W["to_v"].T).reshape(B, L, nkv, hd).transpose(0, 2, 1, 3)
+    res["q"] = _excess(g_q, r(q), H).max()
+    res["k"] = _excess(g_k, r(k), H).max()
+    res["vt"] = _excess(g_vt, r(v).transpose(0, 1, 3, 2), H).max()
+    res["g"] = _excess(g_g, r(g_x1 @ W["to_gate"].T), H).max()
+    # attention from the GPU's q, k, v^T and gate
+    g_v = g_vt.transpose(0, 1, 3, 2)
+    kv = O.key_valid_mask(B, L, T, inp["mask"])
+    o_ref = O.attention(g_q, g_k, g_v, kv, rnd=r, flash=True).transpose(0, 2, 1, 3).reshape(B, L, nq)
+    spread = O.attention(g_q, g_k, np.abs(g_v), kv).transpose(0, 2, 1, 3).reshape(B, L, nq)  # sum_j p_j |v_j|
+    sg = O.sigmoid(g_g)
+    og_ref = r(r(o_ref) * sg)
+    ulp = lambda x: np.exp2(np.floor(np.log2(np.maximum(np.abs(x), 2.0 ** -126))) - 7)
+    bound = sg * ((2.0 ** -8 + 1e-5) * spread + 2 * ulp(o_ref)) + 2 * ulp(og_ref)
+    excess = np.abs(g_og - og_ref) - bound
+    res["og"] = excess.max()
+    # residual, second norm, SwiGLU and down projection from the GPU's og, x2 and a
+    h1 = h + pg * (g_og @ W["to_out"].T)
+    res["x2"] = _excess(g_x2, r((1 + qs) * O.rms_norm(h1, W["norm2_w"], eps) + qt), nq).max()
+    res["a"] = _excess(g_a, r(O.silu(g_x2 @ W["ff_gate"].T) * (g_x2 @ W["ff_up"].T)), H).max()
+    out = h1 + qg * (g_a @ W["ff_down"].T)
+    res["out"] = rel_err(got, out)[0]
+    print(f"{wl.name} bf16 stage chain (largest excess over the per-element bound; out: max rel err): " +
+          ", ".join(f"{k_} {v_:.3g}" for k_, v_ in res.items()), flush=True)
+    print(f"{wl.name} bf16 stage chain, max |gpu - ref| / rms(ref) per stage: " +
+          ", ".join(f"{k_} {rel[i]:.3g}" for i, k_ in enumerate(("x1", "q", "k", "vt", "g", "x2", "a"))), flush=True)
+    for key in ("x1", "q", "k", "vt", "g", "og", "x2", "a"):
+        assert res[key] <= 0.0, f"{key} exceeds its per-element bound by {res[key]:.3e}"
+    assert res["out"] <= 1e-4, f"out: {res['out']:.3e}"
+
+
+def test_block_bf16_stage_chain_micro():
+    dims, dt, B, T, grid, valid = MICRO["g4_hd128_bf16"]
+    wl = S.Workload("stages16", 131, dt, B, T, grid, valid, dims=dims)
+    inp = S.block_inputs(wl)
+    _bf16_stage_chain(wl, inp, temb_for(wl, inp))
+
+
+def test_block_bf16_stage_chain_block512():
+    wl = workload("block512")
+    inp = S.block_inputs(wl)
+    _bf16_stage_chain(wl, inp, temb_for(wl, inp))
