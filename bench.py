@@ -12,11 +12,14 @@ same resolution as denoise steps/s (one call = one CFG step), the sampler on one
 as the base checkpoint's 28 steps and without as the distilled 8 steps) as time per image, both with
 the text rows computed once per prompt pair (k2_text_embed, then k2_denoise_step_cached) and with
 the text path run at every step (k2_denoise_step), the block-causal block variant on the same pair
-(a condition block then the target block), the block's backward pass (k2_block_backward), per-kernel times, the roofline of the dominant kernel, and
-the CPU oracle on a bounded sample.
+(a condition block then the target block), the block's backward pass (k2_block_backward),
+per-kernel times, the roofline of the dominant kernel, the 512^2 and 2048^2 blocks (TFLOP/s, % of
+peak, median and min, per-kernel split), the matrix-core rate a pure-MFMA probe sustains, and the
+CPU oracle on a bounded sample. Per-step median and min come from events recorded between steps.
 
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-backbone] [--no-cpu-baseline]
-                       [--no-block-causal] [--no-backward] [--cpu-rows R] [--copy-calibration]
+                       [--no-block-causal] [--no-backward] [--no-probe] [--no-other-blocks] [--cpu-rows R]
+                       [--copy-calibration]
 --copy-calibration first runs a plain elementwise copy (negation) of 1 GiB float32, a kernel of known
 HBM traffic against which the rocprofv3 FETCH_SIZE / WRITE_SIZE counters are scaled.
 """
@@ -75,6 +78,80 @@ def traffic_for(key):
     return e["fetch_bytes"] + e["write_bytes"]
 
 
+def block_leg(k2, S, torch, dev, wl, steps, warmup):
+    """k2_block_forward on workload wl (device-generated inputs of its shape): mean / median / min time
+    per step, TFLOP/s and % of the bf16 peak, and the per-kernel split from further steps with events
+    around every launch."""
+    import ctypes
+
+    import numpy as np
+    d = wl.dims
+    B, T, N, L = wl.B, wl.T, wl.N, wl.L
+    f32 = torch.float32
+    w = S.device_block_weights(wl.seed, "block.", d, wl.dtype, dev)
+    h = S.device_normal(wl.seed, "hidden", (B, L, d.hidden), 1.0, f32, dev)
+    if wl.t is not None:
+        tw = S.device_model_weights(wl.seed, S.replace(wl, num_layers=0), dev)["time"]
+        temb, _ = k2.timestep_modulation_forward(d.hidden, wl.timestep_embed_dim, wl.dtype, tw,
+                                                 torch.tensor(wl.t, dtype=f32, device=dev))
+    else:
+        temb = S.device_normal(wl.seed, "temb", (B, 6 * d.hidden), 1.0, f32, dev)
+    pos = torch.from_numpy(S.position_ids(T, *wl.grid)).to(dev)
+    m = S.text_mask(B, T, wl.valid)
+    mask = None if m is None else torch.from_numpy(m).to(dev)
+    cfg = k2.block_cfg(d, wl.dtype)
+    out = torch.empty_like(h)
+    ws = torch.empty(k2.load().k2_block_workspace_bytes(ctypes.byref(cfg), B, T, N), dtype=torch.uint8, device=dev)
+
+    def step():
+        k2.block_forward(cfg, w, h, temb, pos, mask, T, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        step()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    evs[0].record()
+    for i in range(steps):
+        step()
+        evs[i + 1].record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per = [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+    ms = max(wall, evs[0].elapsed_time(evs[-1]) / steps)
+    valid = [L if wl.valid is None else N + v for v in (wl.valid or [L] * B)]
+    flops = block_flops(d, B, L, valid)
+    k2.profile_reset()
+    k2.profile_filter(None)
+    k2.profile_enable(True)
+    nsplit = max(1, steps // 4)
+    for _ in range(nsplit):
+        step()
+    torch.cuda.synchronize()
+    k2.profile_enable(False)
+    M = B * L
+    kernels = {}
+    for name in KERNELS:
+        tot, n = k2.profile_query(name)
+        if n:
+            kernels[name] = {"avg_ms": round(tot / n, 4), "launches_per_step": n // nsplit}
+            kf = kernel_flops(d, M, name)
+            if name == "attention":
+                kf = sum(4 * d.head_dim * d.num_heads * L * v for v in valid)
+            if kf:
+                kernels[name]["tflops"] = round(kf / (tot / n * 1e-3) / 1e12, 1)
+                kernels[name]["pct_bf16_peak"] = round(100 * kf / (tot / n * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)
+    del w, h, out, ws
+    torch.cuda.empty_cache()
+    med = float(np.median(per))
+    return {"config": {"B": B, "text_tokens": T, "valid_text": list(wl.valid or []), "grid": list(wl.grid), "L": L},
+            "steps": steps, "ms_per_step": round(ms, 4), "median_ms": round(med, 4), "min_ms": round(min(per), 4),
+            "tflops": round(flops / (ms * 1e-3) / 1e12, 1), "pct_bf16_peak": round(100 * flops / (ms * 1e-3) / 1e12 /
+                                                                                  PEAK_BF16_TFLOPS, 2),
+            "tflops_median": round(flops / (med * 1e-3) / 1e12, 1), "block_gflop": round(flops / 1e9, 1),
+            "kernels": kernels}
+
+
 def cpu_baseline(wl, rows):
     """The CPU oracle as it stands on a bounded sample of the same workload: batch row 0, keys and
     values for all of its rows, the whole block for `rows` sampled query rows."""
@@ -124,6 +201,8 @@ def main():
     ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4608)
     ap.add_argument("--copy-calibration", action="store_true")
+    ap.add_argument("--no-probe", action="store_true")
+    ap.add_argument("--no-other-blocks", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py: the library runs on one GPU only; --gpus must be 1 (no multi-GPU path exists)",
@@ -176,19 +255,20 @@ def main():
     k2.profile_reset()
     k2.profile_filter(dom)
     k2.profile_enable(True)
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    e0.record()
-    for _ in range(args.steps):
+    evs[0].record()
+    for i in range(args.steps):
         step()
-    e1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     k2.profile_enable(False)
     dom_tot, dom_n = k2.profile_query(dom)
     wall_ms = (t1 - t0) * 1e3 / args.steps
-    ev_ms = e0.elapsed_time(e1) / args.steps
+    per_step = [evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps)]
+    ev_ms = evs[0].elapsed_time(evs[-1]) / args.steps
     ms = max(wall_ms, ev_ms)
     valid_keys = [L if wl.valid is None else N + v for v in (wl.valid or [L] * B)]
     flops = block_flops(d, B, L, valid_keys)
@@ -211,10 +291,12 @@ def main():
             kf = kernel_flops(d, M, name)
             if kf:
                 kernels[name]["tflops"] = round(kf / (tot / n * 1e-3) / 1e12, 1)
+                kernels[name]["pct_bf16_peak"] = round(100 * kf / (tot / n * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 1)
     kernels[dom]["avg_ms_timed_region"] = round(dom_tot / dom_n, 4)
     attn_flops = sum(4 * d.head_dim * d.num_heads * L * v for v in valid_keys)
     if "attention" in kernels:
         kernels["attention"]["tflops"] = round(attn_flops / (kernels["attention"]["avg_ms"] * 1e-3) / 1e12, 1)
+        kernels["attention"]["pct_bf16_peak"] = round(100 * kernels["attention"]["tflops"] / PEAK_BF16_TFLOPS, 1)
     if "modnorm" in kernels:
         nbytes = M * d.hidden * (4 + (2 if wl.dtype == "bf16" else 4))
         kernels["modnorm"]["gbs"] = round(nbytes / (kernels["modnorm"]["avg_ms"] * 1e-3) / 1e9, 1)
@@ -236,10 +318,43 @@ def main():
                    "grid": list(wl.grid), "L": L, "hidden": d.hidden, "heads": d.num_heads, "kv_heads": d.num_kv_heads,
                    "head_dim": d.head_dim, "intermediate": d.intermediate, "timestep": list(wl.t or [])},
         "pct_bf16_peak": round(100 * tflops / PEAK_BF16_TFLOPS, 2),
+        "step_ms": {"mean": round(ms, 4), "median": round(float(np.median(per_step)), 4),
+                    "min": round(min(per_step), 4), "max": round(max(per_step), 4),
+                    "note": "value uses the mean over the timed region (max of wall clock and events); "
+                            "median / min from events recorded between steps"},
+        "pct_bf16_peak_median": round(100 * flops / (float(np.median(per_step)) * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 2),
         "block_gflop": round(flops / 1e9, 1),
         "kernels": kernels,
         "roofline": roofline,
     }
+
+    # The matrix-core rate the part sustains with no memory traffic (k2_mfma_rate_probe), beside the
+    # 2.4 GHz specification figure the percentages use.
+    if not args.no_probe:
+        pout = torch.zeros(4, dtype=torch.float32, device=dev)
+        iters, blocks = 4000, 512
+        k2.mfma_rate_probe(iters // 10, blocks, pout)
+        torch.cuda.synchronize()
+        pe = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        pe[0].record()
+        k2.mfma_rate_probe(iters, blocks, pout)
+        pe[1].record()
+        torch.cuda.synchronize()
+        p_tf = blocks * iters * 524288 / (pe[0].elapsed_time(pe[1]) * 1e-3) / 1e12
+        result["mfma_probe"] = {"tflops": round(p_tf, 1), "pct_of_spec_peak": round(100 * p_tf / PEAK_BF16_TFLOPS, 1),
+                                "block_pct_of_probe": round(100 * tflops / p_tf, 2),
+                                "what": f"{blocks} workgroups x 4 waves, {iters} x 4 independent bf16 32x32x16 "
+                                        "products per wave on registers, no memory traffic"}
+        del pout
+
+    # The other block workloads of the same full-size dims: the 512^2 block (B = 1, L = 1280, the small-M
+    # GEMM case) and the 2048^2 long-sequence block (B = 1, L = 16896, attention-heavy), each timed like
+    # the headline with its per-kernel split.
+    if not args.no_other_blocks:
+        legs = {}
+        for name, nsteps in (("block512", max(args.steps, 50)), ("block2048", max(5, args.steps // 2))):
+            legs[name] = block_leg(k2, S, torch, dev, S.WORKLOADS[name], nsteps, args.warmup)
+        result["blocks"] = legs
 
     # The block-causal variant (k2_block_forward_block_causal) on the same pair: the image tokens as
     # a 1024-token condition block followed by the target block (condition images first, target

@@ -465,3 +465,11 @@ def profile_query(kernel: str):
     n = ctypes.c_int()
     check(load().k2_profile_query(kernel.encode(), ctypes.byref(ms), ctypes.byref(n)))
     return ms.value, n.value
+
+
+def mfma_rate_probe(iters: int, blocks: int, out, stream=None):
+    """k2_mfma_rate_probe: enqueue the matrix-core rate probe (blocks * iters * 524288 bf16 FLOP).
+    out: a float32 device tensor of at least one element."""
+    torch = _torch()
+    _dev_tensor(out, "out", torch.float32)
+    check(load().k2_mfma_rate_probe(int(iters), int(blocks), _ptr(out), _stream(stream)))

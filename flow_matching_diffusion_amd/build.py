@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libk2.so")
-SOURCES = ["k2_api.cpp", "gemm.hip", "attention.hip", "elementwise.hip", "backward.hip"]
+SOURCES = ["k2_api.cpp", "gemm.hip", "attention.hip", "elementwise.hip", "backward.hip", "probe.hip"]
 
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HIPCC = os.path.join(ROCM, "bin", "hipcc")

@@ -7,6 +7,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <atomic>
 #include <climits>
 #include <mutex>
 #include <initializer_list>
@@ -42,8 +43,10 @@ struct ProfEvent {
   std::string name;
   hipEvent_t a, b;
 };
+// The one piece of process-wide state: the timing facility below (a diagnostic, off by default).
+// The flag is atomic; the event lists and the filter are guarded by g_pm.
 std::mutex g_pm;
-bool g_prof = false;
+std::atomic<bool> g_prof{false};
 std::string g_pfilter;  // record only kernels of this name ("" = all)
 std::vector<ProfEvent> g_pev;
 std::vector<hipEvent_t> g_pool;
@@ -62,7 +65,7 @@ hipEvent_t take_event() {
 template <class F>
 int run(const char* name, hipStream_t s, F f) {
   hipEvent_t a = nullptr, b = nullptr;
-  if (g_prof) {
+  if (g_prof.load(std::memory_order_relaxed)) {
     std::lock_guard<std::mutex> lk(g_pm);
     if (g_pfilter.empty() || g_pfilter == name) {
       a = take_event();
@@ -1269,9 +1272,19 @@ int k2_denoise_step_cached(const k2_model_cfg* cfg, const k2_model_weights* w, i
 
 const char* k2_last_error(void) { return g_err.c_str(); }
 
+int k2_mfma_rate_probe(int iters, int blocks, float* out, void* stream) {
+  if (!out) return fail(K2_ERR_NULL, "out is NULL");
+  if (iters <= 0 || blocks <= 0 || blocks > 65535) return fail(K2_ERR_SHAPE, "need iters >= 1 and 1 <= blocks <= 65535");
+  int rc;
+  if ((rc = check_align("out", {out})) != K2_OK) return rc;
+  g_err.clear();
+  K2_RUN("mfma_probe", (hipStream_t)stream, mfma_probe(iters, blocks, out, (hipStream_t)stream));
+  return K2_OK;
+}
+
 void k2_profile_enable(int enable) {
   std::lock_guard<std::mutex> lk(g_pm);
-  g_prof = enable != 0;
+  g_prof.store(enable != 0);
 }
 
 void k2_profile_filter(const char* kernel) {

@@ -226,4 +226,8 @@ hipError_t cfg_euler(const float* x, float* x_out, const float* vc, const float*
 // out[i] = v for i < n
 hipError_t fill_f32(float* out, int n, float v, hipStream_t s);
 
+// Matrix-core rate probe: blocks workgroups of 4 waves, each wave iters x 4 bf16 32x32x16 products
+// (blocks * 4 * iters * 4 * 32768 FLOP); writes one float to out[0].
+hipError_t mfma_probe(int iters, int blocks, float* out, hipStream_t s);
+
 }  // namespace k2

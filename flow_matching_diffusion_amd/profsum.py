@@ -13,6 +13,19 @@
       bytes (FETCH) and write N bytes (WRITE). Prints Markdown and merges
       {KEY: {fetch_bytes, write_bytes, ...}} into profiles/traffic.json, stamped with the
       hash of the kernel sources so that a stale record is never reported.
+
+  python -m flow_matching_diffusion_amd.profsum trace TRACE_CSV --cmd "..." [--skip N]
+      Per-launch-shape statistics from a `rocprofv3 --kernel-trace` run (the *_kernel_trace.csv
+      file): dispatches grouped by kernel and grid, so that one kernel's launches on different
+      workloads stay apart; the first N dispatches of each group (warm-up) are left out.
+
+  python -m flow_matching_diffusion_amd.profsum counters CSV --cmd "..." [--xcds 8] [--cus 256]
+      Matrix-core and LDS counters per kernel from a `rocprofv3 --pmc SQ_VALU_MFMA_BUSY_CYCLES
+      SQ_INSTS_MFMA SQ_INSTS_LDS SQ_LDS_BANK_CONFLICT SQ_WAVES GRBM_GUI_ACTIVE` run, dispatches
+      grouped by kernel and by their matrix-core instruction count (so that launches of one kernel
+      on different shapes stay apart). MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES over (GRBM_GUI_ACTIVE /
+      xcds) x cus x 4 SIMDs; the pure matrix-core probe kernel, if present, shows what a fully busy
+      unit reads.
 """
 from __future__ import annotations
 
@@ -100,6 +113,60 @@ def traffic(a) -> str:
         f"{(fetch_b + write_b) / 1e9:.3f} GB of HBM traffic per launch."])
 
 
+def trace(path: str, cmd: str, skip: int = 0) -> str:
+    groups: dict[tuple, list[dict]] = collections.defaultdict(list)
+    for r in csv.DictReader(open(path)):
+        key = (r["Kernel_Name"], int(r["Grid_Size_X"]), int(r["Grid_Size_Y"]), int(r["Grid_Size_Z"]))
+        groups[key].append(r)
+    rows = []
+    for (name, gx, gy, gz), rs in groups.items():
+        rs.sort(key=lambda r: int(r["Start_Timestamp"]))
+        used = rs[skip:] if len(rs) > skip else rs
+        d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in used]
+        r0 = used[0]
+        rows.append((sum(d), name, gx, gy, gz, len(used), sum(d) / len(d), min(d), max(d), r0))
+    rows.sort(key=lambda x: -x[0])
+    out = [f"Command: `{cmd}`", "", f"First {skip} dispatches of each kernel and grid left out (warm-up).", "",
+           "| kernel | grid (threads) | calls | avg us | min us | max us | VGPR | AGPR | LDS B | scratch B |",
+           "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for tot, name, gx, gy, gz, n, avg, mn, mx, r0 in rows:
+        out.append(f"| `{_short(name, 80)}` | {gx}x{gy}x{gz} | {n} | {avg:.1f} | {mn:.1f} | {mx:.1f} | {r0['VGPR_Count']} | "
+                   f"{r0['Accum_VGPR_Count']} | {r0['LDS_Block_Size']} | {r0['Scratch_Size']} |")
+    return "\n".join(out)
+
+
+def counters(path: str, cmd: str, xcds: int = 8, cus: int = 256) -> str:
+    names = ("SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_MFMA", "SQ_INSTS_LDS", "SQ_LDS_BANK_CONFLICT", "SQ_WAVES",
+             "GRBM_GUI_ACTIVE")
+    per: dict[tuple[str, str], dict[str, float]] = collections.defaultdict(lambda: collections.defaultdict(float))
+    for r in csv.DictReader(open(path)):
+        c = r["Counter_Name"]
+        if c in names:
+            per[(r["Dispatch_Id"], r["Kernel_Name"])][c] += float(r["Counter_Value"])
+    groups: dict[tuple[str, int], list[dict[str, float]]] = collections.defaultdict(list)
+    for (_, name), v in per.items():
+        groups[(name, round(v.get("SQ_INSTS_MFMA", 0.0) / 1e5))].append(v)
+    rows = []
+    for (name, _), vs in groups.items():
+        avg = {c: sum(v.get(c, 0.0) for v in vs) / len(vs) for c in names}
+        cycles = avg["GRBM_GUI_ACTIVE"] / xcds
+        busy = 100.0 * avg["SQ_VALU_MFMA_BUSY_CYCLES"] / (cycles * cus * 4) if cycles else 0.0
+        rows.append((avg["SQ_INSTS_MFMA"], name, len(vs), avg, cycles, busy))
+    rows.sort(key=lambda r: -r[0])
+    out = [f"Command: `{cmd}`", "",
+           f"MFMA busy % = SQ_VALU_MFMA_BUSY_CYCLES / ((GRBM_GUI_ACTIVE / {xcds}) x {cus} CUs x 4 SIMDs); counters "
+           "summed over their instances, averaged over the dispatches of each row.", "",
+           "| kernel | dispatches | GUI cycles (per XCD) | MFMA insts (M) | LDS insts (M) | LDS insts per MFMA | "
+           "LDS bank conflicts (M) | waves | MFMA busy % |", "|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
+    for minst, name, n, avg, cycles, busy in rows:
+        if minst == 0 and avg["SQ_INSTS_LDS"] == 0:
+            continue
+        ratio = avg["SQ_INSTS_LDS"] / minst if minst else float("nan")
+        out.append(f"| `{_short(name, 90)}` | {n} | {cycles:,.0f} | {minst / 1e6:.2f} | {avg['SQ_INSTS_LDS'] / 1e6:.2f} | "
+                   f"{ratio:.2f} | {avg['SQ_LDS_BANK_CONFLICT'] / 1e6:.3f} | {avg['SQ_WAVES']:,.0f} | {busy:.1f} |")
+    return "\n".join(out)
+
+
 def main():
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="what", required=True)
@@ -115,8 +182,24 @@ def main():
     t.add_argument("--key", required=True)
     t.add_argument("--cmd-fetch", default="")
     t.add_argument("--cmd-write", default="")
+    tr = sub.add_parser("trace")
+    tr.add_argument("csv")
+    tr.add_argument("--cmd", required=True)
+    tr.add_argument("--skip", type=int, default=0)
+    c = sub.add_parser("counters")
+    c.add_argument("csv")
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--cus", type=int, default=256)
     a = ap.parse_args()
-    print(stats(a.csv, a.cmd) if a.what == "stats" else traffic(a))
+    if a.what == "stats":
+        print(stats(a.csv, a.cmd))
+    elif a.what == "trace":
+        print(trace(a.csv, a.cmd, a.skip))
+    elif a.what == "counters":
+        print(counters(a.csv, a.cmd, a.xcds, a.cus))
+    else:
+        print(traffic(a))
 
 
 if __name__ == "__main__":

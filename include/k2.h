@@ -16,7 +16,8 @@
  *
  * Conventions shared by every entry point
  *   - Pointers named *_w, *_b, tables, activations, outputs and workspace are DEVICE pointers owned by
- *     the caller; the library allocates no device memory and keeps no per-call state.
+ *     the caller; the library allocates no device memory and keeps no per-call state (the timing
+ *     diagnostics at the end of this header are its only process-wide state).
  *   - Config and weight-table structs are HOST memory, read during the call only.
  *   - nn.Linear weights use PyTorch's (out_features, in_features) row-major layout, element type
  *     `dtype` (K2_F32: float, K2_BF16: bfloat16). Norm weights, modulation tables, biases, the
@@ -345,8 +346,18 @@ int k2_denoise_step_cached(const k2_model_cfg* cfg, const k2_model_weights* w, i
 /* Message for the last non-OK status returned on this thread ("" if none). */
 const char* k2_last_error(void);
 
+/* Matrix-core rate probe (hardware calibration, not part of the method): `blocks` workgroups of four
+   waves, each wave issuing iters x 4 independent bf16 32x32x16 matrix products on registers with no
+   memory traffic, on `stream`: blocks * iters * 524288 FLOP in one launch. Time it with events on the
+   stream to obtain the bf16 rate the part sustains (512 blocks = two waves per SIMD on 256 CUs).
+   out: device float, 16-byte aligned (one value written, never meaningful). Returns K2_ERR_NULL,
+   K2_ERR_SHAPE (iters < 1, blocks outside 1..65535), K2_ERR_ALIGN or K2_ERR_HIP. */
+int k2_mfma_rate_probe(int iters, int blocks, float* out, void* stream);
+
 /* Kernel timing with HIP events recorded on the launch stream around every kernel the library
-   launches while enabled. k2_profile_query synchronises on the recorded events and returns the
+   launches while enabled. This facility is the library's only process-wide state: the switch, the
+   filter and the recorded events are shared by every thread (guarded by a mutex); timing one
+   stream while another thread enables or resets it mixes their records. k2_profile_query synchronises on the recorded events and returns the
    total milliseconds and launch count of kernels whose name equals `kernel` (names: "modnorm",
    "gemm_qkvg", "attention", "gemm_out", "gemm_swiglu", "gemm_down", "rope", "modulation",
    "gemm_plain", "time_embed", "layer_compress", "convert", "fill", "cfg_euler", ...). Returns K2_OK or
