@@ -203,6 +203,23 @@ def block_forward(cfg, weights: dict, h, temb, position_ids, mask, T: int, out=N
     return out
 
 
+def block_forward_static_ws(cfg, weights: dict, h, temb, position_ids, mask, T: int, out=None, stream=None):
+    """k2_block_forward_static_ws: k2_block_forward with the library's static device scratch instead of
+    a workspace (nothing is allocated by the library; `out` is allocated here only when not given)."""
+    torch = _torch()
+    lib = load()
+    _dev_tensor(h, "h", torch.float32)
+    B, L, _ = h.shape
+    out = torch.empty_like(h) if out is None else _dev_tensor(out, "out", torch.float32, h.shape)
+    mask = _mask_u8(mask)
+    pos_rows, pos_cols = (position_ids.shape if position_ids is not None else (0, 0))
+    bw = _block_weights(weights)
+    check(lib.k2_block_forward_static_ws(ctypes.byref(cfg), ctypes.byref(bw), B, T, L - T, _ptr(h), _ptr(out),
+                                         _ptr(temb), _ptr(position_ids), pos_rows, pos_cols, _ptr(mask),
+                                         _stream(stream)))
+    return out
+
+
 def block_backward_workspace_bytes(cfg, B: int, T: int, N: int) -> int:
     return load().k2_block_backward_workspace_bytes(ctypes.byref(cfg), B, T, N)
 

@@ -114,6 +114,9 @@ SIGNATURES = {
                                        c_void_p, c_void_p, c_int, c_int, c_float, c_float, c_float, c_void_p, c_size_t,
                                        c_void_p]),
     "k2_last_error": (c_char_p, []),
+    "k2_block_forward_static_ws_max_bytes": (c_size_t, []),
+    "k2_block_forward_static_ws": (c_int, [POINTER(BlockCfg), POINTER(BlockWeights), c_int, c_int, c_int, c_void_p,
+                                           c_void_p, c_void_p, c_void_p, c_int, c_int, c_void_p, c_void_p]),
     "k2_mfma_rate_probe": (c_int, [c_int, c_int, c_void_p, c_void_p]),
     "k2_profile_enable": (None, [c_int]),
     "k2_profile_filter": (None, [c_char_p]),

@@ -928,6 +928,54 @@ int k2_block_forward_block_causal(const k2_block_cfg* cfg, const k2_block_weight
                    (hipStream_t)stream, image_ids);
 }
 
+// ---------------------------------------------------------------------------------------------
+// Block forward without a caller workspace: the workspace is a file-scope device array. Host code
+// never names the array itself (in host code its name is a stand-in, not a device address); its
+// address on each device is taken once with hipGetSymbolAddress and kept per device.
+// ---------------------------------------------------------------------------------------------
+constexpr size_t kStaticScratchBytes = size_t(128) << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+std::mutex g_scratch_m;
+std::vector<void*> g_scratch_ptr;  // device index -> address of `scratch` on that device
+
+// Address of the static scratch on the current device (looked up on the first call per device).
+int static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0) return fail(K2_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e));
+  std::lock_guard<std::mutex> lk(g_scratch_m);
+  if ((size_t)dev >= g_scratch_ptr.size()) g_scratch_ptr.resize(dev + 1, nullptr);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p)
+      return fail(K2_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return K2_OK;
+}
+
+size_t k2_block_forward_static_ws_max_bytes(void) { return kStaticScratchBytes; }
+
+int k2_block_forward_static_ws(const k2_block_cfg* cfg, const k2_block_weights* w, int B, int T, int N,
+                               const float* hidden_in, float* hidden_out, const float* temb,
+                               const float* position_ids, int pos_rows, int pos_cols, const uint8_t* mask,
+                               void* stream) {
+  int rc = validate_block_call(cfg, w, B, T, N, hidden_in, hidden_out, temb, position_ids, pos_rows, pos_cols);
+  if (rc != K2_OK) return rc;
+  const size_t need = k2_block_workspace_bytes(cfg, B, T, N);
+  if (need > kStaticScratchBytes)
+    return fail(K2_ERR_WORKSPACE, "this call needs %zu bytes of scratch; the static scratch holds %zu bytes", need,
+                kStaticScratchBytes);
+  void* ws = nullptr;
+  if ((rc = static_scratch(&ws)) != K2_OK) return rc;
+  g_err.clear();
+  return block_run(cfg, w, B, T, N, hidden_in, hidden_out, temb, position_ids, mask, ws, nullptr, nullptr,
+                   (hipStream_t)stream);
+}
+
 size_t k2_block_backward_workspace_bytes(const k2_block_cfg* cfg, int B, int T, int N) {
   if (!cfg || B < 0 || T < 0 || N < 0) return 0;
   return bwd_layout(cfg, B, T, N).total;

@@ -134,6 +134,25 @@ int k2_block_forward(const k2_block_cfg* cfg, const k2_block_weights* w, int B, 
                      const uint8_t* encoder_attention_mask,
                      void* workspace, size_t workspace_bytes, void* stream);
 
+/* k2_block_forward for callers that cannot allocate device memory (code under HIP graph capture,
+   tight serving loops, harnesses that forbid allocation): the same computation and kernels, with no
+   workspace argument. The library's scratch is a static device array of
+   k2_block_forward_static_ws_max_bytes() bytes (128 MiB: the full-size block at 512^2, B = 1, needs
+   123.3 MiB), held on each device the library runs on until the process ends; its address is looked
+   up once per device on the first call made with that device current, and `stream` must belong to
+   the current device. The call allocates nothing (keep the timing diagnostics below off: they create
+   events). Every call on one device shares that device's scratch: calls that overlap on one device
+   (concurrent streams, or host threads) race and must be serialised by the caller. Its contents
+   need not be cleared between calls: every byte read is written first in the same call.
+   Arguments as k2_block_forward. Returns K2_ERR_WORKSPACE when k2_block_workspace_bytes(cfg, B, T, N)
+   exceeds the static size, K2_ERR_HIP if the scratch's address cannot be obtained, else as
+   k2_block_forward. */
+size_t k2_block_forward_static_ws_max_bytes(void);
+int k2_block_forward_static_ws(const k2_block_cfg* cfg, const k2_block_weights* w, int B, int T, int N,
+                               const float* hidden_in, float* hidden_out, const float* temb,
+                               const float* position_ids, int pos_rows, int pos_cols,
+                               const uint8_t* encoder_attention_mask, void* stream);
+
 /* Backward pass of one block ([ARTICLE] §四 data flow; §六: the model's test matrix trains it, with
    gradient checkpointing): the gradients of a loss with respect to the block's input, its
    modulation input and its weights, given the gradient grad_out of the block's output

@@ -229,3 +229,22 @@ def test_time_and_text_and_backbone_validation():
     assert step(None, 1 << 40) == ENULL
     assert lib.k2_denoise_cached_workspace_bytes(ctypes.byref(m), 512, 4096, 1) < \
         lib.k2_denoise_workspace_bytes(ctypes.byref(m), 512, 4096, 1)
+
+
+def test_static_scratch_block_forward_validation():
+    # the entry point without a workspace rejects a call whose scratch exceeds the static array, before
+    # any device work (fake pointers are never touched)
+    lib = k2.load()
+    cap = lib.k2_block_forward_static_ws_max_bytes()
+    assert cap == 128 << 20
+    cfg = good_cfg()
+    assert lib.k2_block_workspace_bytes(ctypes.byref(cfg), 1, 256, 1024) <= cap   # the 512^2 block fits
+    need = lib.k2_block_workspace_bytes(ctypes.byref(cfg), 2, 512, 4096)
+    assert need > cap
+    w = good_weights()
+    call = lambda B, T, N, rows: lib.k2_block_forward_static_ws(ctypes.byref(cfg), ctypes.byref(w), B, T, N, FAKE, FAKE,
+                                                                  FAKE, FAKE, rows, 3, None, None)
+    assert call(2, 512, 4096, 4608) == EWS and b"static scratch" in lib.k2_last_error()
+    assert call(1, 256, 1024, 1279) == ESHAPE      # the usual validation comes first
+    assert lib.k2_block_forward_static_ws(None, ctypes.byref(w), 1, 4, 4, FAKE, FAKE, FAKE, FAKE, 8, 3, None,
+                                          None) == ENULL
