@@ -1001,9 +1001,10 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
 }
 
 // Workgroups 0 .. nmain-1 each compute a 256x256 tile (tile order: tile_coords). With TAIL, the
-// tiles_total - nmain tiles of the last partial round are split in two 256x128 halves run by
-// workgroups nmain + 2u and nmain + 2u + 1 (u: tail tile index), so that round takes about half as
-// long; TAIL is used when the halves fit in one round.
+// tiles_total - nmain tiles of the last partial round (or all tiles, nmain = 0, when they fill at
+// most half a round) are split in two 256x128 halves run by workgroups nmain + 2u and
+// nmain + 2u + 1 (u: tail tile index), so that round takes about half as long; TAIL is used when
+// the halves fit in one round.
 template <int SPREAD, bool KFULL, int RA, int RB, bool TAIL, class BMap, class Epi>
 __global__ void __launch_bounds__(256)
 gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int scn, int nmain, BMap bmap,
@@ -1066,9 +1067,12 @@ static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap
   if constexpr (sizeof(T) == 2 && C::DMA) {
     int nmain = tiles, grid = tiles;
     if constexpr (TAIL) {
+      // Half tiles where a round is partly idle: the last partial round when it holds at most half
+      // the compute units, or every tile when all of them fill at most half a round (small M: the
+      // 512^2 block's out and down projections are 120 tiles for 256 compute units).
       const int ncu = compute_units();
-      const int tail = tiles % ncu;
-      bool ok = tiles > ncu && tail > 0 && 2 * tail <= ncu;
+      const int tail = 2 * tiles <= ncu ? tiles : tiles % ncu;
+      bool ok = tail > 0 && 2 * tail <= ncu;
       const int tiles_m = (a.M + 255) / 256, tiles_n = (Ntot + 255) / 256;
       for (int u = tiles - tail; ok && u < tiles; ++u) {
         int tm, tn;
