@@ -135,24 +135,43 @@ struct EpiResid : EpiNoStage {
   float* hout;
   const float* gate;
   int gate_stride, L, N;
+  // Branch-free through buffer resources over the wave's rows (rows past M read zero and their
+  // stores are dropped; columns past N take an offset past every resource), so each 32-row block
+  // issues all of its residual and gate loads before a single wait. Written with a bounds branch,
+  // a wait and a store per float4, the compiled epilogue made 2 x 64 dependent memory round trips
+  // per lane.
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
                                         int M, float* stg = nullptr) const {
+    constexpr int NQ = LY::NQ, ROWS = MI * (NQ == 1 ? 16 : 32);  // rows of the wave's block
+    const int nrow = M - row0 < 0 ? 0 : (M - row0 < ROWS ? M - row0 : ROWS);
+    const size_t base = (size_t)row0 * N;
+    const rsrc_t rin = make_rsrc(hin + base, (size_t)nrow * N * sizeof(float));
+    const rsrc_t rout = make_rsrc(hout + base, (size_t)nrow * N * sizeof(float));
+    const int nb = M > 0 ? (M - 1) / L + 1 : 0;  // batch rows the gate holds
+    const rsrc_t rg = make_rsrc(gate ? gate : hin, gate && nb ? ((size_t)(nb - 1) * gate_stride + N) * sizeof(float) : 0);
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
-      const int m = row0 + LY::row(i, lane);
-      if (m >= M) continue;
-      const float* gb = gate ? gate + (size_t)(m / L) * gate_stride : nullptr;
+      const int r = LY::row(i, lane);
+      const int m = row0 + r;
+      const uint32_t grow = (uint32_t)((m < M ? m : 0) / L) * (uint32_t)gate_stride;
+      uint32_t off[NJ][NQ];
+      float4 hv[NJ][NQ], gv[NJ][NQ];
 #pragma unroll
       for (int j = 0; j < NJ; ++j)
 #pragma unroll
-        for (int q = 0; q < LY::NQ; ++q) {
+        for (int q = 0; q < NQ; ++q) {
           const int n = col0 + LY::col(j, q, lane);
-          if (n >= N) continue;
-          const size_t idx = (size_t)m * N + n;
-          const float4 g = gb ? ld4(gb + n) : make_float4(1.f, 1.f, 1.f, 1.f);
-          st4(hout + idx, fma4(g, quad(acc[i][j], q), ld4(hin + idx)));
+          off[j][q] = n < N ? (uint32_t)(r * N + n) * (uint32_t)sizeof(float) : kOOB;
+          hv[j][q] = __builtin_bit_cast(float4, bload(rin, off[j][q]));
+          gv[j][q] = gate ? __builtin_bit_cast(float4, bload(rg, n < N ? (grow + (uint32_t)n) * 4u : kOOB))
+                          : make_float4(1.f, 1.f, 1.f, 1.f);
         }
+#pragma unroll
+      for (int j = 0; j < NJ; ++j)
+#pragma unroll
+        for (int q = 0; q < NQ; ++q)
+          bstore(rout, off[j][q], fma4(gv[j][q], quad(acc[i][j], q), hv[j][q]));
     }
   }
 };
