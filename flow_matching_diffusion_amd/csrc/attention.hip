@@ -655,31 +655,39 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
       st[c32 * CPR + (c ^ (c32 & (CPR - 1)))] =
           make_float4(o[hb][4 * j] * inv, o[hb][4 * j + 1] * inv, o[hb][4 * j + 2] * inv, o[hb][4 * j + 3] * inv);
     }
-  // a wave's LDS accesses complete in order: the reads below see the writes above
-  constexpr int LPR = HD / 8, RPI = 64 / LPR;  // lanes per row, rows per instruction
+  // a wave's LDS accesses complete in order: the reads below see the writes above. The wave's 32
+  // rows of gate, output (and saved output) go through buffer resources that end at the sequence
+  // end (rows past it read zero and their stores are dropped), so all gate loads are issued before
+  // the first wait instead of one load-wait-store round trip per row group.
+  constexpr int LPR = HD / 8, RPI = 64 / LPR, NKR = 32 / RPI;  // lanes per row, rows per instruction
   const int rr = lane / LPR, cc = lane % LPR;
+  const int nrow = L - q0 < 0 ? 0 : (L - q0 < 32 ? L - q0 : 32);
+  const size_t gbase = (size_t)(b * L + q0) * ldq + head * HD;
+  const size_t span = nrow ? ((size_t)(nrow - 1) * ldq + HD) * sizeof(bf16) : 0;
+  const rsrc_t rg = make_rsrc((const bf16*)p.g + gbase, span);
+  const rsrc_t ro = make_rsrc((bf16*)p.og + gbase, span);
+  uint4 gq[NKR];
 #pragma unroll
-  for (int k = 0; k < 32 / RPI; ++k) {
+  for (int k = 0; k < NKR; ++k) gq[k] = bload(rg, (uint32_t)((RPI * k + rr) * ldq + 8 * cc) * (uint32_t)sizeof(bf16));
+#pragma unroll
+  for (int k = 0; k < NKR; ++k) {
     const int r = RPI * k + rr;
-    const int row = q0 + r;
+    const uint32_t off = (uint32_t)(r * ldq + 8 * cc) * (uint32_t)sizeof(bf16);
     const float4 a = st[r * CPR + ((2 * cc) ^ (r & (CPR - 1)))];
     const float4 bq = st[r * CPR + ((2 * cc + 1) ^ (r & (CPR - 1)))];
-    if (row < L) {
-      const size_t base = (size_t)(b * L + row) * ldq + head * HD + 8 * cc;
-      const bf16x8 gv = *(const bf16x8*)((const bf16*)p.g + base);
-      const float v[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
-      if (p.o_pre) {
-        bf16x8 ov;
+    const bf16x8 gv = __builtin_bit_cast(bf16x8, gq[k]);
+    const float v[8] = {a.x, a.y, a.z, a.w, bq.x, bq.y, bq.z, bq.w};
+    if (p.o_pre) {
+      bf16x8 ov;
 #pragma unroll
-        for (int e = 0; e < 8; ++e) ov[e] = (bf16)v[e];
-        *(bf16x8*)((bf16*)p.o_pre + base) = ov;
-      }
-      // the attention output is a bf16 tensor in the bf16 model: the gate multiplies the rounded value
-      bf16x8 out;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) out[e] = (bf16)((float)(bf16)v[e] * sigmoidf_((float)gv[e]));
-      *(bf16x8*)((bf16*)p.og + base) = out;
+      for (int e = 0; e < 8; ++e) ov[e] = (bf16)v[e];
+      bstore(make_rsrc((bf16*)p.o_pre + gbase, span), off, __builtin_bit_cast(uint4, ov));
     }
+    // the attention output is a bf16 tensor in the bf16 model: the gate multiplies the rounded value
+    bf16x8 out;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[e] = (bf16)((float)(bf16)v[e] * sigmoidf_((float)gv[e]));
+    bstore(ro, off, __builtin_bit_cast(uint4, out));
   }
 }
 

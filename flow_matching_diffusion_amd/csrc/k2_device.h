@@ -113,6 +113,9 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, float4 v) {
   __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
 }
+__device__ __forceinline__ void bstore(rsrc_t r, uint32_t off, uint4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, v), r, (int)off, 0, 0);
+}
 
 // 16-byte-per-lane DMA from a buffer into LDS at lds + 16 * lane (lds must be wave-uniform), from
 // byte offset off (per lane) + soff (wave-uniform, scalar offset field). The builtin exists for the
