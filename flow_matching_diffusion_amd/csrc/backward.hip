@@ -66,6 +66,16 @@ __device__ __forceinline__ typename FragOf<T>::type zero_frag() {
 // row index of 16-row block kb, accumulator row rho -> position in a 32-wide tile
 __device__ __forceinline__ int perm32(int kb, int rho) { return 8 * (rho >> 2) + 4 * kb + (rho & 3); }
 
+// Position of chunk cc of row r in an LDS tile of 16-chunk rows (bf16, head_dim 128). A fragment read
+// takes the 16 rows perm32(kb, 0..15) = {0-3, 8-11, 16-19, 24-27} (+4 for kb = 1) at one chunk: an
+// XOR of the chunk with row bits 0-1 and 3-4 puts those rows in 16 different 16-byte bank groups.
+// Rows padded by one chunk instead (the other tiles' layout) put rows r and r + 8 in the same banks:
+// the counters read hundreds of millions of conflict cycles per launch that way.
+template <bool SWZ>
+__device__ __forceinline__ int tile_chunk(int r, int cc) {
+  return SWZ ? cc ^ ((r & 3) | (((r >> 3) & 3) << 2)) : cc;
+}
+
 __device__ __forceinline__ float sigm(float x) { return 1.0f / (1.0f + __expf(-x)); }
 
 template <int N>
@@ -556,7 +566,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
   constexpr int E = 16 / sizeof(T);     // elements per 16-byte chunk
   constexpr int NC = HD / 32;            // k steps over head_dim
   constexpr int NDB = HD / 16;           // 16-row head-dim blocks of dQ^T
-  constexpr int RCH = HD / E, RP = RCH + 1;  // chunks per K / V row, row pitch
+  constexpr int RCH = HD / E;                // chunks per K / V row
+  constexpr bool SWZ = sizeof(T) == 2 && RCH == 16;  // bf16 head_dim 128: swizzled rows (tile_chunk)
+  constexpr int RP = SWZ ? RCH : RCH + 1;    // row pitch
   constexpr int TCH = 32 / E, TP = TCH + 1;  // chunks per K^T row (32 keys), row pitch
   constexpr int NKV = 32 * RCH / 256, NT = HD * TCH / 256;  // chunks per thread per tile
   constexpr int QW = 32 * (4 / G);       // queries per workgroup
@@ -625,8 +637,8 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
   do {                                                                                             \
     _Pragma("unroll") for (int i = 0; i < NKV; ++i) {                                              \
       const int ch_ = tid + 256 * i, row_ = ch_ / RCH, cc_ = ch_ % RCH;                             \
-      sK[ST][row_ * RP + cc_] = rk[RS][i];                                                         \
-      sV[ST][row_ * RP + cc_] = rv[RS][i];                                                         \
+      sK[ST][row_ * RP + tile_chunk<SWZ>(row_, cc_)] = rk[RS][i];                                  \
+      sV[ST][row_ * RP + tile_chunk<SWZ>(row_, cc_)] = rv[RS][i];                                  \
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                               \
       const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH;                               \
@@ -653,10 +665,11 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         s[kb][0] = s[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint4* kr = sK[st] + perm32(kb, c) * RP;
+        const int kro = perm32(kb, c);
+        const uint4* kr = sK[st] + kro * RP;
 #pragma unroll
         for (int kc = 0; kc < NC; ++kc) {
-          const Frag ka = lds_frag<T>(kr, (32 * kc + 8 * g) / E);
+          const Frag ka = lds_frag<T>(kr, tile_chunk<SWZ>(kro, (32 * kc + 8 * g) / E));
 #pragma unroll
           for (int qc = 0; qc < 2; ++qc) s[kb][qc] = mma16(s[kb][qc], ka, qf[qc][kc]);
         }
@@ -665,11 +678,12 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         dp[kb][0] = dp[kb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint4* vr = sV[st] + perm32(kb, c) * RP;
+        const int vro = perm32(kb, c);
+        const uint4* vr = sV[st] + vro * RP;
         const float bias[4] = {kbias[kb].x, kbias[kb].y, kbias[kb].z, kbias[kb].w};
 #pragma unroll
         for (int kc = 0; kc < NC; ++kc) {
-          const Frag va = lds_frag<T>(vr, (32 * kc + 8 * g) / E);
+          const Frag va = lds_frag<T>(vr, tile_chunk<SWZ>(vro, (32 * kc + 8 * g) / E));
 #pragma unroll
           for (int qc = 0; qc < 2; ++qc) dp[kb][qc] = mma16(dp[kb][qc], va, df[qc][kc]);
           // 8 / NC exponentials of key block kb per step
@@ -730,7 +744,9 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
   constexpr int E = 16 / sizeof(T);
   constexpr int NC = HD / 32;
   constexpr int NDB = HD / 16;
-  constexpr int RCH = HD / E, RP = RCH + 1;  // chunks per Q / dO row, row pitch
+  constexpr int RCH = HD / E;                // chunks per Q / dO row
+  constexpr bool SWZ = sizeof(T) == 2 && RCH == 16;  // bf16 head_dim 128: swizzled rows (tile_chunk)
+  constexpr int RP = SWZ ? RCH : RCH + 1;    // row pitch
   constexpr int TCH = 32 / E, TP = TCH + 1;  // chunks per Q^T / dO^T row (32 queries), row pitch
   constexpr int NQ = 32 * RCH / 256, NT = HD * TCH / 256;
   static_assert(NQ >= 1 && NT >= 1, "tile / thread mismatch");
@@ -798,8 +814,8 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
   do {                                                                                             \
     _Pragma("unroll") for (int i = 0; i < NQ; ++i) {                                               \
       const int ch_ = tid + 256 * i, row_ = ch_ / RCH, cc_ = ch_ % RCH;                             \
-      sQ[ST][row_ * RP + cc_] = rq[RS][i];                                                         \
-      sD[ST][row_ * RP + cc_] = rd[RS][i];                                                         \
+      sQ[ST][row_ * RP + tile_chunk<SWZ>(row_, cc_)] = rq[RS][i];                                  \
+      sD[ST][row_ * RP + tile_chunk<SWZ>(row_, cc_)] = rd[RS][i];                                  \
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                               \
       const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH;                               \
@@ -835,10 +851,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint4* qr = sQ[st] + perm32(qb, c) * RP;
+        const int qro = perm32(qb, c);
+        const uint4* qr = sQ[st] + qro * RP;
 #pragma unroll
         for (int kc = 0; kc < NC; ++kc) {
-          const Frag qa = lds_frag<T>(qr, (32 * kc + 8 * g) / E);
+          const Frag qa = lds_frag<T>(qr, tile_chunk<SWZ>(qro, (32 * kc + 8 * g) / E));
 #pragma unroll
           for (int j = 0; j < 2; ++j) s[qb][j] = mma16(s[qb][j], qa, kf[j][kc]);
         }
@@ -847,10 +864,11 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
 #pragma unroll
       for (int qb = 0; qb < 2; ++qb) {
         dp[qb][0] = dp[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const uint4* dr = sD[st] + perm32(qb, c) * RP;
+        const int dro = perm32(qb, c);
+        const uint4* dr = sD[st] + dro * RP;
 #pragma unroll
         for (int kc = 0; kc < NC; ++kc) {
-          const Frag da = lds_frag<T>(dr, (32 * kc + 8 * g) / E);
+          const Frag da = lds_frag<T>(dr, tile_chunk<SWZ>(dro, (32 * kc + 8 * g) / E));
 #pragma unroll
           for (int j = 0; j < 2; ++j) dp[qb][j] = mma16(dp[qb][j], da, vf[j][kc]);
           // 8 / NC exponentials of query block qb per step
