@@ -655,8 +655,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
       st[c32 * CPR + (c ^ (c32 & (CPR - 1)))] =
           make_float4(o[hb][4 * j] * inv, o[hb][4 * j + 1] * inv, o[hb][4 * j + 2] * inv, o[hb][4 * j + 3] * inv);
     }
-  // a wave's LDS accesses complete in order: the reads below see the writes above. The wave's 32
-  // rows of gate, output (and saved output) go through buffer resources that end at the sequence
+  wave_lds_sync();  // the reads below see every lane's writes above
+  // The wave's 32 rows of gate, output (and saved output) go through buffer resources that end at the sequence
   // end (rows past it read zero and their stores are dropped), so all gate loads are issued before
   // the first wait instead of one load-wait-store round trip per row group.
   constexpr int LPR = HD / 8, RPI = 64 / LPR, NKR = 32 / RPI;  // lanes per row, rows per instruction

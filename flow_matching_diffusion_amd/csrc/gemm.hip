@@ -129,17 +129,24 @@ struct EpiNoStage {
 };
 
 // hout = hin + gate[batch] * acc (gated residual; gate NULL means 1). hin may alias hout.
+//
+// bf16 operands: each 32-row block of the wave's accumulators goes through the wave's LDS area and
+// is read back row-major, 32 lanes per 128-column row, so every residual load and store moves whole
+// 512-byte row segments. Straight from the accumulator layout an instruction touched 32 rows
+// 24 KiB apart with 32 bytes each, and the epilogue took a fifth of the out projection's time.
+// The block's residual loads are issued before its accumulators are staged, so their latency
+// overlaps the LDS traffic; the gate is one float4 per lane while the wave's rows lie in one batch
+// row. Everything goes through buffer resources over the wave's rows (rows past M read zero and
+// their stores are dropped; columns past N take an offset past every resource).
 template <typename T>
 struct EpiResid : EpiNoStage {
+  static constexpr bool kLdsOut = sizeof(T) == 2;
+  static constexpr int kPitchF = 132;  // floats per staged row: 128 + 4 of padding
+  static constexpr int kLdsOutFloats = sizeof(T) == 2 ? 32 * kPitchF : 0;
   const float* hin;
   float* hout;
   const float* gate;
   int gate_stride, L, N;
-  // Branch-free through buffer resources over the wave's rows (rows past M read zero and their
-  // stores are dropped; columns past N take an offset past every resource), so each 32-row block
-  // issues all of its residual and gate loads before a single wait. Written with a bounds branch,
-  // a wait and a store per float4, the compiled epilogue made 2 x 64 dependent memory round trips
-  // per lane.
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
                                         int M, float* stg = nullptr) const {
@@ -150,28 +157,77 @@ struct EpiResid : EpiNoStage {
     const rsrc_t rout = make_rsrc(hout + base, (size_t)nrow * N * sizeof(float));
     const int nb = M > 0 ? (M - 1) / L + 1 : 0;  // batch rows the gate holds
     const rsrc_t rg = make_rsrc(gate ? gate : hin, gate && nb ? ((size_t)(nb - 1) * gate_stride + N) * sizeof(float) : 0);
+    if constexpr (kLdsOut) {
+      static_assert(NQ == 4 && NJ * 32 <= 128, "staged layout: 32x32 blocks, up to 128 columns per wave");
+      const int hi = lane >> 5, r = lane & 31;   // writer: row r, columns 32 j + 8 q + 4 hi
+      const int rr = lane >> 5, ch = lane & 31;  // reader: rows 2 k + rr, columns 4 ch .. 4 ch + 3
+      const int n = col0 + 4 * ch;
+      const bool colok = ch < 8 * NJ && n < N;  // N is a multiple of 4
+      const int b0 = nrow ? row0 / L : 0;
+      const bool one_b = nrow == 0 || (row0 + nrow - 1) / L == b0;  // wave-uniform
+      const float4 g0 = gate ? __builtin_bit_cast(float4, bload(rg, colok ? (uint32_t)(b0 * gate_stride + n) * 4u : kOOB))
+                             : make_float4(1.f, 1.f, 1.f, 1.f);
+      // residual rows of block i (16 row pairs), loaded one block ahead
+      float4 hv[2][16];
+      auto load = [&](float4 (&h)[16], int i) {
 #pragma unroll
-    for (int i = 0; i < MI; ++i) {
-      const int r = LY::row(i, lane);
-      const int m = row0 + r;
-      const uint32_t grow = (uint32_t)((m < M ? m : 0) / L) * (uint32_t)gate_stride;
-      uint32_t off[NJ][NQ];
-      float4 hv[NJ][NQ], gv[NJ][NQ];
+        for (int k = 0; k < 16; ++k)
+          h[k] = __builtin_bit_cast(float4, bload(rin, colok ? (uint32_t)((32 * i + 2 * k + rr) * N + n) * 4u : kOOB));
+      };
+      load(hv[0], 0);
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int i = 0; i < MI; ++i) {
+        if (i + 1 < MI) load(hv[(i + 1) & 1], i + 1);
 #pragma unroll
-        for (int q = 0; q < NQ; ++q) {
-          const int n = col0 + LY::col(j, q, lane);
-          off[j][q] = n < N ? (uint32_t)(r * N + n) * (uint32_t)sizeof(float) : kOOB;
-          hv[j][q] = __builtin_bit_cast(float4, bload(rin, off[j][q]));
-          gv[j][q] = gate ? __builtin_bit_cast(float4, bload(rg, n < N ? (grow + (uint32_t)n) * 4u : kOOB))
-                          : make_float4(1.f, 1.f, 1.f, 1.f);
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(stg + r * kPitchF + 32 * j + 8 * q + 4 * hi) = quad(acc[i][j], q);
+        wave_lds_sync();  // the reads below see every lane's writes above
+        const float4(&h)[16] = hv[i & 1];
+        if (one_b) {
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const int sr = 2 * k + rr, row = 32 * i + sr;  // staged row, row of the wave's block
+            const float4 v = *reinterpret_cast<const float4*>(stg + sr * kPitchF + 4 * ch);
+            bstore(rout, colok ? (uint32_t)(row * N + n) * 4u : kOOB, fma4(g0, v, h[k]));
+          }
+        } else {  // the wave's rows span two batch rows: the gate per row
+#pragma unroll
+          for (int k = 0; k < 16; ++k) {
+            const int sr = 2 * k + rr, row = 32 * i + sr;
+            const float4 v = *reinterpret_cast<const float4*>(stg + sr * kPitchF + 4 * ch);
+            const int m = row0 + row < M ? row0 + row : M - 1;
+            const float4 gv = gate ? __builtin_bit_cast(float4, bload(rg, colok ? (uint32_t)((m / L) * gate_stride + n) * 4u : kOOB))
+                                   : g0;
+            bstore(rout, colok ? (uint32_t)(row * N + n) * 4u : kOOB, fma4(gv, v, h[k]));
+          }
         }
+        wave_lds_sync();  // the next block's writes come after every lane's reads
+      }
+    } else {
 #pragma unroll
-      for (int j = 0; j < NJ; ++j)
+      for (int i = 0; i < MI; ++i) {
+        const int r = LY::row(i, lane);
+        const int m = row0 + r;
+        const uint32_t grow = (uint32_t)((m < M ? m : 0) / L) * (uint32_t)gate_stride;
+        uint32_t off[NJ][NQ];
+        float4 hv[NJ][NQ], gv[NJ][NQ];
 #pragma unroll
-        for (int q = 0; q < NQ; ++q)
-          bstore(rout, off[j][q], fma4(gv[j][q], quad(acc[i][j], q), hv[j][q]));
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < NQ; ++q) {
+            const int n = col0 + LY::col(j, q, lane);
+            off[j][q] = n < N ? (uint32_t)(r * N + n) * (uint32_t)sizeof(float) : kOOB;
+            hv[j][q] = __builtin_bit_cast(float4, bload(rin, off[j][q]));
+            gv[j][q] = gate ? __builtin_bit_cast(float4, bload(rg, n < N ? (grow + (uint32_t)n) * 4u : kOOB))
+                            : make_float4(1.f, 1.f, 1.f, 1.f);
+          }
+#pragma unroll
+        for (int j = 0; j < NJ; ++j)
+#pragma unroll
+          for (int q = 0; q < NQ; ++q)
+            bstore(rout, off[j][q], fma4(gv[j][q], quad(acc[i][j], q), hv[j][q]));
+      }
     }
   }
 };
@@ -240,8 +296,7 @@ struct EpiPlainF32 : EpiNoStage {
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(stg + r * kPitchF + 32 * j + 8 * q + 4 * hi) = quad(acc[i][j], q);
-        // a wave's LDS accesses complete in order: the reads below see the writes above, and the
-        // next block's writes come after these reads
+        wave_lds_sync();  // the reads below see every lane's writes above
 #pragma unroll
         for (int k = 0; k < 16; ++k) {
           const int row = 2 * k + rr;
@@ -249,6 +304,7 @@ struct EpiPlainF32 : EpiNoStage {
           const int m = row0 + 32 * i + row;
           if (ch < 8 * NJ && m < M && n < N) st4(outf + (size_t)m * ldf + n, v);  // N is a multiple of 4
         }
+        wave_lds_sync();  // the next block's writes come after every lane's reads
       }
     } else {
 #pragma unroll
@@ -293,8 +349,7 @@ struct EpiSwiglu : EpiNoStage {
       // float32 saves through the same LDS area: per 32-row block, gate then up (32 rows x WN/2
       // floats each, rows padded to kSavePitch bytes), read back 16 lanes per 256-byte row so that
       // every store writes whole lines. Stored from the accumulator layout, each 16-byte store hit a
-      // different row. The bf16 staging below reuses the area: a wave's LDS accesses complete in
-      // order, so its writes come after these reads.
+      // different row. The bf16 staging below reuses the area after a wave-scope sync.
       constexpr int kSavePitch = 272;
       static_assert(2 * 32 * kSavePitch <= 4 * kLdsOutFloats, "save staging");
       char* const sm = reinterpret_cast<char*>(stg);
@@ -313,6 +368,7 @@ struct EpiSwiglu : EpiNoStage {
               *reinterpret_cast<float4*>(blk + r * kSavePitch + 128 * j + 32 * q + 16 * hi) =
                   quad(acc[i][j + h * (NJ / 2)], q);
         }
+        wave_lds_sync();  // the reads below see every lane's writes above
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           const char* const blk = sm + h * 32 * kSavePitch;
@@ -325,6 +381,7 @@ struct EpiSwiglu : EpiNoStage {
             if (m < M && c < I) st4(dst + (size_t)m * I + c, v);  // I is a multiple of 4
           }
         }
+        wave_lds_sync();  // later writes to the area come after every lane's reads
       }
     } else if constexpr (kSave) {
 #pragma unroll
@@ -360,7 +417,7 @@ struct EpiSwiglu : EpiNoStage {
                 make_uint2(pack_bf16x2(siluf_(g.x) * u.x, siluf_(g.y) * u.y),
                            pack_bf16x2(siluf_(g.z) * u.z, siluf_(g.w) * u.w));
           }
-        // a wave's LDS accesses complete in order, so the reads below see the writes above
+        wave_lds_sync();  // the reads below see every lane's writes above
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
           const int row = 8 * k + rr;

@@ -87,6 +87,16 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// Lanes of one wave passing data through LDS. The hardware runs a wave's LDS accesses in issue
+// order, but the compiler reasons per lane: with nothing in between it may move or merge one lane's
+// LDS read across another lane's write (it did: a staged epilogue re-used values read for the
+// previous block). The wave-scope fences emit no instruction; they keep every LDS access on its side.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Buffer resources (raw, 32-bit offsets). A load whose offset lies past the resource's byte size
 // returns zeros; kOOB is an offset past every resource, used to switch a lane's load off.
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
