@@ -559,7 +559,9 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
           _Pragma("unroll") for (int r = 0; r < 16; ++r)                                           \
             if (t0 + 32 * kb + 16 * (r >> 3) + 8 * h32 + (r & 7) > rq) SC[kb][r] = -INFINITY;       \
       }                                                                                            \
-      /* phase A: S of tile tn, interleaved with tile t's max, rescale and exponentials */         \
+      /* phase A: S of tile tn, interleaved with tile t's max, rescale and exponentials; at raised */ \
+      /* wave priority, so that the other workgroup's wave on this SIMD (in phase B) fills the gaps */ \
+      __builtin_amdgcn_s_setprio(1);                                                               \
       _Pragma("unroll") for (int kb = 0; kb < 2; ++kb)                                             \
         _Pragma("unroll") for (int r = 0; r < 16; ++r) SN[kb][r] = 0.0f;                           \
       bf16x8 ring[RA + 1];                                                                         \
@@ -592,6 +594,7 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
         K2_FENCE();                                                                                \
       }                                                                                            \
       /* phase B: O^T += V^T P^T for tile t; step j = (kb, h) covers keys 32kb + 16h .. +15, */    \
+      __builtin_amdgcn_s_setprio(0);                                                               \
       /* packed just before its first instruction; the row sum runs alongside */                   \
       bf16x8 vring[RA + 1];                                                                        \
       _Pragma("unroll") for (int i = 0; i < RA; ++i) vring[i] = K2_VFRAG(svc, i);                  \

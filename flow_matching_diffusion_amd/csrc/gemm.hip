@@ -120,6 +120,8 @@ __device__ __forceinline__ float4 fma4(float4 g, float4 a, float4 h) {
 // ---------------------------------------------------------------------------------------------
 // Epilogues that read nothing beyond their own arguments stage nothing in LDS.
 struct EpiNoStage {
+  static constexpr bool kOutStage = false;  // the epilogue takes a per-wave output staging area too
+  static constexpr int kOutFloats = 0;
   static constexpr bool kStaged = false;
   static constexpr bool kLdsOut = false;  // the epilogue writes its output through a per-wave LDS area
   static constexpr int kLdsOutFloats = 0;
@@ -483,6 +485,15 @@ struct EpiQkvg {
   static constexpr bool kStaged = true;
   static constexpr bool kLdsOut = false;
   static constexpr int kLdsOutFloats = 0;
+  // bf16, head_dim 128 (one head per wave): q, k and gate rows leave through a per-wave LDS area
+  // placed after the staged tables, 16 rows at a time (rows of 256 bytes + 16 of padding), read
+  // back 16 lanes per row so every store writes whole 256-byte rows (stored from the accumulator
+  // layout, an instruction wrote 8 bytes into each of 32 rows). Measured at the 1024x1024 CFG pair
+  // this gains under 1 % (1.427 -> 1.420 ms): the projection's remaining 6 % over a float32-output
+  // GEMM of the same shape is not in its stores.
+  static constexpr bool kOutStage = sizeof(T) == 2 && HD == 128;
+  static constexpr int kOutPitch = 272;
+  static constexpr int kOutFloats = kOutStage ? 16 * kOutPitch / 4 : 0;
   static constexpr int kStgRow = HD + 4;
   static constexpr int stage_floats() { return 2 * HD + 256 * kStgRow; }
   __device__ bool wants_stage(int n0) const { return n0 < nq + nk; }
@@ -506,12 +517,118 @@ struct EpiQkvg {
     }
   }
 
+  // q (seg 0), k (1) or gate (3) head of a wave through its output staging area (kOutStage).
+  template <class LY, int MI, int NJ>
+  __device__ __forceinline__ void apply_staged(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
+                                               int M, const float* stg, float* ostg, int seg) const {
+    T* const dst = seg == 0 ? q : seg == 1 ? k : g;
+    const int ld = seg == 1 ? nk : nq;
+    const int cb = seg == 0 ? col0 : seg == 1 ? col0 - nq : col0 - nq - 2 * nk;
+    const float* const wn = seg == 0 ? wnq : wnk;
+    char* const os = reinterpret_cast<char*>(ostg);
+    const int r = lane & 31, hi = lane >> 5;     // accumulator layout: row r, columns 32 jj + 8 qq + 4 hi
+    const int rr = lane >> 4, ch = lane & 15;    // read-back: row 4 kk + rr, columns 8 ch .. 8 ch + 7
+#pragma unroll
+    for (int i = 0; i < MI; ++i) {
+      const int m = row0 + 32 * i + r;
+      uint2 pk[NJ][4];
+      if (seg <= 1) {
+        float* const raw = seg == 0 ? qraw : kraw;
+        if (kSave && m < M) {
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq) st4(raw + (size_t)m * ld + cb + LY::col(jj, qq, lane), quad(acc[i][jj], qq));
+        }
+        float ss = 0.0f;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int e = 0; e < 16; ++e) ss += acc[i][jj][e] * acc[i][jj][e];
+        ss = LY::rowsum(ss);
+        const float inv = rsqrtf(ss * (1.0f / HD) + eps);
+        const int l = (m < M ? m : 0) % L;
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const int d = LY::col(jj, qq, lane);
+            float4 y = quad(acc[i][jj], qq);
+            if (stg) {  // staged multipliers and (cos, sin) pairs
+              const float4 w4 = ld4(stg + (seg == 0 ? 0 : HD) + d);
+              y.x *= inv * w4.x; y.y *= inv * w4.y; y.z *= inv * w4.z; y.w *= inv * w4.w;
+              if (rc) {
+                const float4 cs = ld4(stg + 2 * HD + ((row0 & 255) + 32 * i + r) * kStgRow + d);
+                y = make_float4(y.x * cs.x - y.y * cs.y, y.y * cs.x + y.x * cs.y,
+                                y.z * cs.z - y.w * cs.w, y.w * cs.z + y.z * cs.w);
+              }
+            } else {
+              const float4 w4 = wn ? ld4(wn + d) : make_float4(0.f, 0.f, 0.f, 0.f);
+              y.x *= inv * (1.0f + w4.x); y.y *= inv * (1.0f + w4.y);
+              y.z *= inv * (1.0f + w4.z); y.w *= inv * (1.0f + w4.w);
+              if (rc) {
+                const float2 c2 = *reinterpret_cast<const float2*>(rc + (size_t)l * (HD / 2) + (d >> 1));
+                const float2 s2 = *reinterpret_cast<const float2*>(rs + (size_t)l * (HD / 2) + (d >> 1));
+                y = make_float4(y.x * c2.x - y.y * s2.x, y.y * c2.x + y.x * s2.x,
+                                y.z * c2.y - y.w * s2.y, y.w * c2.y + y.z * s2.y);
+              }
+            }
+            pk[jj][qq] = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+            if (kSave && seg == 1 && m < M) {  // k transposed per (batch, kv head), like vt
+              const int b = m / L;
+              T* kp = kt + (size_t)(b * (nk / HD) + cb / HD) * HD * ldvt + (m - b * L);
+              const int dd = cb % HD + d;
+              kp[(size_t)dd * ldvt] = to_t<T>(y.x);
+              kp[(size_t)(dd + 1) * ldvt] = to_t<T>(y.y);
+              kp[(size_t)(dd + 2) * ldvt] = to_t<T>(y.z);
+              kp[(size_t)(dd + 3) * ldvt] = to_t<T>(y.w);
+            }
+          }
+      } else {
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int qq = 0; qq < 4; ++qq) {
+            const float4 y = quad(acc[i][jj], qq);
+            pk[jj][qq] = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
+          }
+      }
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh) {  // rows 16 hh .. 16 hh + 15 of the block
+        if ((r >> 4) == hh) {
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int qq = 0; qq < 4; ++qq)
+              *reinterpret_cast<uint2*>(os + (r & 15) * kOutPitch + 2 * LY::col(jj, qq, lane)) = pk[jj][qq];
+        }
+        wave_lds_sync();  // the reads below see every lane's writes above
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) {
+          const int row = 4 * kk + rr;
+          const uint4 v = *reinterpret_cast<const uint4*>(os + row * kOutPitch + 16 * ch);
+          const int mm = row0 + 32 * i + 16 * hh + row;
+          if (mm < M) *reinterpret_cast<uint4*>(dst + (size_t)mm * ld + cb + 8 * ch) = v;
+        }
+        wave_lds_sync();  // the next writes come after every lane's reads
+      }
+    }
+  }
+
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
-                                        int M, float* stg = nullptr) const {
+                                        int M, float* stg = nullptr, float* ostg = nullptr) const {
     constexpr int BS = LY::NQ == 1 ? 16 : 32;
     constexpr int HB = HD / BS;  // column blocks per head
     const int ntot = 2 * nq + 2 * nk;
+    if constexpr (kOutStage && LY::NQ == 4 && NJ == HB) {
+      if (col0 >= ntot) return;
+      const int seg = col0 < nq ? 0 : col0 < nq + nk ? 1 : col0 < nq + 2 * nk ? 2 : 3;  // wave-uniform
+      if (seg != 2) {
+        apply_staged<LY, MI, NJ>(acc, row0, col0, lane, M, stg, ostg, seg);
+        return;
+      }
+    }
     if constexpr (NJ % HB != 0) {
       // A wave narrower than a head (the 256x128 halves of a last partial round): the host runs
       // such tiles only over v and gate columns (tail_allowed), which need no per-head reduction.
@@ -1073,7 +1190,15 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
 #undef K2_DMA1
 #undef K2_DMA_B
 #undef K2_DMA_A
-  epi.template apply<Lay<32>, MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M, stg);
+  if constexpr (Epi::kOutStage) {
+    static_assert((Epi::stage_floats() + 4 * Epi::kOutFloats) * sizeof(float) <= Rings<RA, RB>::units(4) * sizeof(uint4),
+                  "LDS output staging");
+    if (!stg) __syncthreads();  // every wave is done with the rings (the staging branch synced already)
+    float* const ostg = reinterpret_cast<float*>(lds) + Epi::stage_floats() + wave * Epi::kOutFloats;
+    epi.template apply<Lay<32>, MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M, stg, ostg);
+  } else {
+    epi.template apply<Lay<32>, MI, NJ>(acc, m0 + wm * WM, n0 + wn * WN, lane, M, stg);
+  }
 }
 
 // Workgroups 0 .. nmain-1 each compute a 256x256 tile (tile order: tile_coords). With TAIL, the
