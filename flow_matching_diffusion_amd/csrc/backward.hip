@@ -837,6 +837,12 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
   // One tile, ordered so that the matrix cores have independent work during the vector steps:
   // S = K Q^T; dP = V dO^T with P = exp2(S log2(e)/sqrt(hd) - lse) computed alongside; dV += P^T dO
   // with dS = P (dP - Delta) computed alongside; dK += dS^T Q.
+  // The tile's 4 NC + 2 NDB LDS fragments (Q rows, dO rows, dO^T rows, Q^T rows, in that order)
+  // stream through a ring RA reads ahead of the matrix-core step that takes them, across the phase
+  // boundaries. With one wave per SIMD nothing else hides an LDS read's latency: read one step
+  // ahead, as the compiler scheduled it, the pass kept the matrix cores 25 % busy.
+  constexpr int NF = 4 * NC + 2 * NDB, RA = sizeof(T) == 2 ? 6 : 2;  // float32 fragments take 8 registers
+  const int qro[2] = {perm32(0, c), perm32(1, c)};
   auto tile = [&](int u, int st) {
     if (active) {
       // queries 8g + 4qb + r of the tile (lse +inf past L, so their P is 0): float4 2g + qb
@@ -847,61 +853,67 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
         ql[4 * qb] = a.x; ql[4 * qb + 1] = a.y; ql[4 * qb + 2] = a.z; ql[4 * qb + 3] = a.w;
         qd[4 * qb] = d4.x; qd[4 * qb + 1] = d4.y; qd[4 * qb + 2] = d4.z; qd[4 * qb + 3] = d4.w;
       }
-      f32x4 s[2][2], dp[2][2];
-#pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        s[qb][0] = s[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int qro = perm32(qb, c);
-        const uint4* qr = sQ[st] + qro * RP;
-#pragma unroll
-        for (int kc = 0; kc < NC; ++kc) {
-          const Frag qa = lds_frag<T>(qr, tile_chunk<SWZ>(qro, (32 * kc + 8 * g) / E));
-#pragma unroll
-          for (int j = 0; j < 2; ++j) s[qb][j] = mma16(s[qb][j], qa, kf[j][kc]);
+      // fragment f of the tile (f is a compile-time constant at every call)
+      auto frag = [&](int f) -> Frag {
+        if (f < 2 * NC) {
+          const int qb = f / NC, kc = f % NC;
+          return lds_frag<T>(sQ[st] + qro[qb] * RP, tile_chunk<SWZ>(qro[qb], (32 * kc + 8 * g) / E));
         }
-      }
+        if (f < 4 * NC) {
+          const int qb = (f - 2 * NC) / NC, kc = (f - 2 * NC) % NC;
+          return lds_frag<T>(sD[st] + qro[qb] * RP, tile_chunk<SWZ>(qro[qb], (32 * kc + 8 * g) / E));
+        }
+        if (f < 4 * NC + NDB) return lds_frag<T>(sDT[st] + (16 * (f - 4 * NC) + c) * TP, (8 * g) / E);
+        return lds_frag<T>(sQT[st] + (16 * (f - 4 * NC - NDB) + c) * TP, (8 * g) / E);
+      };
+      f32x4 s[2][2], dp[2][2];
       float pv[2][8];  // P of key block j: entry 4 qb + r
+      float dsv[2][8];
+      Frag pf[2], dsf[2];
+      Frag ring[RA + 1];
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        dp[qb][0] = dp[qb][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-        const int dro = perm32(qb, c);
-        const uint4* dr = sD[st] + dro * RP;
+      for (int f = 0; f < RA; ++f) ring[f] = frag(f);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kc = 0; kc < NC; ++kc) {
-          const Frag da = lds_frag<T>(dr, tile_chunk<SWZ>(dro, (32 * kc + 8 * g) / E));
+      for (int f = 0; f < NF; ++f) {
+        if (f + RA < NF) ring[(f + RA) % (RA + 1)] = frag(f + RA);
+        const Frag a = ring[f % (RA + 1)];
+        if (f < 2 * NC) {  // S
+          const int qb = f / NC, kc = f % NC;
 #pragma unroll
-          for (int j = 0; j < 2; ++j) dp[qb][j] = mma16(dp[qb][j], da, vf[j][kc]);
-          // 8 / NC exponentials of query block qb per step
+          for (int j = 0; j < 2; ++j) s[qb][j] = mma16(kc ? s[qb][j] : f32x4{0.f, 0.f, 0.f, 0.f}, a, kf[j][kc]);
+        } else if (f < 4 * NC) {  // dP, with 8 / NC exponentials of query block qb per step
+          const int qb = (f - 2 * NC) / NC, kc = (f - 2 * NC) % NC;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) dp[qb][j] = mma16(kc ? dp[qb][j] : f32x4{0.f, 0.f, 0.f, 0.f}, a, vf[j][kc]);
 #pragma unroll
           for (int x = kc * 8 / NC; x < (kc + 1) * 8 / NC; ++x) {
             const int j = x >> 2, r = x & 3;
             pv[j][4 * qb + r] = kok[j] ? __builtin_amdgcn_exp2f(fmaf(s[qb][j][r], scale_log2, -ql[4 * qb + r])) : 0.0f;
           }
+          if (f == 4 * NC - 1) {
+            pack8(pf[0], pv[0]);
+            pack8(pf[1], pv[1]);
+          }
+        } else if (f < 4 * NC + NDB) {  // dV, with 16 / NDB entries of dS per step
+          const int db = f - 4 * NC;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) dv[db][j] = mma16(dv[db][j], a, pf[j]);
+#pragma unroll
+          for (int x = db * 16 / NDB; x < (db + 1) * 16 / NDB; ++x) {
+            const int j = x >> 3, e = x & 7;
+            dsv[j][e] = pv[j][e] * (dp[e >> 2][j][e & 3] - qd[e]);
+          }
+          if (db == NDB - 1) {
+            pack8(dsf[0], dsv[0]);
+            pack8(dsf[1], dsv[1]);
+          }
+        } else {  // dK
+          const int db = f - 4 * NC - NDB;
+#pragma unroll
+          for (int j = 0; j < 2; ++j) dk[db][j] = mma16(dk[db][j], a, dsf[j]);
         }
-      }
-      Frag pf[2], dsf[2];
-      pack8(pf[0], pv[0]);
-      pack8(pf[1], pv[1]);
-      float dsv[2][8];
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const Frag ta = lds_frag<T>(sDT[st] + (16 * db + c) * TP, (8 * g) / E);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dv[db][j] = mma16(dv[db][j], ta, pf[j]);
-        // 16 / NDB entries of dS per step
-#pragma unroll
-        for (int x = db * 16 / NDB; x < (db + 1) * 16 / NDB; ++x) {
-          const int j = x >> 3, e = x & 7;
-          dsv[j][e] = pv[j][e] * (dp[e >> 2][j][e & 3] - qd[e]);
-        }
-      }
-      pack8(dsf[0], dsv[0]);
-      pack8(dsf[1], dsv[1]);
-#pragma unroll
-      for (int db = 0; db < NDB; ++db) {
-        const Frag qa = lds_frag<T>(sQT[st] + (16 * db + c) * TP, (8 * g) / E);
-#pragma unroll
-        for (int j = 0; j < 2; ++j) dk[db][j] = mma16(dk[db][j], qa, dsf[j]);
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
   };
