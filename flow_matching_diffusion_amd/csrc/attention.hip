@@ -414,16 +414,8 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
     rq = p.reach[min(q0 + c32, L - 1)];
   }
 
-  // validity bits of the text tiles (bit j: key 64t + j is a valid key)
-  const int ntt = (T_ + KT - 1) / KT;
-  for (int u = wave; u < ntt; u += 4) {
-    const int key = u * KT + lane;
-    const bool ok = key < L && (key >= T_ || !p.mask || p.mask[(size_t)b * T_ + key] != 0);
-    const uint64_t bits = __ballot(ok);
-    if (lane == 0) sBits[u] = bits;
-  }
-
-  // Q^T fragments (B operand of S^T = K Q^T): lane l holds query q0 + l%32, head dims 16s + 8(l/32)..+7
+  // Q^T fragments (B operand of S^T = K Q^T): lane l holds query q0 + l%32, head dims 16s + 8(l/32)..+7;
+  // loaded first, so that their latency overlaps the validity bits below
   bf16x8 qf[NS];
   {
     const int row = q0 + c32;
@@ -431,6 +423,15 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
 #pragma unroll
     for (int s = 0; s < NS; ++s)
       qf[s] = row < L ? *(const bf16x8*)(src + 16 * s + 8 * h32) : bf16x8{};
+  }
+
+  // validity bits of the text tiles (bit j: key 64t + j is a valid key)
+  const int ntt = (T_ + KT - 1) / KT;
+  for (int u = wave; u < ntt; u += 4) {
+    const int key = u * KT + lane;
+    const bool ok = key < L && (key >= T_ || !p.mask || p.mask[(size_t)b * T_ + key] != 0);
+    const uint64_t bits = __ballot(ok);
+    if (lane == 0) sBits[u] = bits;
   }
 
   // DMA duties. K: wave w moves tile rows 16w.. (hd 128: 4 blocks of 4 rows; hd 64: 2 blocks of 8).
@@ -639,6 +640,19 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
 #undef K2_VFRAG
 #undef K2_SK
 #undef K2_SV
+  // Epilogue. The wave's 32 rows of gate, output (and saved output) go through buffer resources that
+  // end at the sequence end (rows past it read zero and their stores are dropped); all gate loads
+  // are issued first, so that their latency overlaps the barrier and the staging below.
+  constexpr int LPR = HD / 8, RPI = 64 / LPR, NKR = 32 / RPI;  // lanes per row, rows per instruction
+  const int rr = lane / LPR, cc = lane % LPR;
+  const int nrow = L - q0 < 0 ? 0 : (L - q0 < 32 ? L - q0 : 32);
+  const size_t gbase = (size_t)(b * L + q0) * ldq + head * HD;
+  const size_t span = nrow ? ((size_t)(nrow - 1) * ldq + HD) * sizeof(bf16) : 0;
+  const rsrc_t rg = make_rsrc((const bf16*)p.g + gbase, span);
+  const rsrc_t ro = make_rsrc((bf16*)p.og + gbase, span);
+  uint4 gq[NKR];
+#pragma unroll
+  for (int k = 0; k < NKR; ++k) gq[k] = bload(rg, (uint32_t)((RPI * k + rr) * ldq + 8 * cc) * (uint32_t)sizeof(bf16));
   // normalise into this wave's LDS area (the K/V stages are free now): 32 query rows of HD floats,
   // 16-byte chunk c of row r at chunk c ^ (r % 32); then gate and store row-major, HD/8 lanes per
   // query row with 8 head dims each, so the gate reads and output stores cover whole rows
@@ -659,19 +673,6 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
           make_float4(o[hb][4 * j] * inv, o[hb][4 * j + 1] * inv, o[hb][4 * j + 2] * inv, o[hb][4 * j + 3] * inv);
     }
   wave_lds_sync();  // the reads below see every lane's writes above
-  // The wave's 32 rows of gate, output (and saved output) go through buffer resources that end at the sequence
-  // end (rows past it read zero and their stores are dropped), so all gate loads are issued before
-  // the first wait instead of one load-wait-store round trip per row group.
-  constexpr int LPR = HD / 8, RPI = 64 / LPR, NKR = 32 / RPI;  // lanes per row, rows per instruction
-  const int rr = lane / LPR, cc = lane % LPR;
-  const int nrow = L - q0 < 0 ? 0 : (L - q0 < 32 ? L - q0 : 32);
-  const size_t gbase = (size_t)(b * L + q0) * ldq + head * HD;
-  const size_t span = nrow ? ((size_t)(nrow - 1) * ldq + HD) * sizeof(bf16) : 0;
-  const rsrc_t rg = make_rsrc((const bf16*)p.g + gbase, span);
-  const rsrc_t ro = make_rsrc((bf16*)p.og + gbase, span);
-  uint4 gq[NKR];
-#pragma unroll
-  for (int k = 0; k < NKR; ++k) gq[k] = bload(rg, (uint32_t)((RPI * k + rr) * ldq + 8 * cc) * (uint32_t)sizeof(bf16));
 #pragma unroll
   for (int k = 0; k < NKR; ++k) {
     const int r = RPI * k + rr;
