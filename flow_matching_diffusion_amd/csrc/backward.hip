@@ -786,28 +786,40 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
   // lambdas keep both sets in registers. Tile u: query head kvh G + u / nt, queries 32 (u % nt) ..
   uint4 rq[2][NQ], rd[2][NQ], rqt[2][NT], rdt[2][NT];
   float rl[2] = {INFINITY, INFINITY}, rdl[2] = {0.0f, 0.0f};
+  bool rok[2] = {false, false};
+  // Tile loads are branch-free (buffer resources: rows past L read zero; every thread loads an lse /
+  // Delta entry, the first 32 keep theirs), so the wait before a tile's LDS stores covers only that
+  // tile's loads. Loaded through branches, the compiler waited for every load in flight there,
+  // including the next tile's, and the loads were effectively one tile ahead instead of two.
+  const size_t qspan = ((size_t)(L - 1) * ldq + HD) * sizeof(T);
+  const size_t tspan = (size_t)HD * p.ldt * sizeof(T);  // a (batch, head) plane of Q^T / dO^T
 #define K2_DKV_GLOAD(RS, u)                                                                        \
   do {                                                                                             \
     const int head_ = kvh * G + (u) / nt, t0_ = 32 * ((u) % nt);                                   \
-    const T* qg_ = (const T*)p.q + (size_t)b * L * ldq + head_ * HD;                               \
-    const T* dg_ = (const T*)p.dout + (size_t)b * L * ldq + head_ * HD;                            \
-    const size_t tb_ = (size_t)(b * p.nh + head_) * HD * p.ldt + t0_;                              \
+    const rsrc_t qr_ = make_rsrc((const T*)p.q + (size_t)b * L * ldq + head_ * HD, qspan);         \
+    const rsrc_t dr_ = make_rsrc((const T*)p.dout + (size_t)b * L * ldq + head_ * HD, qspan);      \
+    const size_t tb_ = (size_t)(b * p.nh + head_) * HD * p.ldt;                                    \
+    const rsrc_t qtr_ = make_rsrc((const T*)p.qt + tb_, tspan);                                    \
+    const rsrc_t dtr_ = make_rsrc((const T*)p.dot + tb_, tspan);                                   \
     _Pragma("unroll") for (int i = 0; i < NQ; ++i) {                                               \
       const int ch_ = tid + 256 * i, row_ = ch_ / RCH, cc_ = ch_ % RCH, q_ = t0_ + row_;            \
-      rq[RS][i] = ld16_or_zero(qg_ + (size_t)(q_ < L ? q_ : 0) * ldq + cc_ * E, q_ < L);           \
-      rd[RS][i] = ld16_or_zero(dg_ + (size_t)(q_ < L ? q_ : 0) * ldq + cc_ * E, q_ < L);           \
+      const uint32_t off_ = q_ < L ? (uint32_t)(q_ * ldq + cc_ * E) * (uint32_t)sizeof(T) : kOOB;  \
+      rq[RS][i] = bload(qr_, off_);                                                                \
+      rd[RS][i] = bload(dr_, off_);                                                                \
     }                                                                                              \
     /* Q^T, dO^T: zero past L (written so by the transposes) */                                    \
     _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                               \
       const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH;                               \
-      rqt[RS][i] = ld16_or_zero((const T*)p.qt + tb_ + (size_t)d_ * p.ldt + cc_ * E, true);           \
-      rdt[RS][i] = ld16_or_zero((const T*)p.dot + tb_ + (size_t)d_ * p.ldt + cc_ * E, true);          \
+      const uint32_t off_ = (uint32_t)(d_ * p.ldt + t0_ + cc_ * E) * (uint32_t)sizeof(T);          \
+      rqt[RS][i] = bload(qtr_, off_);                                                              \
+      rdt[RS][i] = bload(dtr_, off_);                                                              \
     }                                                                                              \
-    if (tid < 32) {                                                                                \
-      const int q_ = t0_ + tid;                                                                    \
-      const size_t ri_ = ((size_t)b * p.nh + head_) * L + (q_ < L ? q_ : 0);                       \
-      rl[RS] = q_ < L ? p.lse[ri_] : INFINITY;                                                     \
-      rdl[RS] = q_ < L ? p.delta[ri_] : 0.0f;                                                      \
+    {  /* raw values; queries past L get lse +inf and Delta 0 at the LDS store */                  \
+      const int q_ = t0_ + (tid & 31);                                                             \
+      const size_t ri_ = ((size_t)b * p.nh + head_) * L + (q_ < L ? q_ : L - 1);                   \
+      rl[RS] = p.lse[ri_];                                                                         \
+      rdl[RS] = p.delta[ri_];                                                                      \
+      rok[RS] = q_ < L;                                                                            \
     }                                                                                              \
   } while (0)
 #define K2_DKV_LSTORE(RS, ST)                                                                      \
@@ -823,16 +835,22 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
       sDT[ST][d_ * TP + cc_] = rdt[RS][i];                                                         \
     }                                                                                              \
     if (tid < 32) {                                                                                \
-      reinterpret_cast<float*>(sL[ST])[tid] = rl[RS];                                              \
-      reinterpret_cast<float*>(sDl[ST])[tid] = rdl[RS];                                            \
+      reinterpret_cast<float*>(sL[ST])[tid] = rok[RS] ? rl[RS] : INFINITY;                         \
+      reinterpret_cast<float*>(sDl[ST])[tid] = rok[RS] ? rdl[RS] : 0.0f;                           \
     }                                                                                              \
   } while (0)
 
   const int nu = G * nt;
   const int u0 = split * nu / nsplit, u1 = (split + 1) * nu / nsplit;  // u0 < u1: nu >= nsplit
+  // Tile u's loads go out at the start of tile u - 2 and its LDS stores at the start of tile u - 1,
+  // so the wait before a store covers loads two tiles old while the next tile's stay in flight. The
+  // loads are issued on every path (past the last tile they reload it, unused): with a load skipped
+  // on some path, the compiler's wait before a store had to cover every load in flight.
+  const int ulast = u1 - 1;
   K2_DKV_GLOAD(0, u0);
-  if (u0 + 1 < u1) K2_DKV_GLOAD(1, u0 + 1);
+  K2_DKV_GLOAD(1, min(u0 + 1, ulast));
   K2_DKV_LSTORE(0, 0);
+  K2_DKV_GLOAD(0, min(u0 + 2, ulast));
   __syncthreads();
   // One tile, ordered so that the matrix cores have independent work during the vector steps:
   // S = K Q^T; dP = V dO^T with P = exp2(S log2(e)/sqrt(hd) - lse) computed alongside; dV += P^T dO
@@ -918,14 +936,14 @@ __global__ void __launch_bounds__(256) attn_bwd_dkv_kernel(AttnBwdArgs p, float 
     }
   };
   for (int u = u0; u < u1; u += 2) {
-    if (u + 2 < u1) K2_DKV_GLOAD(0, u + 2);
+    if (u + 1 < u1) K2_DKV_LSTORE(1, 1);  // stage 1 was last read by tile u - 1 (before the barrier)
+    K2_DKV_GLOAD(1, min(u + 3, ulast));
     tile(u, 0);
-    if (u + 1 < u1) K2_DKV_LSTORE(1, 1);
     __syncthreads();
     if (u + 1 >= u1) break;
-    if (u + 3 < u1) K2_DKV_GLOAD(1, u + 3);
-    tile(u + 1, 1);
     if (u + 2 < u1) K2_DKV_LSTORE(0, 0);
+    K2_DKV_GLOAD(0, min(u + 4, ulast));
+    tile(u + 1, 1);
     __syncthreads();
   }
 #undef K2_DKV_GLOAD
