@@ -560,6 +560,8 @@ __device__ __forceinline__ typename FragOf<T>::type lds_frag(const uint4* row, i
 
 }  // namespace
 
+constexpr int kBwdTextTiles = 512;  // 32-key text tiles the dQ pass's validity bits hold: T <= 16384
+
 template <typename T, int HD, int G>
 __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, float scale_log2, float scale) {
   typedef typename FragOf<T>::type Frag;
@@ -574,9 +576,9 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
   constexpr int QW = 32 * (4 / G);       // queries per workgroup
   static_assert(NKV >= 1 && NT >= 1, "tile / thread mismatch");
   __shared__ uint4 sK[2][32 * RP], sV[2][32 * RP], sT[2][HD * TP];
-  __shared__ float4 sB[2][8];  // per key of the tile: 0 if it may be attended, -inf if not
+  __shared__ uint32_t sMb[kBwdTextTiles];  // bit j of word t: text key 32t + j may be attended
   // at most one workgroup's LDS per compute unit; two per compute unit (the launch bounds' aim) in bf16
-  K2_LDS_CHECK(sizeof(sK) + sizeof(sV) + sizeof(sT) + sizeof(sB), sizeof(T) == 2 ? 2 : 1);
+  K2_LDS_CHECK(sizeof(sK) + sizeof(sV) + sizeof(sT) + sizeof(sMb), sizeof(T) == 2 ? 2 : 1);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = lane >> 4, c = lane & 15;
   const int b = blockIdx.z, kvh = blockIdx.y;
@@ -602,6 +604,18 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
     lse[qc] = ok ? p.lse[rs] : INFINITY;
     dl[qc] = ok ? p.delta[rs] : 0.0f;
   }
+  // validity bits of the text tiles, once per workgroup (one wave ballot covers two tiles); the key
+  // loop reads its tile's word instead of loading mask bytes per tile
+  const int ntt = (T_ + 31) / 32;
+  for (int u = wave; 2 * u < ntt; u += 4) {
+    const int key = 64 * u + lane;
+    const bool ok = key < L && (key >= T_ || !p.mask || p.mask[(size_t)b * T_ + key] != 0);
+    const uint64_t bits = __ballot(ok);
+    if (lane == 0) {
+      sMb[2 * u] = (uint32_t)bits;
+      if (2 * u + 1 < ntt) sMb[2 * u + 1] = (uint32_t)(bits >> 32);
+    }
+  }
   f32x4 acc[NDB][2];
 #pragma unroll
   for (int db = 0; db < NDB; ++db) acc[db][0] = acc[db][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -613,24 +627,28 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
   // 256 registers, so two waves share a SIMD and one's exponentials overlap the other's matrix-core
   // work (two sets, two tiles ahead, took 324 registers and one wave per SIMD: 2.9 ms at block1024)
   uint4 rk[1][NKV], rv[1][NKV], rt[1][NT];
-  float rb[1] = {0.0f};
+  int rt0[1] = {0};  // first key of the loaded tile
+  // Tile loads are branch-free (buffer resources: keys past L read zero) and the K^T chunk at the
+  // sequence end is trimmed at the LDS store, where the tile's loads are waited for anyway. Key
+  // validity comes from the bits above. A mask byte loaded per tile in a branch and tested at once
+  // made wave 0 wait for it right after issuing the tile's loads, and the workgroup with it at the
+  // next barrier.
+  const rsrc_t krs = make_rsrc(kg, ((size_t)(L - 1) * ldk + HD) * sizeof(T));
+  const rsrc_t vrs = make_rsrc(vg, ((size_t)(L - 1) * ldk + HD) * sizeof(T));
+  const rsrc_t trs = make_rsrc(tg, (size_t)HD * p.ldt * sizeof(T));
 #define K2_DQ_GLOAD(RS, t)                                                                         \
   do {                                                                                             \
     const int t0_ = 32 * (t);                                                                      \
-    if (tid < 32) {                                                                                \
-      const int key_ = t0_ + tid;                                                                  \
-      rb[RS] = key_ < L && (key_ >= T_ || !p.mask || p.mask[(size_t)b * T_ + key_] != 0) ? 0.0f : -INFINITY; \
-    }                                                                                              \
+    rt0[RS] = t0_;                                                                                 \
     _Pragma("unroll") for (int i = 0; i < NKV; ++i) {                                              \
       const int ch_ = tid + 256 * i, row_ = ch_ / RCH, cc_ = ch_ % RCH, key_ = t0_ + row_;          \
-      rk[RS][i] = ld16_or_zero(kg + (size_t)(key_ < L ? key_ : 0) * ldk + cc_ * E, key_ < L);      \
-      rv[RS][i] = ld16_or_zero(vg + (size_t)(key_ < L ? key_ : 0) * ldk + cc_ * E, key_ < L);      \
+      const uint32_t off_ = key_ < L ? (uint32_t)(key_ * ldk + cc_ * E) * (uint32_t)sizeof(T) : kOOB; \
+      rk[RS][i] = bload(krs, off_);                                                                \
+      rv[RS][i] = bload(vrs, off_);                                                                \
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                               \
       const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH, k0_ = t0_ + cc_ * E;          \
-      rt[RS][i] = ld16_or_zero(tg + (size_t)d_ * p.ldt + (k0_ < L ? k0_ : 0), k0_ < L);           \
-      /* the workspace past L holds anything */                                                    \
-      if (k0_ < L && k0_ + E > L) rt[RS][i] = chunk_keep<T>(rt[RS][i], L - k0_);                   \
+      rt[RS][i] = bload(trs, k0_ < L ? (uint32_t)(d_ * p.ldt + k0_) * (uint32_t)sizeof(T) : kOOB); \
     }                                                                                              \
   } while (0)
 #define K2_DQ_LSTORE(RS, ST)                                                                       \
@@ -641,10 +659,10 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
       sV[ST][row_ * RP + tile_chunk<SWZ>(row_, cc_)] = rv[RS][i];                                  \
     }                                                                                              \
     _Pragma("unroll") for (int i = 0; i < NT; ++i) {                                               \
-      const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH;                               \
-      sT[ST][d_ * TP + cc_] = rt[RS][i];                                                           \
+      const int ch_ = tid + 256 * i, d_ = ch_ / TCH, cc_ = ch_ % TCH, k0_ = rt0[RS] + cc_ * E;      \
+      /* the workspace past L holds anything */                                                    \
+      sT[ST][d_ * TP + cc_] = k0_ < L && k0_ + E > L ? chunk_keep<T>(rt[RS][i], L - k0_) : rt[RS][i]; \
     }                                                                                              \
-    if (tid < 32) reinterpret_cast<float*>(sB[ST])[tid] = rb[RS];                                  \
   } while (0)
 
   const int nt = (L + 31) / 32;
@@ -659,8 +677,16 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
   // dQ += dS K.
   auto tile = [&](int t, int st) {
     if (active) {
-      // keys 8g + 4kb + r of the tile: their biases are float4 2g + kb
-      const float4 kbias[2] = {sB[st][2 * g], sB[st][2 * g + 1]};
+      // keys 8g + 4kb + r of the tile: bias 0 if the key may be attended, -inf if not
+      const int t0 = 32 * t;
+      const uint32_t vb = t < ntt ? sMb[t] : (t0 + 32 <= L ? ~0u : (1u << (L - t0)) - 1u);
+      float4 kbias[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const uint32_t nib = vb >> (8 * g + 4 * kb);
+        kbias[kb] = make_float4((nib & 1u) ? 0.0f : -INFINITY, (nib & 2u) ? 0.0f : -INFINITY,
+                                (nib & 4u) ? 0.0f : -INFINITY, (nib & 8u) ? 0.0f : -INFINITY);
+      }
       f32x4 s[2][2], dp[2][2];
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
@@ -710,15 +736,18 @@ __global__ void __launch_bounds__(256, 2) attn_bwd_dq_kernel(AttnBwdArgs p, floa
       }
     }
   };
+  // The loads and stores run on every path (past the last tile they repeat it into the stage no
+  // tile reads): with one skipped on some path, the compiler's waits in the loads covered loads
+  // already stored.
   for (int t = 0; t < nt; t += 2) {
-    if (t + 1 < nt) K2_DQ_GLOAD(0, t + 1);
+    K2_DQ_GLOAD(0, min(t + 1, nt - 1));
     tile(t, 0);
-    if (t + 1 < nt) K2_DQ_LSTORE(0, 1);
+    K2_DQ_LSTORE(0, 1);
     __syncthreads();
     if (t + 1 >= nt) break;
-    if (t + 2 < nt) K2_DQ_GLOAD(0, t + 2);
+    K2_DQ_GLOAD(0, min(t + 2, nt - 1));
     tile(t + 1, 1);
-    if (t + 2 < nt) K2_DQ_LSTORE(0, 0);
+    K2_DQ_LSTORE(0, 0);
     __syncthreads();
   }
 #undef K2_DQ_GLOAD
@@ -1049,7 +1078,7 @@ static hipError_t attn_bwd_g(const AttnBwdArgs& p, hipStream_t s) {
 hipError_t attention_backward(int dt, const AttnBwdArgs& p, hipStream_t s) {
   if (p.B <= 0 || p.L <= 0) return hipSuccess;
   // the K^T, Q^T and dO^T rows hold 32-key / 32-query tiles up to the last one
-  if (p.nh % p.nkv || p.ldt < (p.L + 31) / 32 * 32 || p.ldt % 8) return hipErrorInvalidValue;
+  if (p.nh % p.nkv || p.ldt < (p.L + 31) / 32 * 32 || p.ldt % 8 || p.T > kBwdTextTiles * 32) return hipErrorInvalidValue;
   if (p.hd == 128) return dt == DT_BF16 ? attn_bwd_g<bf16, 128>(p, s) : attn_bwd_g<float, 128>(p, s);
   if (p.hd == 64) return dt == DT_BF16 ? attn_bwd_g<bf16, 64>(p, s) : attn_bwd_g<float, 64>(p, s);
   return hipErrorInvalidValue;
