@@ -134,13 +134,15 @@ struct EpiNoStage {
 //
 // bf16 operands: each 32-row block of the wave's accumulators goes through the wave's LDS area and
 // is read back row-major, 32 lanes per 128-column row, so every residual load and store moves whole
-// 512-byte row segments. Straight from the accumulator layout an instruction touched 32 rows
-// 24 KiB apart with 32 bytes each, and the epilogue took a fifth of the out projection's time.
-// The block's residual loads are issued before its accumulators are staged, so their latency
-// overlaps the LDS traffic; the gate is one float4 per lane while the wave's rows lie in one batch
-// row. Everything goes through buffer resources over the wave's rows (rows past M read zero and
-// their stores are dropped; columns past N take an offset past every resource).
-template <typename T>
+// 512-byte row segments (straight from the accumulator layout an instruction touched 32 rows 24 KiB
+// apart with 32 bytes each). The next block's residual rows are loaded while the current one is
+// written. Everything goes through buffer resources over the wave's rows (rows past M read zero and
+// their stores are dropped; columns past N take an offset past every resource) and nothing sits in
+// a branch: with the gate loaded per row in a branch, the compiler waited for every memory
+// operation in flight (the next block's loads and all earlier stores) before each row's store.
+// kWideL (L >= 128, chosen by the host): a wave's 128 rows span at most two batch rows, whose two
+// gate vectors are loaded once; otherwise every row's gate is loaded with its residual.
+template <typename T, bool kWideL = true>
 struct EpiResid : EpiNoStage {
   static constexpr bool kLdsOut = sizeof(T) == 2;
   static constexpr int kPitchF = 132;  // floats per staged row: 128 + 4 of padding
@@ -160,49 +162,58 @@ struct EpiResid : EpiNoStage {
     const int nb = M > 0 ? (M - 1) / L + 1 : 0;  // batch rows the gate holds
     const rsrc_t rg = make_rsrc(gate ? gate : hin, gate && nb ? ((size_t)(nb - 1) * gate_stride + N) * sizeof(float) : 0);
     if constexpr (kLdsOut) {
-      static_assert(NQ == 4 && NJ * 32 <= 128, "staged layout: 32x32 blocks, up to 128 columns per wave");
+      static_assert(NQ == 4 && NJ * 32 <= 128 && MI * 32 <= 128, "staged layout: 32x32 blocks, up to 128 x 128 per wave");
       const int hi = lane >> 5, r = lane & 31;   // writer: row r, columns 32 j + 8 q + 4 hi
       const int rr = lane >> 5, ch = lane & 31;  // reader: rows 2 k + rr, columns 4 ch .. 4 ch + 3
       const int n = col0 + 4 * ch;
       const bool colok = ch < 8 * NJ && n < N;  // N is a multiple of 4
-      const int b0 = nrow ? row0 / L : 0;
-      const bool one_b = nrow == 0 || (row0 + nrow - 1) / L == b0;  // wave-uniform
-      const float4 g0 = gate ? __builtin_bit_cast(float4, bload(rg, colok ? (uint32_t)(b0 * gate_stride + n) * 4u : kOOB))
-                             : make_float4(1.f, 1.f, 1.f, 1.f);
-      // residual rows of block i (16 row pairs), loaded one block ahead
-      float4 hv[2][16];
-      auto load = [&](float4 (&h)[16], int i) {
+      const float4 one = make_float4(1.f, 1.f, 1.f, 1.f);
+      // kWideL: gate rows of the first and the last batch row of the wave's rows; rows from
+      // `split` on (within the wave's block) take the second
+      const int b0 = nrow ? row0 / L : 0, bl = nrow ? (row0 + nrow - 1) / L : 0;
+      const int split = (b0 + 1) * L - row0;
+      float4 g0 = one, g1 = one;
+      if constexpr (kWideL) {
+        const float4 g0l = __builtin_bit_cast(float4, bload(rg, colok ? (uint32_t)(b0 * gate_stride + n) * 4u : kOOB));
+        const float4 g1l = __builtin_bit_cast(float4, bload(rg, colok ? (uint32_t)(bl * gate_stride + n) * 4u : kOOB));
+        g0 = gate ? g0l : one;
+        g1 = gate ? g1l : one;
+      }
+      // residual rows of block i (16 row pairs) and, for !kWideL, their gates; loaded one block ahead
+      // for kWideL (at the start of the block otherwise, which keeps that variant's registers)
+      float4 hv[2][16], gq[2][16];
+      auto load = [&](int s, int i) {
 #pragma unroll
-        for (int k = 0; k < 16; ++k)
-          h[k] = __builtin_bit_cast(float4, bload(rin, colok ? (uint32_t)((32 * i + 2 * k + rr) * N + n) * 4u : kOOB));
+        for (int k = 0; k < 16; ++k) {
+          const int row = 32 * i + 2 * k + rr;
+          hv[s][k] = __builtin_bit_cast(float4, bload(rin, colok ? (uint32_t)(row * N + n) * 4u : kOOB));
+          if constexpr (!kWideL) {
+            const int m = row0 + row < M ? row0 + row : (M > 0 ? M - 1 : 0);
+            gq[s][k] = __builtin_bit_cast(float4, bload(rg, colok ? (uint32_t)((m / L) * gate_stride + n) * 4u : kOOB));
+          }
+        }
       };
-      load(hv[0], 0);
+      load(0, 0);
 #pragma unroll
       for (int i = 0; i < MI; ++i) {
-        if (i + 1 < MI) load(hv[(i + 1) & 1], i + 1);
+        if constexpr (kWideL) {
+          if (i + 1 < MI) load((i + 1) & 1, i + 1);
+        } else if (i > 0) {
+          load(i & 1, i);
+        }
 #pragma unroll
         for (int j = 0; j < NJ; ++j)
 #pragma unroll
           for (int q = 0; q < 4; ++q) *reinterpret_cast<float4*>(stg + r * kPitchF + 32 * j + 8 * q + 4 * hi) = quad(acc[i][j], q);
         wave_lds_sync();  // the reads below see every lane's writes above
-        const float4(&h)[16] = hv[i & 1];
-        if (one_b) {
 #pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const int sr = 2 * k + rr, row = 32 * i + sr;  // staged row, row of the wave's block
-            const float4 v = *reinterpret_cast<const float4*>(stg + sr * kPitchF + 4 * ch);
-            bstore(rout, colok ? (uint32_t)(row * N + n) * 4u : kOOB, fma4(g0, v, h[k]));
-          }
-        } else {  // the wave's rows span two batch rows: the gate per row
-#pragma unroll
-          for (int k = 0; k < 16; ++k) {
-            const int sr = 2 * k + rr, row = 32 * i + sr;
-            const float4 v = *reinterpret_cast<const float4*>(stg + sr * kPitchF + 4 * ch);
-            const int m = row0 + row < M ? row0 + row : M - 1;
-            const float4 gv = gate ? __builtin_bit_cast(float4, bload(rg, colok ? (uint32_t)((m / L) * gate_stride + n) * 4u : kOOB))
-                                   : g0;
-            bstore(rout, colok ? (uint32_t)(row * N + n) * 4u : kOOB, fma4(gv, v, h[k]));
-          }
+        for (int k = 0; k < 16; ++k) {
+          const int sr = 2 * k + rr, row = 32 * i + sr;  // staged row, row of the wave's block
+          const float4 v = *reinterpret_cast<const float4*>(stg + sr * kPitchF + 4 * ch);
+          float4 gv;
+          if constexpr (kWideL) gv = row >= split ? g1 : g0;
+          else gv = gate ? gq[i & 1][k] : one;
+          bstore(rout, colok ? (uint32_t)(row * N + n) * 4u : kOOB, fma4(gv, v, hv[i & 1][k]));
         }
         wave_lds_sync();  // the next block's writes come after every lane's reads
       }
@@ -1354,9 +1365,14 @@ template <typename T>
 static hipError_t resid_t(const GemmA& a, const ResidArgs& p, hipStream_t s) {
   BSegs<T> bm = {};
   bm.p[0] = (const T*)p.w; bm.start[0] = 0; bm.start[1] = p.N; bm.nseg = 1; bm.ldb = a.K;
-  EpiResid<T> e;
+  if (p.L >= 128) {  // a wave's 128 rows span at most two batch rows
+    EpiResid<T, true> e;
+    e.hin = p.hin; e.hout = p.hout; e.gate = p.gate; e.gate_stride = p.gate_stride; e.L = p.L; e.N = p.N;
+    return launch<T, BSegs<T>, EpiResid<T, true>, true>(a, p.N, bm, e, s);
+  }
+  EpiResid<T, false> e;
   e.hin = p.hin; e.hout = p.hout; e.gate = p.gate; e.gate_stride = p.gate_stride; e.L = p.L; e.N = p.N;
-  return launch<T, BSegs<T>, EpiResid<T>, true>(a, p.N, bm, e, s);
+  return launch<T, BSegs<T>, EpiResid<T, false>, true>(a, p.N, bm, e, s);
 }
 
 template <typename T>
