@@ -44,9 +44,10 @@ def test_backbone1024_against_oracle_fixture():
 
     mw["blocks"] = []
     with ThreadPoolExecutor(8) as ex:
-        for w in ex.map(one, range(wl.num_layers)):
+        for i, w in enumerate(ex.map(one, range(wl.num_layers))):
             mw["blocks"].append(k2.upload(w, "bf16", dev))
             del w
+            print(f"backbone1024: block {i + 1}/{wl.num_layers} weights on the device", flush=True)
     inp = S.backbone_inputs(wl)
     t = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(dev)
     x = t(S.as_dtype(inp["x"], "bf16")).to(torch.bfloat16)
