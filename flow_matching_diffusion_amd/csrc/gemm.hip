@@ -127,7 +127,7 @@ struct EpiNoStage {
   static constexpr int kLdsOutFloats = 0;
   static constexpr int stage_floats() { return 0; }
   __device__ bool wants_stage(int) const { return false; }
-  __device__ void stage(float*, int, int, int, int) const {}
+  __device__ void stage(float*, int, int, int) const {}
 };
 
 // hout = hin + gate[batch] * acc (gated residual; gate NULL means 1). hin may alias hout.
@@ -508,23 +508,40 @@ struct EpiQkvg {
   static constexpr int kStgRow = HD + 4;
   static constexpr int stage_floats() { return 2 * HD + 256 * kStgRow; }
   __device__ bool wants_stage(int n0) const { return n0 < nq + nk; }
-  __device__ void stage(float* st, int m0, int M, int tid, int nthr) const {
-    for (int i = tid; i < 2 * HD; i += nthr) {
-      const float* w = i < HD ? wnq : wnk;
-      st[i] = 1.0f + (w ? w[i % HD] : 0.0f);
+  // Run by the workgroup's 256 threads. Every table load is issued before the first LDS store, so
+  // the staging costs one memory round trip (in batches of four loads per thread it took four).
+  __device__ void stage(float* st, int m0, int M, int tid) const {
+    constexpr int NTHR = 256;
+    constexpr int P4 = HD / 8;              // float4s of cos (or sin) per row: HD / 2 pairs
+    constexpr int NI = 256 * P4 / NTHR;     // (cos, sin) float4 pairs per thread
+    static_assert(256 * P4 % NTHR == 0 && 2 * HD <= 2 * NTHR, "staging split");
+    float4 cv[NI], sv[NI];
+    if (rc) {
+#pragma unroll
+      for (int k = 0; k < NI; ++k) {
+        const int i = tid + NTHR * k, r = i / P4, c4 = i - r * P4;
+        const int m = m0 + r;
+        const int l = (m < M ? m : 0) % L;
+        cv[k] = ld4(rc + (size_t)l * (HD / 2) + 4 * c4);
+        sv[k] = ld4(rs + (size_t)l * (HD / 2) + 4 * c4);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int i = tid + NTHR * k;
+      if (i < 2 * HD) {
+        const float* w = i < HD ? wnq : wnk;
+        st[i] = 1.0f + (w ? w[i % HD] : 0.0f);
+      }
     }
     if (!rc) return;
-    constexpr int P4 = HD / 8;  // float4s of cos (or sin) per row: HD / 2 pairs
     float* t = st + 2 * HD;
-#pragma unroll 4
-    for (int i = tid; i < 256 * P4; i += nthr) {
-      const int r = i / P4, c4 = i - r * P4;
-      const int m = m0 + r;
-      const int l = (m < M ? m : 0) % L;
-      const float4 c = ld4(rc + (size_t)l * (HD / 2) + 4 * c4), sn = ld4(rs + (size_t)l * (HD / 2) + 4 * c4);
+#pragma unroll
+    for (int k = 0; k < NI; ++k) {
+      const int i = tid + NTHR * k, r = i / P4, c4 = i - r * P4;
       float* d = t + r * kStgRow + 8 * c4;
-      st4(d, make_float4(c.x, sn.x, c.y, sn.y));
-      st4(d + 4, make_float4(c.z, sn.z, c.w, sn.w));
+      st4(d, make_float4(cv[k].x, sv[k].x, cv[k].y, sv[k].y));
+      st4(d + 4, make_float4(cv[k].z, sv[k].z, cv[k].w, sv[k].w));
     }
   }
 
@@ -1187,7 +1204,7 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
     static_assert(Epi::stage_floats() * sizeof(float) <= Rings<RA, RB>::units(4) * sizeof(uint4), "LDS staging");
     if (epi.wants_stage(n0)) {  // tile-uniform
       __syncthreads();  // every wave is done with the rings
-      epi.stage(reinterpret_cast<float*>(lds), m0, M, tid, 256);
+      epi.stage(reinterpret_cast<float*>(lds), m0, M, tid);  // 256 threads
       __syncthreads();
       stg = reinterpret_cast<float*>(lds);
     }
