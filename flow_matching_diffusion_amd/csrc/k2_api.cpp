@@ -991,6 +991,12 @@ int k2_block_backward(const k2_block_cfg* cfg, const k2_block_weights* w, int B,
   if (!grads) return fail(K2_ERR_NULL, "grads is NULL (pass a struct of NULLs for no weight gradients)");
   if (grad_in == hidden_in || grad_in == grad_out) return fail(K2_ERR_CONFIG, "grad_in may not alias hidden_in or grad_out");
   if (cfg->hidden % 4 || cfg->hidden > 8192) return fail(K2_ERR_CONFIG, "the backward needs hidden <= 8192");
+  {  // the attention backward addresses a batch row's query-side rows through one 32-bit-offset resource
+    const long long L = (long long)T + N, nq = (long long)cfg->num_heads * cfg->head_dim;
+    if (L * nq * (long long)dt_size(cfg->dtype) > 0x7FFFFFF0LL)
+      return fail(K2_ERR_SHAPE, "sequence of %lld tokens too long for the backward: its query rows (%lld bytes per batch row) "
+                  "exceed 2^31 - 16 bytes", L, L * nq * (long long)dt_size(cfg->dtype));
+  }
   if (grad_temb && !w->scale_shift_table) return fail(K2_ERR_CONFIG, "grad_temb given for an unmodulated block");
   if (grads->scale_shift_table && !w->scale_shift_table)
     return fail(K2_ERR_CONFIG, "a scale_shift_table gradient asked of an unmodulated block");

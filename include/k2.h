@@ -166,7 +166,8 @@ int k2_block_forward_static_ws(const k2_block_cfg* cfg, const k2_block_weights* 
    grad_temb: (B, 6*hidden) float32 or NULL; NULL is required when the block has no
    scale_shift_table.  grads: one float32 device pointer per weight, same shapes as
    k2_block_weights' tensors, each written (not accumulated), or NULL to skip that gradient (the
-   product it needs is then not run). Requires hidden <= 8192.
+   product it needs is then not run). Requires hidden <= 8192, text tokens T <= 16384 and
+   (T + N) * num_heads * head_dim * element size <= 2^31 - 16 bytes (K2_ERR_SHAPE above it).
    Workspace: k2_block_backward_workspace_bytes(cfg, B, T, N). */
 typedef struct {
   float* scale_shift_table; /* (6, hidden) */

@@ -140,6 +140,23 @@ def test_block_validation_codes():
     assert call_block(w=w) == EALIGN
 
 
+def test_block_backward_validation_codes():
+    lib = k2.load()
+    grads = _abi.BlockGrads()
+
+    def call(B=1, T=4, N=4, rows=8, gout=FAKE, gin=FAKE + 0x10000000, ws_bytes=0):
+        return lib.k2_block_backward(ctypes.byref(good_cfg()), ctypes.byref(good_weights()), B, T, N, FAKE, FAKE,
+                                     FAKE, rows, 3, None, gout, gin, None, ctypes.byref(grads), FAKE, ws_bytes, None)
+
+    assert call(gout=None) == ENULL
+    assert call(gin=FAKE) == ECONFIG  # grad_in aliases hidden_in
+    # the attention backward addresses a batch row's query rows (48 x 128 bf16 per token) through
+    # one 2 GiB buffer range
+    L_max = 0x7FFFFFF0 // (48 * 128 * 2)
+    assert call(T=512, N=L_max - 512, rows=L_max) == EWS  # passes validation, fails on ws
+    assert call(T=512, N=L_max - 511, rows=L_max + 1) == ESHAPE and b"too long for the backward" in lib.k2_last_error()
+
+
 def test_workspace_layout_is_ordered_and_aligned():
     lib = k2.load()
     lay = k2.block_workspace_layout(good_cfg(), 2, 512, 4096)
