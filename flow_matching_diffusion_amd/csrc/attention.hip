@@ -26,6 +26,7 @@
 // the float32 sum and the bf16 P operand), which the final division by the row sum undoes exactly.
 #include "k2_device.h"
 #include "k2_kernels.h"
+#include "k2_tiles.h"
 
 namespace k2 {
 
@@ -396,17 +397,22 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int b = blockIdx.z, kvh = blockIdx.y;
-  const int head = kvh * G + wave % G;
-  const int q0 = blockIdx.x * BQ + (wave / G) * 32;
   const int L = p.L, T_ = p.T;
+  // (batch row, kv head, query block) items in that order, each XCD taking a contiguous range
+  // (xcd_item), so that the workgroups running together on an XCD share K / V^T in its L2; dealt
+  // round-robin, all eight XCDs streamed the same K / V^T into their own L2s
+  const int nqb = (L + BQ - 1) / BQ;
+  const int item = xcd_item(blockIdx.x, nqb * p.nkv * p.B);
+  const int qb = item % nqb, kvh = (item / nqb) % p.nkv, b = item / nqb / p.nkv;
+  const int head = kvh * G + wave % G;
+  const int q0 = qb * BQ + (wave / G) * 32;
   const int ldq = p.nh * HD, ldk = p.nkv * HD;
   const int h32 = lane >> 5, c32 = lane & 31;
 
   // Block-causal restriction: query i sees keys j <= reach[i], non-decreasing in i, so the
   // workgroup's first and last queries bound which tiles need it and where the keys end; rq is
   // this lane's query's reach.
-  const int qlo = blockIdx.x * BQ;
+  const int qlo = qb * BQ;
   int kmin = L - 1, kmax = L - 1, rq = L - 1;
   if (p.reach) {
     kmin = p.reach[qlo];
@@ -846,7 +852,9 @@ static hipError_t launch_attn_bf16(const AttnArgs& p, hipStream_t s) {
   constexpr int BQ = 32 * (4 / G);
   if (p.L <= 0 || p.B <= 0) return hipSuccess;
   if (p.T > kMaxTextTiles64 * 64 || p.ldvt % 64 != 0) return hipErrorInvalidValue;
-  dim3 grid((p.L + BQ - 1) / BQ, p.nkv, p.B);
+  const long long items = (long long)((p.L + BQ - 1) / BQ) * p.nkv * p.B;
+  if (items > 0x7FFFFFFFLL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)items);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)HD);
   hipLaunchKernelGGL((attn_bf16_kernel<HD, G>), grid, dim3(256), 0, s, p, scale_log2);
   return hipGetLastError();

@@ -51,6 +51,16 @@ __host__ __device__ inline void tile_coords(int bid, int tiles_m, int tiles_n, i
   }
 }
 
+// Workgroup bid (of total) -> work item, such that each XCD (bid % 8) takes one contiguous range of
+// items, in order: XCD x gets total / 8 items (one more for x < total % 8) starting at
+// x * (total / 8) + min(x, total % 8). A bijection on [0, total). Items next to each other in the
+// caller's order (e.g. query blocks of one attention head) then run together on one XCD and share
+// its L2, instead of being dealt across all eight.
+__host__ __device__ inline int xcd_item(int bid, int total) {
+  const int x = bid & 7, s = bid >> 3, q = total >> 3, r = total & 7;
+  return x * q + (x < r ? x : r) + s;
+}
+
 // N-tiles per super-column: about kSuperColumnBytes of weight rows, in equal super-columns.
 constexpr size_t kSuperColumnBytes = size_t(96) << 20;
 inline int super_cols(int tiles_n, int BN, int K, int elem) {

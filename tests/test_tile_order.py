@@ -1,6 +1,7 @@
 """Host logic of the GEMM tile order (flow_matching_diffusion_amd/csrc/k2_tiles.h), compiled with the
 host C++ compiler: every workgroup index maps to a distinct output tile, for every grid shape and
-super-column width, and the super-column widths cover the N tiles in near-equal parts."""
+super-column width, and the super-column widths cover the N tiles in near-equal parts; the attention
+grid's XCD-contiguous work map is a bijection too."""
 import os
 import shutil
 import subprocess
@@ -32,6 +33,20 @@ int main() {
         }
         for (int v : seen) bad += v != 1;
       }
+  // xcd_item: a bijection, each XCD's items contiguous and in slot order
+  for (int total = 1; total <= 5000; total += (total < 100 ? 1 : 37)) {
+    ++cases;
+    std::vector<int> seen(total, 0), last(8, -1);
+    for (int bid = 0; bid < total; ++bid) {
+      const int it = k2::xcd_item(bid, total);
+      if (it < 0 || it >= total) { ++bad; continue; }
+      seen[it]++;
+      const int x = bid & 7;
+      if (last[x] >= 0 && it != last[x] + 1) ++bad;
+      last[x] = it;
+    }
+    for (int v : seen) bad += v != 1;
+  }
   // the block's GEMM shapes at 1024^2: 36 M tiles; N tiles 60 (qkvg), 24 (out, down), 128 (swiglu)
   const int shapes[][3] = {{60, 6144, 0}, {24, 6144, 0}, {128, 6144, 0}, {24, 16384, 0}};
   for (auto& sh : shapes) {
