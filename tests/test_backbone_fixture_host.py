@@ -45,3 +45,18 @@ def test_fixture_key_ignores_docstrings_only():
         assert m.code_hash(p) == h0
         open(p, "w").write(src.replace("x + 1", "x + 2"))
         assert m.code_hash(p) != h0
+
+
+def test_stored_model_statistics_match_the_code():
+    """The committed oracle outputs (the 28-block fixture, the block512 gradient statistics) were
+    written by the oracle and generators in the tree: a stale file fails here, on the CPU."""
+    import json
+    from tests.golden.block512_backward_stats import OUT, stats_key
+    m = _script()
+    fx = np.load(m.OUT, allow_pickle=False)
+    assert str(fx["key"]) == m.fixture_key(S.WORKLOADS["backbone1024"])
+    st = json.load(open(OUT))
+    assert st["key"] == stats_key(S.WORKLOADS["block512"])
+    for k in ("h", "temb", "ff_down"):
+        for f in ("A", "B", "C"):
+            assert 0 < st["stats"][k][f]["rms"] <= st["stats"][k][f]["p999"] <= st["stats"][k][f]["max"]

@@ -5,12 +5,14 @@ weight gradient, as max |gpu - oracle| / rms(oracle). float32: <= 1e-4 against t
 bf16: tests/k2_testutil.parity's bounds for gradients, derived from legitimate realisations of the
 bf16 model that the oracle computes (its rounding points include the backward's matrix-product
 operands, reading R20)."""
+import json
+
 import numpy as np
 import pytest
 
 from flow_matching_diffusion_amd import synth as S
 from oracle import k2_oracle as O
-from tests.k2_testutil import device, parity, rel_err, temb_for
+from tests.k2_testutil import SPREAD, device, err_stats, parity, temb_for
 
 pytestmark = pytest.mark.gpu
 
@@ -119,8 +121,12 @@ def test_block1024_backward_properties():
     - float32: directional derivatives of L = <g, block(h)> from k2_block_backward (along a random
       direction of h, of temb and of the down-projection weight) against central differences of
       two k2_block_forward runs;
-    - bf16: its gradients against the float32 ones, within the size of bf16's deviation (the
-      block512 full-width test measures about 4e-3 rms against the exact gradients)."""
+    - bf16: its input, temb and down-projection gradients against the float32 ones (which sit within
+      1e-4 of the exact function), each statistic (max, p99.9, rms) within the bf16 model's own
+      deviation for that gradient at the full-size 512^2 block: the largest of the oracle's three bf16
+      realisations against its exact gradients there (tests/golden/block512_backward_bf16_stats.json,
+      written from oracle/ alone), times the backward spread factor. Same hidden and intermediate
+      sizes, so the same products and reductions; block1024 only has the longer sequence."""
     import torch
     import flow_matching_diffusion_amd as k2
     from tests.k2_testutil import workload
@@ -171,10 +177,16 @@ def test_block1024_backward_properties():
     gi, gtemb, grads = k2.block_backward(cfg16, w16, h, tb, pos, mask, wl.T, g, want=["ff_down", "to_q", "norm2_w"])
     torch.cuda.synchronize()
     got = {"h": gi.cpu().numpy(), "temb": gtemb.cpu().numpy(), "ff_down": grads["ff_down"].cpu().numpy()}
+    from tests.golden.block512_backward_stats import OUT as STATS, stats_key
+    model = json.load(open(STATS))
+    assert model["key"] == stats_key(workload("block512")), \
+        "the oracle or the generators changed since the statistics were written: run tests/golden/block512_backward_stats.py"
     for k in got:
         assert np.all(np.isfinite(got[k])), k
-        err, rms = rel_err(got[k], ref[k])
-        print(f"block1024 bf16 vs f32 d{k}: max {err:.3e} rms {rms:.3e}", flush=True)
-        assert rms <= 2e-2 and err <= 0.5, f"d{k}: max {err:.3e} rms {rms:.3e}"
+        st = err_stats(got[k], ref[k], float(np.sqrt(np.mean(np.square(ref[k], dtype=np.float64)))))
+        for stat in ("max", "p999", "rms"):
+            bound = SPREAD["backward"][stat] * max(model["stats"][k][f][stat] for f in ("A", "B", "C"))
+            print(f"block1024 bf16 vs f32 d{k}: {stat} {st[stat]:.3e} (bound {bound:.3e})", flush=True)
+            assert st[stat] <= bound, f"d{k}: {stat} {st[stat]:.3e} > {bound:.3e}"
     for k in ("to_q", "norm2_w"):
         assert np.all(np.isfinite(grads[k].cpu().numpy())), k
