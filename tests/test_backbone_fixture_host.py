@@ -60,3 +60,19 @@ def test_stored_model_statistics_match_the_code():
     for k in ("h", "temb", "ff_down"):
         for f in ("A", "B", "C"):
             assert 0 < st["stats"][k][f]["rms"] <= st["stats"][k][f]["p999"] <= st["stats"][k][f]["max"]
+
+
+def test_block512_statistics_give_finite_backward_bounds():
+    """The bound the block1024 backward test applies, computed here from the stored statistics: each
+    is finite, no tighter than the largest realisation and, for max, within the spread's range."""
+    import json
+    from tests.golden.block512_backward_stats import OUT
+    from tests.k2_testutil import SPREAD, spread_bound
+    st = json.load(open(OUT))["stats"]
+    for k in ("h", "temb", "ff_down"):
+        for stat in ("max", "p999", "rms"):
+            forms = [st[k][f] for f in ("A", "B", "C")]
+            b = spread_bound("backward", stat, forms)
+            top = max(f[stat] for f in forms)
+            assert np.isfinite(b) and top <= b <= SPREAD["factor"]["backward"]["max"] * top, (k, stat, b)
+

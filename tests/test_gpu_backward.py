@@ -12,7 +12,7 @@ import pytest
 
 from flow_matching_diffusion_amd import synth as S
 from oracle import k2_oracle as O
-from tests.k2_testutil import SPREAD, device, err_stats, parity, temb_for
+from tests.k2_testutil import device, err_stats, parity, spread_bound, temb_for
 
 pytestmark = pytest.mark.gpu
 
@@ -181,12 +181,15 @@ def test_block1024_backward_properties():
     model = json.load(open(STATS))
     assert model["key"] == stats_key(workload("block512")), \
         "the oracle or the generators changed since the statistics were written: run tests/golden/block512_backward_stats.py"
+    bad = []
     for k in got:
         assert np.all(np.isfinite(got[k])), k
         st = err_stats(got[k], ref[k], float(np.sqrt(np.mean(np.square(ref[k], dtype=np.float64)))))
         for stat in ("max", "p999", "rms"):
-            bound = SPREAD["backward"][stat] * max(model["stats"][k][f][stat] for f in ("A", "B", "C"))
+            bound = spread_bound("backward", stat, [model["stats"][k][f] for f in ("A", "B", "C")])
             print(f"block1024 bf16 vs f32 d{k}: {stat} {st[stat]:.3e} (bound {bound:.3e})", flush=True)
-            assert st[stat] <= bound, f"d{k}: {stat} {st[stat]:.3e} > {bound:.3e}"
+            if st[stat] > bound:
+                bad.append(f"d{k}: {stat} {st[stat]:.3e} > {bound:.3e}")
+    assert not bad, "; ".join(bad)
     for k in ("to_q", "norm2_w"):
         assert np.all(np.isfinite(grads[k].cpu().numpy())), k
