@@ -41,8 +41,11 @@ PEAK_HBM_GBS = 8000.0
 COPY_BYTES = 1 << 30
 KERNELS = ("modulation", "modnorm", "gemm_qkvg", "attention", "gemm_out", "gemm_swiglu", "gemm_down", "rope")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
-KERNEL_SOURCES = [os.path.join(ROOT, "flow_matching_diffusion_amd", "csrc", f) for f in
-                  ("gemm.hip", "k2_device.h", "k2_tiles.h", "attention.hip", "elementwise.hip")]
+_CSRC = os.path.join(ROOT, "flow_matching_diffusion_amd", "csrc")
+_HEADERS = ("k2_device.h", "k2_kernels.h", "k2_tiles.h")
+# The translation unit (and the headers it includes) that builds each kernel a traffic record covers.
+KERNEL_SOURCES = {"gemm": ("gemm.hip",) + _HEADERS, "attention": ("attention.hip",) + _HEADERS,
+                  "modnorm": ("elementwise.hip",) + _HEADERS}
 
 
 def block_flops(d, B, L, valid_keys):
@@ -58,10 +61,14 @@ def kernel_flops(d, M, name):
             "gemm_swiglu": 4 * M * H * I, "gemm_down": 2 * M * I * H}.get(name)
 
 
-def source_hash():
+def source_hash(key):
+    """Hash of the sources that build the kernel of traffic record `key` ("gemm_swiglu@block1024"):
+    a record stays valid while they are unchanged, whatever happens to the other kernels."""
+    dom = key.split("@")[0]
+    files = next(v for k, v in KERNEL_SOURCES.items() if dom.startswith(k))
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        h.update(open(p, "rb").read())
+    for f in files:
+        h.update(open(os.path.join(_CSRC, f), "rb").read())
     return h.hexdigest()[:16]
 
 
@@ -73,7 +80,7 @@ def traffic_for(key):
     except (OSError, ValueError):
         return None
     e = t.get(key)
-    if not e or e.get("source_sha") != source_hash():
+    if not e or e.get("source_sha") != source_hash(key):
         return None
     return e["fetch_bytes"] + e["write_bytes"]
 

@@ -12,7 +12,7 @@
       plain copy kernel of known size (COPY-MATCH, reading and writing N bytes) read N
       bytes (FETCH) and write N bytes (WRITE). Prints Markdown and merges
       {KEY: {fetch_bytes, write_bytes, ...}} into profiles/traffic.json, stamped with the
-      hash of the kernel sources so that a stale record is never reported.
+      hash of the sources that build KEY's kernel so that a stale record is never reported.
 
   python -m flow_matching_diffusion_amd.profsum trace TRACE_CSV --cmd "..." [--skip N]
       Per-launch-shape statistics from a `rocprofv3 --kernel-trace` run (the *_kernel_trace.csv
@@ -92,7 +92,7 @@ def traffic(a) -> str:
     rec = {"kernel": kname, "fetch_bytes": round(fetch_b), "write_bytes": round(write_b),
            "fetch_kib_raw": round(f_kib, 1), "write_kib_raw": round(w_kib, 1),
            "copy_kernel": cname, "copy_bytes": a.copy_bytes, "fetch_scale": round(f_scale, 4),
-           "write_scale": round(w_scale, 4), "source_sha": bench.source_hash(),
+           "write_scale": round(w_scale, 4), "source_sha": bench.source_hash(a.key),
            "cmd_fetch": a.cmd_fetch, "cmd_write": a.cmd_write}
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
