@@ -126,7 +126,10 @@ def trace(path: str, cmd: str, skip: int = 0) -> str:
         r0 = used[0]
         rows.append((sum(d), name, gx, gy, gz, len(used), sum(d) / len(d), min(d), max(d), r0))
     rows.sort(key=lambda x: -x[0])
-    out = [f"Command: `{cmd}`", "", f"First {skip} dispatches of each kernel and grid left out (warm-up).", "",
+    out = [f"Command: `{cmd}`", "", f"First {skip} dispatches of each kernel and grid left out (warm-up).",
+           "VGPR and AGPR are the trace's VGPR_Count and Accum_VGPR_Count columns; on this part VGPR_Count reads",
+           "half of the register total the compiler reports for the kernel (for example 192 for a kernel built",
+           "with 384, which runs one wave per SIMD).", "",
            "| kernel | grid (threads) | calls | avg us | min us | max us | VGPR | AGPR | LDS B | scratch B |",
            "|---|---|---:|---:|---:|---:|---:|---:|---:|---:|"]
     for tot, name, gx, gy, gz, n, avg, mn, mx, r0 in rows:
