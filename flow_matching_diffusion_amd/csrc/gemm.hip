@@ -126,8 +126,8 @@ struct EpiNoStage {
   static constexpr bool kLdsOut = false;  // the epilogue writes its output through a per-wave LDS area
   static constexpr int kLdsOutFloats = 0;
   static constexpr int stage_floats() { return 0; }
-  __device__ bool wants_stage(int) const { return false; }
-  __device__ void stage(float*, int, int, int) const {}
+  __device__ __forceinline__ bool wants_stage(int) const { return false; }
+  __device__ __forceinline__ void stage(float*, int, int, int) const {}
 };
 
 // hout = hin + gate[batch] * acc (gated residual; gate NULL means 1). hin may alias hout.
@@ -507,10 +507,10 @@ struct EpiQkvg {
   static constexpr int kOutFloats = kOutStage ? 16 * kOutPitch / 4 : 0;
   static constexpr int kStgRow = HD + 4;
   static constexpr int stage_floats() { return 2 * HD + 256 * kStgRow; }
-  __device__ bool wants_stage(int n0) const { return n0 < nq + nk; }
+  __device__ __forceinline__ bool wants_stage(int n0) const { return n0 < nq + nk; }
   // Run by the workgroup's 256 threads. Every table load is issued before the first LDS store, so
   // the staging costs one memory round trip (in batches of four loads per thread it took four).
-  __device__ void stage(float* st, int m0, int M, int tid) const {
+  __device__ __forceinline__ void stage(float* st, int m0, int M, int tid) const {
     constexpr int NTHR = 256;
     constexpr int P4 = HD / 8;              // float4s of cos (or sin) per row: HD / 2 pairs
     constexpr int NI = 256 * P4 / NTHR;     // (cos, sin) float4 pairs per thread
