@@ -545,16 +545,30 @@ struct EpiQkvg {
     }
   }
 
-  // q (seg 0), k (1) or gate (3) head of a wave through its output staging area (kOutStage).
+  // q (seg 0), k (1) or gate (3) head of a wave through its output staging area (kOutStage). A q or
+  // k tile always has its multipliers and (cos, sin) pairs staged in stg (wants_stage holds for every
+  // tile that holds q or k columns), and whether RoPE applies is decided once, outside the unrolled
+  // loops. With a test per group of four columns, and a global-memory path behind it, the compiler
+  // waited for every memory operation in flight, the epilogue's own stores included, at each join
+  // (198 full waits in the kernel).
   template <class LY, int MI, int NJ>
   __device__ __forceinline__ void apply_staged(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
                                                int M, const float* stg, float* ostg, int seg) const {
+    if (seg <= 1 && rc)
+      apply_staged_t<LY, MI, NJ, true>(acc, row0, col0, lane, M, stg, ostg, seg);
+    else
+      apply_staged_t<LY, MI, NJ, false>(acc, row0, col0, lane, M, stg, ostg, seg);
+  }
+
+  template <class LY, int MI, int NJ, bool kRope>
+  __device__ __forceinline__ void apply_staged_t(const typename LY::F (&acc)[MI][NJ], int row0, int col0, int lane,
+                                                 int M, const float* stg, float* ostg, int seg) const {
     T* const dst = seg == 0 ? q : seg == 1 ? k : g;
     const int ld = seg == 1 ? nk : nq;
     const int cb = seg == 0 ? col0 : seg == 1 ? col0 - nq : col0 - nq - 2 * nk;
-    const float* const wn = seg == 0 ? wnq : wnk;
+    const float* const wst = stg + (seg == 0 ? 0 : HD);  // staged 1 + w of this head's norm
     char* const os = reinterpret_cast<char*>(ostg);
-    const int r = lane & 31, hi = lane >> 5;     // accumulator layout: row r, columns 32 jj + 8 qq + 4 hi
+    const int r = lane & 31;                      // accumulator layout: row r, columns 32 jj + 8 qq + 4 (lane >> 5)
     const int rr = lane >> 4, ch = lane & 15;    // read-back: row 4 kk + rr, columns 8 ch .. 8 ch + 7
 #pragma unroll
     for (int i = 0; i < MI; ++i) {
@@ -575,31 +589,30 @@ struct EpiQkvg {
           for (int e = 0; e < 16; ++e) ss += acc[i][jj][e] * acc[i][jj][e];
         ss = LY::rowsum(ss);
         const float inv = rsqrtf(ss * (1.0f / HD) + eps);
-        const int l = (m < M ? m : 0) % L;
+        const float* const cst = stg + 2 * HD + ((row0 & 255) + 32 * i + r) * kStgRow;  // this row's (cos, sin)
 #pragma unroll
-        for (int jj = 0; jj < NJ; ++jj)
+        for (int jq = 0; jq < 2 * NJ; ++jq) {
+          // the LDS operands of two groups of four columns in one batch, so that one wait covers
+          // them (read one group at a time, each read waited for its own latency: the output
+          // staging's writes may alias them as far as the compiler can tell)
+          const int jj = jq >> 1;
+          float4 w4[2], cs[2];
 #pragma unroll
-          for (int qq = 0; qq < 4; ++qq) {
+          for (int x = 0; x < 2; ++x) {
+            w4[x] = ld4(wst + LY::col(jj, 2 * (jq & 1) + x, lane));
+            if constexpr (kRope) cs[x] = ld4(cst + LY::col(jj, 2 * (jq & 1) + x, lane));
+          }
+#pragma unroll
+          for (int x = 0; x < 2; ++x) {
+            const int qq = 2 * (jq & 1) + x;
             const int d = LY::col(jj, qq, lane);
             float4 y = quad(acc[i][jj], qq);
-            if (stg) {  // staged multipliers and (cos, sin) pairs
-              const float4 w4 = ld4(stg + (seg == 0 ? 0 : HD) + d);
-              y.x *= inv * w4.x; y.y *= inv * w4.y; y.z *= inv * w4.z; y.w *= inv * w4.w;
-              if (rc) {
-                const float4 cs = ld4(stg + 2 * HD + ((row0 & 255) + 32 * i + r) * kStgRow + d);
-                y = make_float4(y.x * cs.x - y.y * cs.y, y.y * cs.x + y.x * cs.y,
-                                y.z * cs.z - y.w * cs.w, y.w * cs.z + y.z * cs.w);
-              }
-            } else {
-              const float4 w4 = wn ? ld4(wn + d) : make_float4(0.f, 0.f, 0.f, 0.f);
-              y.x *= inv * (1.0f + w4.x); y.y *= inv * (1.0f + w4.y);
-              y.z *= inv * (1.0f + w4.z); y.w *= inv * (1.0f + w4.w);
-              if (rc) {
-                const float2 c2 = *reinterpret_cast<const float2*>(rc + (size_t)l * (HD / 2) + (d >> 1));
-                const float2 s2 = *reinterpret_cast<const float2*>(rs + (size_t)l * (HD / 2) + (d >> 1));
-                y = make_float4(y.x * c2.x - y.y * s2.x, y.y * c2.x + y.x * s2.x,
-                                y.z * c2.y - y.w * s2.y, y.w * c2.y + y.z * s2.y);
-              }
+            const float4 w = w4[x];
+            y.x *= inv * w.x; y.y *= inv * w.y; y.z *= inv * w.z; y.w *= inv * w.w;
+            if constexpr (kRope) {
+              const float4 c = cs[x];
+              y = make_float4(y.x * c.x - y.y * c.y, y.y * c.x + y.x * c.y,
+                              y.z * c.z - y.w * c.w, y.w * c.z + y.z * c.w);
             }
             pk[jj][qq] = make_uint2(pack_bf16x2(y.x, y.y), pack_bf16x2(y.z, y.w));
             if (kSave && seg == 1 && m < M) {  // k transposed per (batch, kv head), like vt
@@ -612,6 +625,7 @@ struct EpiQkvg {
               kp[(size_t)(dd + 3) * ldvt] = to_t<T>(y.w);
             }
           }
+        }
       } else {
 #pragma unroll
         for (int jj = 0; jj < NJ; ++jj)
@@ -656,6 +670,32 @@ struct EpiQkvg {
         apply_staged<LY, MI, NJ>(acc, row0, col0, lane, M, stg, ostg, seg);
         return;
       }
+      // one v head, transposed per (batch, kv head); a path of its own so that the code for the
+      // other segments, never taken here, does not weigh on this one
+      const int vc0 = col0 - nq - nk;  // first column within v (a head boundary)
+      const int kvh = vc0 / HD, nkvh = nk / HD;
+#pragma unroll
+      for (int i = 0; i < MI; ++i) {
+        const int m = row0 + LY::row(i, lane);
+        if (m >= M) continue;
+        const int b = m / L, l = m - b * L;
+        T* const base = vt + (size_t)(b * nkvh + kvh) * HD * ldvt + l;
+        if constexpr (kSave) {
+#pragma unroll
+          for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+            for (int qq = 0; qq < LY::NQ; ++qq) st4(vrow + (size_t)m * nk + vc0 + LY::col(jj, qq, lane), quad(acc[i][jj], qq));
+        }
+#pragma unroll
+        for (int jj = 0; jj < NJ; ++jj)
+#pragma unroll
+          for (int qq = 0; qq < LY::NQ; ++qq) {
+            const int d = LY::col(jj, qq, lane);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) base[(size_t)(d + e) * ldvt] = to_t<T>(acc[i][jj][4 * qq + e]);
+          }
+      }
+      return;
     }
     if constexpr (NJ % HB != 0) {
       // A wave narrower than a head (the 256x128 halves of a last partial round): the host runs
