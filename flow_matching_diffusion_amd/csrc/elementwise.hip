@@ -127,8 +127,9 @@ __global__ void __launch_bounds__(256) modnorm_kernel(ModnormArgs p) {
 }
 
 // bf16 output, H a multiple of 8 up to 8 NT: each thread owns 8 consecutive columns of R rows (two
-// 16-byte loads and one 16-byte store per row); NT threads cover the row. At 9216 x 6144: 65 us
-// against 75-77 us for modnorm_kernel (4-column chunks, 256 threads), 5.2 TB/s.
+// 16-byte loads and one 16-byte store per row); NT threads cover the row. Both rows' loads are issued
+// before the first reduction and the two wave sums run side by side (issued row by row behind a
+// branch, the second row's loads waited for the first row's reduction).
 template <int R, int NT>
 __global__ void __launch_bounds__(NT) modnorm8_kernel(ModnormArgs p) {
   __shared__ float red[R][NT / 64];
@@ -137,6 +138,7 @@ __global__ void __launch_bounds__(NT) modnorm8_kernel(ModnormArgs p) {
   const int nr = min(R, p.rows - r0);
   const int c = threadIdx.x;  // 8-column chunk
   const bool on = c < (p.H >> 3);
+  const int cc = on ? c : 0;  // a thread past the row loads chunk 0 and never stores
   const float4* x[R];
   bf16* y[R];
   int bb[R];
@@ -149,18 +151,22 @@ __global__ void __launch_bounds__(NT) modnorm8_kernel(ModnormArgs p) {
     y[k] = (bf16*)p.out + (size_t)r * p.H;
   }
   float4 v[R][2];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    v[k][0] = x[k][2 * cc];
+    v[k][1] = x[k][2 * cc + 1];
+  }
   float ss[R];
 #pragma unroll
   for (int k = 0; k < R; ++k) {
-    v[k][0] = v[k][1] = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (on) {
-      v[k][0] = x[k][2 * c];
-      v[k][1] = x[k][2 * c + 1];
-    }
+    if (!on) v[k][0] = v[k][1] = make_float4(0.f, 0.f, 0.f, 0.f);
     ss[k] = v[k][0].x * v[k][0].x + v[k][0].y * v[k][0].y + v[k][0].z * v[k][0].z + v[k][0].w * v[k][0].w +
             v[k][1].x * v[k][1].x + v[k][1].y * v[k][1].y + v[k][1].z * v[k][1].z + v[k][1].w * v[k][1].w;
-    ss[k] = wave_sum(ss[k]);
   }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1)  // the rows' wave sums side by side (wave_sum's order per row)
+#pragma unroll
+    for (int k = 0; k < R; ++k) ss[k] += __shfl_xor(ss[k], o);
   const int wv = threadIdx.x >> 6;
   if ((threadIdx.x & 63) == 0) {
 #pragma unroll
