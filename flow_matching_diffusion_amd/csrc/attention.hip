@@ -398,11 +398,14 @@ __global__ void __launch_bounds__(256, 2) attn_bf16_kernel(AttnArgs p, float sca
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int L = p.L, T_ = p.T;
-  // (batch row, kv head, query block) items in that order, each XCD taking a contiguous range
-  // (xcd_item), so that the workgroups running together on an XCD share K / V^T in its L2; dealt
-  // round-robin, all eight XCDs streamed the same K / V^T into their own L2s
+  // (batch row, kv head, query block) items in that order, each XCD taking a contiguous range of
+  // every batch row's items (xcd_item_rows), so that the workgroups running together on an XCD share
+  // K / V^T in its L2 (dealt round-robin, all eight XCDs streamed the same K / V^T into their own
+  // L2s) and every XCD gets the same share of each batch row, whose text padding makes its items
+  // cheaper or dearer (one contiguous range of all items gave the first half of the XCDs one batch
+  // row and the second half the other)
   const int nqb = (L + BQ - 1) / BQ;
-  const int item = xcd_item(blockIdx.x, nqb * p.nkv * p.B);
+  const int item = xcd_item_rows(blockIdx.x, nqb * p.nkv, p.B);
   const int qb = item % nqb, kvh = (item / nqb) % p.nkv, b = item / nqb / p.nkv;
   const int head = kvh * G + wave % G;
   const int q0 = qb * BQ + (wave / G) * 32;

@@ -127,9 +127,9 @@ __global__ void __launch_bounds__(256) modnorm_kernel(ModnormArgs p) {
 }
 
 // bf16 output, H a multiple of 8 up to 8 NT: each thread owns 8 consecutive columns of R rows (two
-// 16-byte loads and one 16-byte store per row); NT threads cover the row. Both rows' loads are issued
-// before the first reduction and the two wave sums run side by side (issued row by row behind a
-// branch, the second row's loads waited for the first row's reduction).
+// 16-byte loads and one 16-byte store per row); NT threads cover the row. Every row's loads are issued
+// before the first reduction and the rows' wave sums run side by side (issued row by row behind a
+// branch, each row's loads had waited for the previous row's reduction).
 template <int R, int NT>
 __global__ void __launch_bounds__(NT) modnorm8_kernel(ModnormArgs p) {
   __shared__ float red[R][NT / 64];
@@ -201,10 +201,13 @@ __global__ void __launch_bounds__(NT) modnorm8_kernel(ModnormArgs p) {
 }
 
 constexpr int kModnormRows = 2;
+// rows per workgroup of modnorm8_kernel, measured at 9216 x 6144 (same process, three runs each):
+// 1 row 0.075 ms, 2 rows 0.067, 4 rows 0.065, 6 rows 0.074, 8 rows 0.077 (fewer waves per SIMD)
+constexpr int kModnorm8Rows = 4;
 
 template <int NT>
 static hipError_t modnorm8(const ModnormArgs& p, hipStream_t s) {
-  hipLaunchKernelGGL((modnorm8_kernel<kModnormRows, NT>), dim3((p.rows + kModnormRows - 1) / kModnormRows), dim3(NT),
+  hipLaunchKernelGGL((modnorm8_kernel<kModnorm8Rows, NT>), dim3((p.rows + kModnorm8Rows - 1) / kModnorm8Rows), dim3(NT),
                      0, s, p);
   return hipGetLastError();
 }

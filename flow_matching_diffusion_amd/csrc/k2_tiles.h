@@ -61,6 +61,17 @@ __host__ __device__ inline int xcd_item(int bid, int total) {
   return x * q + (x < r ? x : r) + s;
 }
 
+// The same for items in B consecutive groups of per_b (one group per batch row, whose items can
+// cost different amounts from one group to the next): when per_b is a multiple of 8, XCD x takes
+// items [x per_b / 8, (x + 1) per_b / 8) of every group, one group after the other, so that every
+// XCD gets the same share of each group's work while its neighbouring slots still share one group's
+// data; otherwise xcd_item over all B per_b items. A bijection on [0, B per_b).
+__host__ __device__ inline int xcd_item_rows(int bid, int per_b, int B) {
+  if (per_b & 7) return xcd_item(bid, per_b * B);
+  const int x = bid & 7, s = bid >> 3, cnt = per_b >> 3;
+  return (s / cnt) * per_b + x * cnt + s % cnt;
+}
+
 // N-tiles per super-column: about kSuperColumnBytes of weight rows, in equal super-columns.
 constexpr size_t kSuperColumnBytes = size_t(96) << 20;
 inline int super_cols(int tiles_n, int BN, int K, int elem) {

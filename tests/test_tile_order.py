@@ -47,6 +47,28 @@ int main() {
     }
     for (int v : seen) bad += v != 1;
   }
+  // xcd_item_rows: a bijection; with per_b a multiple of 8 every XCD takes per_b / 8 items of each
+  // group, contiguous within the group and in slot order
+  for (int B = 1; B <= 5; ++B)
+    for (int per_b = 1; per_b <= 700; per_b += (per_b < 64 ? 1 : 29)) {
+      ++cases;
+      const int total = B * per_b;
+      std::vector<int> seen(total, 0), last(8, -1);
+      std::vector<std::vector<int>> share(8, std::vector<int>(B, 0));
+      for (int bid = 0; bid < total; ++bid) {
+        const int it = k2::xcd_item_rows(bid, per_b, B);
+        if (it < 0 || it >= total) { ++bad; continue; }
+        seen[it]++;
+        const int x = bid & 7;
+        share[x][it / per_b]++;
+        if (per_b % 8 == 0 && last[x] >= 0 && it / per_b == last[x] / per_b && it != last[x] + 1) ++bad;
+        last[x] = it;
+      }
+      for (int v : seen) bad += v != 1;
+      if (per_b % 8 == 0)
+        for (int x = 0; x < 8; ++x)
+          for (int b = 0; b < B; ++b) bad += share[x][b] != per_b / 8;
+    }
   // the block's GEMM shapes at 1024^2: 36 M tiles; N tiles 60 (qkvg), 24 (out, down), 128 (swiglu)
   const int shapes[][3] = {{60, 6144, 0}, {24, 6144, 0}, {128, 6144, 0}, {24, 16384, 0}};
   for (auto& sh : shapes) {
