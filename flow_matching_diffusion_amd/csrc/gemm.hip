@@ -126,6 +126,7 @@ struct EpiNoStage {
   static constexpr bool kLdsOut = false;  // the epilogue writes its output through a per-wave LDS area
   static constexpr int kLdsOutFloats = 0;
   static constexpr int stage_floats() { return 0; }
+  static constexpr bool kColumnHalves = true;  // a wave 64 columns wide is fine (256x128 half tiles)
   __device__ __forceinline__ bool wants_stage(int) const { return false; }
   __device__ __forceinline__ void stage(float*, int, int, int) const {}
 };
@@ -347,6 +348,7 @@ struct EpiSwiglu : EpiNoStage {
   // an instruction wrote 16 bytes into each of 32 rows 32 KiB apart, and the kernel wrote 2.6x its
   // output to memory (partial lines).
   static constexpr bool kLdsOut = sizeof(T) == 2;
+  static constexpr bool kColumnHalves = false;  // gate and up columns pair across the wave's WN
   static constexpr int kPitch = 144;  // bytes per staged row: 128 + 16 of padding
   static constexpr int kLdsOutFloats = sizeof(T) == 2 ? 128 * kPitch / 4 : 0;  // 128 rows per wave
   T* a;
@@ -496,6 +498,7 @@ struct EpiQkvg {
   static constexpr bool kStaged = true;
   static constexpr bool kLdsOut = false;
   static constexpr int kLdsOutFloats = 0;
+  static constexpr bool kColumnHalves = true;  // for v and gate columns only (tail_allowed)
   // bf16, head_dim 128 (one head per wave): q, k and gate rows leave through a per-wave LDS area
   // placed after the staged tables, 16 rows at a time (rows of 256 bytes + 16 of padding), read
   // back 16 lanes per row so every store writes whole 256-byte rows (stored from the accumulator
@@ -1034,8 +1037,10 @@ gemm_kernel(const T* __restrict__ A, int lda, int M, int K, int Ntot, int scn, B
 // K offset goes in the instruction's scalar offset; slabs past K (fetched ahead, never read) reload
 // slab 0. Otherwise each lane checks its chunk against K and chunks past it read as zero.
 //
-// NJ picks the wave's N width (32 * NJ): 4 gives the 256x256 tile; 2 a 256x128 half tile, used to
-// split the last partial round of tiles so that it takes half as long (see gemm_bf16_kernel).
+// MI_ and NJ pick the wave's M height (32 * MI_) and N width (32 * NJ): 4 and 4 give the 256x256
+// tile; (4, 2) a 256x128 and (2, 4) a 128x256 half tile, used to split the last partial round of
+// tiles so that it takes half as long (see gemm_bf16_kernel). A 128x256 half keeps the wave's full
+// 128 columns, which the SwiGLU pairs and the per-head q/k norms need.
 // ---------------------------------------------------------------------------------------------
 template <int RA, int RB>
 struct Rings {
@@ -1046,14 +1051,14 @@ struct Rings {
   static constexpr int units(int NJ) { return (RA * 256 + RB * 64 * NJ) * 8; }
 };
 
-template <int SPREAD, bool KFULL, int NJ, int RA, int RB, class BMap, class Epi>
+template <int SPREAD, bool KFULL, int MI_, int NJ, int RA, int RB, class BMap, class Epi>
 __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int m0, int n0,
                                           const BMap& bmap, const Epi& epi, uint4* lds) {
   typedef Rings<RA, RB> R;
-  constexpr int BM = 256, BN = 64 * NJ, WM = 128, WN = 32 * NJ, BK = 64;
-  constexpr int MI = WM / 32;
+  constexpr int BM = 64 * MI_, BN = 64 * NJ, WM = 32 * MI_, WN = 32 * NJ, BK = 64;
+  constexpr int MI = MI_;
   constexpr int NRD = MI + NJ, NMF = MI * NJ;  // fragment reads / matrix-core ops per sub-step
-  constexpr int NBA = 8, NBB = BN / 32;        // 1 KB DMA blocks (8 rows) per wave per slab: A, B
+  constexpr int NBA = BM / 32, NBB = BN / 32;  // 1 KB DMA blocks (8 rows) per wave per slab: A, B
   constexpr int DPW = NBA + NBB;               // DMA instructions per wave per slab
   constexpr int SA = BM * 8, SB = BN * 8;      // stage sizes in 16-byte units
   // DMAs a wait before a slab's reads may leave in flight: the deeper ring's of the last turn
@@ -1068,7 +1073,7 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: resources live in SGPRs
   const int wm = wave >> 1, wn = wave & 1;
 
-  // DMA duties: wave w moves A rows 64w .. 64w+63 and B rows 8*NBB*w .. of the tile, in blocks of
+  // DMA duties: wave w moves A rows 8*NBA*w .. and B rows 8*NBB*w .. of the tile, in blocks of
   // 8 rows. Block j's rows are 8j .. 8j+7 past the wave's first row; swz128 of its rows depends only
   // on j's parity, so two chunk choices cover all blocks.
   const int pos = lane & 7, lr = lane >> 3;
@@ -1077,7 +1082,7 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
   uint32_t avo[2], bvo[2];
 #pragma unroll
   for (int p = 0; p < 2; ++p) {
-    avo[p] = (uint32_t)((64 * wave + lr) * lda + cc[p] * 8) * sizeof(bf16);
+    avo[p] = (uint32_t)((8 * NBA * wave + lr) * lda + cc[p] * 8) * sizeof(bf16);
     bvo[p] = (uint32_t)(lr * bmap.ldb + cc[p] * 8) * sizeof(bf16);
   }
   const uint32_t arow8 = (uint32_t)(8 * lda) * sizeof(bf16);  // byte distance of consecutive A blocks
@@ -1095,10 +1100,10 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
   do {                                                                                           \
     const int k0_ = (kt) * BK;                                                                   \
     if (KFULL)                                                                                   \
-      dma16(ra, (ST) + (64 * wave + 8 * (j)) * 8, avo[(j) & 1] + (j) * arow8,                    \
+      dma16(ra, (ST) + (8 * NBA * wave + 8 * (j)) * 8, avo[(j) & 1] + (j) * arow8,                    \
             (uint32_t)(k0_ < K ? k0_ : 0) * sizeof(bf16));                                       \
     else                                                                                         \
-      dma16(ra, (ST) + (64 * wave + 8 * (j)) * 8,                                                \
+      dma16(ra, (ST) + (8 * NBA * wave + 8 * (j)) * 8,                                                \
             k0_ + cc[(j) & 1] * 8 < K ? avo[(j) & 1] + (j) * arow8 + (uint32_t)k0_ * sizeof(bf16) : kOOB, 0); \
   } while (0)
 #define K2_DMA_B(ST, kt, j)                                                                      \
@@ -1244,7 +1249,7 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
     static_assert(Epi::stage_floats() * sizeof(float) <= Rings<RA, RB>::units(4) * sizeof(uint4), "LDS staging");
     if (epi.wants_stage(n0)) {  // tile-uniform
       __syncthreads();  // every wave is done with the rings
-      epi.stage(reinterpret_cast<float*>(lds), m0, M, tid);  // 256 threads
+      epi.stage(reinterpret_cast<float*>(lds), m0 & ~255, M, tid);  // 256 threads; the whole 256-row tile's rows
       __syncthreads();
       stg = reinterpret_cast<float*>(lds);
     }
@@ -1271,10 +1276,11 @@ __device__ __forceinline__ void gemm_tile(const bf16* __restrict__ A, int lda, i
 
 // Workgroups 0 .. nmain-1 each compute a 256x256 tile (tile order: tile_coords). With TAIL, the
 // tiles_total - nmain tiles of the last partial round (or all tiles, nmain = 0, when they fill at
-// most half a round) are split in two 256x128 halves run by workgroups nmain + 2u and
-// nmain + 2u + 1 (u: tail tile index), so that round takes about half as long; TAIL is used when
-// the halves fit in one round.
-template <int SPREAD, bool KFULL, int RA, int RB, bool TAIL, class BMap, class Epi>
+// most half a round) are split in two halves run by workgroups nmain + 2u and nmain + 2u + 1 (u:
+// tail tile index), so that round takes about half as long; TAIL is used when the halves fit in
+// one round. TAIL 1: 256x128 halves (column halves); TAIL 2: 128x256 halves (row halves), for the
+// epilogues that need a wave's full 128 columns (SwiGLU; q and k heads). TAIL 0: no halves.
+template <int SPREAD, bool KFULL, int RA, int RB, int TAIL, class BMap, class Epi>
 __global__ void __launch_bounds__(256)
 gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, int scn, int nmain, BMap bmap,
                  Epi epi) {
@@ -1283,13 +1289,19 @@ gemm_bf16_kernel(const bf16* __restrict__ A, int lda, int M, int K, int Ntot, in
   const int tiles_m = (M + 255) / 256, tiles_n = (Ntot + 255) / 256;
   const int bid = blockIdx.x;
   int tm, tn;
-  if (!TAIL || bid < nmain) {
+  if (TAIL == 0 || bid < nmain) {
     tile_coords(bid, tiles_m, tiles_n, scn, tm, tn);
-    gemm_tile<SPREAD, KFULL, 4, RA, RB>(A, lda, M, K, Ntot, tm * 256, tn * 256, bmap, epi, lds);
-  } else if constexpr (TAIL) {
+    gemm_tile<SPREAD, KFULL, 4, 4, RA, RB>(A, lda, M, K, Ntot, tm * 256, tn * 256, bmap, epi, lds);
+  } else if constexpr (TAIL == 2) {
     const int u = bid - nmain;
     tile_coords(nmain + (u >> 1), tiles_m, tiles_n, scn, tm, tn);
-    gemm_tile<SPREAD, KFULL, 2, RA, RB>(A, lda, M, K, Ntot, tm * 256, tn * 256 + (u & 1) * 128, bmap, epi, lds);
+    const int m0 = tm * 256 + (u & 1) * 128;
+    if (m0 >= M) return;  // the second half of a last M-tile of at most 128 rows (workgroup-uniform)
+    gemm_tile<SPREAD, KFULL, 2, 4, RA, RB>(A, lda, M, K, Ntot, m0, tn * 256, bmap, epi, lds);
+  } else if constexpr (TAIL == 1 && Epi::kColumnHalves) {
+    const int u = bid - nmain;
+    tile_coords(nmain + (u >> 1), tiles_m, tiles_n, scn, tm, tn);
+    gemm_tile<SPREAD, KFULL, 4, 2, RA, RB>(A, lda, M, K, Ntot, tm * 256, tn * 256 + (u & 1) * 128, bmap, epi, lds);
   }
 }
 
@@ -1326,35 +1338,46 @@ constexpr int kRingA = 2, kRingB = 3;
 // Whether the 256x128 halves of a last partial round may start at column n0 (every epilogue but
 // the QKV+gate one takes any column; that one takes only v and gate columns in narrow waves).
 template <class Epi>
-static bool tail_allowed(const Epi&, int) { return true; }
+static bool tail_allowed(const Epi&, int) { return Epi::kColumnHalves; }
 template <typename T, int HD, bool kSave>
 static bool tail_allowed(const EpiQkvg<T, HD, kSave>& e, int n0) { return n0 >= e.nq + e.nk; }
-template <typename T, class C, class BMap, class Epi, int SPREAD, bool KFULL, bool TAIL>
+// TAIL: the last partial round may run as half tiles; ROWS: row halves are built for this
+// configuration too (the one every model shape takes: K a multiple of 64, cache-resident weights).
+template <typename T, class C, class BMap, class Epi, int SPREAD, bool KFULL, bool TAIL, bool ROWS = false>
 static hipError_t launch_cfg(const GemmA& a, int Ntot, int scn, const BMap& bmap, const Epi& epi, hipStream_t s) {
   constexpr int NT = (C::BM / C::WM) * (C::BN / C::WN) * 64;
   const int tiles = ((a.M + C::BM - 1) / C::BM) * ((Ntot + C::BN - 1) / C::BN);
   if constexpr (sizeof(T) == 2 && C::DMA) {
-    int nmain = tiles, grid = tiles;
+    int nmain = tiles, grid = tiles, mrows = 0;
     if constexpr (TAIL) {
       // Half tiles where a round is partly idle: the last partial round when it holds at most half
       // the compute units, or every tile when all of them fill at most half a round (small M: the
       // 512^2 block's out and down projections are 120 tiles for 256 compute units).
       const int ncu = compute_units();
       const int tail = 2 * tiles <= ncu ? tiles : tiles % ncu;
-      bool ok = tail > 0 && 2 * tail <= ncu;
-      const int tiles_m = (a.M + 255) / 256, tiles_n = (Ntot + 255) / 256;
-      for (int u = tiles - tail; ok && u < tiles; ++u) {
-        int tm, tn;
-        tile_coords(u, tiles_m, tiles_n, scn, tm, tn);
-        ok = tail_allowed(epi, tn * 256);
-      }
-      if (ok) {
-        nmain = tiles - tail;
-        grid = nmain + 2 * tail;
+      if (tail > 0 && 2 * tail <= ncu) {
+        // column halves (measured on the block's shapes) where every tail tile's epilogue takes
+        // them, row halves otherwise
+        const int tiles_m = (a.M + 255) / 256, tiles_n = (Ntot + 255) / 256;
+        bool cols = true;
+        for (int u = tiles - tail; cols && u < tiles; ++u) {
+          int tm, tn;
+          tile_coords(u, tiles_m, tiles_n, scn, tm, tn);
+          cols = tail_allowed(epi, tn * 256);
+        }
+        if (cols || ROWS) {
+          mrows = cols ? 0 : 1;
+          nmain = tiles - tail;
+          grid = nmain + 2 * tail;
+        }
       }
     }
-    hipLaunchKernelGGL((gemm_bf16_kernel<SPREAD, KFULL, kRingA, kRingB, TAIL, BMap, Epi>), dim3(grid), dim3(256), 0, s, (const bf16*)a.A,
-                       a.lda, a.M, a.K, Ntot, scn, nmain, bmap, epi);
+    if (!TAIL || !mrows)
+      hipLaunchKernelGGL((gemm_bf16_kernel<SPREAD, KFULL, kRingA, kRingB, TAIL ? 1 : 0, BMap, Epi>), dim3(grid),
+                         dim3(256), 0, s, (const bf16*)a.A, a.lda, a.M, a.K, Ntot, scn, nmain, bmap, epi);
+    else if constexpr (ROWS)
+      hipLaunchKernelGGL((gemm_bf16_kernel<SPREAD, KFULL, kRingA, kRingB, 2, BMap, Epi>), dim3(grid), dim3(256), 0, s,
+                         (const bf16*)a.A, a.lda, a.M, a.K, Ntot, scn, nmain, bmap, epi);
   } else {
     hipLaunchKernelGGL((gemm_kernel<T, C::BM, C::BN, C::WM, C::WN, BMap, Epi>), dim3(tiles), dim3(NT), 0, s,
                        (const T*)a.A, a.lda, a.M, a.K, Ntot, scn, bmap, epi);
@@ -1383,7 +1406,7 @@ static hipError_t launch(const GemmA& a, int Ntot, const BMap& bmap, const Epi& 
     if (a.K % 64 != 0) return launch_cfg<T, C, BMap, Epi, 2, false, TAIL>(a, Ntot, scn, bmap, epi, s);
     if ((size_t)scn * C::BN * a.K * sizeof(T) > kLastLevelCacheBytes)
       return launch_cfg<T, C, BMap, Epi, 0, true, TAIL>(a, Ntot, scn, bmap, epi, s);
-    return launch_cfg<T, C, BMap, Epi, SPREAD_CACHED, true, TAIL>(a, Ntot, scn, bmap, epi, s);
+    return launch_cfg<T, C, BMap, Epi, SPREAD_CACHED, true, TAIL, TAIL>(a, Ntot, scn, bmap, epi, s);
   } else {
     return launch_cfg<T, C, BMap, Epi, 0, false, TAIL>(a, Ntot, scn, bmap, epi, s);
   }
@@ -1415,7 +1438,7 @@ static hipError_t swiglu_t(const GemmA& a, const SwigluArgs& p, hipStream_t s) {
   EpiSwiglu<T, WN, kSave> e;
   e.a = (T*)p.a; e.I = p.I; e.gsave = p.gsave; e.usave = p.usave;
   const int ntot = ((p.I + WN / 2 - 1) / (WN / 2)) * WN;
-  return launch<T, BSwiglu<T, WN>, EpiSwiglu<T, WN, kSave>, false, 2>(a, ntot, bm, e, s);
+  return launch<T, BSwiglu<T, WN>, EpiSwiglu<T, WN, kSave>, true, 2>(a, ntot, bm, e, s);
 }
 
 template <typename T>
